@@ -1,0 +1,527 @@
+// C ABI of the DFlash draft pass: argument validation, context and workspace
+// layout, and the launch sequence of each call.  Declared in include/dflash.h.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "dflash.h"
+#include "kernels.h"
+
+using namespace dflash;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  return fail(DFLASH_EHIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+constexpr int kIngestChunk = 4096;  // rows of one fusion / K-V projection pass
+
+size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Padded row count: the skinny GEMM works on 16-row groups (up to 32 rows),
+// the tiled GEMM on 64-row tiles.
+int rows_pad(int m) { return m <= 32 ? (m + 15) / 16 * 16 : (m + 63) / 64 * 64; }
+
+struct LayerW {
+  const u16 *attn_norm, *wq, *wk, *wv, *wo, *mlp_norm, *wgate, *wup, *wdown;
+};
+
+int check_config(const dflash_config* c) {
+  if (!c) return fail(DFLASH_EINVAL, "config is NULL");
+  if (c->n_layers < 1 || c->hidden < 1 || c->n_q_heads < 1 || c->n_kv_heads < 1 || c->head_dim < 1 ||
+      c->intermediate < 1 || c->vocab < 1 || c->n_target_layers < 1)
+    return fail(DFLASH_EINVAL, "config sizes must be positive");
+  if (c->mask_token_id < 0 || c->mask_token_id >= c->vocab)
+    return fail(DFLASH_EINVAL, "mask_token_id %d outside [0, vocab)", c->mask_token_id);
+  if (!(c->rms_eps > 0.f) || !(c->rope_theta > 0.0)) return fail(DFLASH_EINVAL, "rms_eps and rope_theta must be > 0");
+  if (c->max_block < 2 || c->max_block > 32) return fail(DFLASH_EUNSUPPORTED, "max_block must be in [2, 32]");
+  if (c->head_dim != 64 && c->head_dim != 128) return fail(DFLASH_EUNSUPPORTED, "head_dim must be 64 or 128");
+  if (c->n_q_heads % c->n_kv_heads) return fail(DFLASH_ESHAPE, "n_q_heads must be a multiple of n_kv_heads");
+  if (c->hidden % 256 || c->intermediate % 256 || (c->n_q_heads * c->head_dim) % 256 ||
+      ((int64_t)c->n_target_layers * c->hidden) % 256)
+    return fail(DFLASH_EUNSUPPORTED, "hidden, intermediate, n_q_heads*head_dim and n_target_layers*hidden must be multiples of 256");
+  if (c->vocab % 64) return fail(DFLASH_EUNSUPPORTED, "vocab must be a multiple of 64");
+  return DFLASH_OK;
+}
+
+bool same_config(const dflash_config& a, const dflash_config& b) {
+  return a.n_layers == b.n_layers && a.hidden == b.hidden && a.n_q_heads == b.n_q_heads &&
+         a.n_kv_heads == b.n_kv_heads && a.head_dim == b.head_dim && a.intermediate == b.intermediate &&
+         a.vocab == b.vocab && a.n_target_layers == b.n_target_layers && a.mask_token_id == b.mask_token_id &&
+         a.max_block == b.max_block && a.rms_eps == b.rms_eps && a.rope_theta == b.rope_theta;
+}
+
+// Context layout: RoPE cos / sin tables, then per layer the K planes
+// [2][n_kv][slots][d] and the transposed V planes [2][n_kv][d][slots].
+struct CtxLayout {
+  std::vector<int64_t> slot_base;
+  int64_t slots = 0;
+  int64_t max_pos = 0;
+  size_t cos_off = 0, sin_off = 0, kv_off = 0, layer_bytes = 0, k_bytes = 0, total = 0;
+};
+
+int ctx_layout(const dflash_config* c, int32_t n_seqs, const int64_t* cap, CtxLayout* L) {
+  if (n_seqs < 1 || n_seqs > kMaxSeqs) return fail(DFLASH_EUNSUPPORTED, "n_seqs must be in [1, %d]", kMaxSeqs);
+  if (!cap) return fail(DFLASH_EINVAL, "capacity is NULL");
+  L->slot_base.resize(n_seqs);
+  int64_t slots = 0, max_pos = 0;
+  for (int b = 0; b < n_seqs; ++b) {
+    if (cap[b] < 0) return fail(DFLASH_EINVAL, "capacity[%d] < 0", b);
+    const int64_t s = (cap[b] + c->max_block + 63) / 64 * 64;
+    L->slot_base[b] = slots;
+    slots += s;
+    max_pos = std::max(max_pos, s);
+  }
+  if (slots >= (int64_t(1) << 30)) return fail(DFLASH_EUNSUPPORTED, "total context slots %lld too large", (long long)slots);
+  L->slots = slots;
+  L->max_pos = max_pos;
+  const size_t half = c->head_dim / 2;
+  L->cos_off = 0;
+  L->sin_off = align_up(max_pos * half * sizeof(float));
+  L->kv_off = L->sin_off + align_up(max_pos * half * sizeof(float));
+  L->k_bytes = align_up((size_t)2 * c->n_kv_heads * slots * c->head_dim * sizeof(u16));
+  L->layer_bytes = 2 * L->k_bytes;
+  L->total = L->kv_off + (size_t)c->n_layers * L->layer_bytes;
+  return DFLASH_OK;
+}
+
+struct WsLayout {
+  int M = 0, Mp = 0, units = 0, splits = 0, R = 0, Rp = 0;
+  size_t x = 0, a_hi = 0, a_lo = 0, b_hi = 0, b_lo = 0, q_hi = 0, q_lo = 0, part_o = 0, part_ml = 0,
+         amax = 0, draft_end = 0;
+  size_t h_hi = 0, h_lo = 0, ingest_end = 0;
+  size_t total() const { return std::max(draft_end, ingest_end); }
+};
+
+WsLayout ws_layout(const dflash_config* c, int n_seqs, int block, int64_t max_new) {
+  WsLayout W;
+  const size_t H = c->hidden, I = c->intermediate, QD = (size_t)c->n_q_heads * c->head_dim;
+  W.M = n_seqs * block;
+  W.Mp = rows_pad(W.M);
+  W.units = n_seqs * c->n_q_heads * ((block + 15) / 16);
+  W.splits = attention_splits(W.units);
+  size_t o = 0;
+  auto take = [&](size_t bytes) { const size_t at = o; o += align_up(bytes); return at; };
+  const size_t Mp = W.Mp, wa = std::max(H, QD);
+  W.x = take(Mp * H * 4);
+  W.a_hi = take(Mp * wa * 2);
+  W.a_lo = take(Mp * wa * 2);
+  W.b_hi = take(Mp * I * 2);
+  W.b_lo = take(Mp * I * 2);
+  W.q_hi = take(Mp * QD * 2);
+  W.q_lo = take(Mp * QD * 2);
+  W.part_o = take((size_t)W.units * W.splits * 16 * c->head_dim * 4);
+  W.part_ml = take((size_t)W.units * W.splits * 32 * 4);
+  W.amax = take((size_t)(c->vocab / 16) * Mp * 8);
+  W.draft_end = o;
+  o = 0;
+  W.R = (int)std::min<int64_t>(std::max<int64_t>(max_new, 0), kIngestChunk);
+  W.Rp = W.R > 0 ? rows_pad(W.R) : 0;
+  W.h_hi = take((size_t)W.Rp * H * 2);
+  W.h_lo = take((size_t)W.Rp * H * 2);
+  W.ingest_end = o;
+  return W;
+}
+
+}  // namespace
+
+struct dflash_model {
+  dflash_config cfg;
+  const u16* w_fc;
+  const u16* embed;
+  const u16* final_norm;
+  std::vector<LayerW> layers;
+};
+
+struct dflash_ctx {
+  dflash_config cfg;
+  char* base;
+  size_t bytes;
+  int n_seqs;
+  std::vector<int64_t> cap, len;
+  CtxLayout L;
+  u16* k_cache(int l) const { return (u16*)(base + L.kv_off + (size_t)l * L.layer_bytes); }
+  u16* vt_cache(int l) const { return (u16*)(base + L.kv_off + (size_t)l * L.layer_bytes + L.k_bytes); }
+  const float* rope_cos() const { return (const float*)(base + L.cos_off); }
+  const float* rope_sin() const { return (const float*)(base + L.sin_off); }
+};
+
+extern "C" {
+
+const char* dflash_status_str(int s) {
+  switch (s) {
+    case DFLASH_OK: return "ok";
+    case DFLASH_EINVAL: return "invalid argument";
+    case DFLASH_ESHAPE: return "shape mismatch";
+    case DFLASH_ECAPACITY: return "context capacity exceeded";
+    case DFLASH_EWORKSPACE: return "workspace too small";
+    case DFLASH_EALIGN: return "misaligned pointer";
+    case DFLASH_EHIP: return "HIP runtime error";
+    case DFLASH_EUNSUPPORTED: return "unsupported configuration";
+    default: return "unknown status";
+  }
+}
+
+const char* dflash_last_error(void) { return g_last_error.c_str(); }
+
+int32_t dflash_weight_count(const dflash_config* cfg) {
+  if (!cfg || cfg->n_layers < 1) return -1;
+  return 3 + 9 * cfg->n_layers;
+}
+
+int dflash_model_create(const dflash_config* cfg, const void* const* weights, dflash_model** out) {
+  if (!out) return fail(DFLASH_EINVAL, "out is NULL");
+  *out = nullptr;
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (!weights) return fail(DFLASH_EINVAL, "weights is NULL");
+  const int n = 3 + 9 * cfg->n_layers;
+  for (int i = 0; i < n; ++i) {
+    if (!weights[i]) return fail(DFLASH_EINVAL, "weights[%d] is NULL", i);
+    if (!aligned(weights[i], 16)) return fail(DFLASH_EALIGN, "weights[%d] is not 16-byte aligned", i);
+  }
+  dflash_model* m = new (std::nothrow) dflash_model;
+  if (!m) return fail(DFLASH_EINVAL, "out of host memory");
+  m->cfg = *cfg;
+  m->w_fc = (const u16*)weights[0];
+  m->embed = (const u16*)weights[1];
+  m->final_norm = (const u16*)weights[2];
+  m->layers.resize(cfg->n_layers);
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    const void* const* w = weights + 3 + 9 * l;
+    m->layers[l] = LayerW{(const u16*)w[0], (const u16*)w[1], (const u16*)w[2], (const u16*)w[3], (const u16*)w[4],
+                          (const u16*)w[5], (const u16*)w[6], (const u16*)w[7], (const u16*)w[8]};
+  }
+  *out = m;
+  return DFLASH_OK;
+}
+
+void dflash_model_destroy(dflash_model* m) { delete m; }
+
+size_t dflash_ctx_bytes(const dflash_config* cfg, int32_t n_seqs, const int64_t* capacity) {
+  if (check_config(cfg)) return 0;
+  CtxLayout L;
+  if (ctx_layout(cfg, n_seqs, capacity, &L)) return 0;
+  return L.total;
+}
+
+int dflash_ctx_create(const dflash_model* model, void* dev_buf, size_t bytes, int32_t n_seqs,
+                      const int64_t* capacity, dflash_stream stream, dflash_ctx** out) {
+  if (!out) return fail(DFLASH_EINVAL, "out is NULL");
+  *out = nullptr;
+  if (!model) return fail(DFLASH_EINVAL, "model is NULL");
+  if (!dev_buf) return fail(DFLASH_EINVAL, "dev_buf is NULL");
+  if (!aligned(dev_buf, kAlign)) return fail(DFLASH_EALIGN, "dev_buf is not 256-byte aligned");
+  CtxLayout L;
+  int rc = ctx_layout(&model->cfg, n_seqs, capacity, &L);
+  if (rc) return rc;
+  if (bytes < L.total) return fail(DFLASH_ECAPACITY, "context buffer holds %zu bytes, %zu needed", bytes, L.total);
+
+  const dflash_config& c = model->cfg;
+  const int half = c.head_dim / 2;
+  std::vector<float> cs((size_t)L.max_pos * half), sn((size_t)L.max_pos * half);
+  for (int64_t p = 0; p < L.max_pos; ++p)
+    for (int j = 0; j < half; ++j) {
+      const double ang = (double)p * pow(c.rope_theta, -2.0 * j / c.head_dim);
+      cs[(size_t)p * half + j] = (float)cos(ang);
+      sn[(size_t)p * half + j] = (float)sin(ang);
+    }
+  hipStream_t s = (hipStream_t)stream;
+  char* base = (char*)dev_buf;
+  hipError_t e = hipMemsetAsync(base + L.kv_off, 0, L.total - L.kv_off, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(base + L.cos_off, cs.data(), cs.size() * 4, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(base + L.sin_off, sn.data(), sn.size() * 4, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "dflash_ctx_create");
+
+  dflash_ctx* x = new (std::nothrow) dflash_ctx;
+  if (!x) return fail(DFLASH_EINVAL, "out of host memory");
+  x->cfg = c;
+  x->base = base;
+  x->bytes = bytes;
+  x->n_seqs = n_seqs;
+  x->cap.assign(capacity, capacity + n_seqs);
+  x->len.assign(n_seqs, 0);
+  x->L = L;
+  *out = x;
+  return DFLASH_OK;
+}
+
+void dflash_ctx_destroy(dflash_ctx* ctx) { delete ctx; }
+
+int64_t dflash_ctx_length(const dflash_ctx* ctx, int32_t seq) {
+  if (!ctx || seq < 0 || seq >= ctx->n_seqs) return -1;
+  return ctx->len[seq];
+}
+
+int dflash_ctx_truncate(dflash_ctx* ctx, int32_t seq, int64_t new_len) {
+  if (!ctx) return fail(DFLASH_EINVAL, "ctx is NULL");
+  if (seq < 0 || seq >= ctx->n_seqs) return fail(DFLASH_EINVAL, "seq %d outside [0, %d)", seq, ctx->n_seqs);
+  if (new_len < 0 || new_len > ctx->len[seq])
+    return fail(DFLASH_EINVAL, "new_len %lld outside [0, %lld]", (long long)new_len, (long long)ctx->len[seq]);
+  ctx->len[seq] = new_len;
+  return DFLASH_OK;
+}
+
+size_t dflash_workspace_bytes(const dflash_model* model, int32_t n_seqs, int32_t block, int64_t max_new_tokens) {
+  if (!model || n_seqs < 1 || n_seqs > kMaxSeqs || block < 2 || block > model->cfg.max_block) return 0;
+  return ws_layout(&model->cfg, n_seqs, block, max_new_tokens).total();
+}
+
+int dflash_fuse_ctx(const dflash_model* model, dflash_ctx* ctx, const void* features, const int32_t* n_new,
+                    void* ws, size_t ws_bytes, dflash_stream stream) {
+  if (!model || !ctx) return fail(DFLASH_EINVAL, "model or ctx is NULL");
+  if (!same_config(model->cfg, ctx->cfg)) return fail(DFLASH_ESHAPE, "ctx was created for another configuration");
+  if (!n_new) return fail(DFLASH_EINVAL, "n_new is NULL");
+  const dflash_config& c = model->cfg;
+  int64_t total = 0;
+  for (int b = 0; b < ctx->n_seqs; ++b) {
+    if (n_new[b] < 0) return fail(DFLASH_EINVAL, "n_new[%d] < 0", b);
+    if (ctx->len[b] + n_new[b] > ctx->cap[b])
+      return fail(DFLASH_ECAPACITY, "sequence %d: length %lld + %d exceeds capacity %lld", b,
+                  (long long)ctx->len[b], n_new[b], (long long)ctx->cap[b]);
+    total += n_new[b];
+  }
+  if (total == 0) return DFLASH_OK;
+  if (!features) return fail(DFLASH_EINVAL, "features is NULL");
+  if (!aligned(features, 16)) return fail(DFLASH_EALIGN, "features is not 16-byte aligned");
+  if (!ws) return fail(DFLASH_EINVAL, "workspace is NULL");
+  if (!aligned(ws, kAlign)) return fail(DFLASH_EALIGN, "workspace is not 256-byte aligned");
+  const WsLayout W = ws_layout(&c, 1, 2, total);
+  if (ws_bytes < W.ingest_end)
+    return fail(DFLASH_EWORKSPACE, "workspace holds %zu bytes, %zu needed", ws_bytes, W.ingest_end);
+
+  hipStream_t s = (hipStream_t)stream;
+  char* wsb = (char*)ws;
+  u16* h_hi = (u16*)(wsb + W.h_hi);
+  u16* h_lo = (u16*)(wsb + W.h_lo);
+  const int fw = c.n_target_layers * c.hidden;
+  std::vector<int64_t> gstart(ctx->n_seqs + 1, 0);
+  for (int b = 0; b < ctx->n_seqs; ++b) gstart[b + 1] = gstart[b] + n_new[b];
+
+  for (int64_t r0 = 0; r0 < total; r0 += kIngestChunk) {
+    const int R = (int)std::min<int64_t>(kIngestChunk, total - r0);
+    const int Rp = rows_pad(R);
+    SeqTable st;
+    memset(&st, 0, sizeof(st));
+    int n = 0;
+    for (int b = 0; b < ctx->n_seqs; ++b) {
+      const int64_t lo = std::max(gstart[b], r0), hi = std::min(gstart[b + 1], r0 + R);
+      if (hi <= lo) continue;
+      st.row_start[n] = (int32_t)(lo - r0);
+      st.pos_base[n] = (int32_t)(ctx->len[b] + (lo - gstart[b]));
+      st.slot_base[n] = (int32_t)ctx->L.slot_base[b];
+      ++n;
+    }
+    st.n = n;
+    st.row_start[n] = R;
+
+    GemmArgs f;
+    memset(&f, 0, sizeof(f));
+    f.a_hi = (const u16*)features + (size_t)r0 * fw;
+    f.a_lo = nullptr;
+    f.lda = fw;
+    f.a_rows = R;
+    f.K = fw;
+    f.n_tiles = c.hidden / 16;
+    f.w.w0 = model->w_fc;
+    f.map = MAP_PLAIN;
+    f.epi = EPI_SPLIT;
+    f.ep.M = R;
+    f.ep.Mp = Rp;
+    f.ep.out_hi = h_hi;
+    f.ep.out_lo = h_lo;
+    f.ep.ldh = c.hidden;
+    hipError_t e = launch_gemm(f, st, Rp, s);
+    if (e != hipSuccess) return hip_fail(e, "fuse_ctx: fusion GEMM");
+
+    for (int l = 0; l < c.n_layers; ++l) {
+      GemmArgs g;
+      memset(&g, 0, sizeof(g));
+      g.a_hi = h_hi;
+      g.a_lo = h_lo;
+      g.lda = c.hidden;
+      g.a_rows = Rp;
+      g.K = c.hidden;
+      g.n_tiles = 2 * c.n_kv_heads * c.head_dim / 16;
+      g.w = WeightSeg{model->layers[l].wq, model->layers[l].wk, model->layers[l].wv};
+      g.map = MAP_ROPE;
+      g.epi = EPI_QKV;
+      g.ep.M = R;
+      g.ep.Mp = Rp;
+      g.ep.n_q = c.n_q_heads;
+      g.ep.n_kv = c.n_kv_heads;
+      g.ep.head_dim = c.head_dim;
+      g.ep.head0 = c.n_q_heads;
+      g.ep.rope_cos = ctx->rope_cos();
+      g.ep.rope_sin = ctx->rope_sin();
+      g.ep.k_cache = ctx->k_cache(l);
+      g.ep.vt_cache = ctx->vt_cache(l);
+      g.ep.slots = ctx->L.slots;
+      e = launch_gemm(g, st, Rp, s);
+      if (e != hipSuccess) return hip_fail(e, "fuse_ctx: K/V projection");
+    }
+  }
+  for (int b = 0; b < ctx->n_seqs; ++b) ctx->len[b] += n_new[b];
+  return DFLASH_OK;
+}
+
+int dflash_draft_block(const dflash_model* model, const dflash_ctx* ctx, const int32_t* anchors, int32_t block,
+                       int32_t* draft, float* logits, void* ws, size_t ws_bytes, dflash_stream stream) {
+  if (!model || !ctx) return fail(DFLASH_EINVAL, "model or ctx is NULL");
+  if (!same_config(model->cfg, ctx->cfg)) return fail(DFLASH_ESHAPE, "ctx was created for another configuration");
+  const dflash_config& c = model->cfg;
+  if (block < 2 || block > c.max_block) return fail(DFLASH_EINVAL, "block %d outside [2, %d]", block, c.max_block);
+  if (!anchors || !draft) return fail(DFLASH_EINVAL, "anchors or draft is NULL");
+  if (!aligned(anchors, 4) || !aligned(draft, 4) || (logits && !aligned(logits, 4)))
+    return fail(DFLASH_EALIGN, "anchors, draft and logits must be 4-byte aligned");
+  if (!ws) return fail(DFLASH_EINVAL, "workspace is NULL");
+  if (!aligned(ws, kAlign)) return fail(DFLASH_EALIGN, "workspace is not 256-byte aligned");
+  const int n = ctx->n_seqs;
+  const WsLayout W = ws_layout(&c, n, block, 0);
+  if (ws_bytes < W.draft_end)
+    return fail(DFLASH_EWORKSPACE, "workspace holds %zu bytes, %zu needed", ws_bytes, W.draft_end);
+
+  hipStream_t s = (hipStream_t)stream;
+  char* wsb = (char*)ws;
+  float* x = (float*)(wsb + W.x);
+  u16* a_hi = (u16*)(wsb + W.a_hi);
+  u16* a_lo = (u16*)(wsb + W.a_lo);
+  u16* b_hi = (u16*)(wsb + W.b_hi);
+  u16* b_lo = (u16*)(wsb + W.b_lo);
+  u16* q_hi = (u16*)(wsb + W.q_hi);
+  u16* q_lo = (u16*)(wsb + W.q_lo);
+  float* part_o = (float*)(wsb + W.part_o);
+  float* part_ml = (float*)(wsb + W.part_ml);
+  unsigned long long* amax = (unsigned long long*)(wsb + W.amax);
+  const int M = W.M, Mp = W.Mp, H = c.hidden, QD = c.n_q_heads * c.head_dim, I = c.intermediate;
+
+  SeqTable st;
+  memset(&st, 0, sizeof(st));
+  st.n = n;
+  for (int b = 0; b < n; ++b) {
+    st.row_start[b] = b * block;
+    st.pos_base[b] = (int32_t)ctx->len[b];
+    st.slot_base[b] = (int32_t)ctx->L.slot_base[b];
+  }
+  st.row_start[n] = n * block;
+
+  auto base_args = [&](const u16* ah, const u16* al, int lda, int K, int n_tiles, int epi, int map) {
+    GemmArgs g;
+    memset(&g, 0, sizeof(g));
+    g.a_hi = ah;
+    g.a_lo = al;
+    g.lda = lda;
+    g.a_rows = Mp;
+    g.K = K;
+    g.n_tiles = n_tiles;
+    g.epi = epi;
+    g.map = map;
+    g.ep.M = M;
+    g.ep.Mp = Mp;
+    return g;
+  };
+
+  hipError_t e = launch_embed(x, anchors, model->embed, H, M, Mp, block, c.mask_token_id, c.vocab, s);
+  if (e != hipSuccess) return hip_fail(e, "draft_block: embed");
+  for (int l = 0; l < c.n_layers; ++l) {
+    const LayerW& Lw = model->layers[l];
+    e = launch_rmsnorm_split(x, Lw.attn_norm, a_hi, a_lo, H, M, Mp, c.rms_eps, s);
+    if (e != hipSuccess) return hip_fail(e, "draft_block: attention norm");
+
+    GemmArgs g = base_args(a_hi, a_lo, H, H, (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim / 16, EPI_QKV, MAP_ROPE);
+    g.w = WeightSeg{Lw.wq, Lw.wk, Lw.wv};
+    g.ep.out_hi = q_hi;
+    g.ep.out_lo = q_lo;
+    g.ep.ldh = QD;
+    g.ep.n_q = c.n_q_heads;
+    g.ep.n_kv = c.n_kv_heads;
+    g.ep.head_dim = c.head_dim;
+    g.ep.head0 = 0;
+    g.ep.rope_cos = ctx->rope_cos();
+    g.ep.rope_sin = ctx->rope_sin();
+    g.ep.k_cache = ctx->k_cache(l);
+    g.ep.vt_cache = ctx->vt_cache(l);
+    g.ep.slots = ctx->L.slots;
+    e = launch_gemm(g, st, Mp, s);
+    if (e != hipSuccess) return hip_fail(e, "draft_block: QKV projection");
+
+    e = launch_attention(q_hi, q_lo, ctx->k_cache(l), ctx->vt_cache(l), ctx->L.slots, part_o, part_ml, a_hi, a_lo,
+                         Mp, n, block, c.n_q_heads, c.n_kv_heads, c.head_dim, W.splits, st, s);
+    if (e != hipSuccess) return hip_fail(e, "draft_block: attention");
+
+    g = base_args(a_hi, a_lo, QD, QD, H / 16, EPI_RESID, MAP_PLAIN);
+    g.w.w0 = Lw.wo;
+    g.ep.out_f32 = x;
+    g.ep.ldo = H;
+    e = launch_gemm(g, st, Mp, s);
+    if (e != hipSuccess) return hip_fail(e, "draft_block: output projection");
+
+    e = launch_rmsnorm_split(x, Lw.mlp_norm, a_hi, a_lo, H, M, Mp, c.rms_eps, s);
+    if (e != hipSuccess) return hip_fail(e, "draft_block: MLP norm");
+
+    g = base_args(a_hi, a_lo, H, H, I / 8, EPI_SWIGLU, MAP_SWIGLU);
+    g.w = WeightSeg{Lw.wgate, Lw.wup, nullptr};
+    g.ep.out_hi = b_hi;
+    g.ep.out_lo = b_lo;
+    g.ep.ldh = I;
+    e = launch_gemm(g, st, Mp, s);
+    if (e != hipSuccess) return hip_fail(e, "draft_block: gate/up projection");
+
+    g = base_args(b_hi, b_lo, I, I, H / 16, EPI_RESID, MAP_PLAIN);
+    g.w.w0 = Lw.wdown;
+    g.ep.out_f32 = x;
+    g.ep.ldo = H;
+    e = launch_gemm(g, st, Mp, s);
+    if (e != hipSuccess) return hip_fail(e, "draft_block: down projection");
+  }
+  e = launch_rmsnorm_split(x, model->final_norm, a_hi, a_lo, H, M, Mp, c.rms_eps, s);
+  if (e != hipSuccess) return hip_fail(e, "draft_block: final norm");
+  GemmArgs g = base_args(a_hi, a_lo, H, H, c.vocab / 16, EPI_ARGMAX, MAP_PLAIN);
+  g.w.w0 = model->embed;
+  g.ep.amax_part = amax;
+  g.ep.logits = logits;
+  g.ep.vocab = c.vocab;
+  g.ep.block = block;
+  e = launch_gemm(g, st, Mp, s);
+  if (e != hipSuccess) return hip_fail(e, "draft_block: LM head");
+  e = launch_argmax_reduce(amax, c.vocab / 16, Mp, n, block, draft, s);
+  if (e != hipSuccess) return hip_fail(e, "draft_block: argmax");
+  return DFLASH_OK;
+}
+
+int dflash_accept_len(const int32_t* draft, const int32_t* target, int32_t n_seqs, int32_t block, int32_t* accept,
+                      int32_t* next_anchor, dflash_stream stream) {
+  if (n_seqs < 0) return fail(DFLASH_EINVAL, "n_seqs < 0");
+  if (block < 2 || block > 4096) return fail(DFLASH_EINVAL, "block %d outside [2, 4096]", block);
+  if (n_seqs == 0) return DFLASH_OK;
+  if (!draft || !target || !accept) return fail(DFLASH_EINVAL, "draft, target or accept is NULL");
+  if (!aligned(draft, 4) || !aligned(target, 4) || !aligned(accept, 4) || (next_anchor && !aligned(next_anchor, 4)))
+    return fail(DFLASH_EALIGN, "int32 arrays must be 4-byte aligned");
+  hipError_t e = launch_accept(draft, target, n_seqs, block, accept, next_anchor, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "accept_len");
+  return DFLASH_OK;
+}
+
+}  // extern "C"

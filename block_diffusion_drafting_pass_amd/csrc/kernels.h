@@ -1,0 +1,102 @@
+// Internal interface between the C ABI (api.hip) and the gfx950 kernels
+// (kernels.hip).  Not part of the public header.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dflash {
+
+typedef uint16_t u16;
+
+constexpr int kMaxSeqs = 128;
+
+// Per-call sequence table, passed to kernels by value.  Rows of sequence b in
+// the current row space are [row_start[b], row_start[b+1]); row r of sequence
+// b sits at position pos_base[b] + (r - row_start[b]) and its cache slot is
+// slot_base[b] + position.
+struct SeqTable {
+  int32_t n;
+  int32_t row_start[kMaxSeqs + 1];
+  int32_t pos_base[kMaxSeqs];
+  int32_t slot_base[kMaxSeqs];
+};
+
+// Weight-row maps: which weight row feeds column c (0..15) of 16-wide tile t.
+enum MapKind : int {
+  MAP_PLAIN = 0,   // row 16 t + c of w0
+  MAP_ROPE = 1,    // head-structured [q | k | v]: cols c and c^8 are a RoPE pair
+  MAP_SWIGLU = 2,  // c < 8: row 8 t + c of w0 (gate); c >= 8: row 8 t + c - 8 of w1 (up)
+};
+
+// Epilogues applied to a finished 16x16 fp32 tile.
+enum EpiKind : int {
+  EPI_F32 = 0,     // out_f32[row][16 t + c] = y
+  EPI_SPLIT = 1,   // out_hi/lo[row][16 t + c] = hi/lo(y)
+  EPI_RESID = 2,   // out_f32[row][16 t + c] += y   (residual stream)
+  EPI_SWIGLU = 3,  // out_hi/lo[row][8 t + c] = hi/lo(silu(gate) * up)
+  EPI_QKV = 4,     // RoPE(q), RoPE(k), v -> q workspace and the layer's K/V cache
+  EPI_ARGMAX = 5,  // per-row (max, lowest index) partial over the tile, optional logits
+};
+
+struct WeightSeg {
+  const u16* w0;
+  const u16* w1;
+  const u16* w2;
+};
+
+struct EpiParams {
+  int M;          // valid rows
+  int Mp;         // padded rows (plane stride of split outputs, row stride of partials)
+  // EPI_F32 / EPI_RESID
+  float* out_f32;
+  int ldo;
+  // EPI_SPLIT / EPI_SWIGLU / q of EPI_QKV
+  u16* out_hi;
+  u16* out_lo;
+  int ldh;
+  // EPI_QKV (and MAP_ROPE)
+  int n_q, n_kv, head_dim, head0;
+  const float* rope_cos;  // [pos][head_dim/2]
+  const float* rope_sin;
+  u16* k_cache;   // [2][n_kv][slots][head_dim] bf16 hi/lo planes
+  u16* vt_cache;  // [2][n_kv][head_dim][slots]
+  int64_t slots;
+  // EPI_ARGMAX
+  unsigned long long* amax_part;  // [n_tiles][Mp]
+  float* logits;                  // [n_seqs][block-1][vocab] or null
+  int vocab;
+  int block;
+};
+
+struct GemmArgs {
+  const u16* a_hi;   // A rows (bf16); with split A this is the hi plane
+  const u16* a_lo;   // lo plane or null (single product)
+  int lda;           // row stride of A in elements
+  int a_rows;        // rows of A that exist in memory; others read as zero
+  int K;
+  int n_tiles;       // 16-wide output tiles in the mapped column space
+  WeightSeg w;
+  int map;
+  int epi;
+  EpiParams ep;
+};
+
+hipError_t launch_embed(float* x, const int32_t* anchors, const u16* embed, int H, int M, int Mp,
+                        int block, int mask_id, int vocab, hipStream_t s);
+hipError_t launch_rmsnorm_split(const float* x, const u16* gain, u16* out_hi, u16* out_lo, int H,
+                                int M, int Mp, float eps, hipStream_t s);
+hipError_t launch_gemm(const GemmArgs& g, const SeqTable& st, int Mp, hipStream_t s);
+hipError_t launch_attention(const u16* q_hi, const u16* q_lo, const u16* k_cache,
+                            const u16* vt_cache, int64_t slots, float* part_o, float* part_ml,
+                            u16* o_hi, u16* o_lo, int Mp, int n_seqs, int block, int n_q, int n_kv,
+                            int head_dim, int splits, const SeqTable& st, hipStream_t s);
+hipError_t launch_argmax_reduce(const unsigned long long* part, int n_tiles, int Mp, int n_seqs,
+                                int block, int32_t* draft, hipStream_t s);
+hipError_t launch_accept(const int32_t* draft, const int32_t* target, int n, int block,
+                         int32_t* accept, int32_t* next_anchor, hipStream_t s);
+
+// Number of key splits per (sequence, head, 16-row query tile) unit.
+int attention_splits(int n_units);
+size_t attention_partial_bytes(int n_units, int splits, int head_dim);
+
+}  // namespace dflash

@@ -1,0 +1,763 @@
+// gfx950 (MI355X, CDNA4) kernels of the DFlash block-diffusion draft pass.
+//
+// Precision scheme.  Weights are bf16 and enter the matrix cores unchanged.
+// Every activation is an fp32 value carried as an unevaluated pair of bf16
+// numbers hi + lo (hi = bf16(x), lo = bf16(x - hi)), so one fp32 x bf16
+// product is two bf16 MFMAs into the same fp32 accumulator.  Attention needs
+// fp32 x fp32 products (q.k and p.v), done as hi*hi + hi*lo + lo*hi.  The
+// injected K/V cache stores its fp32 values as such pairs, in the layout the
+// attention kernel feeds straight into MFMA registers.
+//
+// MFMA used throughout: v_mfma_f32_16x16x32_bf16.  A is 16 rows x 32 k, B is
+// 32 k x 16 columns; lane l holds row / column (l % 16) and eight k values of
+// group (l / 16); the 16x16 fp32 result gives lane l column (l % 16) and rows
+// 4 (l / 16) + i, i = 0..3.  The k order inside a group never matters as long
+// as A and B use the same one, which every kernel here does by construction.
+#include <math.h>
+
+#include "kernels.h"
+
+namespace dflash {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned long long u64;
+
+// ---------------------------------------------------------------------------
+// small helpers
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ float bf16_val(uint32_t b) { return __uint_as_float(b << 16); }
+
+// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi); x - hi is exact in fp32.
+__device__ __forceinline__ void split_pair(float x, u16& hi, u16& lo) {
+  const uint32_t h = bf16_rne(x);
+  hi = (u16)h;
+  lo = (u16)bf16_rne(x - bf16_val(h));
+}
+
+__device__ __forceinline__ bf16x8 ld_frag(const u16* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+__device__ __forceinline__ bf16x8 zero_frag() {
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  return __builtin_bit_cast(bf16x8, z);
+}
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Eight fp32 values -> two bf16x8 fragments (hi and lo parts).
+__device__ __forceinline__ void split_frag(const float* v, bf16x8& hi, bf16x8& lo) {
+  u32x4 h, l;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    u16 h0, l0, h1, l1;
+    split_pair(v[2 * j], h0, l0);
+    split_pair(v[2 * j + 1], h1, l1);
+    h[j] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+    l[j] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+  }
+  hi = __builtin_bit_cast(bf16x8, h);
+  lo = __builtin_bit_cast(bf16x8, l);
+}
+
+__device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
+__device__ __forceinline__ u64 shfl_xor_u64(u64 v, int m) {
+  const uint32_t lo = __shfl_xor((uint32_t)v, m, 64);
+  const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m, 64);
+  return ((u64)hi << 32) | lo;
+}
+
+// Sequence owning `row` in the current row space (row_start is ascending).
+__device__ __forceinline__ int seq_of_row(const SeqTable& st, int row) {
+  int b = 0;
+  for (int j = 1; j < st.n; ++j)
+    if (row >= st.row_start[j]) b = j;
+  return b;
+}
+
+// Order-preserving key of an fp32 value (finite inputs), packed with the
+// complemented column so that a u64 max picks the largest value and, among
+// equal values, the lowest column.
+__device__ __forceinline__ u64 argmax_key(float v, int col) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((u64)o << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)col);
+}
+
+// ---------------------------------------------------------------------------
+// weight-row maps and epilogues (shared by both GEMM kernels)
+// ---------------------------------------------------------------------------
+
+template <int MAP>
+__device__ __forceinline__ const u16* weight_row(const WeightSeg& w, const EpiParams& ep, int tile,
+                                                 int c, int K) {
+  if (MAP == MAP_PLAIN) return w.w0 + (size_t)(tile * 16 + c) * K;
+  if (MAP == MAP_SWIGLU) return (c < 8 ? w.w0 : w.w1) + (size_t)(tile * 8 + (c & 7)) * K;
+  // MAP_ROPE: head hh of [q heads | k heads | v heads]; the tile holds the
+  // eight RoPE pairs (j, j + d/2), j = j0 .. j0+7, in columns c and c + 8.
+  const int d = ep.head_dim, tph = d / 16;
+  const int hh = ep.head0 + tile / tph, j0 = (tile % tph) * 8;
+  const int r = (c < 8) ? (j0 + c) : (d / 2 + j0 + (c - 8));
+  if (hh < ep.n_q) return w.w0 + (size_t)(hh * d + r) * K;
+  if (hh < ep.n_q + ep.n_kv) return w.w1 + (size_t)((hh - ep.n_q) * d + r) * K;
+  return w.w2 + (size_t)((hh - ep.n_q - ep.n_kv) * d + r) * K;
+}
+
+// v: the 16x16 fp32 tile in MFMA result layout (lane: column c = lane % 16,
+// rows r0 + 4 (lane / 16) + i).  All 64 lanes must call this together.
+template <int EPI>
+__device__ __forceinline__ void epilogue(const EpiParams& ep, const SeqTable& st, int tile, int r0,
+                                         f32x4 v, int lane) {
+  const int c = lane & 15, g = lane >> 4;
+  if (EPI == EPI_F32 || EPI == EPI_RESID || EPI == EPI_SPLIT) {
+    const int col = tile * 16 + c;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = r0 + 4 * g + i;
+      if (EPI == EPI_F32) {
+        if (row < ep.M) ep.out_f32[(size_t)row * ep.ldo + col] = v[i];
+      } else if (EPI == EPI_RESID) {
+        if (row < ep.M) ep.out_f32[(size_t)row * ep.ldo + col] += v[i];
+      } else {
+        if (row < ep.Mp) {
+          u16 h = 0, l = 0;
+          if (row < ep.M) split_pair(v[i], h, l);
+          ep.out_hi[(size_t)row * ep.ldh + col] = h;
+          ep.out_lo[(size_t)row * ep.ldh + col] = l;
+        }
+      }
+    }
+  } else if (EPI == EPI_SWIGLU) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float up = shfl_xor_f(v[i], 8);  // lane c+8 holds the up projection
+      const int row = r0 + 4 * g + i;
+      if (c < 8 && row < ep.Mp) {
+        u16 h = 0, l = 0;
+        if (row < ep.M) {
+          const float gt = v[i];
+          split_pair(gt / (1.0f + expf(-gt)) * up, h, l);
+        }
+        const size_t o = (size_t)row * ep.ldh + tile * 8 + c;
+        ep.out_hi[o] = h;
+        ep.out_lo[o] = l;
+      }
+    }
+  } else if (EPI == EPI_QKV) {
+    const int d = ep.head_dim, tph = d / 16, half = d / 2;
+    const int hh = ep.head0 + tile / tph;
+    const int jj = (tile % tph) * 8 + (c & 7);
+    const int dcol = (c < 8) ? jj : half + jj;
+    const bool rope = hh < ep.n_q + ep.n_kv;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float partner = shfl_xor_f(v[i], 8);
+      const int row = r0 + 4 * g + i;
+      if (row >= ep.M) continue;
+      const int b = seq_of_row(st, row);
+      const int pos = st.pos_base[b] + (row - st.row_start[b]);
+      float val = v[i];
+      if (rope) {
+        const float cs = ep.rope_cos[(size_t)pos * half + jj];
+        const float sn = ep.rope_sin[(size_t)pos * half + jj];
+        val = (c < 8) ? (v[i] * cs - partner * sn) : (v[i] * cs + partner * sn);
+      }
+      u16 h, l;
+      split_pair(val, h, l);
+      if (hh < ep.n_q) {
+        const size_t o = (size_t)row * ep.ldh + hh * d + dcol;
+        ep.out_hi[o] = h;
+        ep.out_lo[o] = l;
+      } else if (hh < ep.n_q + ep.n_kv) {
+        const int64_t slot = st.slot_base[b] + pos;
+        const size_t o = ((size_t)(hh - ep.n_q) * ep.slots + slot) * d + dcol;
+        const size_t plane = (size_t)ep.n_kv * ep.slots * d;
+        ep.k_cache[o] = h;
+        ep.k_cache[o + plane] = l;
+      } else {
+        const int64_t slot = st.slot_base[b] + pos;
+        const size_t o = ((size_t)(hh - ep.n_q - ep.n_kv) * d + dcol) * ep.slots + slot;
+        const size_t plane = (size_t)ep.n_kv * ep.slots * d;
+        ep.vt_cache[o] = h;
+        ep.vt_cache[o + plane] = l;
+      }
+    }
+  } else if (EPI == EPI_ARGMAX) {
+    const int col = tile * 16 + c;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = r0 + 4 * g + i;
+      const int bi = row % ep.block;
+      const bool draft_row = row < ep.M && bi != 0;
+      if (draft_row && ep.logits)
+        ep.logits[((size_t)(row / ep.block) * (ep.block - 1) + (bi - 1)) * ep.vocab + col] = v[i];
+      u64 key = draft_row ? argmax_key(v[i], col) : 0ull;
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1) {
+        const u64 o = shfl_xor_u64(key, m);
+        key = o > key ? o : key;
+      }
+      if (c == 0 && row < ep.Mp) ep.amax_part[(size_t)tile * ep.Mp + row] = key;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Skinny weight-streaming GEMM: Y[M<=32][N] = A[M][K] W^T, W [N][K] bf16.
+// One workgroup per 16-column tile; its waves split K and stream their
+// slice of the 16 weight rows straight into MFMA B registers (16 B per lane
+// per k-step, all of a 256-k batch in flight, the next batch prefetched).
+// Partial sums meet in LDS in a fixed order, then wave 0 runs the epilogue.
+// ---------------------------------------------------------------------------
+
+template <int EPI, int MAP, bool SPLIT, int RG>
+__global__ __launch_bounds__(512) void k_gemm_skinny(GemmArgs ga, SeqTable st) {
+  constexpr int U = 8;  // 32-k steps per batch
+  const int tile = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const int K = ga.K;
+  const u16* wp = weight_row<MAP>(ga.w, ga.ep, tile, c, K) + g * 8;
+  const int kw = K / nw;
+  const int kb = wave * kw, ke = kb + kw;
+
+  const u16* ah[RG];
+  const u16* al[RG];
+  bool aval[RG];
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg) {
+    const int row = rg * 16 + c;
+    aval[rg] = row < ga.a_rows;
+    ah[rg] = ga.a_hi + (size_t)row * ga.lda + g * 8;
+    al[rg] = SPLIT ? ga.a_lo + (size_t)row * ga.lda + g * 8 : nullptr;
+  }
+  f32x4 acc[RG];
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg) acc[rg] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  int k = kb;
+  if (k + 32 * U <= ke) {
+    bf16x8 wf[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) wf[u] = ld_frag(wp + k + u * 32);
+    for (; k + 32 * U <= ke; k += 32 * U) {
+      bf16x8 wn[U];
+      const bool more = k + 64 * U <= ke;
+      if (more) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) wn[u] = ld_frag(wp + k + 32 * U + u * 32);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg) {
+          const bf16x8 a = aval[rg] ? ld_frag(ah[rg] + k + u * 32) : zero_frag();
+          acc[rg] = mfma(a, wf[u], acc[rg]);
+          if (SPLIT) {
+            const bf16x8 b = aval[rg] ? ld_frag(al[rg] + k + u * 32) : zero_frag();
+            acc[rg] = mfma(b, wf[u], acc[rg]);
+          }
+        }
+      }
+      if (more) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) wf[u] = wn[u];
+      }
+    }
+  }
+  for (; k < ke; k += 32) {
+    const bf16x8 w = ld_frag(wp + k);
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg) {
+      const bf16x8 a = aval[rg] ? ld_frag(ah[rg] + k) : zero_frag();
+      acc[rg] = mfma(a, w, acc[rg]);
+      if (SPLIT) {
+        const bf16x8 b = aval[rg] ? ld_frag(al[rg] + k) : zero_frag();
+        acc[rg] = mfma(b, w, acc[rg]);
+      }
+    }
+  }
+
+  __shared__ f32x4 red[8][RG][64];
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg) red[wave][rg][lane] = acc[rg];
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg) {
+      f32x4 s = red[0][rg][lane];
+      for (int w = 1; w < nw; ++w) s += red[w][rg][lane];
+      epilogue<EPI>(ga.ep, st, tile, rg * 16, s, lane);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// LDS-tiled GEMM for many rows (M a multiple of 64): 64x64 output tile per
+// workgroup of four waves (2x2, each 32x32 = 2x2 MFMA tiles), k staged in
+// 64-wide slabs through padded LDS, the next slab's global loads in flight
+// while the current one is multiplied.
+// ---------------------------------------------------------------------------
+
+template <int EPI, int MAP, bool SPLIT>
+__global__ __launch_bounds__(256) void k_gemm_tiled(GemmArgs ga, SeqTable st) {
+  constexpr int BK = 64, LDS_STRIDE = BK + 8;
+  constexpr int NP = SPLIT ? 2 : 1;
+  __shared__ u16 sA[NP][64][LDS_STRIDE];
+  __shared__ u16 sW[64][LDS_STRIDE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int tile0 = blockIdx.x * 4;
+  const int row0 = blockIdx.y * 64;
+  const int K = ga.K;
+
+  // global -> register staging: each thread moves two 16-byte chunks per operand plane
+  const u16* gA[NP][2];
+  bool av[2];
+  const u16* gW[2];
+  int ldr[2], ldk[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int q = tid + 256 * j;
+    ldr[j] = q >> 3;
+    ldk[j] = (q & 7) * 8;
+    const int arow = row0 + ldr[j];
+    av[j] = arow < ga.a_rows;
+    gA[0][j] = ga.a_hi + (size_t)arow * ga.lda + ldk[j];
+    if (SPLIT) gA[NP - 1][j] = ga.a_lo + (size_t)arow * ga.lda + ldk[j];
+    gW[j] = weight_row<MAP>(ga.w, ga.ep, tile0 + (ldr[j] >> 4), ldr[j] & 15, K) + ldk[j];
+  }
+  u32x4 rA[NP][2], rW[2];
+  auto load_slab = [&](int k0) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int p = 0; p < NP; ++p)
+        rA[p][j] = av[j] ? *reinterpret_cast<const u32x4*>(gA[p][j] + k0) : u32x4{0u, 0u, 0u, 0u};
+      rW[j] = *reinterpret_cast<const u32x4*>(gW[j] + k0);
+    }
+  };
+  auto store_slab = [&]() {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int p = 0; p < NP; ++p) *reinterpret_cast<u32x4*>(&sA[p][ldr[j]][ldk[j]]) = rA[p][j];
+      *reinterpret_cast<u32x4*>(&sW[ldr[j]][ldk[j]]) = rW[j];
+    }
+  };
+
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = K / BK;
+  load_slab(0);
+  store_slab();
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + 1 < nk) load_slab((kt + 1) * BK);
+#pragma unroll
+    for (int ks = 0; ks < BK / 32; ++ks) {
+      bf16x8 wf[2];
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+        wf[ct] = *reinterpret_cast<const bf16x8*>(&sW[wn * 32 + ct * 16 + c][ks * 32 + g * 8]);
+#pragma unroll
+      for (int rg = 0; rg < 2; ++rg) {
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sA[p][wm * 32 + rg * 16 + c][ks * 32 + g * 8]);
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct) acc[rg][ct] = mfma(a, wf[ct], acc[rg][ct]);
+        }
+      }
+    }
+    __syncthreads();
+    if (kt + 1 < nk) {
+      store_slab();
+      __syncthreads();
+    }
+  }
+#pragma unroll
+  for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+      epilogue<EPI>(ga.ep, st, tile0 + wn * 2 + ct, row0 + wm * 32 + rg * 16, acc[rg][ct], lane);
+}
+
+// ---------------------------------------------------------------------------
+// Attention over [injected context | block] keys, split along the keys.
+// One wave per (sequence, q head, 16-row query tile, key split).  It computes
+// S^T = K Q^T (keys as MFMA rows, so the probabilities land in the register
+// layout the P.V product takes as its B operand), keeps a running max / sum
+// per query row (online softmax), and accumulates O^T = V^T P^T, V^T coming
+// straight from the transposed V cache.  Partial (m, l, O) go to a
+// workspace; the merge kernel combines the splits in a fixed order.
+// Within each 32-key step, MFMA row rho of key tile kt (0 or 1) is key
+// 8 (rho / 4) + 4 kt + rho % 4, so lane group q ends up holding keys
+// 8q .. 8q+7 — exactly one B fragment of the P.V product.
+// ---------------------------------------------------------------------------
+
+template <int D>
+__global__ __launch_bounds__(256) void k_attn_partial(const u16* __restrict__ q_hi,
+                                                      const u16* __restrict__ q_lo,
+                                                      const u16* __restrict__ k_cache,
+                                                      const u16* __restrict__ vt_cache,
+                                                      int64_t slots, float* __restrict__ part_o,
+                                                      float* __restrict__ part_ml, int n_seqs,
+                                                      int block, int n_q, int n_kv, int splits,
+                                                      int qtiles, float scale, SeqTable st) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int item = blockIdx.x * 4 + wave;
+  if (item >= n_seqs * n_q * qtiles * splits) return;
+  const int unit = item / splits, s = item % splits;
+  const int t = unit % qtiles, h = (unit / qtiles) % n_q, b = unit / (qtiles * n_q);
+  const int gkv = (h * n_kv) / n_q;
+  const int c = lane & 15, g = lane >> 4;
+  const int n_keys = st.pos_base[b] + block;
+  int chunk = (n_keys + splits - 1) / splits;
+  chunk = (chunk + 31) & ~31;
+  const int k0 = s * chunk, k1 = min(n_keys, k0 + chunk);
+
+  constexpr int DS = D / 32, DT = D / 16;
+  const int qi = t * 16 + c;
+  const bool qvalid = qi < block;
+  const size_t qoff = (size_t)(b * block + qi) * (n_q * D) + h * D + g * 8;
+  bf16x8 qh[DS], ql[DS];
+#pragma unroll
+  for (int ds = 0; ds < DS; ++ds) {
+    qh[ds] = qvalid ? ld_frag(q_hi + qoff + ds * 32) : zero_frag();
+    ql[ds] = qvalid ? ld_frag(q_lo + qoff + ds * 32) : zero_frag();
+  }
+  f32x4 o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, l = 0.f;
+
+  const int64_t slot0 = st.slot_base[b];
+  const size_t kplane = (size_t)n_kv * slots * D;
+  const u16* kbase = k_cache + ((size_t)gkv * slots + slot0) * D + g * 8;
+  const u16* vbase = vt_cache + (size_t)gkv * D * slots + slot0 + g * 8;
+
+  for (int kk = k0; kk < k1; kk += 32) {
+    f32x4 sacc[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      sacc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int key = kk + 8 * (c >> 2) + 4 * kt + (c & 3);
+      const u16* kp = kbase + (size_t)key * D;
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds) {
+        const bf16x8 kh = ld_frag(kp + ds * 32);
+        const bf16x8 kl = ld_frag(kp + kplane + ds * 32);
+        sacc[kt] = mfma(kh, qh[ds], sacc[kt]);
+        sacc[kt] = mfma(kh, ql[ds], sacc[kt]);
+        sacc[kt] = mfma(kl, qh[ds], sacc[kt]);
+      }
+    }
+    float sv[8];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = kk + 8 * g + 4 * kt + i;
+        const float x = key < k1 ? sacc[kt][i] * scale : -INFINITY;
+        sv[kt * 4 + i] = x;
+        mx = fmaxf(mx, x);
+      }
+    mx = fmaxf(mx, shfl_xor_f(mx, 16));
+    mx = fmaxf(mx, shfl_xor_f(mx, 32));
+    const float m_new = fmaxf(m, mx);
+    const float corr = expf(m - m_new);
+    float p[8], ps = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      p[j] = expf(sv[j] - m_new);
+      ps += p[j];
+    }
+    ps += shfl_xor_f(ps, 16);
+    ps += shfl_xor_f(ps, 32);
+    l = l * corr + ps;
+    m = m_new;
+    bf16x8 ph, pl;
+    split_frag(p, ph, pl);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const u16* vp = vbase + (size_t)(dt * 16 + c) * slots + kk;
+      const bf16x8 vh = ld_frag(vp);
+      const bf16x8 vl = ld_frag(vp + kplane);
+      f32x4 acc = o[dt] * corr;
+      acc = mfma(vh, ph, acc);
+      acc = mfma(vh, pl, acc);
+      acc = mfma(vl, ph, acc);
+      o[dt] = acc;
+    }
+  }
+  float* po = part_o + (size_t)item * 16 * D + c * D + g * 4;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16) = o[dt];
+  if (g == 0) {
+    part_ml[(size_t)item * 32 + c] = m;
+    part_ml[(size_t)item * 32 + 16 + c] = l;
+  }
+}
+
+// Combine the key splits of each unit (fixed order) and write the attention
+// output as hi/lo planes [row][n_q * D].
+template <int D>
+__global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ part_o,
+                                                    const float* __restrict__ part_ml,
+                                                    u16* __restrict__ o_hi, u16* __restrict__ o_lo,
+                                                    int block, int n_q, int splits, int qtiles) {
+  const int unit = blockIdx.x;
+  const int t = unit % qtiles, h = (unit / qtiles) % n_q, b = unit / (qtiles * n_q);
+  const float* ml = part_ml + (size_t)unit * splits * 32;
+  for (int idx = threadIdx.x; idx < 16 * D; idx += blockDim.x) {
+    const int row = idx / D, dcol = idx % D;
+    const int qi = t * 16 + row;
+    if (qi >= block) continue;
+    float M = -INFINITY;
+    for (int s = 0; s < splits; ++s) M = fmaxf(M, ml[s * 32 + row]);
+    float L = 0.f, acc = 0.f;
+    for (int s = 0; s < splits; ++s) {
+      const float w = expf(ml[s * 32 + row] - M);
+      L += ml[s * 32 + 16 + row] * w;
+      acc += part_o[((size_t)(unit * splits + s) * 16 + row) * D + dcol] * w;
+    }
+    u16 hi, lo;
+    split_pair(acc / L, hi, lo);
+    const size_t o = (size_t)(b * block + qi) * (n_q * D) + h * D + dcol;
+    o_hi[o] = hi;
+    o_lo[o] = lo;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// small kernels
+// ---------------------------------------------------------------------------
+
+// x[row] = E[token] (fp32); token = anchor for block row 0, the mask id
+// otherwise; rows >= M are zero.  Out-of-range anchors are clamped.
+__global__ __launch_bounds__(256) void k_embed(float* __restrict__ x, const int32_t* __restrict__ anchors,
+                                               const u16* __restrict__ E, int H, int M, int block,
+                                               int mask_id, int vocab) {
+  const int row = blockIdx.x;
+  float* xr = x + (size_t)row * H;
+  if (row >= M) {
+    for (int j = threadIdx.x * 4; j < H; j += blockDim.x * 4)
+      *reinterpret_cast<f32x4*>(xr + j) = f32x4{0.f, 0.f, 0.f, 0.f};
+    return;
+  }
+  int tok = (row % block == 0) ? anchors[row / block] : mask_id;
+  tok = tok < 0 ? 0 : (tok >= vocab ? vocab - 1 : tok);
+  const u16* er = E + (size_t)tok * H;
+  for (int j = threadIdx.x * 8; j < H; j += blockDim.x * 8) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(er + j);
+    f32x4 lo4, hi4;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      lo4[2 * q] = bf16_val(w[q] & 0xFFFFu);
+      lo4[2 * q + 1] = bf16_val(w[q] >> 16);
+      hi4[2 * q] = bf16_val(w[q + 2] & 0xFFFFu);
+      hi4[2 * q + 1] = bf16_val(w[q + 2] >> 16);
+    }
+    *reinterpret_cast<f32x4*>(xr + j) = lo4;
+    *reinterpret_cast<f32x4*>(xr + j + 4) = hi4;
+  }
+}
+
+// u = gain * x / sqrt(mean(x^2) + eps) per row, written as hi/lo planes; rows
+// >= M are written as zeros.  Fixed-order reduction (deterministic).
+__global__ __launch_bounds__(256) void k_rmsnorm_split(const float* __restrict__ x,
+                                                       const u16* __restrict__ gain,
+                                                       u16* __restrict__ out_hi,
+                                                       u16* __restrict__ out_lo, int H, int M,
+                                                       float eps) {
+  const int row = blockIdx.x;
+  u16* oh = out_hi + (size_t)row * H;
+  u16* ol = out_lo + (size_t)row * H;
+  if (row >= M) {
+    for (int j = threadIdx.x; j < H; j += blockDim.x) {
+      oh[j] = 0;
+      ol[j] = 0;
+    }
+    return;
+  }
+  const float* xr = x + (size_t)row * H;
+  float ss = 0.f;
+  for (int j = threadIdx.x * 4; j < H; j += blockDim.x * 4) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(xr + j);
+    ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) ss += shfl_xor_f(ss, m);
+  __shared__ float wsum[4];
+  if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+  const float r = 1.0f / sqrtf(tot / (float)H + eps);
+  for (int j = threadIdx.x; j < H; j += blockDim.x) {
+    u16 h, l;
+    split_pair(bf16_val(gain[j]) * xr[j] * r, h, l);
+    oh[j] = h;
+    ol[j] = l;
+  }
+}
+
+// draft[b][i-1] = lowest column of the largest logit of block row i.
+__global__ __launch_bounds__(256) void k_argmax_reduce(const u64* __restrict__ part, int n_tiles,
+                                                       int Mp, int block, int32_t* __restrict__ draft) {
+  const int dr = blockIdx.x;
+  const int b = dr / (block - 1), i = dr % (block - 1) + 1;
+  const int row = b * block + i;
+  u64 best = 0;
+  for (int t = threadIdx.x; t < n_tiles; t += blockDim.x) {
+    const u64 v = part[(size_t)t * Mp + row];
+    best = v > best ? v : best;
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const u64 o = shfl_xor_u64(best, m);
+    best = o > best ? o : best;
+  }
+  __shared__ u64 wbest[4];
+  if ((threadIdx.x & 63) == 0) wbest[threadIdx.x >> 6] = best;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    u64 r = wbest[0];
+    for (int w = 1; w < 4; ++w) r = wbest[w] > r ? wbest[w] : r;
+    draft[dr] = (int32_t)(0xFFFFFFFFu - (uint32_t)(r & 0xFFFFFFFFull));
+  }
+}
+
+__global__ __launch_bounds__(256) void k_accept(const int32_t* __restrict__ draft,
+                                                const int32_t* __restrict__ target, int n, int block,
+                                                int32_t* __restrict__ accept,
+                                                int32_t* __restrict__ next_anchor) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= n) return;
+  const int32_t* dr = draft + (size_t)b * (block - 1);
+  const int32_t* tg = target + (size_t)b * block;
+  int k = 0;
+  while (k < block - 1 && dr[k] == tg[k]) ++k;
+  accept[b] = k;
+  if (next_anchor) next_anchor[b] = tg[k];
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+
+hipError_t launch_embed(float* x, const int32_t* anchors, const u16* embed, int H, int M, int Mp,
+                        int block, int mask_id, int vocab, hipStream_t s) {
+  hipLaunchKernelGGL(k_embed, dim3(Mp), dim3(256), 0, s, x, anchors, embed, H, M, block, mask_id, vocab);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_split(const float* x, const u16* gain, u16* out_hi, u16* out_lo, int H,
+                                int M, int Mp, float eps, hipStream_t s) {
+  hipLaunchKernelGGL(k_rmsnorm_split, dim3(Mp), dim3(256), 0, s, x, gain, out_hi, out_lo, H, M, eps);
+  return hipGetLastError();
+}
+
+template <int EPI, int MAP, bool SPLIT>
+static hipError_t gemm_dispatch(const GemmArgs& g, const SeqTable& st, int Mp, hipStream_t s) {
+  if (Mp <= 32) {
+    int nw = 8;
+    while (nw > 1 && g.K % (32 * nw) != 0) nw >>= 1;
+    if (Mp <= 16)
+      hipLaunchKernelGGL((k_gemm_skinny<EPI, MAP, SPLIT, 1>), dim3(g.n_tiles), dim3(64 * nw), 0, s, g, st);
+    else
+      hipLaunchKernelGGL((k_gemm_skinny<EPI, MAP, SPLIT, 2>), dim3(g.n_tiles), dim3(64 * nw), 0, s, g, st);
+  } else {
+    hipLaunchKernelGGL((k_gemm_tiled<EPI, MAP, SPLIT>), dim3(g.n_tiles / 4, Mp / 64), dim3(256), 0, s, g, st);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm(const GemmArgs& g, const SeqTable& st, int Mp, hipStream_t s) {
+  const bool split = g.a_lo != nullptr;
+  switch (g.epi) {
+    case EPI_SPLIT:
+      return split ? gemm_dispatch<EPI_SPLIT, MAP_PLAIN, true>(g, st, Mp, s)
+                   : gemm_dispatch<EPI_SPLIT, MAP_PLAIN, false>(g, st, Mp, s);
+    case EPI_QKV:
+      return gemm_dispatch<EPI_QKV, MAP_ROPE, true>(g, st, Mp, s);
+    case EPI_RESID:
+      return gemm_dispatch<EPI_RESID, MAP_PLAIN, true>(g, st, Mp, s);
+    case EPI_SWIGLU:
+      return gemm_dispatch<EPI_SWIGLU, MAP_SWIGLU, true>(g, st, Mp, s);
+    case EPI_ARGMAX:
+      return gemm_dispatch<EPI_ARGMAX, MAP_PLAIN, true>(g, st, Mp, s);
+    case EPI_F32:
+      return split ? gemm_dispatch<EPI_F32, MAP_PLAIN, true>(g, st, Mp, s)
+                   : gemm_dispatch<EPI_F32, MAP_PLAIN, false>(g, st, Mp, s);
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+int attention_splits(int n_units) {
+  int s = (2048 + n_units - 1) / n_units;
+  return s < 1 ? 1 : (s > 64 ? 64 : s);
+}
+
+size_t attention_partial_bytes(int n_units, int splits, int head_dim) {
+  return (size_t)n_units * splits * 16 * head_dim * sizeof(float) +
+         (size_t)n_units * splits * 32 * sizeof(float);
+}
+
+hipError_t launch_attention(const u16* q_hi, const u16* q_lo, const u16* k_cache,
+                            const u16* vt_cache, int64_t slots, float* part_o, float* part_ml,
+                            u16* o_hi, u16* o_lo, int Mp, int n_seqs, int block, int n_q, int n_kv,
+                            int head_dim, int splits, const SeqTable& st, hipStream_t s) {
+  (void)Mp;
+  const int qtiles = (block + 15) / 16;
+  const int units = n_seqs * n_q * qtiles;
+  const int items = units * splits;
+  const float scale = (float)(1.0 / sqrt((double)head_dim));
+  const dim3 grid((items + 3) / 4);
+  if (head_dim == 128) {
+    hipLaunchKernelGGL(k_attn_partial<128>, grid, dim3(256), 0, s, q_hi, q_lo, k_cache, vt_cache, slots,
+                       part_o, part_ml, n_seqs, block, n_q, n_kv, splits, qtiles, scale, st);
+    hipLaunchKernelGGL(k_attn_merge<128>, dim3(units), dim3(256), 0, s, part_o, part_ml, o_hi, o_lo, block,
+                       n_q, splits, qtiles);
+  } else if (head_dim == 64) {
+    hipLaunchKernelGGL(k_attn_partial<64>, grid, dim3(256), 0, s, q_hi, q_lo, k_cache, vt_cache, slots,
+                       part_o, part_ml, n_seqs, block, n_q, n_kv, splits, qtiles, scale, st);
+    hipLaunchKernelGGL(k_attn_merge<64>, dim3(units), dim3(256), 0, s, part_o, part_ml, o_hi, o_lo, block,
+                       n_q, splits, qtiles);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_argmax_reduce(const unsigned long long* part, int n_tiles, int Mp, int n_seqs,
+                                int block, int32_t* draft, hipStream_t s) {
+  hipLaunchKernelGGL(k_argmax_reduce, dim3(n_seqs * (block - 1)), dim3(256), 0, s, part, n_tiles, Mp,
+                     block, draft);
+  return hipGetLastError();
+}
+
+hipError_t launch_accept(const int32_t* draft, const int32_t* target, int n, int block,
+                         int32_t* accept, int32_t* next_anchor, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_accept, dim3((n + 255) / 256), dim3(256), 0, s, draft, target, n, block, accept,
+                     next_anchor);
+  return hipGetLastError();
+}
+
+}  // namespace dflash

@@ -1,0 +1,173 @@
+/*
+ * dflash.h — C ABI of the MI355X (gfx950) DFlash block-diffusion draft pass.
+ *
+ * DFlash ("DFlash: Block Diffusion for Flash Speculative Decoding",
+ * arXiv 2602.06036) drafts a whole block of tokens in one forward pass of a
+ * small block-diffusion drafter.  Hidden features from several layers of the
+ * frozen target model are fused and injected as key/value entries into every
+ * draft layer's KV cache (paper Fig. 2, "DFlash Inference Design"; atlas
+ * summary, "Approach").  The target verifies the block in parallel and the
+ * matched prefix is accepted; the reported metric is the acceptance length
+ * tau at temperature 0 (atlas summary, "Key results", "Experimental setup").
+ *
+ * The three calls follow that statement of the problem:
+ *   dflash_fuse_ctx     fuse target features of newly verified positions and
+ *                       append them as injected K/V to every layer's cache;
+ *   dflash_draft_block  one pass over (anchor, mask, ..., mask) for every
+ *                       sequence, ending in an LM-head argmax per mask row;
+ *   dflash_accept_len   greedy verification: matched-prefix length and the
+ *                       next anchor.
+ *
+ * Conventions
+ *   - Every device pointer is owned by the caller (e.g. allocated through
+ *     PyTorch).  The library never allocates, frees or retains device memory;
+ *     the host descriptors it creates (dflash_model, dflash_ctx) hold only
+ *     pointers into caller memory and host-side metadata.
+ *   - Calls are stream-ordered and asynchronous: they enqueue kernels on the
+ *     given stream and return.  Only dflash_ctx_create waits for its own
+ *     stream (it uploads a host-computed RoPE table).
+ *   - Validation happens before any launch: on error nothing is enqueued and
+ *     no context length changes.  Errors are negative dflash_status codes; the
+ *     detail is in dflash_last_error() (thread-local).  No C++ exception
+ *     crosses this interface.  A failed kernel launch returns DFLASH_EHIP.
+ *   - A context is used by one stream at a time; different contexts may be
+ *     used concurrently with different workspaces.
+ *
+ * Numerics: weights are bf16; activations, the residual stream, the injected
+ * K/V cache, softmax probabilities and logits carry fp32-quality values (each
+ * stored as an unevaluated pair of bf16 numbers hi + lo where it feeds a
+ * matrix-core product); all products accumulate in fp32.
+ */
+#ifndef DFLASH_H
+#define DFLASH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* HIP stream handle (hipStream_t); NULL means the default stream. */
+typedef void* dflash_stream;
+
+typedef enum {
+  DFLASH_OK = 0,
+  DFLASH_EINVAL = -1,      /* null pointer or invalid argument value          */
+  DFLASH_ESHAPE = -2,      /* shapes inconsistent with the model / context    */
+  DFLASH_ECAPACITY = -3,   /* appending would exceed a sequence's capacity    */
+  DFLASH_EWORKSPACE = -4,  /* workspace smaller than dflash_workspace_bytes() */
+  DFLASH_EALIGN = -5,      /* a pointer is not 16-byte (buffers: 256-byte) aligned */
+  DFLASH_EHIP = -6,        /* the HIP runtime reported an error               */
+  DFLASH_EUNSUPPORTED = -7 /* valid but outside what the kernels implement    */
+} dflash_status;
+
+/* Drafter hyper-parameters.  Supported: head_dim 64 or 128; hidden,
+ * intermediate, n_q_heads*head_dim and n_target_layers*hidden multiples of
+ * 256; n_q_heads a multiple of n_kv_heads; vocab a multiple of 16;
+ * 2 <= max_block <= 32.  mask_token_id is an ordinary embedding row. */
+typedef struct {
+  int32_t n_layers;
+  int32_t hidden;
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t intermediate;
+  int32_t vocab;
+  int32_t n_target_layers;
+  int32_t mask_token_id;
+  int32_t max_block;
+  float rms_eps;      /* RMSNorm epsilon, inside the square root */
+  double rope_theta;  /* rotate-half RoPE base */
+} dflash_config;
+
+typedef struct dflash_model dflash_model;
+typedef struct dflash_ctx dflash_ctx;
+
+/* Number of weight pointers dflash_model_create expects: 3 + 9 * n_layers. */
+int32_t dflash_weight_count(const dflash_config* cfg);
+
+/* Describe a drafter whose bf16 weights already sit in device memory.
+ * weights[] order: w_fc [H][L_t*H], embed [V][H] (also the LM head),
+ * final_norm [H]; then for each layer l: attn_norm [H], wq [n_q*d][H],
+ * wk [n_kv*d][H], wv [n_kv*d][H], wo [H][n_q*d], mlp_norm [H],
+ * wgate [I][H], wup [I][H], wdown [H][I].  Matrices are row-major
+ * [out][in] (the nn.Linear layout); every pointer 16-byte aligned.
+ * The pointers must stay valid for the model's lifetime. */
+int dflash_model_create(const dflash_config* cfg, const void* const* weights, dflash_model** out);
+void dflash_model_destroy(dflash_model* model);
+
+/* Device bytes needed for a context of n_seqs sequences holding up to
+ * capacity[b] verified positions each (host array).  The layout keeps, per
+ * layer, K as [hi/lo][kv_head][slot][d] and V transposed as
+ * [hi/lo][kv_head][d][slot] (bf16 pairs carrying fp32 values), a per-sequence
+ * headroom of max_block slots that dflash_draft_block writes its block K/V
+ * into, and an fp32 RoPE cos/sin table computed in fp64 on the host.
+ * Returns 0 if the arguments are invalid. */
+size_t dflash_ctx_bytes(const dflash_config* cfg, int32_t n_seqs, const int64_t* capacity);
+
+/* Lay a context over caller memory dev_buf (256-byte aligned, >= bytes from
+ * dflash_ctx_bytes).  Zero-fills the K/V region and uploads the RoPE table on
+ * `stream`, then waits for that stream.  All sequences start empty.
+ * 1 <= n_seqs <= 128. */
+int dflash_ctx_create(const dflash_model* model, void* dev_buf, size_t bytes, int32_t n_seqs,
+                      const int64_t* capacity, dflash_stream stream, dflash_ctx** out);
+void dflash_ctx_destroy(dflash_ctx* ctx);
+
+/* Current number of verified positions of sequence `seq` (host metadata). */
+int64_t dflash_ctx_length(const dflash_ctx* ctx, int32_t seq);
+
+/* Forget positions >= new_len of sequence `seq` (host metadata only; the
+ * stale cache entries are overwritten by later appends). */
+int dflash_ctx_truncate(dflash_ctx* ctx, int32_t seq, int64_t new_len);
+
+/* Workspace bytes for dflash_draft_block over all sequences of a context
+ * with n_seqs sequences at block size `block`, and for dflash_fuse_ctx calls
+ * appending up to max_new_tokens positions in total. */
+size_t dflash_workspace_bytes(const dflash_model* model, int32_t n_seqs, int32_t block,
+                              int64_t max_new_tokens);
+
+/* Append n_new[b] newly verified positions to each sequence (DFlash paper
+ * Fig. 2: fused target features are injected into every draft layer's KV
+ * cache).  features: device bf16 [sum_b n_new[b]][n_target_layers*hidden],
+ * sequences packed in order, each row the selected target layers
+ * concatenated.  For every row: h = W_fc f (fp32 accumulate), then for each
+ * layer K = RoPE(W_k h, p) and V = W_v h are written at position
+ * p = length(b) + t.  n_new is a host array [n_seqs]; entries may be 0.
+ * Lengths advance on the host when the call is enqueued.
+ * Errors: DFLASH_ECAPACITY if length(b) + n_new[b] > capacity[b]. */
+int dflash_fuse_ctx(const dflash_model* model, dflash_ctx* ctx, const void* features,
+                    const int32_t* n_new, void* ws, size_t ws_bytes, dflash_stream stream);
+
+/* One block-diffusion draft pass for every sequence of the context (forum
+ * post, section 1: a candidate block in a single forward pass; atlas summary,
+ * "Approach").  Sequence b's block is the token anchors[b] followed by
+ * block-1 mask tokens at positions length(b) .. length(b)+block-1; each layer
+ * attends over [injected context K/V | block K/V] with no mask.  Row i >= 1
+ * predicts the token at its own position: draft[b][i-1] is the lowest index
+ * of the largest logit.
+ *   anchors: device int32 [n_seqs];   draft: device int32 [n_seqs][block-1]
+ *   logits:  NULL, or device fp32 [n_seqs][block-1][vocab] (written if given)
+ * The block's K/V are written into the context's headroom slots (positions
+ * >= length), which does not change any length.  2 <= block <= max_block. */
+int dflash_draft_block(const dflash_model* model, const dflash_ctx* ctx, const int32_t* anchors,
+                       int32_t block, int32_t* draft, float* logits, void* ws, size_t ws_bytes,
+                       dflash_stream stream);
+
+/* Greedy verification (atlas summary, "Key results": temperature 0; metric:
+ * acceptance length tau).  draft: device int32 [n_seqs][block-1] for block
+ * positions 1..block-1; target: device int32 [n_seqs][block], the target's
+ * tokens for positions 1..block (the last is the bonus token).
+ * accept[b] = number of leading positions where draft == target (0..block-1),
+ * next_anchor[b] = target[b][accept[b]] (skipped when NULL); tau = accept + 1.
+ * n_seqs >= 0, 2 <= block <= 4096. */
+int dflash_accept_len(const int32_t* draft, const int32_t* target, int32_t n_seqs, int32_t block,
+                      int32_t* accept, int32_t* next_anchor, dflash_stream stream);
+
+const char* dflash_status_str(int status);
+const char* dflash_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DFLASH_H */

@@ -1,0 +1,173 @@
+"""Host-side checks of the C ABI: the library loads, exports every symbol the
+header declares, and validates arguments before touching the GPU.  CPU only:
+none of these calls reaches a kernel launch."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_diffusion_drafting_pass_amd import binding as B
+from block_diffusion_drafting_pass_amd import inputs as I
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.skip("libdflash.so not built (run __graft_entry__.build())")
+    return B.lib()
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "dflash.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dflash_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_three_calls():
+    names = _declared_functions()
+    for n in ("dflash_fuse_ctx", "dflash_draft_block", "dflash_accept_len"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib()
+    names = _declared_functions()
+    assert set(names) == set(B.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def _cfg(name="tiny", **kw):
+    c = B.Config.from_spec(I.spec(name))
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def _err(rc):
+    return B.STATUS[rc]
+
+
+def test_status_strings():
+    L = _lib()
+    for code in B.STATUS:
+        assert L.dflash_status_str(code)
+    assert L.dflash_status_str(12345) == b"unknown status"
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("head_dim", 96, "DFLASH_EUNSUPPORTED"),
+    ("n_kv_heads", 3, "DFLASH_ESHAPE"),
+    ("hidden", 200, "DFLASH_EUNSUPPORTED"),
+    ("vocab", 4104, "DFLASH_EUNSUPPORTED"),
+    ("max_block", 33, "DFLASH_EUNSUPPORTED"),
+    ("max_block", 1, "DFLASH_EUNSUPPORTED"),
+    ("mask_token_id", 4096, "DFLASH_EINVAL"),
+    ("n_layers", 0, "DFLASH_EINVAL"),
+    ("rms_eps", 0.0, "DFLASH_EINVAL"),
+])
+def test_model_create_rejects_bad_configs(field, value, code):
+    L = _lib()
+    cfg = _cfg(**{field: value})
+    n = max(3, 3 + 9 * max(cfg.n_layers, 0))
+    ptrs = (ctypes.c_void_p * n)(*([0x10000] * n))
+    h = ctypes.c_void_p()
+    rc = L.dflash_model_create(ctypes.byref(cfg), ptrs, ctypes.byref(h))
+    assert _err(rc) == code
+    assert not h.value
+    assert L.dflash_last_error()
+
+
+def test_model_create_checks_pointers():
+    L = _lib()
+    cfg = _cfg()
+    n = L.dflash_weight_count(ctypes.byref(cfg))
+    assert n == 3 + 9 * cfg.n_layers
+    h = ctypes.c_void_p()
+    ptrs = (ctypes.c_void_p * n)(*([0x10000] * n))
+    ptrs[4] = None
+    assert _err(L.dflash_model_create(ctypes.byref(cfg), ptrs, ctypes.byref(h))) == "DFLASH_EINVAL"
+    ptrs[4] = 0x10008
+    assert _err(L.dflash_model_create(ctypes.byref(cfg), ptrs, ctypes.byref(h))) == "DFLASH_EALIGN"
+    ptrs[4] = 0x10010
+    assert L.dflash_model_create(ctypes.byref(cfg), ptrs, ctypes.byref(h)) == 0
+    assert h.value
+    L.dflash_model_destroy(h)
+
+
+def _fake_model(name="tiny"):
+    L = _lib()
+    cfg = _cfg(name)
+    n = L.dflash_weight_count(ctypes.byref(cfg))
+    ptrs = (ctypes.c_void_p * n)(*([0x100000] * n))
+    h = ctypes.c_void_p()
+    assert L.dflash_model_create(ctypes.byref(cfg), ptrs, ctypes.byref(h)) == 0
+    return cfg, h
+
+
+def test_ctx_bytes_layout():
+    L = _lib()
+    cfg = _cfg("q8b_ctx1024")
+    cap = (ctypes.c_int64 * 1)(1024)
+    nbytes = L.dflash_ctx_bytes(ctypes.byref(cfg), 1, cap)
+    slots = (1024 + cfg.max_block + 63) // 64 * 64
+    kv = 5 * 2 * (2 * 8 * slots * 128 * 2)
+    rope = 2 * slots * 64 * 4
+    assert kv <= nbytes <= kv + rope + 12 * 256
+    # K/V planes cost 8 bytes per (token, kv head, dim) — the same as fp32 K and V
+    assert kv == 5 * slots * 8 * 128 * 8
+    bad = (ctypes.c_int64 * 1)(-1)
+    assert L.dflash_ctx_bytes(ctypes.byref(cfg), 1, bad) == 0
+    assert L.dflash_ctx_bytes(ctypes.byref(cfg), 0, cap) == 0
+    assert L.dflash_ctx_bytes(ctypes.byref(cfg), 129, (ctypes.c_int64 * 129)(*[1] * 129)) == 0
+
+
+def test_ctx_create_validates_before_any_device_call():
+    L = _lib()
+    cfg, m = _fake_model()
+    cap = (ctypes.c_int64 * 1)(128)
+    h = ctypes.c_void_p()
+    assert _err(L.dflash_ctx_create(m, None, 1 << 20, 1, cap, None, ctypes.byref(h))) == "DFLASH_EINVAL"
+    assert _err(L.dflash_ctx_create(m, 0x1000 + 16, 1 << 20, 1, cap, None, ctypes.byref(h))) == "DFLASH_EALIGN"
+    assert _err(L.dflash_ctx_create(m, 0x1000, 16, 1, cap, None, ctypes.byref(h))) == "DFLASH_ECAPACITY"
+    assert _err(L.dflash_ctx_create(m, 0x1000, 1 << 20, 0, cap, None, ctypes.byref(h))) == "DFLASH_EUNSUPPORTED"
+    assert not h.value
+    L.dflash_model_destroy(m)
+
+
+def test_workspace_bytes():
+    L = _lib()
+    cfg, m = _fake_model("q8b_ctx1024")
+    a = L.dflash_workspace_bytes(m, 1, 16, 0)
+    b = L.dflash_workspace_bytes(m, 32, 16, 0)
+    c = L.dflash_workspace_bytes(m, 1, 16, 65536)
+    assert 0 < a < b and a <= c
+    assert L.dflash_workspace_bytes(m, 1, 1, 0) == 0
+    assert L.dflash_workspace_bytes(m, 1, cfg.max_block + 1, 0) == 0
+    assert L.dflash_workspace_bytes(m, 0, 16, 0) == 0
+    L.dflash_model_destroy(m)
+
+
+def test_accept_len_validation():
+    L = _lib()
+    assert _err(L.dflash_accept_len(None, None, -1, 16, None, None, None)) == "DFLASH_EINVAL"
+    assert _err(L.dflash_accept_len(None, None, 1, 1, None, None, None)) == "DFLASH_EINVAL"
+    assert _err(L.dflash_accept_len(None, 0x1000, 1, 16, 0x1000, None, None)) == "DFLASH_EINVAL"
+    assert _err(L.dflash_accept_len(0x1002, 0x1000, 1, 16, 0x1000, None, None)) == "DFLASH_EALIGN"
+    # nothing to do is not an error
+    assert L.dflash_accept_len(None, None, 0, 16, None, None, None) == 0
+
+
+def test_draft_and_fuse_validation_without_context():
+    L = _lib()
+    cfg, m = _fake_model()
+    assert _err(L.dflash_draft_block(m, None, 0x1000, 16, 0x1000, None, 0x1000, 1 << 20, None)) == "DFLASH_EINVAL"
+    n_new = (ctypes.c_int32 * 1)(1)
+    assert _err(L.dflash_fuse_ctx(m, None, 0x1000, n_new, 0x1000, 1 << 20, None)) == "DFLASH_EINVAL"
+    assert _err(L.dflash_ctx_truncate(None, 0, 0)) == "DFLASH_EINVAL"
+    assert L.dflash_ctx_length(None, 0) == -1
+    L.dflash_model_destroy(m)

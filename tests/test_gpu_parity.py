@@ -1,0 +1,211 @@
+"""GPU parity: the HIP path, called through the C ABI, against the CPU oracle
+on identical seeded inputs.  Covers the five workload shapes (tiny drafter;
+Qwen3-8B-shaped drafter at context 1024, 8192, concurrency 32, and a ragged
+3-layer block-32 batch) plus edge cases: empty context, ragged lengths, block
+sizes 2/4/32, the tiled (many-row) GEMM path, incremental appends with a
+truncation, determinism, and the accepted-prefix scan."""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+import pytest
+
+from block_diffusion_drafting_pass_amd import binding as B
+from block_diffusion_drafting_pass_amd import inputs as I
+from oracle import dflash_oracle as O
+from tests.gpu_harness import GpuRun, accept_check, assert_parity, oracle_run, say
+
+pytestmark = pytest.mark.gpu
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+@pytest.fixture(scope="session")
+def torch_cuda():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    B.lib()  # fails loudly when the library is missing
+    return torch
+
+
+@pytest.fixture(scope="session")
+def q8(torch_cuda):
+    """Qwen3-8B-shaped drafter weights (5 layers), host bits and device tensors."""
+    spec = I.spec("q8b_ctx1024")
+    say("generating 5-layer Qwen3-8B-shaped weights")
+    w = I.gen_weights(spec, seed=0)
+    dev = B.upload_weights(spec, w)
+    torch_cuda.cuda.synchronize()
+    return spec, w, dev
+
+
+def _feats(spec, seed, lens):
+    return [I.gen_features(spec, seed, b, c) for b, c in enumerate(lens)]
+
+
+# ----------------------------------------------------------------------------
+# accepted-prefix scan
+# ----------------------------------------------------------------------------
+
+def test_accept_len_golden_cases(torch_cuda):
+    torch = torch_cuda
+    path = os.path.join(HERE, "golden", "accept_cases.txt")
+    for line in open(path):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        blk, dr, tg, res = (p.split() for p in line.split("|"))
+        Bk = int(blk[0])
+        d = torch.tensor([[int(v) for v in dr]], dtype=torch.int32, device="cuda")
+        t = torch.tensor([[int(v) for v in tg]], dtype=torch.int32, device="cuda")
+        acc, nxt = B.accept_len(d, t, Bk)
+        assert (int(acc.item()), int(nxt.item())) == (int(res[0]), int(res[1])), line
+
+
+@pytest.mark.parametrize("block,n", [(16, 1000), (32, 777), (2, 5), (16, 1)])
+def test_accept_len_constructed(torch_cuda, block, n):
+    torch = torch_cuda
+    spec = I.spec("q8b_conc32").with_(block=block, ctx_lens=(0,) * n)
+    rng = np.random.default_rng(block * 1000 + n)
+    draft = rng.integers(0, spec.vocab, size=(n, block - 1)).astype(np.int32)
+    K, r, bonus = I.gen_accept_construction(spec, seed=block)
+    target = I.make_targets(draft, K, r, bonus, spec.vocab)
+    acc_ref, nxt_ref = O.accept_len(draft, target)
+    acc, nxt = B.accept_len(torch.from_numpy(draft).cuda(), torch.from_numpy(target).cuda(), block)
+    np.testing.assert_array_equal(acc.cpu().numpy(), acc_ref)
+    np.testing.assert_array_equal(nxt.cpu().numpy(), nxt_ref)
+    np.testing.assert_array_equal(acc_ref, np.minimum(K, block - 1))
+
+
+def test_accept_len_empty_batch(torch_cuda):
+    torch = torch_cuda
+    d = torch.empty((0, 15), dtype=torch.int32, device="cuda")
+    t = torch.empty((0, 16), dtype=torch.int32, device="cuda")
+    acc, _ = B.accept_len(d, t, 16)
+    assert acc.numel() == 0
+
+
+# ----------------------------------------------------------------------------
+# tiny drafter: full configuration and edge cases
+# ----------------------------------------------------------------------------
+
+def _tiny_case(spec, lens, block, wseed=0, jitter=0.0, std=0.02, label=""):
+    say(f"tiny case {label}: lens={lens} block={block}")
+    spec = spec.with_(ctx_lens=tuple(lens), block=block)
+    w = I.gen_weights(spec, seed=wseed, gain_jitter=jitter, std=std)
+    run = GpuRun(spec, B.upload_weights(spec, w), capacity=[c + 8 for c in lens], max_new=sum(lens))
+    feats = _feats(spec, 1, lens)
+    run.ingest(feats)
+    anchors = I.gen_anchors(spec, 2)
+    drafts, logits = run.draft(anchors, block)
+    ref = oracle_run(spec, w, feats, anchors, block)
+    assert_parity(logits, drafts, ref, label)
+    accept_check(drafts, ref, spec, 3, label)
+    return run, drafts, logits
+
+
+def test_tiny_config(torch_cuda):
+    _tiny_case(I.spec("tiny"), (128,), 16, label="tiny ctx128 B16")
+
+
+@pytest.mark.parametrize("lens,block,jitter,std,label", [
+    ((0,), 16, 0.0, 0.02, "empty context"),
+    ((37, 5, 0), 4, 0.0, 0.05, "ragged 3 seqs B4"),
+    ((10, 20), 16, 0.0, 0.05, "two seqs M32 skinny"),
+    ((100, 64, 33), 16, 0.0, 0.05, "three seqs M48 tiled"),
+    ((64, 200), 32, 0.1, 0.05, "B32 two seqs tiled"),
+    ((50,), 2, 0.1, 0.05, "block 2"),
+    ((128,), 16, 0.1, 0.05, "gain jitter"),
+    ((300,) * 5, 32, 0.0, 0.03, "five seqs B32 M160"),
+])
+def test_tiny_variants(torch_cuda, lens, block, jitter, std, label):
+    _tiny_case(I.spec("tiny"), lens, block, jitter=jitter, std=std, label=label)
+
+
+def test_tiny_incremental_append_and_truncate(torch_cuda):
+    spec = I.spec("tiny").with_(ctx_lens=(0, 0))
+    w = I.gen_weights(spec, seed=4, std=0.05)
+    run = GpuRun(spec, B.upload_weights(spec, w), capacity=[300, 300], max_new=200)
+    model = O.OracleModel.from_spec(spec, w)
+    octx = O.OracleContext(model, 2)
+    anchors = I.gen_anchors(spec, 5)
+    steps = [([100, 7], 0), ([40, 0], 1), ([1, 33], 2)]
+    for n_new, fseed in steps:
+        feats = [I.gen_features(spec, 10 + fseed, b, n) for b, n in enumerate(n_new)]
+        run.ingest(feats)
+        for b in range(2):
+            O.fuse_ctx(model, octx, b, feats[b])
+        assert run.ctx.lengths() == [octx.length(0), octx.length(1)]
+        drafts, logits = run.draft(anchors, 16)
+        assert_parity(logits, drafts, O.draft_block(model, octx, anchors, 16), f"append {n_new}")
+    # roll sequence 0 back and append different positions there
+    run.ctx.truncate(0, 90)
+    O.truncate_ctx(octx, 0, 90)
+    feats = [I.gen_features(spec, 99, 0, 12), I.gen_features(spec, 99, 1, 0)]
+    run.ingest(feats)
+    O.fuse_ctx(model, octx, 0, feats[0])
+    drafts, logits = run.draft(anchors, 16)
+    assert_parity(logits, drafts, O.draft_block(model, octx, anchors, 16), "after truncate")
+
+
+def test_capacity_error_leaves_lengths(torch_cuda):
+    spec = I.spec("tiny").with_(ctx_lens=(10,))
+    w = I.gen_weights(spec, seed=0)
+    run = GpuRun(spec, B.upload_weights(spec, w), capacity=[20], max_new=40)
+    run.ingest(_feats(spec, 1, [10]))
+    with pytest.raises(B.DFlashError) as e:
+        run.ingest(_feats(spec, 1, [11]))
+    assert e.value.name == "DFLASH_ECAPACITY"
+    assert run.ctx.lengths() == [10]
+
+
+def test_draft_is_deterministic(torch_cuda):
+    run, d1, l1 = _tiny_case(I.spec("tiny"), (128, 3), 16, std=0.05, label="determinism")
+    anchors = I.gen_anchors(run.spec, 2)
+    for _ in range(3):
+        d2, l2 = run.draft(anchors, 16)
+        assert np.array_equal(d1, d2)
+        assert np.array_equal(l1.view(np.uint32), l2.view(np.uint32))
+
+
+# ----------------------------------------------------------------------------
+# Qwen3-8B-shaped drafter at the workload sizes
+# ----------------------------------------------------------------------------
+
+def _q8_case(q8, name, seqs=None, n_layers=None, label=""):
+    spec5, w, dev = q8
+    spec = I.spec(name)
+    nl = spec.n_layers
+    dev_w = dev[: 3 + 9 * nl]
+    lens = spec.ctx_lens
+    say(f"{label}: {name} lens[:4]={lens[:4]} n_seqs={len(lens)} block={spec.block} layers={nl}")
+    run = GpuRun(spec, dev_w, capacity=[c + 64 for c in lens], max_new=sum(lens))
+    feats = _feats(spec, 1, lens)
+    run.ingest(feats)
+    anchors = I.gen_anchors(spec, 2)
+    drafts, logits = run.draft(anchors, spec.block)
+    say(f"{label}: GPU pass done; running the oracle on sequences {seqs if seqs else 'all'}")
+    ref = oracle_run(spec, w, feats, anchors, spec.block, seqs=seqs)
+    sel = list(range(len(lens))) if seqs is None else seqs
+    assert_parity(logits[sel], drafts[sel], ref, label)
+    accept_check(drafts[sel], ref, spec, 3, label)
+    return run, drafts, logits
+
+
+def test_q8_ctx1024(q8):
+    _q8_case(q8, "q8b_ctx1024", label="5-layer ctx1024")
+
+
+def test_q8_ctx8192(q8):
+    _q8_case(q8, "q8b_ctx8192", label="5-layer ctx8192")
+
+
+def test_q8_conc32(q8):
+    _q8_case(q8, "q8b_conc32", seqs=[0, 13, 31], label="5-layer conc32")
+
+
+def test_q8_ragged_b32(q8):
+    lens = I.spec("q8b_l3_b32_ragged").ctx_lens
+    seqs = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 3})
+    _q8_case(q8, "q8b_l3_b32_ragged", seqs=seqs, label="3-layer ragged B32")
