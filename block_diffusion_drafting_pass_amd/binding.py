@@ -22,7 +22,11 @@ STATUS = {0: "DFLASH_OK", -1: "DFLASH_EINVAL", -2: "DFLASH_ESHAPE", -3: "DFLASH_
 EXPORTS = ("dflash_weight_count", "dflash_model_create", "dflash_model_destroy", "dflash_ctx_bytes",
            "dflash_ctx_create", "dflash_ctx_destroy", "dflash_ctx_length", "dflash_ctx_truncate",
            "dflash_workspace_bytes", "dflash_fuse_ctx", "dflash_draft_block", "dflash_accept_len",
-           "dflash_status_str", "dflash_last_error")
+           "dflash_probe_arm", "dflash_probe_read", "dflash_status_str", "dflash_last_error")
+
+# Stages a measurement probe can bracket (dflash_stage in include/dflash.h).
+STAGES = {"lm_head": 1, "gate_up": 2, "down": 3, "qkv": 4, "oproj": 5, "attention": 6, "fusion": 7,
+          "kv_proj": 8}
 
 
 class DFlashError(RuntimeError):
@@ -80,6 +84,10 @@ def lib():
         L.dflash_draft_block.restype = ctypes.c_int
         L.dflash_accept_len.argtypes = [vp, vp, i32, i32, vp, vp, vp]
         L.dflash_accept_len.restype = ctypes.c_int
+        L.dflash_probe_arm.argtypes = [vp, ctypes.c_int, i32]
+        L.dflash_probe_arm.restype = ctypes.c_int
+        L.dflash_probe_read.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32), ctypes.POINTER(i32)]
+        L.dflash_probe_read.restype = ctypes.c_int
         L.dflash_status_str.argtypes = [ctypes.c_int]
         L.dflash_status_str.restype = ctypes.c_char_p
         L.dflash_last_error.argtypes = []
@@ -158,6 +166,18 @@ class Context:
             self.handle = None
 
     __del__ = close
+
+
+def probe_arm(model: Model, stage: str, max_launches: int) -> None:
+    """Bracket every later launch of ``stage`` with HIP events (measurement only)."""
+    check(lib().dflash_probe_arm(model.handle, STAGES[stage], int(max_launches)))
+
+
+def probe_read(model: Model):
+    """Wait for the probe's events; return (total_ms, timed_launches, missed) and disarm it."""
+    ms, n, missed = ctypes.c_double(), ctypes.c_int32(), ctypes.c_int32()
+    check(lib().dflash_probe_read(model.handle, ctypes.byref(ms), ctypes.byref(n), ctypes.byref(missed)))
+    return ms.value, n.value, missed.value
 
 
 def workspace_bytes(model: Model, n_seqs: int, block: int, max_new_tokens: int = 0) -> int:

@@ -146,12 +146,42 @@ WsLayout ws_layout(const dflash_config* c, int n_seqs, int block, int64_t max_ne
 
 }  // namespace
 
+// Event pairs bracketing the launches of one stage (measurement only).
+struct Probe {
+  int stage = DFLASH_STAGE_NONE;
+  std::vector<hipEvent_t> ev;  // start, stop, start, stop, ...
+  int used = 0, missed = 0;
+
+  void release() {
+    for (hipEvent_t e : ev) (void)hipEventDestroy(e);
+    ev.clear();
+    stage = DFLASH_STAGE_NONE;
+    used = missed = 0;
+  }
+  bool on(int st) const { return stage == st; }
+  void start(int st, hipStream_t s) {
+    if (stage != st) return;
+    if (2 * used < (int)ev.size()) (void)hipEventRecord(ev[2 * used], s);
+  }
+  void stop(int st, hipStream_t s) {
+    if (stage != st) return;
+    if (2 * used < (int)ev.size()) {
+      (void)hipEventRecord(ev[2 * used + 1], s);
+      ++used;
+    } else {
+      ++missed;
+    }
+  }
+};
+
 struct dflash_model {
   dflash_config cfg;
   const u16* w_fc;
   const u16* embed;
   const u16* final_norm;
   std::vector<LayerW> layers;
+  mutable Probe probe;
+  ~dflash_model() { probe.release(); }
 };
 
 struct dflash_ctx {
@@ -353,7 +383,9 @@ int dflash_fuse_ctx(const dflash_model* model, dflash_ctx* ctx, const void* feat
     f.ep.out_hi = h_hi;
     f.ep.out_lo = h_lo;
     f.ep.ldh = c.hidden;
+    model->probe.start(DFLASH_STAGE_FUSION, s);
     hipError_t e = launch_gemm(f, st, Rp, s);
+    model->probe.stop(DFLASH_STAGE_FUSION, s);
     if (e != hipSuccess) return hip_fail(e, "fuse_ctx: fusion GEMM");
 
     for (int l = 0; l < c.n_layers; ++l) {
@@ -379,7 +411,9 @@ int dflash_fuse_ctx(const dflash_model* model, dflash_ctx* ctx, const void* feat
       g.ep.k_cache = ctx->k_cache(l);
       g.ep.vt_cache = ctx->vt_cache(l);
       g.ep.slots = ctx->L.slots;
+      model->probe.start(DFLASH_STAGE_KV_PROJ, s);
       e = launch_gemm(g, st, Rp, s);
+      model->probe.stop(DFLASH_STAGE_KV_PROJ, s);
       if (e != hipSuccess) return hip_fail(e, "fuse_ctx: K/V projection");
     }
   }
@@ -464,18 +498,24 @@ int dflash_draft_block(const dflash_model* model, const dflash_ctx* ctx, const i
     g.ep.k_cache = ctx->k_cache(l);
     g.ep.vt_cache = ctx->vt_cache(l);
     g.ep.slots = ctx->L.slots;
+    model->probe.start(DFLASH_STAGE_QKV, s);
     e = launch_gemm(g, st, Mp, s);
+    model->probe.stop(DFLASH_STAGE_QKV, s);
     if (e != hipSuccess) return hip_fail(e, "draft_block: QKV projection");
 
+    model->probe.start(DFLASH_STAGE_ATTENTION, s);
     e = launch_attention(q_hi, q_lo, ctx->k_cache(l), ctx->vt_cache(l), ctx->L.slots, part_o, part_ml, a_hi, a_lo,
                          Mp, n, block, c.n_q_heads, c.n_kv_heads, c.head_dim, W.splits, st, s);
+    model->probe.stop(DFLASH_STAGE_ATTENTION, s);
     if (e != hipSuccess) return hip_fail(e, "draft_block: attention");
 
     g = base_args(a_hi, a_lo, QD, QD, H / 16, EPI_RESID, MAP_PLAIN);
     g.w.w0 = Lw.wo;
     g.ep.out_f32 = x;
     g.ep.ldo = H;
+    model->probe.start(DFLASH_STAGE_OPROJ, s);
     e = launch_gemm(g, st, Mp, s);
+    model->probe.stop(DFLASH_STAGE_OPROJ, s);
     if (e != hipSuccess) return hip_fail(e, "draft_block: output projection");
 
     e = launch_rmsnorm_split(x, Lw.mlp_norm, a_hi, a_lo, H, M, Mp, c.rms_eps, s);
@@ -486,14 +526,18 @@ int dflash_draft_block(const dflash_model* model, const dflash_ctx* ctx, const i
     g.ep.out_hi = b_hi;
     g.ep.out_lo = b_lo;
     g.ep.ldh = I;
+    model->probe.start(DFLASH_STAGE_GATE_UP, s);
     e = launch_gemm(g, st, Mp, s);
+    model->probe.stop(DFLASH_STAGE_GATE_UP, s);
     if (e != hipSuccess) return hip_fail(e, "draft_block: gate/up projection");
 
     g = base_args(b_hi, b_lo, I, I, H / 16, EPI_RESID, MAP_PLAIN);
     g.w.w0 = Lw.wdown;
     g.ep.out_f32 = x;
     g.ep.ldo = H;
+    model->probe.start(DFLASH_STAGE_DOWN, s);
     e = launch_gemm(g, st, Mp, s);
+    model->probe.stop(DFLASH_STAGE_DOWN, s);
     if (e != hipSuccess) return hip_fail(e, "draft_block: down projection");
   }
   e = launch_rmsnorm_split(x, model->final_norm, a_hi, a_lo, H, M, Mp, c.rms_eps, s);
@@ -504,10 +548,53 @@ int dflash_draft_block(const dflash_model* model, const dflash_ctx* ctx, const i
   g.ep.logits = logits;
   g.ep.vocab = c.vocab;
   g.ep.block = block;
+  model->probe.start(DFLASH_STAGE_LM_HEAD, s);
   e = launch_gemm(g, st, Mp, s);
+  model->probe.stop(DFLASH_STAGE_LM_HEAD, s);
   if (e != hipSuccess) return hip_fail(e, "draft_block: LM head");
   e = launch_argmax_reduce(amax, c.vocab / 16, Mp, n, block, draft, s);
   if (e != hipSuccess) return hip_fail(e, "draft_block: argmax");
+  return DFLASH_OK;
+}
+
+int dflash_probe_arm(dflash_model* model, int stage, int32_t max_launches) {
+  if (!model) return fail(DFLASH_EINVAL, "model is NULL");
+  if (stage <= DFLASH_STAGE_NONE || stage >= DFLASH_STAGE_COUNT) return fail(DFLASH_EINVAL, "stage %d unknown", stage);
+  if (max_launches < 1 || max_launches > (1 << 20)) return fail(DFLASH_EINVAL, "max_launches %d outside [1, 2^20]", max_launches);
+  Probe& p = model->probe;
+  p.release();
+  p.ev.reserve(2 * (size_t)max_launches);
+  for (int i = 0; i < 2 * max_launches; ++i) {
+    hipEvent_t e;
+    const hipError_t r = hipEventCreate(&e);
+    if (r != hipSuccess) {
+      p.release();
+      return hip_fail(r, "probe_arm: hipEventCreate");
+    }
+    p.ev.push_back(e);
+  }
+  p.stage = stage;
+  return DFLASH_OK;
+}
+
+int dflash_probe_read(dflash_model* model, double* total_ms, int32_t* launches, int32_t* missed) {
+  if (!model || !total_ms || !launches) return fail(DFLASH_EINVAL, "model, total_ms or launches is NULL");
+  Probe& p = model->probe;
+  double sum = 0.0;
+  for (int i = 0; i < p.used; ++i) {
+    hipError_t r = hipEventSynchronize(p.ev[2 * i + 1]);
+    float ms = 0.f;
+    if (r == hipSuccess) r = hipEventElapsedTime(&ms, p.ev[2 * i], p.ev[2 * i + 1]);
+    if (r != hipSuccess) {
+      p.release();
+      return hip_fail(r, "probe_read");
+    }
+    sum += ms;
+  }
+  *total_ms = sum;
+  *launches = p.used;
+  if (missed) *missed = p.missed;
+  p.release();
   return DFLASH_OK;
 }
 

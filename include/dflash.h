@@ -164,6 +164,34 @@ int dflash_draft_block(const dflash_model* model, const dflash_ctx* ctx, const i
 int dflash_accept_len(const int32_t* draft, const int32_t* target, int32_t n_seqs, int32_t block,
                       int32_t* accept, int32_t* next_anchor, dflash_stream stream);
 
+/* Stages of the draft pass that a measurement probe can bracket. */
+typedef enum {
+  DFLASH_STAGE_NONE = 0,
+  DFLASH_STAGE_LM_HEAD = 1,    /* final-norm output x shared embedding, with the argmax partials */
+  DFLASH_STAGE_GATE_UP = 2,    /* gate|up projection with the SwiGLU product (once per layer) */
+  DFLASH_STAGE_DOWN = 3,       /* down projection + residual (once per layer) */
+  DFLASH_STAGE_QKV = 4,        /* q|k|v projection with RoPE and the block K/V write (once per layer) */
+  DFLASH_STAGE_OPROJ = 5,      /* output projection + residual (once per layer) */
+  DFLASH_STAGE_ATTENTION = 6,  /* split-key attention and its merge (once per layer) */
+  DFLASH_STAGE_FUSION = 7,     /* feature fusion GEMM of dflash_fuse_ctx (once per row chunk) */
+  DFLASH_STAGE_KV_PROJ = 8,    /* context K/V projection of dflash_fuse_ctx (per layer and chunk) */
+  DFLASH_STAGE_COUNT = 9
+} dflash_stage;
+
+/* Measurement probe (instrumentation, not part of the method).  After
+ * dflash_probe_arm, every launch of `stage` made by dflash_draft_block or
+ * dflash_fuse_ctx with this model is bracketed by a pair of HIP events
+ * recorded on the call's stream, for up to max_launches launches (later ones
+ * are counted as missed and not timed).  The events are created here (host
+ * API objects, no device memory).  dflash_probe_read waits for the recorded
+ * events, returns the summed duration in milliseconds and the number of timed
+ * launches, then disarms the probe and releases its events.  Arming an armed
+ * probe discards the earlier recording.  One probe per model; not for use
+ * from several host threads at once.  Errors: DFLASH_EINVAL for a bad stage
+ * or count, DFLASH_EHIP if event creation or timing fails. */
+int dflash_probe_arm(dflash_model* model, int stage, int32_t max_launches);
+int dflash_probe_read(dflash_model* model, double* total_ms, int32_t* launches, int32_t* missed);
+
 const char* dflash_status_str(int status);
 const char* dflash_last_error(void);
 

@@ -171,3 +171,18 @@ def test_draft_and_fuse_validation_without_context():
     assert _err(L.dflash_ctx_truncate(None, 0, 0)) == "DFLASH_EINVAL"
     assert L.dflash_ctx_length(None, 0) == -1
     L.dflash_model_destroy(m)
+
+
+def test_probe_validation_and_empty_read():
+    L = _lib()
+    cfg, m = _fake_model()
+    assert _err(L.dflash_probe_arm(None, 1, 4)) == "DFLASH_EINVAL"
+    assert _err(L.dflash_probe_arm(m, 0, 4)) == "DFLASH_EINVAL"
+    assert _err(L.dflash_probe_arm(m, len(B.STAGES) + 1, 4)) == "DFLASH_EINVAL"
+    assert _err(L.dflash_probe_arm(m, B.STAGES["lm_head"], 0)) == "DFLASH_EINVAL"
+    ms, n, missed = ctypes.c_double(-1.0), ctypes.c_int32(-1), ctypes.c_int32(-1)
+    # a probe that was never armed reads as nothing timed, without any device call
+    assert L.dflash_probe_read(m, ctypes.byref(ms), ctypes.byref(n), ctypes.byref(missed)) == 0
+    assert (ms.value, n.value, missed.value) == (0.0, 0, 0)
+    assert _err(L.dflash_probe_read(m, None, ctypes.byref(n), None)) == "DFLASH_EINVAL"
+    L.dflash_model_destroy(m)
