@@ -58,6 +58,7 @@ int check_config(const dflash_config* c) {
   if (c->max_block < 2 || c->max_block > 32) return fail(DFLASH_EUNSUPPORTED, "max_block must be in [2, 32]");
   if (c->head_dim != 64 && c->head_dim != 128) return fail(DFLASH_EUNSUPPORTED, "head_dim must be 64 or 128");
   if (c->n_q_heads % c->n_kv_heads) return fail(DFLASH_ESHAPE, "n_q_heads must be a multiple of n_kv_heads");
+  if (c->n_q_heads / c->n_kv_heads > 8) return fail(DFLASH_EUNSUPPORTED, "at most 8 query heads per kv head");
   if (c->hidden % 256 || c->intermediate % 256 || (c->n_q_heads * c->head_dim) % 256 ||
       ((int64_t)c->n_target_layers * c->hidden) % 256)
     return fail(DFLASH_EUNSUPPORTED, "hidden, intermediate, n_q_heads*head_dim and n_target_layers*hidden must be multiples of 256");
@@ -72,13 +73,14 @@ bool same_config(const dflash_config& a, const dflash_config& b) {
          a.max_block == b.max_block && a.rms_eps == b.rms_eps && a.rope_theta == b.rope_theta;
 }
 
-// Context layout: RoPE cos / sin tables, then per layer the K planes
-// [2][n_kv][slots][d] and the transposed V planes [2][n_kv][d][slots].
+// Context layout: RoPE cos / sin tables, then per layer the tiled K/V cache
+// (kv_tile_offset: per kv head, 64-slot tiles of K hi/lo and transposed V
+// hi/lo planes).  Each sequence owns a whole number of tiles.
 struct CtxLayout {
   std::vector<int64_t> slot_base;
   int64_t slots = 0;
   int64_t max_pos = 0;
-  size_t cos_off = 0, sin_off = 0, kv_off = 0, layer_bytes = 0, k_bytes = 0, total = 0;
+  size_t cos_off = 0, sin_off = 0, kv_off = 0, layer_bytes = 0, total = 0;
 };
 
 int ctx_layout(const dflash_config* c, int32_t n_seqs, const int64_t* cap, CtxLayout* L) {
@@ -88,7 +90,7 @@ int ctx_layout(const dflash_config* c, int32_t n_seqs, const int64_t* cap, CtxLa
   int64_t slots = 0, max_pos = 0;
   for (int b = 0; b < n_seqs; ++b) {
     if (cap[b] < 0) return fail(DFLASH_EINVAL, "capacity[%d] < 0", b);
-    const int64_t s = (cap[b] + c->max_block + 63) / 64 * 64;
+    const int64_t s = (cap[b] + c->max_block + kTileKeys - 1) / kTileKeys * kTileKeys;
     L->slot_base[b] = slots;
     slots += s;
     max_pos = std::max(max_pos, s);
@@ -100,14 +102,13 @@ int ctx_layout(const dflash_config* c, int32_t n_seqs, const int64_t* cap, CtxLa
   L->cos_off = 0;
   L->sin_off = align_up(max_pos * half * sizeof(float));
   L->kv_off = L->sin_off + align_up(max_pos * half * sizeof(float));
-  L->k_bytes = align_up((size_t)2 * c->n_kv_heads * slots * c->head_dim * sizeof(u16));
-  L->layer_bytes = 2 * L->k_bytes;
+  L->layer_bytes = align_up((size_t)4 * c->n_kv_heads * slots * c->head_dim * sizeof(u16));
   L->total = L->kv_off + (size_t)c->n_layers * L->layer_bytes;
   return DFLASH_OK;
 }
 
 struct WsLayout {
-  int M = 0, Mp = 0, units = 0, splits = 0, R = 0, Rp = 0;
+  int M = 0, Mp = 0, max_splits = 0, R = 0, Rp = 0;
   size_t x = 0, a_hi = 0, a_lo = 0, b_hi = 0, b_lo = 0, q_hi = 0, q_lo = 0, part_o = 0, part_ml = 0,
          amax = 0, draft_end = 0;
   size_t h_hi = 0, h_lo = 0, ingest_end = 0;
@@ -119,8 +120,8 @@ WsLayout ws_layout(const dflash_config* c, int n_seqs, int block, int64_t max_ne
   const size_t H = c->hidden, I = c->intermediate, QD = (size_t)c->n_q_heads * c->head_dim;
   W.M = n_seqs * block;
   W.Mp = rows_pad(W.M);
-  W.units = n_seqs * c->n_q_heads * ((block + 15) / 16);
-  W.splits = attention_splits(W.units);
+  const int qtiles = (block + 15) / 16;
+  W.max_splits = attention_max_splits(n_seqs * c->n_kv_heads);
   size_t o = 0;
   auto take = [&](size_t bytes) { const size_t at = o; o += align_up(bytes); return at; };
   const size_t Mp = W.Mp, wa = std::max(H, QD);
@@ -131,8 +132,8 @@ WsLayout ws_layout(const dflash_config* c, int n_seqs, int block, int64_t max_ne
   W.b_lo = take(Mp * I * 2);
   W.q_hi = take(Mp * QD * 2);
   W.q_lo = take(Mp * QD * 2);
-  W.part_o = take((size_t)W.units * W.splits * 16 * c->head_dim * 4);
-  W.part_ml = take((size_t)W.units * W.splits * 32 * 4);
+  W.part_o = take(attention_partial_bytes(n_seqs, c->n_q_heads, qtiles, W.max_splits, c->head_dim));
+  W.part_ml = take(attention_ml_bytes(n_seqs, c->n_q_heads, qtiles, W.max_splits));
   W.amax = take((size_t)(c->vocab / 16) * Mp * 8);
   W.draft_end = o;
   o = 0;
@@ -191,8 +192,8 @@ struct dflash_ctx {
   int n_seqs;
   std::vector<int64_t> cap, len;
   CtxLayout L;
-  u16* k_cache(int l) const { return (u16*)(base + L.kv_off + (size_t)l * L.layer_bytes); }
-  u16* vt_cache(int l) const { return (u16*)(base + L.kv_off + (size_t)l * L.layer_bytes + L.k_bytes); }
+  u16* kv_cache(int l) const { return (u16*)(base + L.kv_off + (size_t)l * L.layer_bytes); }
+  int64_t kv_tiles() const { return L.slots / kTileKeys; }
   const float* rope_cos() const { return (const float*)(base + L.cos_off); }
   const float* rope_sin() const { return (const float*)(base + L.sin_off); }
 };
@@ -408,9 +409,8 @@ int dflash_fuse_ctx(const dflash_model* model, dflash_ctx* ctx, const void* feat
       g.ep.head0 = c.n_q_heads;
       g.ep.rope_cos = ctx->rope_cos();
       g.ep.rope_sin = ctx->rope_sin();
-      g.ep.k_cache = ctx->k_cache(l);
-      g.ep.vt_cache = ctx->vt_cache(l);
-      g.ep.slots = ctx->L.slots;
+      g.ep.kv_cache = ctx->kv_cache(l);
+      g.ep.kv_tiles = ctx->kv_tiles();
       model->probe.start(DFLASH_STAGE_KV_PROJ, s);
       e = launch_gemm(g, st, Rp, s);
       model->probe.stop(DFLASH_STAGE_KV_PROJ, s);
@@ -460,6 +460,10 @@ int dflash_draft_block(const dflash_model* model, const dflash_ctx* ctx, const i
     st.slot_base[b] = (int32_t)ctx->L.slot_base[b];
   }
   st.row_start[n] = n * block;
+  int max_tiles = 1;
+  for (int b = 0; b < n; ++b)
+    max_tiles = std::max<int>(max_tiles, (int)((ctx->len[b] + block + kTileKeys - 1) / kTileKeys));
+  const int splits = std::min(W.max_splits, attention_splits(n * c.n_kv_heads, max_tiles));
 
   auto base_args = [&](const u16* ah, const u16* al, int lda, int K, int n_tiles, int epi, int map) {
     GemmArgs g;
@@ -495,17 +499,16 @@ int dflash_draft_block(const dflash_model* model, const dflash_ctx* ctx, const i
     g.ep.head0 = 0;
     g.ep.rope_cos = ctx->rope_cos();
     g.ep.rope_sin = ctx->rope_sin();
-    g.ep.k_cache = ctx->k_cache(l);
-    g.ep.vt_cache = ctx->vt_cache(l);
-    g.ep.slots = ctx->L.slots;
+    g.ep.kv_cache = ctx->kv_cache(l);
+    g.ep.kv_tiles = ctx->kv_tiles();
     model->probe.start(DFLASH_STAGE_QKV, s);
     e = launch_gemm(g, st, Mp, s);
     model->probe.stop(DFLASH_STAGE_QKV, s);
     if (e != hipSuccess) return hip_fail(e, "draft_block: QKV projection");
 
     model->probe.start(DFLASH_STAGE_ATTENTION, s);
-    e = launch_attention(q_hi, q_lo, ctx->k_cache(l), ctx->vt_cache(l), ctx->L.slots, part_o, part_ml, a_hi, a_lo,
-                         Mp, n, block, c.n_q_heads, c.n_kv_heads, c.head_dim, W.splits, st, s);
+    e = launch_attention(q_hi, q_lo, ctx->kv_cache(l), ctx->kv_tiles(), part_o, part_ml, a_hi, a_lo, n, block,
+                         c.n_q_heads, c.n_kv_heads, c.head_dim, splits, st, s);
     model->probe.stop(DFLASH_STAGE_ATTENTION, s);
     if (e != hipSuccess) return hip_fail(e, "draft_block: attention");
 

@@ -58,9 +58,8 @@ struct EpiParams {
   int n_q, n_kv, head_dim, head0;
   const float* rope_cos;  // [pos][head_dim/2]
   const float* rope_sin;
-  u16* k_cache;   // [2][n_kv][slots][head_dim] bf16 hi/lo planes
-  u16* vt_cache;  // [2][n_kv][head_dim][slots]
-  int64_t slots;
+  u16* kv_cache;   // one layer's injected K/V cache, tiled (see kv_tile_offset)
+  int64_t kv_tiles; // 64-slot tiles per kv head (all sequences)
   // EPI_ARGMAX
   unsigned long long* amax_part;  // [n_tiles][Mp]
   float* logits;                  // [n_seqs][block-1][vocab] or null
@@ -86,17 +85,31 @@ hipError_t launch_embed(float* x, const int32_t* anchors, const u16* embed, int 
 hipError_t launch_rmsnorm_split(const float* x, const u16* gain, u16* out_hi, u16* out_lo, int H,
                                 int M, int Mp, float eps, hipStream_t s);
 hipError_t launch_gemm(const GemmArgs& g, const SeqTable& st, int Mp, hipStream_t s);
-hipError_t launch_attention(const u16* q_hi, const u16* q_lo, const u16* k_cache,
-                            const u16* vt_cache, int64_t slots, float* part_o, float* part_ml,
-                            u16* o_hi, u16* o_lo, int Mp, int n_seqs, int block, int n_q, int n_kv,
-                            int head_dim, int splits, const SeqTable& st, hipStream_t s);
+hipError_t launch_attention(const u16* q_hi, const u16* q_lo, const u16* kv_cache, int64_t kv_tiles,
+                            float* part_o, float* part_ml, u16* o_hi, u16* o_lo, int n_seqs, int block,
+                            int n_q, int n_kv, int head_dim, int splits, const SeqTable& st, hipStream_t s);
 hipError_t launch_argmax_reduce(const unsigned long long* part, int n_tiles, int Mp, int n_seqs,
                                 int block, int32_t* draft, hipStream_t s);
 hipError_t launch_accept(const int32_t* draft, const int32_t* target, int n, int block,
                          int32_t* accept, int32_t* next_anchor, hipStream_t s);
 
-// Number of key splits per (sequence, head, 16-row query tile) unit.
-int attention_splits(int n_units);
-size_t attention_partial_bytes(int n_units, int splits, int head_dim);
+// Injected K/V cache layout of one layer.  Slots are grouped in tiles of
+// kTileKeys; tile t of kv head g is one contiguous block of four planes:
+//   K hi [kTileKeys][d], K lo [kTileKeys][d]      (key-major)
+//   V hi [d][kTileKeys], V lo [d][kTileKeys]      (transposed)
+// so a tile streams from HBM as 4 * kTileKeys * d bf16 values in one piece.
+constexpr int kTileKeys = 64;
+constexpr int kMaxSplits = 64;
+
+__host__ __device__ inline size_t kv_tile_offset(int g, int64_t tile, int64_t kv_tiles, int d) {
+  return ((size_t)g * kv_tiles + tile) * (size_t)(4 * kTileKeys * d);
+}
+
+// Key splits per (sequence, kv head) for the attention pass: enough
+// workgroups to fill the chip, never more than there are tiles.
+int attention_splits(int pairs, int max_tiles);
+int attention_max_splits(int pairs);
+size_t attention_partial_bytes(int n_seqs, int n_q, int qtiles, int splits, int head_dim);
+size_t attention_ml_bytes(int n_seqs, int n_q, int qtiles, int splits);
 
 }  // namespace dflash

@@ -175,18 +175,19 @@ __device__ __forceinline__ void epilogue(const EpiParams& ep, const SeqTable& st
         const size_t o = (size_t)row * ep.ldh + hh * d + dcol;
         ep.out_hi[o] = h;
         ep.out_lo[o] = l;
-      } else if (hh < ep.n_q + ep.n_kv) {
-        const int64_t slot = st.slot_base[b] + pos;
-        const size_t o = ((size_t)(hh - ep.n_q) * ep.slots + slot) * d + dcol;
-        const size_t plane = (size_t)ep.n_kv * ep.slots * d;
-        ep.k_cache[o] = h;
-        ep.k_cache[o + plane] = l;
       } else {
         const int64_t slot = st.slot_base[b] + pos;
-        const size_t o = ((size_t)(hh - ep.n_q - ep.n_kv) * d + dcol) * ep.slots + slot;
-        const size_t plane = (size_t)ep.n_kv * ep.slots * d;
-        ep.vt_cache[o] = h;
-        ep.vt_cache[o + plane] = l;
+        const int sl = (int)(slot % kTileKeys);
+        const bool is_k = hh < ep.n_q + ep.n_kv;
+        const int gk = is_k ? hh - ep.n_q : hh - ep.n_q - ep.n_kv;
+        u16* tb = ep.kv_cache + kv_tile_offset(gk, slot / kTileKeys, ep.kv_tiles, d);
+        if (is_k) {
+          tb[sl * d + dcol] = h;
+          tb[kTileKeys * d + sl * d + dcol] = l;
+        } else {
+          tb[2 * kTileKeys * d + dcol * kTileKeys + sl] = h;
+          tb[3 * kTileKeys * d + dcol * kTileKeys + sl] = l;
+        }
       }
     }
   } else if (EPI == EPI_ARGMAX) {
@@ -397,43 +398,81 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(GemmArgs ga, SeqTable st) {
 }
 
 // ---------------------------------------------------------------------------
-// Attention over [injected context | block] keys, split along the keys.
-// One wave per (sequence, q head, 16-row query tile, key split).  It computes
-// S^T = K Q^T (keys as MFMA rows, so the probabilities land in the register
-// layout the P.V product takes as its B operand), keeps a running max / sum
-// per query row (online softmax), and accumulates O^T = V^T P^T, V^T coming
-// straight from the transposed V cache.  Partial (m, l, O) go to a
-// workspace; the merge kernel combines the splits in a fixed order.
-// Within each 32-key step, MFMA row rho of key tile kt (0 or 1) is key
-// 8 (rho / 4) + 4 kt + rho % 4, so lane group q ends up holding keys
-// 8q .. 8q+7 — exactly one B fragment of the P.V product.
+// Attention over [injected context | block] keys.
+//
+// One workgroup per (sequence, kv head, key split).  Its waves are the query
+// units that read this kv head: (q head of the GQA group) x (16-row query
+// tile); at least four waves are launched so that a cache tile is staged by
+// enough threads (surplus waves only stage).  Each 64-key cache tile is
+// copied once from HBM (contiguous, prefetched into registers while the
+// previous tile is used) into LDS, where every query unit of the group reads
+// it.  Per 32-key half a wave computes S^T = K Q^T with keys as MFMA rows, so
+// that the probabilities land in the register layout the P.V product takes as
+// its B operand, keeps a running max / sum per query row (online softmax) and
+// accumulates O^T = V^T P^T from the transposed V planes.  MFMA row rho of
+// key tile kt (0 or 1) is key 8 (rho / 4) + 4 kt + rho % 4 of the half, so
+// lane group q ends up holding keys 8q .. 8q+7 — exactly one B fragment.
+// fp32 x fp32 products are taken as hi*hi + hi*lo + lo*hi.
+// With one split the result is normalised and written directly; otherwise
+// partial (m, l, O) go to a workspace and the merge kernel combines them in
+// split order.
 // ---------------------------------------------------------------------------
 
-template <int D>
-__global__ __launch_bounds__(256) void k_attn_partial(const u16* __restrict__ q_hi,
-                                                      const u16* __restrict__ q_lo,
-                                                      const u16* __restrict__ k_cache,
-                                                      const u16* __restrict__ vt_cache,
-                                                      int64_t slots, float* __restrict__ part_o,
-                                                      float* __restrict__ part_ml, int n_seqs,
-                                                      int block, int n_q, int n_kv, int splits,
-                                                      int qtiles, float scale, SeqTable st) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int item = blockIdx.x * 4 + wave;
-  if (item >= n_seqs * n_q * qtiles * splits) return;
-  const int unit = item / splits, s = item % splits;
-  const int t = unit % qtiles, h = (unit / qtiles) % n_q, b = unit / (qtiles * n_q);
-  const int gkv = (h * n_kv) / n_q;
-  const int c = lane & 15, g = lane >> 4;
-  const int n_keys = st.pos_base[b] + block;
-  int chunk = (n_keys + splits - 1) / splits;
-  chunk = (chunk + 31) & ~31;
-  const int k0 = s * chunk, k1 = min(n_keys, k0 + chunk);
+// 16-byte chunk swizzles of the LDS copy of a tile (bijections within a row):
+// the 16 keys one K fragment read touches, and the 16 V^T rows one V fragment
+// read touches, fall in distinct bank groups.
+__device__ __forceinline__ int k_swz(int key) { return (((key >> 3) & 3) << 2) | (key & 3); }
+__device__ __forceinline__ int v_swz(int drow) { return (drow >> 1) & 7; }
 
+template <int D>
+__device__ __forceinline__ int lds_chunk(int cidx) {
+  constexpr int CH = D / 8, PL = kTileKeys * CH;  // chunks per K row, per plane
+  const int plane = cidx / PL, w = cidx % PL;
+  if (plane < 2) {
+    const int key = w / CH, ch = w % CH;
+    return plane * PL + key * CH + (ch ^ (k_swz(key) & (CH - 1)));
+  }
+  const int drow = w / 8, ch = w % 8;
+  return plane * PL + drow * 8 + (ch ^ v_swz(drow));
+}
+
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) void k_attn_tiles(const u16* __restrict__ q_hi,
+                                                         const u16* __restrict__ q_lo,
+                                                         const u16* __restrict__ kv, int64_t kv_tiles,
+                                                         float* __restrict__ part_o,
+                                                         float* __restrict__ part_ml,
+                                                         u16* __restrict__ o_hi, u16* __restrict__ o_lo,
+                                                         int block, int n_q, int n_kv, int splits,
+                                                         float scale, SeqTable st) {
+  constexpr int CH = D / 8, PL = kTileKeys * CH;
+  constexpr int TILE_CH = 4 * PL;  // 16-byte chunks per cache tile
+  constexpr int NT = NW * 64;
+  constexpr int CPT = TILE_CH / NT;
+  static_assert(TILE_CH % NT == 0, "tile must split evenly over the threads");
   constexpr int DS = D / 32, DT = D / 16;
-  const int qi = t * 16 + c;
-  const bool qvalid = qi < block;
-  const size_t qoff = (size_t)(b * block + qi) * (n_q * D) + h * D + g * 8;
+  __shared__ u32x4 lds[TILE_CH];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const int s = blockIdx.x % splits;
+  const int pair = blockIdx.x / splits;
+  const int gkv = pair % n_kv, b = pair / n_kv;
+  const int G = n_q / n_kv, qtiles = (block + 15) / 16;
+  const bool comp = wave < G * qtiles;
+  const int h = gkv * G + wave % G, qt = wave / G;
+
+  const int n_keys = st.pos_base[b] + block;
+  const int ntile = (n_keys + kTileKeys - 1) / kTileKeys;
+  const int tps = (ntile + splits - 1) / splits;
+  const int t0 = s * tps, t1 = min(ntile, t0 + tps);
+  const u32x4* src = reinterpret_cast<const u32x4*>(
+      kv + kv_tile_offset(gkv, st.slot_base[b] / kTileKeys, kv_tiles, D));
+
+  const int qi = qt * 16 + c;
+  const bool qvalid = comp && qi < block;
+  const size_t qrow = (size_t)(st.row_start[b] + qi);
+  const size_t qoff = qrow * (n_q * D) + h * D + g * 8;
   bf16x8 qh[DS], ql[DS];
 #pragma unroll
   for (int ds = 0; ds < DS; ++ds) {
@@ -445,45 +484,61 @@ __global__ __launch_bounds__(256) void k_attn_partial(const u16* __restrict__ q_
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, l = 0.f;
 
-  const int64_t slot0 = st.slot_base[b];
-  const size_t kplane = (size_t)n_kv * slots * D;
-  const u16* kbase = k_cache + ((size_t)gkv * slots + slot0) * D + g * 8;
-  const u16* vbase = vt_cache + (size_t)gkv * D * slots + slot0 + g * 8;
-
-  for (int kk = k0; kk < k1; kk += 32) {
-    f32x4 sacc[2];
+  u32x4 stage[CPT];
+  if (t0 < t1) {
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      sacc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int key = kk + 8 * (c >> 2) + 4 * kt + (c & 3);
-      const u16* kp = kbase + (size_t)key * D;
+    for (int j = 0; j < CPT; ++j) stage[j] = src[(size_t)t0 * TILE_CH + tid + j * NT];
+  }
+  for (int t = t0; t < t1; ++t) {
+    __syncthreads();
 #pragma unroll
-      for (int ds = 0; ds < DS; ++ds) {
-        const bf16x8 kh = ld_frag(kp + ds * 32);
-        const bf16x8 kl = ld_frag(kp + kplane + ds * 32);
-        sacc[kt] = mfma(kh, qh[ds], sacc[kt]);
-        sacc[kt] = mfma(kh, ql[ds], sacc[kt]);
-        sacc[kt] = mfma(kl, qh[ds], sacc[kt]);
-      }
+    for (int j = 0; j < CPT; ++j) lds[lds_chunk<D>(tid + j * NT)] = stage[j];
+    __syncthreads();
+    if (t + 1 < t1) {
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) stage[j] = src[(size_t)(t + 1) * TILE_CH + tid + j * NT];
     }
-    float sv[8];
+    if (!comp) continue;
+
+    f32x4 sacc[2][2];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        sacc[hf][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int key = hf * 32 + 8 * (c >> 2) + 4 * kt + (c & 3);
+        const int sw = k_swz(key) & (CH - 1);
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds) {
+          const int ch = (ds * 4 + g) ^ sw;
+          const bf16x8 kh = __builtin_bit_cast(bf16x8, lds[key * CH + ch]);
+          const bf16x8 kl = __builtin_bit_cast(bf16x8, lds[PL + key * CH + ch]);
+          sacc[hf][kt] = mfma(kh, qh[ds], sacc[hf][kt]);
+          sacc[hf][kt] = mfma(kh, ql[ds], sacc[hf][kt]);
+          sacc[hf][kt] = mfma(kl, qh[ds], sacc[hf][kt]);
+        }
+      }
+    const int kbase = t * kTileKeys;
+    float sv[16];
     float mx = -INFINITY;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = kk + 8 * g + 4 * kt + i;
-        const float x = key < k1 ? sacc[kt][i] * scale : -INFINITY;
-        sv[kt * 4 + i] = x;
-        mx = fmaxf(mx, x);
-      }
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = kbase + hf * 32 + 8 * g + 4 * kt + i;
+          const float x = key < n_keys ? sacc[hf][kt][i] * scale : -INFINITY;
+          sv[hf * 8 + kt * 4 + i] = x;
+          mx = fmaxf(mx, x);
+        }
     mx = fmaxf(mx, shfl_xor_f(mx, 16));
     mx = fmaxf(mx, shfl_xor_f(mx, 32));
     const float m_new = fmaxf(m, mx);
     const float corr = expf(m - m_new);
-    float p[8], ps = 0.f;
+    float p[16], ps = 0.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < 16; ++j) {
       p[j] = expf(sv[j] - m_new);
       ps += p[j];
     }
@@ -491,57 +546,79 @@ __global__ __launch_bounds__(256) void k_attn_partial(const u16* __restrict__ q_
     ps += shfl_xor_f(ps, 32);
     l = l * corr + ps;
     m = m_new;
-    bf16x8 ph, pl;
-    split_frag(p, ph, pl);
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const u16* vp = vbase + (size_t)(dt * 16 + c) * slots + kk;
-      const bf16x8 vh = ld_frag(vp);
-      const bf16x8 vl = ld_frag(vp + kplane);
-      f32x4 acc = o[dt] * corr;
-      acc = mfma(vh, ph, acc);
-      acc = mfma(vh, pl, acc);
-      acc = mfma(vl, ph, acc);
-      o[dt] = acc;
+    for (int dt = 0; dt < DT; ++dt) o[dt] *= corr;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      bf16x8 ph, pl;
+      split_frag(p + hf * 8, ph, pl);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int drow = dt * 16 + c;
+        const int ch = (hf * 4 + g) ^ v_swz(drow);
+        const bf16x8 vh = __builtin_bit_cast(bf16x8, lds[2 * PL + drow * 8 + ch]);
+        const bf16x8 vl = __builtin_bit_cast(bf16x8, lds[3 * PL + drow * 8 + ch]);
+        o[dt] = mfma(vh, ph, o[dt]);
+        o[dt] = mfma(vh, pl, o[dt]);
+        o[dt] = mfma(vl, ph, o[dt]);
+      }
     }
   }
-  float* po = part_o + (size_t)item * 16 * D + c * D + g * 4;
+  if (!comp) return;
+  if (splits == 1) {
+    if (!qvalid) return;
+    const float inv = 1.0f / l;
+    const size_t ob = qrow * (n_q * D) + h * D + g * 4;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        u16 hv, lv;
+        split_pair(o[dt][i] * inv, hv, lv);
+        o_hi[ob + dt * 16 + i] = hv;
+        o_lo[ob + dt * 16 + i] = lv;
+      }
+    return;
+  }
+  const size_t pidx = ((size_t)(b * n_q + h) * qtiles + qt) * splits + s;
+  float* po = part_o + pidx * 16 * D + c * D + g * 4;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16) = o[dt];
   if (g == 0) {
-    part_ml[(size_t)item * 32 + c] = m;
-    part_ml[(size_t)item * 32 + 16 + c] = l;
+    part_ml[pidx * 32 + c] = m;
+    part_ml[pidx * 32 + 16 + c] = l;
   }
 }
 
-// Combine the key splits of each unit (fixed order) and write the attention
-// output as hi/lo planes [row][n_q * D].
+// Combine the key splits (fixed split order) of every output element and
+// write the attention output as hi/lo planes [row][n_q * D].
 template <int D>
 __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ part_o,
                                                     const float* __restrict__ part_ml,
                                                     u16* __restrict__ o_hi, u16* __restrict__ o_lo,
-                                                    int block, int n_q, int splits, int qtiles) {
-  const int unit = blockIdx.x;
-  const int t = unit % qtiles, h = (unit / qtiles) % n_q, b = unit / (qtiles * n_q);
-  const float* ml = part_ml + (size_t)unit * splits * 32;
-  for (int idx = threadIdx.x; idx < 16 * D; idx += blockDim.x) {
-    const int row = idx / D, dcol = idx % D;
-    const int qi = t * 16 + row;
-    if (qi >= block) continue;
-    float M = -INFINITY;
-    for (int s = 0; s < splits; ++s) M = fmaxf(M, ml[s * 32 + row]);
-    float L = 0.f, acc = 0.f;
-    for (int s = 0; s < splits; ++s) {
-      const float w = expf(ml[s * 32 + row] - M);
-      L += ml[s * 32 + 16 + row] * w;
-      acc += part_o[((size_t)(unit * splits + s) * 16 + row) * D + dcol] * w;
-    }
-    u16 hi, lo;
-    split_pair(acc / L, hi, lo);
-    const size_t o = (size_t)(b * block + qi) * (n_q * D) + h * D + dcol;
-    o_hi[o] = hi;
-    o_lo[o] = lo;
+                                                    int block, int n_q, int splits, int total, SeqTable st) {
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= total) return;
+  const int dcol = idx % D;
+  int r = idx / D;
+  const int qi = r % block;
+  r /= block;
+  const int h = r % n_q, b = r / n_q;
+  const int qtiles = (block + 15) / 16, qt = qi / 16, row = qi % 16;
+  const size_t p0 = ((size_t)(b * n_q + h) * qtiles + qt) * splits;
+  float M = -INFINITY;
+  for (int s = 0; s < splits; ++s) M = fmaxf(M, part_ml[(p0 + s) * 32 + row]);
+  float L = 0.f, acc = 0.f;
+  for (int s = 0; s < splits; ++s) {
+    const float w = expf(part_ml[(p0 + s) * 32 + row] - M);
+    L += part_ml[(p0 + s) * 32 + 16 + row] * w;
+    acc += part_o[((p0 + s) * 16 + row) * D + dcol] * w;
   }
+  u16 hi, lo;
+  split_pair(acc / L, hi, lo);
+  const size_t o = (size_t)(st.row_start[b] + qi) * (n_q * D) + h * D + dcol;
+  o_hi[o] = hi;
+  o_lo[o] = lo;
 }
 
 // ---------------------------------------------------------------------------
@@ -709,40 +786,61 @@ hipError_t launch_gemm(const GemmArgs& g, const SeqTable& st, int Mp, hipStream_
   }
 }
 
-int attention_splits(int n_units) {
-  int s = (2048 + n_units - 1) / n_units;
-  return s < 1 ? 1 : (s > 64 ? 64 : s);
+int attention_max_splits(int pairs) {
+  const int s = (512 + pairs - 1) / pairs;
+  return s < 1 ? 1 : (s > kMaxSplits ? kMaxSplits : s);
 }
 
-size_t attention_partial_bytes(int n_units, int splits, int head_dim) {
-  return (size_t)n_units * splits * 16 * head_dim * sizeof(float) +
-         (size_t)n_units * splits * 32 * sizeof(float);
+int attention_splits(int pairs, int max_tiles) {
+  const int s = attention_max_splits(pairs);
+  return max_tiles < s ? (max_tiles < 1 ? 1 : max_tiles) : s;
 }
 
-hipError_t launch_attention(const u16* q_hi, const u16* q_lo, const u16* k_cache,
-                            const u16* vt_cache, int64_t slots, float* part_o, float* part_ml,
-                            u16* o_hi, u16* o_lo, int Mp, int n_seqs, int block, int n_q, int n_kv,
-                            int head_dim, int splits, const SeqTable& st, hipStream_t s) {
-  (void)Mp;
-  const int qtiles = (block + 15) / 16;
-  const int units = n_seqs * n_q * qtiles;
-  const int items = units * splits;
-  const float scale = (float)(1.0 / sqrt((double)head_dim));
-  const dim3 grid((items + 3) / 4);
-  if (head_dim == 128) {
-    hipLaunchKernelGGL(k_attn_partial<128>, grid, dim3(256), 0, s, q_hi, q_lo, k_cache, vt_cache, slots,
-                       part_o, part_ml, n_seqs, block, n_q, n_kv, splits, qtiles, scale, st);
-    hipLaunchKernelGGL(k_attn_merge<128>, dim3(units), dim3(256), 0, s, part_o, part_ml, o_hi, o_lo, block,
-                       n_q, splits, qtiles);
-  } else if (head_dim == 64) {
-    hipLaunchKernelGGL(k_attn_partial<64>, grid, dim3(256), 0, s, q_hi, q_lo, k_cache, vt_cache, slots,
-                       part_o, part_ml, n_seqs, block, n_q, n_kv, splits, qtiles, scale, st);
-    hipLaunchKernelGGL(k_attn_merge<64>, dim3(units), dim3(256), 0, s, part_o, part_ml, o_hi, o_lo, block,
-                       n_q, splits, qtiles);
-  } else {
+size_t attention_partial_bytes(int n_seqs, int n_q, int qtiles, int splits, int head_dim) {
+  return (size_t)n_seqs * n_q * qtiles * splits * 16 * head_dim * sizeof(float);
+}
+
+size_t attention_ml_bytes(int n_seqs, int n_q, int qtiles, int splits) {
+  return (size_t)n_seqs * n_q * qtiles * splits * 32 * sizeof(float);
+}
+
+template <int D>
+static hipError_t attention_dispatch(const u16* q_hi, const u16* q_lo, const u16* kv, int64_t kv_tiles,
+                                     float* part_o, float* part_ml, u16* o_hi, u16* o_lo, int n_seqs,
+                                     int block, int n_q, int n_kv, int splits, const SeqTable& st,
+                                     hipStream_t s) {
+  const int units = (n_q / n_kv) * ((block + 15) / 16);
+  const float scale = (float)(1.0 / sqrt((double)D));
+  const dim3 grid(n_seqs * n_kv * splits);
+  if (units <= 4)
+    hipLaunchKernelGGL((k_attn_tiles<D, 4>), grid, dim3(256), 0, s, q_hi, q_lo, kv, kv_tiles, part_o, part_ml,
+                       o_hi, o_lo, block, n_q, n_kv, splits, scale, st);
+  else if (units <= 8)
+    hipLaunchKernelGGL((k_attn_tiles<D, 8>), grid, dim3(512), 0, s, q_hi, q_lo, kv, kv_tiles, part_o, part_ml,
+                       o_hi, o_lo, block, n_q, n_kv, splits, scale, st);
+  else if (units <= 16)
+    hipLaunchKernelGGL((k_attn_tiles<D, 16>), grid, dim3(1024), 0, s, q_hi, q_lo, kv, kv_tiles, part_o,
+                       part_ml, o_hi, o_lo, block, n_q, n_kv, splits, scale, st);
+  else
     return hipErrorInvalidValue;
+  if (splits > 1) {
+    const int total = n_seqs * n_q * block * D;
+    hipLaunchKernelGGL(k_attn_merge<D>, dim3((total + 255) / 256), dim3(256), 0, s, part_o, part_ml, o_hi, o_lo,
+                       block, n_q, splits, total, st);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_attention(const u16* q_hi, const u16* q_lo, const u16* kv_cache, int64_t kv_tiles,
+                            float* part_o, float* part_ml, u16* o_hi, u16* o_lo, int n_seqs, int block,
+                            int n_q, int n_kv, int head_dim, int splits, const SeqTable& st, hipStream_t s) {
+  if (head_dim == 128)
+    return attention_dispatch<128>(q_hi, q_lo, kv_cache, kv_tiles, part_o, part_ml, o_hi, o_lo, n_seqs, block,
+                                   n_q, n_kv, splits, st, s);
+  if (head_dim == 64)
+    return attention_dispatch<64>(q_hi, q_lo, kv_cache, kv_tiles, part_o, part_ml, o_hi, o_lo, n_seqs, block, n_q,
+                                  n_kv, splits, st, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_argmax_reduce(const unsigned long long* part, int n_tiles, int Mp, int n_seqs,

@@ -64,8 +64,9 @@ typedef enum {
 
 /* Drafter hyper-parameters.  Supported: head_dim 64 or 128; hidden,
  * intermediate, n_q_heads*head_dim and n_target_layers*hidden multiples of
- * 256; n_q_heads a multiple of n_kv_heads; vocab a multiple of 16;
- * 2 <= max_block <= 32.  mask_token_id is an ordinary embedding row. */
+ * 256; n_q_heads a multiple of n_kv_heads with at most 8 query heads per kv
+ * head; vocab a multiple of 64; 2 <= max_block <= 32.  mask_token_id is an
+ * ordinary embedding row. */
 typedef struct {
   int32_t n_layers;
   int32_t hidden;
@@ -98,11 +99,13 @@ int dflash_model_create(const dflash_config* cfg, const void* const* weights, df
 void dflash_model_destroy(dflash_model* model);
 
 /* Device bytes needed for a context of n_seqs sequences holding up to
- * capacity[b] verified positions each (host array).  The layout keeps, per
- * layer, K as [hi/lo][kv_head][slot][d] and V transposed as
- * [hi/lo][kv_head][d][slot] (bf16 pairs carrying fp32 values), a per-sequence
- * headroom of max_block slots that dflash_draft_block writes its block K/V
- * into, and an fp32 RoPE cos/sin table computed in fp64 on the host.
+ * capacity[b] verified positions each (host array).  Per layer and kv head
+ * the cache is a run of 64-slot tiles, each one contiguous block of four
+ * planes: K hi and K lo as [slot][d], V hi and V lo transposed as [d][slot]
+ * (bf16 pairs carrying fp32 values, 8 bytes per cached element pair).  Each
+ * sequence owns whole tiles covering its capacity plus a headroom of
+ * max_block slots that dflash_draft_block writes its block K/V into.  An fp32
+ * RoPE cos/sin table computed in fp64 on the host precedes the cache.
  * Returns 0 if the arguments are invalid. */
 size_t dflash_ctx_bytes(const dflash_config* cfg, int32_t n_seqs, const int64_t* capacity);
 

@@ -186,3 +186,12 @@ def test_probe_validation_and_empty_read():
     assert (ms.value, n.value, missed.value) == (0.0, 0, 0)
     assert _err(L.dflash_probe_read(m, None, ctypes.byref(n), None)) == "DFLASH_EINVAL"
     L.dflash_model_destroy(m)
+
+
+def test_model_create_rejects_wide_gqa_groups():
+    L = _lib()
+    cfg = _cfg("q8b_ctx1024", n_kv_heads=2)  # 16 query heads per kv head
+    n = L.dflash_weight_count(ctypes.byref(cfg))
+    ptrs = (ctypes.c_void_p * n)(*([0x10000] * n))
+    h = ctypes.c_void_p()
+    assert _err(L.dflash_model_create(ctypes.byref(cfg), ptrs, ctypes.byref(h))) == "DFLASH_EUNSUPPORTED"
