@@ -110,10 +110,18 @@ int ctx_layout(const dflash_config* c, int32_t n_seqs, const int64_t* cap, CtxLa
 struct WsLayout {
   int M = 0, Mp = 0, max_splits = 0, R = 0, Rp = 0;
   size_t x = 0, a_hi = 0, a_lo = 0, b_hi = 0, b_lo = 0, q_hi = 0, q_lo = 0, part_o = 0, part_ml = 0,
-         amax = 0, draft_end = 0;
-  size_t h_hi = 0, h_lo = 0, ingest_end = 0;
+         amax = 0, part = 0, draft_end = 0;
+  size_t h_hi = 0, h_lo = 0, part_f = 0, ingest_end = 0;
   size_t total() const { return std::max(draft_end, ingest_end); }
 };
+
+// fp32 bytes of the K-chunk partial sums of one skinny GEMM (rows padded to Mp).
+size_t skinny_part_bytes(int n_tiles, int K, int Mp, int N) {
+  return (size_t)skinny_plan(n_tiles, K, true).kc * Mp * N * sizeof(float);
+}
+
+// Layers covered by one all-layer K/V projection launch.
+int kv_group(const dflash_config* c) { return std::min(c->n_layers, kMaxKvLayers); }
 
 WsLayout ws_layout(const dflash_config* c, int n_seqs, int block, int64_t max_new) {
   WsLayout W;
@@ -135,12 +143,27 @@ WsLayout ws_layout(const dflash_config* c, int n_seqs, int block, int64_t max_ne
   W.part_o = take(attention_partial_bytes(n_seqs, c->n_q_heads, qtiles, W.max_splits, c->head_dim));
   W.part_ml = take(attention_ml_bytes(n_seqs, c->n_q_heads, qtiles, W.max_splits));
   W.amax = take((size_t)(c->vocab / 16) * Mp * 8);
+  if (W.Mp <= 32) {
+    const int nqkv = (c->n_q_heads + 2 * c->n_kv_heads) * c->head_dim;
+    size_t pb = skinny_part_bytes(nqkv / 16, (int)H, W.Mp, nqkv);
+    pb = std::max(pb, skinny_part_bytes((int)H / 16, (int)QD, W.Mp, (int)H));
+    pb = std::max(pb, skinny_part_bytes((int)H / 16, (int)I, W.Mp, (int)H));
+    W.part = take(pb);
+  }
   W.draft_end = o;
   o = 0;
   W.R = (int)std::min<int64_t>(std::max<int64_t>(max_new, 0), kIngestChunk);
   W.Rp = W.R > 0 ? rows_pad(W.R) : 0;
   W.h_hi = take((size_t)W.Rp * H * 2);
   W.h_lo = take((size_t)W.Rp * H * 2);
+  if (W.R > 0) {
+    // a chunk of at most 32 rows takes the skinny path with K-chunk partials
+    const int fw = c->n_target_layers * c->hidden, kd2 = 2 * c->n_kv_heads * c->head_dim;
+    size_t pb = skinny_part_bytes((int)H / 16, fw, 32, (int)H);
+    for (int nl = 1; nl <= kv_group(c); ++nl)  // the last layer group may be smaller
+      pb = std::max(pb, skinny_part_bytes(nl * kd2 / 16, (int)H, 32, nl * kd2));
+    W.part_f = take(pb);
+  }
   W.ingest_end = o;
   return W;
 }
@@ -347,6 +370,7 @@ int dflash_fuse_ctx(const dflash_model* model, dflash_ctx* ctx, const void* feat
   char* wsb = (char*)ws;
   u16* h_hi = (u16*)(wsb + W.h_hi);
   u16* h_lo = (u16*)(wsb + W.h_lo);
+  float* part_f = (float*)(wsb + W.part_f);
   const int fw = c.n_target_layers * c.hidden;
   std::vector<int64_t> gstart(ctx->n_seqs + 1, 0);
   for (int b = 0; b < ctx->n_seqs; ++b) gstart[b + 1] = gstart[b] + n_new[b];
@@ -378,14 +402,61 @@ int dflash_fuse_ctx(const dflash_model* model, dflash_ctx* ctx, const void* feat
     f.n_tiles = c.hidden / 16;
     f.w.w0 = model->w_fc;
     f.map = MAP_PLAIN;
-    f.epi = EPI_SPLIT;
     f.ep.M = R;
     f.ep.Mp = Rp;
+    hipError_t e;
+    if (Rp <= 32) {
+      // few rows: weight-streaming GEMMs with K-chunk partials, then small
+      // kernels that sum the chunks in order and finish each output
+      f.epi = EPI_PARTIAL;
+      f.ep.out_f32 = part_f;
+      f.ep.ldo = c.hidden;
+      const int kcf = skinny_plan(f.n_tiles, f.K, true).kc;
+      model->probe.start(DFLASH_STAGE_FUSION, s);
+      e = launch_gemm(f, st, Rp, s);
+      if (e == hipSuccess) e = launch_reduce_split(part_f, kcf, c.hidden, h_hi, h_lo, R, Rp, s);
+      model->probe.stop(DFLASH_STAGE_FUSION, s);
+      if (e != hipSuccess) return hip_fail(e, "fuse_ctx: fusion GEMM");
+      const int lg = kv_group(&c);
+      for (int l0 = 0; l0 < c.n_layers; l0 += lg) {
+        const int nl = std::min(lg, c.n_layers - l0);
+        GemmArgs g;
+        memset(&g, 0, sizeof(g));
+        g.a_hi = h_hi;
+        g.a_lo = h_lo;
+        g.lda = c.hidden;
+        g.a_rows = Rp;
+        g.K = c.hidden;
+        g.n_tiles = nl * 2 * c.n_kv_heads * c.head_dim / 16;
+        for (int j = 0; j < nl; ++j) {
+          g.w.wk[j] = model->layers[l0 + j].wk;
+          g.w.wv[j] = model->layers[l0 + j].wv;
+        }
+        g.map = MAP_KVL;
+        g.epi = EPI_PARTIAL;
+        g.ep.M = R;
+        g.ep.Mp = Rp;
+        g.ep.n_kv = c.n_kv_heads;
+        g.ep.head_dim = c.head_dim;
+        g.ep.out_f32 = part_f;
+        g.ep.ldo = g.n_tiles * 16;
+        const int kck = skinny_plan(g.n_tiles, g.K, true).kc;
+        model->probe.start(DFLASH_STAGE_KV_PROJ, s);
+        e = launch_gemm(g, st, Rp, s);
+        if (e == hipSuccess)
+          e = launch_kv_finish(part_f, kck, R, Rp, nl, c.n_kv_heads, c.head_dim, ctx->rope_cos(), ctx->rope_sin(),
+                               ctx->kv_cache(l0), ctx->L.layer_bytes / sizeof(u16), ctx->kv_tiles(), st, s);
+        model->probe.stop(DFLASH_STAGE_KV_PROJ, s);
+        if (e != hipSuccess) return hip_fail(e, "fuse_ctx: K/V projection");
+      }
+      continue;
+    }
+    f.epi = EPI_SPLIT;
     f.ep.out_hi = h_hi;
     f.ep.out_lo = h_lo;
     f.ep.ldh = c.hidden;
     model->probe.start(DFLASH_STAGE_FUSION, s);
-    hipError_t e = launch_gemm(f, st, Rp, s);
+    e = launch_gemm(f, st, Rp, s);
     model->probe.stop(DFLASH_STAGE_FUSION, s);
     if (e != hipSuccess) return hip_fail(e, "fuse_ctx: fusion GEMM");
 
@@ -398,7 +469,9 @@ int dflash_fuse_ctx(const dflash_model* model, dflash_ctx* ctx, const void* feat
       g.a_rows = Rp;
       g.K = c.hidden;
       g.n_tiles = 2 * c.n_kv_heads * c.head_dim / 16;
-      g.w = WeightSeg{model->layers[l].wq, model->layers[l].wk, model->layers[l].wv};
+      g.w.w0 = model->layers[l].wq;
+      g.w.w1 = model->layers[l].wk;
+      g.w.w2 = model->layers[l].wv;
       g.map = MAP_ROPE;
       g.epi = EPI_QKV;
       g.ep.M = R;
@@ -449,6 +522,7 @@ int dflash_draft_block(const dflash_model* model, const dflash_ctx* ctx, const i
   float* part_o = (float*)(wsb + W.part_o);
   float* part_ml = (float*)(wsb + W.part_ml);
   unsigned long long* amax = (unsigned long long*)(wsb + W.amax);
+  float* part = (float*)(wsb + W.part);
   const int M = W.M, Mp = W.Mp, H = c.hidden, QD = c.n_q_heads * c.head_dim, I = c.intermediate;
 
   SeqTable st;
@@ -481,28 +555,48 @@ int dflash_draft_block(const dflash_model* model, const dflash_ctx* ctx, const i
     return g;
   };
 
-  hipError_t e = launch_embed(x, anchors, model->embed, H, M, Mp, block, c.mask_token_id, c.vocab, s);
-  if (e != hipSuccess) return hip_fail(e, "draft_block: embed");
+  // Few rows (<= 32): weight-streaming GEMMs; the narrow ones split K over
+  // workgroups into partials that the following small kernel sums in order
+  // (residual + RMSNorm, or RoPE + cache write).  Many rows: tiled GEMMs that
+  // apply residual / RoPE epilogues directly.
+  const bool skinny = Mp <= 32;
+  const int nqkv = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
+  const int kc_qkv = skinny_plan(nqkv / 16, H, true).kc;
+  const int kc_o = skinny_plan(H / 16, QD, true).kc;
+  const int kc_d = skinny_plan(H / 16, I, true).kc;
+
+  hipError_t e = launch_resid_norm(x, nullptr, 0, anchors, model->embed, block, c.mask_token_id, c.vocab,
+                                   model->layers[0].attn_norm, a_hi, a_lo, H, M, Mp, c.rms_eps, s);
+  if (e != hipSuccess) return hip_fail(e, "draft_block: embed + attention norm");
   for (int l = 0; l < c.n_layers; ++l) {
     const LayerW& Lw = model->layers[l];
-    e = launch_rmsnorm_split(x, Lw.attn_norm, a_hi, a_lo, H, M, Mp, c.rms_eps, s);
-    if (e != hipSuccess) return hip_fail(e, "draft_block: attention norm");
-
-    GemmArgs g = base_args(a_hi, a_lo, H, H, (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim / 16, EPI_QKV, MAP_ROPE);
-    g.w = WeightSeg{Lw.wq, Lw.wk, Lw.wv};
-    g.ep.out_hi = q_hi;
-    g.ep.out_lo = q_lo;
-    g.ep.ldh = QD;
+    GemmArgs g;
+    if (skinny) {
+      g = base_args(a_hi, a_lo, H, H, nqkv / 16, EPI_PARTIAL, MAP_QKV);
+      g.ep.out_f32 = part;
+      g.ep.ldo = nqkv;
+    } else {
+      g = base_args(a_hi, a_lo, H, H, nqkv / 16, EPI_QKV, MAP_ROPE);
+      g.ep.out_hi = q_hi;
+      g.ep.out_lo = q_lo;
+      g.ep.ldh = QD;
+      g.ep.head0 = 0;
+      g.ep.rope_cos = ctx->rope_cos();
+      g.ep.rope_sin = ctx->rope_sin();
+      g.ep.kv_cache = ctx->kv_cache(l);
+      g.ep.kv_tiles = ctx->kv_tiles();
+    }
+    g.w.w0 = Lw.wq;
+    g.w.w1 = Lw.wk;
+    g.w.w2 = Lw.wv;
     g.ep.n_q = c.n_q_heads;
     g.ep.n_kv = c.n_kv_heads;
     g.ep.head_dim = c.head_dim;
-    g.ep.head0 = 0;
-    g.ep.rope_cos = ctx->rope_cos();
-    g.ep.rope_sin = ctx->rope_sin();
-    g.ep.kv_cache = ctx->kv_cache(l);
-    g.ep.kv_tiles = ctx->kv_tiles();
     model->probe.start(DFLASH_STAGE_QKV, s);
     e = launch_gemm(g, st, Mp, s);
+    if (e == hipSuccess && skinny)
+      e = launch_qkv_finish(part, kc_qkv, M, Mp, c.n_q_heads, c.n_kv_heads, c.head_dim, ctx->rope_cos(),
+                            ctx->rope_sin(), q_hi, q_lo, ctx->kv_cache(l), ctx->kv_tiles(), st, s);
     model->probe.stop(DFLASH_STAGE_QKV, s);
     if (e != hipSuccess) return hip_fail(e, "draft_block: QKV projection");
 
@@ -512,20 +606,22 @@ int dflash_draft_block(const dflash_model* model, const dflash_ctx* ctx, const i
     model->probe.stop(DFLASH_STAGE_ATTENTION, s);
     if (e != hipSuccess) return hip_fail(e, "draft_block: attention");
 
-    g = base_args(a_hi, a_lo, QD, QD, H / 16, EPI_RESID, MAP_PLAIN);
+    g = base_args(a_hi, a_lo, QD, QD, H / 16, skinny ? EPI_PARTIAL : EPI_RESID, MAP_PLAIN);
     g.w.w0 = Lw.wo;
-    g.ep.out_f32 = x;
+    g.ep.out_f32 = skinny ? part : x;
     g.ep.ldo = H;
     model->probe.start(DFLASH_STAGE_OPROJ, s);
     e = launch_gemm(g, st, Mp, s);
     model->probe.stop(DFLASH_STAGE_OPROJ, s);
     if (e != hipSuccess) return hip_fail(e, "draft_block: output projection");
 
-    e = launch_rmsnorm_split(x, Lw.mlp_norm, a_hi, a_lo, H, M, Mp, c.rms_eps, s);
+    e = launch_resid_norm(x, skinny ? part : nullptr, skinny ? kc_o : 0, nullptr, nullptr, block, 0, c.vocab,
+                          Lw.mlp_norm, a_hi, a_lo, H, M, Mp, c.rms_eps, s);
     if (e != hipSuccess) return hip_fail(e, "draft_block: MLP norm");
 
     g = base_args(a_hi, a_lo, H, H, I / 8, EPI_SWIGLU, MAP_SWIGLU);
-    g.w = WeightSeg{Lw.wgate, Lw.wup, nullptr};
+    g.w.w0 = Lw.wgate;
+    g.w.w1 = Lw.wup;
     g.ep.out_hi = b_hi;
     g.ep.out_lo = b_lo;
     g.ep.ldh = I;
@@ -534,17 +630,20 @@ int dflash_draft_block(const dflash_model* model, const dflash_ctx* ctx, const i
     model->probe.stop(DFLASH_STAGE_GATE_UP, s);
     if (e != hipSuccess) return hip_fail(e, "draft_block: gate/up projection");
 
-    g = base_args(b_hi, b_lo, I, I, H / 16, EPI_RESID, MAP_PLAIN);
+    g = base_args(b_hi, b_lo, I, I, H / 16, skinny ? EPI_PARTIAL : EPI_RESID, MAP_PLAIN);
     g.w.w0 = Lw.wdown;
-    g.ep.out_f32 = x;
+    g.ep.out_f32 = skinny ? part : x;
     g.ep.ldo = H;
     model->probe.start(DFLASH_STAGE_DOWN, s);
     e = launch_gemm(g, st, Mp, s);
     model->probe.stop(DFLASH_STAGE_DOWN, s);
     if (e != hipSuccess) return hip_fail(e, "draft_block: down projection");
+
+    const u16* next_gain = l + 1 < c.n_layers ? model->layers[l + 1].attn_norm : model->final_norm;
+    e = launch_resid_norm(x, skinny ? part : nullptr, skinny ? kc_d : 0, nullptr, nullptr, block, 0, c.vocab,
+                          next_gain, a_hi, a_lo, H, M, Mp, c.rms_eps, s);
+    if (e != hipSuccess) return hip_fail(e, "draft_block: residual + norm");
   }
-  e = launch_rmsnorm_split(x, model->final_norm, a_hi, a_lo, H, M, Mp, c.rms_eps, s);
-  if (e != hipSuccess) return hip_fail(e, "draft_block: final norm");
   GemmArgs g = base_args(a_hi, a_lo, H, H, c.vocab / 16, EPI_ARGMAX, MAP_PLAIN);
   g.w.w0 = model->embed;
   g.ep.amax_part = amax;
@@ -555,7 +654,7 @@ int dflash_draft_block(const dflash_model* model, const dflash_ctx* ctx, const i
   e = launch_gemm(g, st, Mp, s);
   model->probe.stop(DFLASH_STAGE_LM_HEAD, s);
   if (e != hipSuccess) return hip_fail(e, "draft_block: LM head");
-  e = launch_argmax_reduce(amax, c.vocab / 16, Mp, n, block, draft, s);
+  e = launch_argmax_reduce(amax, argmax_parts(c.vocab / 16, Mp), Mp, n, block, draft, s);
   if (e != hipSuccess) return hip_fail(e, "draft_block: argmax");
   return DFLASH_OK;
 }

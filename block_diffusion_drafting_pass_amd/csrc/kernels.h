@@ -9,6 +9,7 @@ namespace dflash {
 typedef uint16_t u16;
 
 constexpr int kMaxSeqs = 128;
+constexpr int kMaxKvLayers = 8;  // layers one all-layer K/V projection launch covers
 
 // Per-call sequence table, passed to kernels by value.  Rows of sequence b in
 // the current row space are [row_start[b], row_start[b+1]); row r of sequence
@@ -26,42 +27,48 @@ enum MapKind : int {
   MAP_PLAIN = 0,   // row 16 t + c of w0
   MAP_ROPE = 1,    // head-structured [q | k | v]: cols c and c^8 are a RoPE pair
   MAP_SWIGLU = 2,  // c < 8: row 8 t + c of w0 (gate); c >= 8: row 8 t + c - 8 of w1 (up)
+  MAP_QKV = 3,     // row 16 t + c of the stacked [w0; w1; w2] (q rows, k rows, v rows)
+  MAP_KVL = 4,     // row 16 t + c of the stacked [wk_0; wv_0; wk_1; wv_1; ...] of all layers
 };
 
 // Epilogues applied to a finished 16x16 fp32 tile.
 enum EpiKind : int {
-  EPI_F32 = 0,     // out_f32[row][16 t + c] = y
-  EPI_SPLIT = 1,   // out_hi/lo[row][16 t + c] = hi/lo(y)
-  EPI_RESID = 2,   // out_f32[row][16 t + c] += y   (residual stream)
-  EPI_SWIGLU = 3,  // out_hi/lo[row][8 t + c] = hi/lo(silu(gate) * up)
-  EPI_QKV = 4,     // RoPE(q), RoPE(k), v -> q workspace and the layer's K/V cache
-  EPI_ARGMAX = 5,  // per-row (max, lowest index) partial over the tile, optional logits
+  EPI_F32 = 0,      // out_f32[row][16 t + c] = y
+  EPI_SPLIT = 1,    // out_hi/lo[row][16 t + c] = hi/lo(y)
+  EPI_RESID = 2,    // out_f32[row][16 t + c] += y   (residual stream)
+  EPI_SWIGLU = 3,   // out_hi/lo[row][8 t + c] = hi/lo(silu(gate) * up)
+  EPI_QKV = 4,      // RoPE(q), RoPE(k), v -> q workspace and the layer's K/V cache
+  EPI_ARGMAX = 5,   // per-row (max, lowest index) partial over the tile, optional logits
+  EPI_PARTIAL = 6,  // out_f32[kc][row][16 t + c] = y (one K chunk's share; rows < Mp)
 };
 
 struct WeightSeg {
   const u16* w0;
   const u16* w1;
   const u16* w2;
+  const u16* wk[kMaxKvLayers];  // MAP_KVL
+  const u16* wv[kMaxKvLayers];
 };
 
 struct EpiParams {
   int M;          // valid rows
   int Mp;         // padded rows (plane stride of split outputs, row stride of partials)
-  // EPI_F32 / EPI_RESID
+  // EPI_F32 / EPI_RESID / EPI_PARTIAL
   float* out_f32;
   int ldo;
   // EPI_SPLIT / EPI_SWIGLU / q of EPI_QKV
   u16* out_hi;
   u16* out_lo;
   int ldh;
-  // EPI_QKV (and MAP_ROPE)
+  // EPI_QKV (and MAP_ROPE / MAP_QKV / MAP_KVL)
   int n_q, n_kv, head_dim, head0;
   const float* rope_cos;  // [pos][head_dim/2]
   const float* rope_sin;
-  u16* kv_cache;   // one layer's injected K/V cache, tiled (see kv_tile_offset)
+  u16* kv_cache;    // one layer's injected K/V cache, tiled (see kv_tile_offset)
   int64_t kv_tiles; // 64-slot tiles per kv head (all sequences)
-  // EPI_ARGMAX
-  unsigned long long* amax_part;  // [n_tiles][Mp]
+  // EPI_ARGMAX: per-row argmax keys of each column tile (many-row GEMM) or of
+  // each workgroup (few-row GEMM), [part][Mp]
+  unsigned long long* amax_part;
   float* logits;                  // [n_seqs][block-1][vocab] or null
   int vocab;
   int block;
@@ -80,16 +87,46 @@ struct GemmArgs {
   EpiParams ep;
 };
 
-hipError_t launch_embed(float* x, const int32_t* anchors, const u16* embed, int H, int M, int Mp,
-                        int block, int mask_id, int vocab, hipStream_t s);
-hipError_t launch_rmsnorm_split(const float* x, const u16* gain, u16* out_hi, u16* out_lo, int H,
-                                int M, int Mp, float eps, hipStream_t s);
+// Launch shape of the skinny (<= 32 rows) weight-streaming GEMM for a given
+// problem: nc column tiles per wave, kc K chunks across workgroups (kc > 1
+// only with EPI_PARTIAL).
+struct SkinnyPlan {
+  int nc, kc;
+};
+SkinnyPlan skinny_plan(int n_tiles, int K, bool may_split);
+constexpr int kSkinnyWaves = 4;  // waves per workgroup, splitting each K chunk
+constexpr int kMaxKc = 16;       // most K chunks a skinny GEMM is split into
+
 hipError_t launch_gemm(const GemmArgs& g, const SeqTable& st, int Mp, hipStream_t s);
+
+// x[row] = E[token] (token: anchor for block row 0, the mask id otherwise), or
+// x[row] += sum over kc of part[kc][row] (fixed kc order); then
+// out = hi/lo(gain * x / sqrt(mean(x^2) + eps)).  Rows M..Mp-1 of out are zero.
+hipError_t launch_resid_norm(float* x, const float* part, int kc, const int32_t* anchors, const u16* embed,
+                             int block, int mask_id, int vocab, const u16* gain, u16* out_hi, u16* out_lo,
+                             int H, int M, int Mp, float eps, hipStream_t s);
+// out[row][j] = hi/lo(sum over kc of part[kc][row][j]) for rows < M, zero for M..Mp-1.
+hipError_t launch_reduce_split(const float* part, int kc, int N, u16* out_hi, u16* out_lo, int M, int Mp,
+                               hipStream_t s);
+// Reduce q|k|v partials [kc][Mp][(n_q + 2 n_kv) d]; RoPE on q and k at each
+// row's position; q -> q_hi/lo [row][n_q d]; k, v -> the layer's cache slots.
+hipError_t launch_qkv_finish(const float* part, int kc, int M, int Mp, int n_q, int n_kv, int head_dim,
+                             const float* rope_cos, const float* rope_sin, u16* q_hi, u16* q_lo,
+                             u16* kv_cache, int64_t kv_tiles, const SeqTable& st, hipStream_t s);
+// Reduce all-layer k|v partials [kc][Mp][n_layers 2 n_kv d]; RoPE on k;
+// write every layer's cache slots.  layer_stride: elements between the
+// caches of consecutive layers.
+hipError_t launch_kv_finish(const float* part, int kc, int M, int Mp, int n_layers, int n_kv, int head_dim,
+                            const float* rope_cos, const float* rope_sin, u16* kv_cache0, size_t layer_stride,
+                            int64_t kv_tiles, const SeqTable& st, hipStream_t s);
 hipError_t launch_attention(const u16* q_hi, const u16* q_lo, const u16* kv_cache, int64_t kv_tiles,
                             float* part_o, float* part_ml, u16* o_hi, u16* o_lo, int n_seqs, int block,
                             int n_q, int n_kv, int head_dim, int splits, const SeqTable& st, hipStream_t s);
-hipError_t launch_argmax_reduce(const unsigned long long* part, int n_tiles, int Mp, int n_seqs,
+// draft[b][i-1] from the largest key of block row i over n_parts partial keys.
+hipError_t launch_argmax_reduce(const unsigned long long* part, int n_parts, int Mp, int n_seqs,
                                 int block, int32_t* draft, hipStream_t s);
+// Number of argmax partials the LM-head GEMM writes per row.
+int argmax_parts(int n_tiles, int Mp);
 hipError_t launch_accept(const int32_t* draft, const int32_t* target, int n, int block,
                          int32_t* accept, int32_t* next_anchor, hipStream_t s);
 

@@ -95,11 +95,26 @@ __device__ __forceinline__ u64 argmax_key(float v, int col) {
 // weight-row maps and epilogues (shared by both GEMM kernels)
 // ---------------------------------------------------------------------------
 
+// ---------------------------------------------------------------------------
+// weight-row maps and epilogues (shared by both GEMM kernels)
+// ---------------------------------------------------------------------------
+
 template <int MAP>
 __device__ __forceinline__ const u16* weight_row(const WeightSeg& w, const EpiParams& ep, int tile,
                                                  int c, int K) {
   if (MAP == MAP_PLAIN) return w.w0 + (size_t)(tile * 16 + c) * K;
   if (MAP == MAP_SWIGLU) return (c < 8 ? w.w0 : w.w1) + (size_t)(tile * 8 + (c & 7)) * K;
+  if (MAP == MAP_QKV) {
+    const int r = tile * 16 + c, qd = ep.n_q * ep.head_dim, kd = ep.n_kv * ep.head_dim;
+    if (r < qd) return w.w0 + (size_t)r * K;
+    if (r < qd + kd) return w.w1 + (size_t)(r - qd) * K;
+    return w.w2 + (size_t)(r - qd - kd) * K;
+  }
+  if (MAP == MAP_KVL) {
+    const int kd = ep.n_kv * ep.head_dim, r = tile * 16 + c;
+    const int l = r / (2 * kd), rr = r % (2 * kd);
+    return rr < kd ? w.wk[l] + (size_t)rr * K : w.wv[l] + (size_t)(rr - kd) * K;
+  }
   // MAP_ROPE: head hh of [q heads | k heads | v heads]; the tile holds the
   // eight RoPE pairs (j, j + d/2), j = j0 .. j0+7, in columns c and c + 8.
   const int d = ep.head_dim, tph = d / 16;
@@ -110,13 +125,23 @@ __device__ __forceinline__ const u16* weight_row(const WeightSeg& w, const EpiPa
   return w.w2 + (size_t)((hh - ep.n_q - ep.n_kv) * d + r) * K;
 }
 
+// Position of a row and its injected-cache element address helpers.
+__device__ __forceinline__ u16* kv_k_elem(u16* cache, int gk, int64_t slot, int64_t kv_tiles, int d, int col) {
+  return cache + kv_tile_offset(gk, slot / kTileKeys, kv_tiles, d) + (slot % kTileKeys) * d + col;
+}
+__device__ __forceinline__ u16* kv_v_elem(u16* cache, int gk, int64_t slot, int64_t kv_tiles, int d, int col) {
+  return cache + kv_tile_offset(gk, slot / kTileKeys, kv_tiles, d) + 2 * kTileKeys * d + col * kTileKeys +
+         slot % kTileKeys;
+}
+
 // v: the 16x16 fp32 tile in MFMA result layout (lane: column c = lane % 16,
 // rows r0 + 4 (lane / 16) + i).  All 64 lanes must call this together.
+// kc: the K chunk this tile sums (EPI_PARTIAL only).
 template <int EPI>
 __device__ __forceinline__ void epilogue(const EpiParams& ep, const SeqTable& st, int tile, int r0,
-                                         f32x4 v, int lane) {
+                                         f32x4 v, int lane, int kc) {
   const int c = lane & 15, g = lane >> 4;
-  if (EPI == EPI_F32 || EPI == EPI_RESID || EPI == EPI_SPLIT) {
+  if (EPI == EPI_F32 || EPI == EPI_RESID || EPI == EPI_SPLIT || EPI == EPI_PARTIAL) {
     const int col = tile * 16 + c;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -125,6 +150,8 @@ __device__ __forceinline__ void epilogue(const EpiParams& ep, const SeqTable& st
         if (row < ep.M) ep.out_f32[(size_t)row * ep.ldo + col] = v[i];
       } else if (EPI == EPI_RESID) {
         if (row < ep.M) ep.out_f32[(size_t)row * ep.ldo + col] += v[i];
+      } else if (EPI == EPI_PARTIAL) {
+        if (row < ep.M) ep.out_f32[((size_t)kc * ep.Mp + row) * ep.ldo + col] = v[i];
       } else {
         if (row < ep.Mp) {
           u16 h = 0, l = 0;
@@ -177,16 +204,14 @@ __device__ __forceinline__ void epilogue(const EpiParams& ep, const SeqTable& st
         ep.out_lo[o] = l;
       } else {
         const int64_t slot = st.slot_base[b] + pos;
-        const int sl = (int)(slot % kTileKeys);
-        const bool is_k = hh < ep.n_q + ep.n_kv;
-        const int gk = is_k ? hh - ep.n_q : hh - ep.n_q - ep.n_kv;
-        u16* tb = ep.kv_cache + kv_tile_offset(gk, slot / kTileKeys, ep.kv_tiles, d);
-        if (is_k) {
-          tb[sl * d + dcol] = h;
-          tb[kTileKeys * d + sl * d + dcol] = l;
+        if (hh < ep.n_q + ep.n_kv) {
+          u16* p = kv_k_elem(ep.kv_cache, hh - ep.n_q, slot, ep.kv_tiles, d, dcol);
+          p[0] = h;
+          p[kTileKeys * d] = l;
         } else {
-          tb[2 * kTileKeys * d + dcol * kTileKeys + sl] = h;
-          tb[3 * kTileKeys * d + dcol * kTileKeys + sl] = l;
+          u16* p = kv_v_elem(ep.kv_cache, hh - ep.n_q - ep.n_kv, slot, ep.kv_tiles, d, dcol);
+          p[0] = h;
+          p[kTileKeys * d] = l;
         }
       }
     }
@@ -210,92 +235,135 @@ __device__ __forceinline__ void epilogue(const EpiParams& ep, const SeqTable& st
   }
 }
 
+// LM-head tail of the few-row GEMM.  Per draft row, the largest logit of the
+// workgroup's tiles (lowest column on ties) as an order-preserving 64-bit key,
+// combined in LDS (max is order-independent, so the result is deterministic)
+// and stored as this workgroup's partial; a small kernel reduces the
+// partials.  Logits are written on the way when asked for.
+template <int RG, int NC, int KS>
+__device__ __forceinline__ void argmax_tail(const EpiParams& ep, int tile0, f32x4 (*red)[RG * NC][64], int lane,
+                                            int ks) {
+  __shared__ u64 rk[RG * 16];
+  const int c = lane & 15, g = lane >> 4;
+  if (threadIdx.x < RG * 16) rk[threadIdx.x] = 0;
+  __syncthreads();
+  for (int it = ks; it < RG * NC; it += KS) {
+    f32x4 s = red[0][it][lane];
+#pragma unroll
+    for (int q = 1; q < KS; ++q) s += red[q][it][lane];
+    const int col = (tile0 + it % NC) * 16 + c, r0 = (it / NC) * 16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = r0 + 4 * g + i;
+      const int bi = row % ep.block;
+      const bool draft_row = row < ep.M && bi != 0;
+      if (draft_row && ep.logits)
+        ep.logits[((size_t)(row / ep.block) * (ep.block - 1) + (bi - 1)) * ep.vocab + col] = s[i];
+      u64 key = draft_row ? argmax_key(s[i], col) : 0ull;
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1) {
+        const u64 o = shfl_xor_u64(key, m);
+        key = o > key ? o : key;
+      }
+      if (c == 0 && key) atomicMax(&rk[row], key);
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < RG * 16 && (int)threadIdx.x < ep.Mp)
+    ep.amax_part[(size_t)blockIdx.x * ep.Mp + threadIdx.x] = rk[threadIdx.x];
+}
+
 // ---------------------------------------------------------------------------
 // Skinny weight-streaming GEMM: Y[M<=32][N] = A[M][K] W^T, W [N][K] bf16.
-// One workgroup per 16-column tile; its waves split K and stream their
-// slice of the 16 weight rows straight into MFMA B registers (16 B per lane
-// per k-step, all of a 256-k batch in flight, the next batch prefetched).
-// Partial sums meet in LDS in a fixed order, then wave 0 runs the epilogue.
+// Workgroup (x, y) owns NC 16-column tiles and K chunk y of gridDim.y; its
+// kSkinnyWaves waves split the chunk.  Each wave streams its NC weight-row
+// slices straight into MFMA B registers (16 B per lane per tile and k-step,
+// two 32-k steps per batch, the next batch in flight while the current one
+// is multiplied) and reuses every A fragment for all NC tiles.  Partial sums
+// meet in LDS in a fixed order; the tiles' epilogues are spread over the
+// waves.  With several K chunks the epilogue is EPI_PARTIAL and a later
+// kernel sums the chunks in order.
 // ---------------------------------------------------------------------------
 
-template <int EPI, int MAP, bool SPLIT, int RG>
-__global__ __launch_bounds__(512) void k_gemm_skinny(GemmArgs ga, SeqTable st) {
-  constexpr int U = 8;  // 32-k steps per batch
-  const int tile = blockIdx.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+template <int EPI, int MAP, int NC, int RG, bool SPLIT>
+__global__ __launch_bounds__(kSkinnyWaves * 64) void k_skinny(GemmArgs ga, SeqTable st) {
+  constexpr int KS = kSkinnyWaves, U = 2;
+  const int lane = threadIdx.x & 63, ks = threadIdx.x >> 6;
   const int c = lane & 15, g = lane >> 4;
-  const int K = ga.K;
-  const u16* wp = weight_row<MAP>(ga.w, ga.ep, tile, c, K) + g * 8;
-  const int kw = K / nw;
-  const int kb = wave * kw, ke = kb + kw;
+  const int tile0 = blockIdx.x * NC;
+  const int kc = blockIdx.y;
+  const int kw = ga.K / ((int)gridDim.y * KS);
+  const int kb = (kc * KS + ks) * kw, ke = kb + kw;
 
+  const u16* wp[NC];
+#pragma unroll
+  for (int j = 0; j < NC; ++j) wp[j] = weight_row<MAP>(ga.w, ga.ep, tile0 + j, c, ga.K) + g * 8;
+  // Rows past a_rows read row a_rows - 1 instead: an output row depends only
+  // on its own A row, and no epilogue consumes rows >= M (M <= a_rows).
   const u16* ah[RG];
   const u16* al[RG];
-  bool aval[RG];
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg) {
-    const int row = rg * 16 + c;
-    aval[rg] = row < ga.a_rows;
+    const int row = min(rg * 16 + c, ga.a_rows - 1);
     ah[rg] = ga.a_hi + (size_t)row * ga.lda + g * 8;
     al[rg] = SPLIT ? ga.a_lo + (size_t)row * ga.lda + g * 8 : nullptr;
   }
-  f32x4 acc[RG];
+  f32x4 acc[RG][NC];
 #pragma unroll
-  for (int rg = 0; rg < RG; ++rg) acc[rg] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+    for (int j = 0; j < NC; ++j) acc[rg][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  int k = kb;
-  if (k + 32 * U <= ke) {
-    bf16x8 wf[U];
+  bf16x8 wf[U][NC];
 #pragma unroll
-    for (int u = 0; u < U; ++u) wf[u] = ld_frag(wp + k + u * 32);
-    for (; k + 32 * U <= ke; k += 32 * U) {
-      bf16x8 wn[U];
-      const bool more = k + 64 * U <= ke;
-      if (more) {
+  for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int u = 0; u < U; ++u) wn[u] = ld_frag(wp + k + 32 * U + u * 32);
-      }
+    for (int j = 0; j < NC; ++j) wf[u][j] = ld_frag(wp[j] + kb + u * 32);
+  for (int k = kb; k < ke; k += 32 * U) {
+    bf16x8 wn[U][NC];
+    const bool more = k + 32 * U < ke;
+    if (more) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
+      for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int rg = 0; rg < RG; ++rg) {
-          const bf16x8 a = aval[rg] ? ld_frag(ah[rg] + k + u * 32) : zero_frag();
-          acc[rg] = mfma(a, wf[u], acc[rg]);
-          if (SPLIT) {
-            const bf16x8 b = aval[rg] ? ld_frag(al[rg] + k + u * 32) : zero_frag();
-            acc[rg] = mfma(b, wf[u], acc[rg]);
-          }
+        for (int j = 0; j < NC; ++j) wn[u][j] = ld_frag(wp[j] + k + 32 * U + u * 32);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg) {
+        const bf16x8 a = ld_frag(ah[rg] + k + u * 32);
+#pragma unroll
+        for (int j = 0; j < NC; ++j) acc[rg][j] = mfma(a, wf[u][j], acc[rg][j]);
+        if (SPLIT) {
+          const bf16x8 b = ld_frag(al[rg] + k + u * 32);
+#pragma unroll
+          for (int j = 0; j < NC; ++j) acc[rg][j] = mfma(b, wf[u][j], acc[rg][j]);
         }
       }
-      if (more) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) wf[u] = wn[u];
-      }
     }
-  }
-  for (; k < ke; k += 32) {
-    const bf16x8 w = ld_frag(wp + k);
+    if (more) {
 #pragma unroll
-    for (int rg = 0; rg < RG; ++rg) {
-      const bf16x8 a = aval[rg] ? ld_frag(ah[rg] + k) : zero_frag();
-      acc[rg] = mfma(a, w, acc[rg]);
-      if (SPLIT) {
-        const bf16x8 b = aval[rg] ? ld_frag(al[rg] + k) : zero_frag();
-        acc[rg] = mfma(b, w, acc[rg]);
-      }
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int j = 0; j < NC; ++j) wf[u][j] = wn[u][j];
     }
   }
 
-  __shared__ f32x4 red[8][RG][64];
+  __shared__ f32x4 red[KS][RG * NC][64];
 #pragma unroll
-  for (int rg = 0; rg < RG; ++rg) red[wave][rg][lane] = acc[rg];
+  for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+    for (int j = 0; j < NC; ++j) red[ks][rg * NC + j][lane] = acc[rg][j];
   __syncthreads();
-  if (wave == 0) {
+  if constexpr (EPI == EPI_ARGMAX) {
+    argmax_tail<RG, NC, KS>(ga.ep, tile0, red, lane, ks);
+  } else {
+    for (int it = ks; it < RG * NC; it += KS) {
+      f32x4 s = red[0][it][lane];
 #pragma unroll
-    for (int rg = 0; rg < RG; ++rg) {
-      f32x4 s = red[0][rg][lane];
-      for (int w = 1; w < nw; ++w) s += red[w][rg][lane];
-      epilogue<EPI>(ga.ep, st, tile, rg * 16, s, lane);
+      for (int q = 1; q < KS; ++q) s += red[q][it][lane];
+      epilogue<EPI>(ga.ep, st, tile0 + it % NC, (it / NC) * 16, s, lane, kc);
     }
   }
 }
@@ -394,7 +462,7 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(GemmArgs ga, SeqTable st) {
   for (int rg = 0; rg < 2; ++rg)
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct)
-      epilogue<EPI>(ga.ep, st, tile0 + wn * 2 + ct, row0 + wm * 32 + rg * 16, acc[rg][ct], lane);
+      epilogue<EPI>(ga.ep, st, tile0 + wn * 2 + ct, row0 + wm * 32 + rg * 16, acc[rg][ct], lane, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -590,117 +658,269 @@ __global__ __launch_bounds__(NW * 64) void k_attn_tiles(const u16* __restrict__ 
   }
 }
 
-// Combine the key splits (fixed split order) of every output element and
-// write the attention output as hi/lo planes [row][n_q * D].
+// Combine the key splits of each (sequence, q head, 16-row query tile) unit.
+// Workgroup = unit x 4-row quad; wave w owns one query row: lane s reads
+// split s's (m, l), the wave forms the log-sum-exp weights
+// exp(m_s - max) / sum_s l_s exp(m_s - max) into LDS, then each lane sums
+// its D/64 output columns over the splits in split order (loads unrolled)
+// and writes the hi/lo planes [row][n_q * D].
 template <int D>
 __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ part_o,
                                                     const float* __restrict__ part_ml,
                                                     u16* __restrict__ o_hi, u16* __restrict__ o_lo,
-                                                    int block, int n_q, int splits, int total, SeqTable st) {
-  const int idx = blockIdx.x * 256 + threadIdx.x;
-  if (idx >= total) return;
-  const int dcol = idx % D;
-  int r = idx / D;
-  const int qi = r % block;
-  r /= block;
-  const int h = r % n_q, b = r / n_q;
-  const int qtiles = (block + 15) / 16, qt = qi / 16, row = qi % 16;
-  const size_t p0 = ((size_t)(b * n_q + h) * qtiles + qt) * splits;
-  float M = -INFINITY;
-  for (int s = 0; s < splits; ++s) M = fmaxf(M, part_ml[(p0 + s) * 32 + row]);
-  float L = 0.f, acc = 0.f;
-  for (int s = 0; s < splits; ++s) {
-    const float w = expf(part_ml[(p0 + s) * 32 + row] - M);
-    L += part_ml[(p0 + s) * 32 + 16 + row] * w;
-    acc += part_o[((p0 + s) * 16 + row) * D + dcol] * w;
+                                                    int block, int n_q, int splits, SeqTable st) {
+  constexpr int PER = D / 64;
+  __shared__ float wgt[4][kMaxSplits];
+  const int quad = blockIdx.x & 3, unit = blockIdx.x >> 2;
+  const int qtiles = (block + 15) / 16;
+  const int qt = unit % qtiles, h = (unit / qtiles) % n_q, b = unit / (qtiles * n_q);
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int row = quad * 4 + wv, qi = qt * 16 + row;
+  const size_t p0 = (size_t)unit * splits;
+  float m = -INFINITY, l = 0.f;
+  if (lane < splits) {
+    m = part_ml[(p0 + lane) * 32 + row];
+    l = part_ml[(p0 + lane) * 32 + 16 + row];
   }
-  u16 hi, lo;
-  split_pair(acc / L, hi, lo);
-  const size_t o = (size_t)(st.row_start[b] + qi) * (n_q * D) + h * D + dcol;
-  o_hi[o] = hi;
-  o_lo[o] = lo;
+  float M = m;
+#pragma unroll
+  for (int k = 32; k >= 1; k >>= 1) M = fmaxf(M, shfl_xor_f(M, k));
+  const float e = lane < splits ? expf(m - M) : 0.f;
+  float L = e * l;
+#pragma unroll
+  for (int k = 32; k >= 1; k >>= 1) L += shfl_xor_f(L, k);
+  if (lane < splits) wgt[wv][lane] = e / L;
+  __syncthreads();
+  if (qi >= block) return;
+  float acc[PER];
+#pragma unroll
+  for (int p = 0; p < PER; ++p) acc[p] = 0.f;
+  const float* po = part_o + (p0 * 16 + row) * D + lane * PER;
+#pragma unroll 8
+  for (int s = 0; s < splits; ++s) {
+    const float w = wgt[wv][s];
+#pragma unroll
+    for (int p = 0; p < PER; ++p) acc[p] += w * po[(size_t)s * 16 * D + p];
+  }
+  const size_t o = (size_t)(st.row_start[b] + qi) * (n_q * D) + h * D + lane * PER;
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    u16 hv, lv;
+    split_pair(acc[p], hv, lv);
+    o_hi[o + p] = hv;
+    o_lo[o + p] = lv;
+  }
 }
 
 // ---------------------------------------------------------------------------
 // small kernels
 // ---------------------------------------------------------------------------
 
-// x[row] = E[token] (fp32); token = anchor for block row 0, the mask id
-// otherwise; rows >= M are zero.  Out-of-range anchors are clamped.
-__global__ __launch_bounds__(256) void k_embed(float* __restrict__ x, const int32_t* __restrict__ anchors,
-                                               const u16* __restrict__ E, int H, int M, int block,
-                                               int mask_id, int vocab) {
-  const int row = blockIdx.x;
-  float* xr = x + (size_t)row * H;
-  if (row >= M) {
-    for (int j = threadIdx.x * 4; j < H; j += blockDim.x * 4)
-      *reinterpret_cast<f32x4*>(xr + j) = f32x4{0.f, 0.f, 0.f, 0.f};
-    return;
-  }
-  int tok = (row % block == 0) ? anchors[row / block] : mask_id;
-  tok = tok < 0 ? 0 : (tok >= vocab ? vocab - 1 : tok);
-  const u16* er = E + (size_t)tok * H;
-  for (int j = threadIdx.x * 8; j < H; j += blockDim.x * 8) {
-    const u32x4 w = *reinterpret_cast<const u32x4*>(er + j);
-    f32x4 lo4, hi4;
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      lo4[2 * q] = bf16_val(w[q] & 0xFFFFu);
-      lo4[2 * q + 1] = bf16_val(w[q] >> 16);
-      hi4[2 * q] = bf16_val(w[q + 2] & 0xFFFFu);
-      hi4[2 * q + 1] = bf16_val(w[q + 2] >> 16);
-    }
-    *reinterpret_cast<f32x4*>(xr + j) = lo4;
-    *reinterpret_cast<f32x4*>(xr + j + 4) = hi4;
-  }
-}
-
-// u = gain * x / sqrt(mean(x^2) + eps) per row, written as hi/lo planes; rows
-// >= M are written as zeros.  Fixed-order reduction (deterministic).
-__global__ __launch_bounds__(256) void k_rmsnorm_split(const float* __restrict__ x,
-                                                       const u16* __restrict__ gain,
-                                                       u16* __restrict__ out_hi,
-                                                       u16* __restrict__ out_lo, int H, int M,
-                                                       float eps) {
-  const int row = blockIdx.x;
+// One workgroup of 1024 threads per row.  x[row] = E[token] (embedding
+// mode) or x[row] += sum_{q < kc} part[q][row] (residual mode, fixed order,
+// all chunk loads issued together); then the RMSNorm of the new x row,
+// gain * x / sqrt(mean(x^2) + eps), is written as hi/lo planes.  Every thread
+// re-reads only the x elements it wrote itself.  Rows M..Mp-1 of the planes
+// are zero.
+__global__ __launch_bounds__(1024) void k_resid_norm(float* __restrict__ x, const float* __restrict__ part,
+                                                     int kc, const int32_t* __restrict__ anchors,
+                                                     const u16* __restrict__ E, int block, int mask_id, int vocab,
+                                                     const u16* __restrict__ gain, u16* __restrict__ out_hi,
+                                                     u16* __restrict__ out_lo, int H, int M, int Mp, float eps) {
+  const int row = blockIdx.x, tid = threadIdx.x;
   u16* oh = out_hi + (size_t)row * H;
   u16* ol = out_lo + (size_t)row * H;
   if (row >= M) {
-    for (int j = threadIdx.x; j < H; j += blockDim.x) {
-      oh[j] = 0;
-      ol[j] = 0;
+    for (int j = tid * 4; j < H; j += 4096) {
+      *reinterpret_cast<uint2*>(oh + j) = make_uint2(0u, 0u);
+      *reinterpret_cast<uint2*>(ol + j) = make_uint2(0u, 0u);
     }
     return;
   }
-  const float* xr = x + (size_t)row * H;
+  float* xr = x + (size_t)row * H;
+  const u16* er = nullptr;
+  if (E) {
+    int tok = (row % block == 0) ? anchors[row / block] : mask_id;
+    tok = tok < 0 ? 0 : (tok >= vocab ? vocab - 1 : tok);
+    er = E + (size_t)tok * H;
+  }
   float ss = 0.f;
-  for (int j = threadIdx.x * 4; j < H; j += blockDim.x * 4) {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(xr + j);
+  for (int j = tid * 4; j < H; j += 4096) {
+    f32x4 v;
+    if (er) {
+      const uint2 w = *reinterpret_cast<const uint2*>(er + j);
+      v = f32x4{bf16_val(w.x & 0xFFFFu), bf16_val(w.x >> 16), bf16_val(w.y & 0xFFFFu), bf16_val(w.y >> 16)};
+    } else {
+      v = *reinterpret_cast<const f32x4*>(xr + j);
+      f32x4 p[kMaxKc];
+#pragma unroll
+      for (int q = 0; q < kMaxKc; ++q)
+        if (q < kc) p[q] = *reinterpret_cast<const f32x4*>(part + ((size_t)q * Mp + row) * H + j);
+#pragma unroll
+      for (int q = 0; q < kMaxKc; ++q)
+        if (q < kc) v += p[q];
+    }
+    *reinterpret_cast<f32x4*>(xr + j) = v;
     ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
   }
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) ss += shfl_xor_f(ss, m);
-  __shared__ float wsum[4];
-  if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = ss;
+  __shared__ float wsum[16];
+  if ((tid & 63) == 0) wsum[tid >> 6] = ss;
   __syncthreads();
-  const float tot = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+  float tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) tot += wsum[w];
   const float r = 1.0f / sqrtf(tot / (float)H + eps);
-  for (int j = threadIdx.x; j < H; j += blockDim.x) {
-    u16 h, l;
-    split_pair(bf16_val(gain[j]) * xr[j] * r, h, l);
-    oh[j] = h;
-    ol[j] = l;
+  for (int j = tid * 4; j < H; j += 4096) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(xr + j);
+    const uint2 gw = *reinterpret_cast<const uint2*>(gain + j);
+    const float gs[4] = {bf16_val(gw.x & 0xFFFFu), bf16_val(gw.x >> 16), bf16_val(gw.y & 0xFFFFu),
+                         bf16_val(gw.y >> 16)};
+    u16 hh[4], ll[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) split_pair(gs[i] * v[i] * r, hh[i], ll[i]);
+    *reinterpret_cast<uint2*>(oh + j) =
+        make_uint2((uint32_t)hh[0] | ((uint32_t)hh[1] << 16), (uint32_t)hh[2] | ((uint32_t)hh[3] << 16));
+    *reinterpret_cast<uint2*>(ol + j) =
+        make_uint2((uint32_t)ll[0] | ((uint32_t)ll[1] << 16), (uint32_t)ll[2] | ((uint32_t)ll[3] << 16));
   }
 }
 
-// draft[b][i-1] = lowest column of the largest logit of block row i.
-__global__ __launch_bounds__(256) void k_argmax_reduce(const u64* __restrict__ part, int n_tiles,
+// out[row][j] = hi/lo(sum_{q < kc} part[q][row][j]); rows M..Mp-1 are zero.
+__global__ __launch_bounds__(256) void k_reduce_split(const float* __restrict__ part, int kc, int N,
+                                                      u16* __restrict__ out_hi, u16* __restrict__ out_lo, int M,
+                                                      int Mp) {
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (size_t)Mp * N) return;
+  const int row = (int)(idx / N);
+  u16 h = 0, l = 0;
+  if (row < M) {
+    float s = 0.f;
+    for (int q = 0; q < kc; ++q) s += part[(size_t)q * Mp * N + idx];
+    split_pair(s, h, l);
+  }
+  out_hi[idx] = h;
+  out_lo[idx] = l;
+}
+
+// One thread per (row, head of [q | k | v], RoPE pair j < d/2).
+__global__ __launch_bounds__(256) void k_qkv_finish(const float* __restrict__ part, int kc, int M, int Mp,
+                                                    int n_q, int n_kv, int d, const float* __restrict__ rc,
+                                                    const float* __restrict__ rs, u16* __restrict__ q_hi,
+                                                    u16* __restrict__ q_lo, u16* __restrict__ kv, int64_t kv_tiles,
+                                                    SeqTable st) {
+  const int half = d / 2, nh = n_q + 2 * n_kv, N = nh * d;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= M * nh * half) return;
+  const int j = idx % half, t = idx / half;
+  const int hh = t % nh, row = t / nh;
+  float a = 0.f, bv = 0.f;
+  for (int q = 0; q < kc; ++q) {
+    const float* p = part + ((size_t)q * Mp + row) * N + hh * d + j;
+    a += p[0];
+    bv += p[half];
+  }
+  const int b = seq_of_row(st, row);
+  const int pos = st.pos_base[b] + (row - st.row_start[b]);
+  if (hh < n_q + n_kv) {
+    const float cs = rc[(size_t)pos * half + j], sn = rs[(size_t)pos * half + j];
+    const float a2 = a * cs - bv * sn, b2 = bv * cs + a * sn;
+    a = a2;
+    bv = b2;
+  }
+  u16 ah, al, bh, bl;
+  split_pair(a, ah, al);
+  split_pair(bv, bh, bl);
+  if (hh < n_q) {
+    const size_t o = (size_t)row * (n_q * d) + hh * d + j;
+    q_hi[o] = ah;
+    q_lo[o] = al;
+    q_hi[o + half] = bh;
+    q_lo[o + half] = bl;
+    return;
+  }
+  const int64_t slot = st.slot_base[b] + pos;
+  if (hh < n_q + n_kv) {
+    u16* p = kv_k_elem(kv, hh - n_q, slot, kv_tiles, d, j);
+    p[0] = ah;
+    p[kTileKeys * d] = al;
+    p[half] = bh;
+    p[kTileKeys * d + half] = bl;
+  } else {
+    u16* p = kv_v_elem(kv, hh - n_q - n_kv, slot, kv_tiles, d, j);
+    u16* p2 = kv_v_elem(kv, hh - n_q - n_kv, slot, kv_tiles, d, j + half);
+    p[0] = ah;
+    p[kTileKeys * d] = al;
+    p2[0] = bh;
+    p2[kTileKeys * d] = bl;
+  }
+}
+
+// One thread per (row, layer, kv head, pair j < d/2): the K pair with RoPE and
+// the V pair, summed over kc chunks, written to that layer's cache.
+__global__ __launch_bounds__(256) void k_kv_finish(const float* __restrict__ part, int kc, int M, int Mp,
+                                                   int n_layers, int n_kv, int d, const float* __restrict__ rc,
+                                                   const float* __restrict__ rs, u16* __restrict__ kv0,
+                                                   size_t layer_stride, int64_t kv_tiles, SeqTable st) {
+  const int half = d / 2, kd = n_kv * d, N = n_layers * 2 * kd;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= M * n_layers * n_kv * half) return;
+  const int j = idx % half;
+  int t = idx / half;
+  const int gk = t % n_kv;
+  t /= n_kv;
+  const int l = t % n_layers, row = t / n_layers;
+  float k1 = 0.f, k2 = 0.f, v1 = 0.f, v2 = 0.f;
+  for (int q = 0; q < kc; ++q) {
+    const float* p = part + ((size_t)q * Mp + row) * N + l * 2 * kd + gk * d + j;
+    k1 += p[0];
+    k2 += p[half];
+    v1 += p[kd];
+    v2 += p[kd + half];
+  }
+  const int b = seq_of_row(st, row);
+  const int pos = st.pos_base[b] + (row - st.row_start[b]);
+  const float cs = rc[(size_t)pos * half + j], sn = rs[(size_t)pos * half + j];
+  const float r1 = k1 * cs - k2 * sn, r2 = k2 * cs + k1 * sn;
+  const int64_t slot = st.slot_base[b] + pos;
+  u16* cache = kv0 + (size_t)l * layer_stride;
+  u16 h, lo;
+  u16* pk = kv_k_elem(cache, gk, slot, kv_tiles, d, j);
+  split_pair(r1, h, lo);
+  pk[0] = h;
+  pk[kTileKeys * d] = lo;
+  split_pair(r2, h, lo);
+  pk[half] = h;
+  pk[kTileKeys * d + half] = lo;
+  u16* pv = kv_v_elem(cache, gk, slot, kv_tiles, d, j);
+  u16* pv2 = kv_v_elem(cache, gk, slot, kv_tiles, d, j + half);
+  split_pair(v1, h, lo);
+  pv[0] = h;
+  pv[kTileKeys * d] = lo;
+  split_pair(v2, h, lo);
+  pv2[0] = h;
+  pv2[kTileKeys * d] = lo;
+}
+
+// draft[b][i-1] = lowest column of the largest logit of block row i: the
+// largest of its n_parts partial keys (four independent loads per thread per
+// step), then a wave and workgroup max.
+__global__ __launch_bounds__(256) void k_argmax_reduce(const u64* __restrict__ part, int n_parts,
                                                        int Mp, int block, int32_t* __restrict__ draft) {
   const int dr = blockIdx.x;
   const int b = dr / (block - 1), i = dr % (block - 1) + 1;
   const int row = b * block + i;
   u64 best = 0;
-  for (int t = threadIdx.x; t < n_tiles; t += blockDim.x) {
+  int t = threadIdx.x;
+  for (; t + 768 < n_parts; t += 1024) {
+    const u64 v0 = part[(size_t)t * Mp + row], v1 = part[(size_t)(t + 256) * Mp + row];
+    const u64 v2 = part[(size_t)(t + 512) * Mp + row], v3 = part[(size_t)(t + 768) * Mp + row];
+    const u64 m01 = v0 > v1 ? v0 : v1, m23 = v2 > v3 ? v2 : v3;
+    const u64 m = m01 > m23 ? m01 : m23;
+    best = m > best ? m : best;
+  }
+  for (; t < n_parts; t += 256) {
     const u64 v = part[(size_t)t * Mp + row];
     best = v > best ? v : best;
   }
@@ -733,35 +953,84 @@ __global__ __launch_bounds__(256) void k_accept(const int32_t* __restrict__ draf
   if (next_anchor) next_anchor[b] = tg[k];
 }
 
+
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 
-hipError_t launch_embed(float* x, const int32_t* anchors, const u16* embed, int H, int M, int Mp,
-                        int block, int mask_id, int vocab, hipStream_t s) {
-  hipLaunchKernelGGL(k_embed, dim3(Mp), dim3(256), 0, s, x, anchors, embed, H, M, block, mask_id, vocab);
+hipError_t launch_resid_norm(float* x, const float* part, int kc, const int32_t* anchors, const u16* embed,
+                             int block, int mask_id, int vocab, const u16* gain, u16* out_hi, u16* out_lo,
+                             int H, int M, int Mp, float eps, hipStream_t s) {
+  if (kc > kMaxKc) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_resid_norm, dim3(Mp), dim3(1024), 0, s, x, part, kc, anchors, embed, block, mask_id, vocab,
+                     gain, out_hi, out_lo, H, M, Mp, eps);
   return hipGetLastError();
 }
 
-hipError_t launch_rmsnorm_split(const float* x, const u16* gain, u16* out_hi, u16* out_lo, int H,
-                                int M, int Mp, float eps, hipStream_t s) {
-  hipLaunchKernelGGL(k_rmsnorm_split, dim3(Mp), dim3(256), 0, s, x, gain, out_hi, out_lo, H, M, eps);
+hipError_t launch_reduce_split(const float* part, int kc, int N, u16* out_hi, u16* out_lo, int M, int Mp,
+                               hipStream_t s) {
+  const size_t total = (size_t)Mp * N;
+  hipLaunchKernelGGL(k_reduce_split, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, part, kc, N, out_hi,
+                     out_lo, M, Mp);
+  return hipGetLastError();
+}
+
+hipError_t launch_qkv_finish(const float* part, int kc, int M, int Mp, int n_q, int n_kv, int head_dim,
+                             const float* rope_cos, const float* rope_sin, u16* q_hi, u16* q_lo,
+                             u16* kv_cache, int64_t kv_tiles, const SeqTable& st, hipStream_t s) {
+  const int total = M * (n_q + 2 * n_kv) * (head_dim / 2);
+  hipLaunchKernelGGL(k_qkv_finish, dim3((total + 255) / 256), dim3(256), 0, s, part, kc, M, Mp, n_q, n_kv, head_dim,
+                     rope_cos, rope_sin, q_hi, q_lo, kv_cache, kv_tiles, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_finish(const float* part, int kc, int M, int Mp, int n_layers, int n_kv, int head_dim,
+                            const float* rope_cos, const float* rope_sin, u16* kv_cache0, size_t layer_stride,
+                            int64_t kv_tiles, const SeqTable& st, hipStream_t s) {
+  const int total = M * n_layers * n_kv * (head_dim / 2);
+  hipLaunchKernelGGL(k_kv_finish, dim3((total + 255) / 256), dim3(256), 0, s, part, kc, M, Mp, n_layers, n_kv,
+                     head_dim, rope_cos, rope_sin, kv_cache0, layer_stride, kv_tiles, st);
+  return hipGetLastError();
+}
+
+SkinnyPlan skinny_plan(int n_tiles, int K, bool may_split) {
+  SkinnyPlan p;
+  p.nc = (n_tiles % 8 == 0 && n_tiles >= 1024) ? 8 : (n_tiles % 4 == 0 ? 4 : (n_tiles % 2 == 0 ? 2 : 1));
+  p.kc = 1;
+  if (may_split) {
+    const int waves = n_tiles / p.nc * kSkinnyWaves;
+    const int chunk = kSkinnyWaves * 64;  // K granularity of one chunk: 64 per wave
+    while (p.kc * 2 <= kMaxKc && p.kc * 2 * waves <= 3072 && K % (p.kc * 2 * chunk) == 0) p.kc *= 2;
+  }
+  return p;
+}
+
+template <int EPI, int MAP, bool SPLIT, int RG>
+static hipError_t skinny_nc(const GemmArgs& g, const SeqTable& st, const SkinnyPlan& p, hipStream_t s) {
+  const dim3 grid(g.n_tiles / p.nc, p.kc), blk(kSkinnyWaves * 64);
+  switch (p.nc) {
+    case 8: hipLaunchKernelGGL((k_skinny<EPI, MAP, 8, RG, SPLIT>), grid, blk, 0, s, g, st); break;
+    case 4: hipLaunchKernelGGL((k_skinny<EPI, MAP, 4, RG, SPLIT>), grid, blk, 0, s, g, st); break;
+    case 2: hipLaunchKernelGGL((k_skinny<EPI, MAP, 2, RG, SPLIT>), grid, blk, 0, s, g, st); break;
+    default: hipLaunchKernelGGL((k_skinny<EPI, MAP, 1, RG, SPLIT>), grid, blk, 0, s, g, st); break;
+  }
   return hipGetLastError();
 }
 
 template <int EPI, int MAP, bool SPLIT>
 static hipError_t gemm_dispatch(const GemmArgs& g, const SeqTable& st, int Mp, hipStream_t s) {
   if (Mp <= 32) {
-    int nw = 8;
-    while (nw > 1 && g.K % (32 * nw) != 0) nw >>= 1;
-    if (Mp <= 16)
-      hipLaunchKernelGGL((k_gemm_skinny<EPI, MAP, SPLIT, 1>), dim3(g.n_tiles), dim3(64 * nw), 0, s, g, st);
-    else
-      hipLaunchKernelGGL((k_gemm_skinny<EPI, MAP, SPLIT, 2>), dim3(g.n_tiles), dim3(64 * nw), 0, s, g, st);
-  } else {
-    hipLaunchKernelGGL((k_gemm_tiled<EPI, MAP, SPLIT>), dim3(g.n_tiles / 4, Mp / 64), dim3(256), 0, s, g, st);
+    if (g.K % (kSkinnyWaves * 64)) return hipErrorInvalidValue;
+    const SkinnyPlan p = skinny_plan(g.n_tiles, g.K, EPI == EPI_PARTIAL);
+    return Mp <= 16 ? skinny_nc<EPI, MAP, SPLIT, 1>(g, st, p, s) : skinny_nc<EPI, MAP, SPLIT, 2>(g, st, p, s);
   }
-  return hipGetLastError();
+  if constexpr (EPI == EPI_PARTIAL || MAP == MAP_QKV || MAP == MAP_KVL) {
+    return hipErrorInvalidValue;  // many-row GEMMs apply their epilogue directly
+  } else {
+    if (g.n_tiles % 4 || g.K % 64) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_gemm_tiled<EPI, MAP, SPLIT>), dim3(g.n_tiles / 4, Mp / 64), dim3(256), 0, s, g, st);
+    return hipGetLastError();
+  }
 }
 
 hipError_t launch_gemm(const GemmArgs& g, const SeqTable& st, int Mp, hipStream_t s) {
@@ -778,9 +1047,11 @@ hipError_t launch_gemm(const GemmArgs& g, const SeqTable& st, int Mp, hipStream_
       return gemm_dispatch<EPI_SWIGLU, MAP_SWIGLU, true>(g, st, Mp, s);
     case EPI_ARGMAX:
       return gemm_dispatch<EPI_ARGMAX, MAP_PLAIN, true>(g, st, Mp, s);
-    case EPI_F32:
-      return split ? gemm_dispatch<EPI_F32, MAP_PLAIN, true>(g, st, Mp, s)
-                   : gemm_dispatch<EPI_F32, MAP_PLAIN, false>(g, st, Mp, s);
+    case EPI_PARTIAL:
+      if (g.map == MAP_QKV) return gemm_dispatch<EPI_PARTIAL, MAP_QKV, true>(g, st, Mp, s);
+      if (g.map == MAP_KVL) return gemm_dispatch<EPI_PARTIAL, MAP_KVL, true>(g, st, Mp, s);
+      return split ? gemm_dispatch<EPI_PARTIAL, MAP_PLAIN, true>(g, st, Mp, s)
+                   : gemm_dispatch<EPI_PARTIAL, MAP_PLAIN, false>(g, st, Mp, s);
     default:
       return hipErrorInvalidValue;
   }
@@ -824,9 +1095,9 @@ static hipError_t attention_dispatch(const u16* q_hi, const u16* q_lo, const u16
   else
     return hipErrorInvalidValue;
   if (splits > 1) {
-    const int total = n_seqs * n_q * block * D;
-    hipLaunchKernelGGL(k_attn_merge<D>, dim3((total + 255) / 256), dim3(256), 0, s, part_o, part_ml, o_hi, o_lo,
-                       block, n_q, splits, total, st);
+    const int units = n_seqs * n_q * ((block + 15) / 16);
+    hipLaunchKernelGGL(k_attn_merge<D>, dim3(units * 4), dim3(256), 0, s, part_o, part_ml, o_hi, o_lo, block, n_q,
+                       splits, st);
   }
   return hipGetLastError();
 }
@@ -843,9 +1114,13 @@ hipError_t launch_attention(const u16* q_hi, const u16* q_lo, const u16* kv_cach
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_argmax_reduce(const unsigned long long* part, int n_tiles, int Mp, int n_seqs,
+int argmax_parts(int n_tiles, int Mp) {
+  return Mp <= 32 ? n_tiles / skinny_plan(n_tiles, 0, false).nc : n_tiles;
+}
+
+hipError_t launch_argmax_reduce(const unsigned long long* part, int n_parts, int Mp, int n_seqs,
                                 int block, int32_t* draft, hipStream_t s) {
-  hipLaunchKernelGGL(k_argmax_reduce, dim3(n_seqs * (block - 1)), dim3(256), 0, s, part, n_tiles, Mp,
+  hipLaunchKernelGGL(k_argmax_reduce, dim3(n_seqs * (block - 1)), dim3(256), 0, s, part, n_parts, Mp,
                      block, draft);
   return hipGetLastError();
 }
