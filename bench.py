@@ -169,6 +169,17 @@ class Workload:
         return d.cpu().numpy(), lg.cpu().numpy()
 
 
+def measured_traffic(workload: str, stage: str):
+    """HBM bytes per launch of `stage` from the committed rocprofv3 counter
+    summary for this workload, if there is one and the kernel sources have not
+    changed since it was taken; else None."""
+    from block_diffusion_drafting_pass_amd import profsum
+    got = profsum.read_traffic(os.path.join(ROOT, "profiles", f"{stage}_{workload}_traffic.txt"))
+    if got is None or got[1] != profsum.kernel_sources_sha256():
+        return None
+    return got[0]
+
+
 def copy_bandwidth(torch, nbytes=1 << 30, reps=10) -> float:
     """Achieved device-to-device copy bandwidth (read + write bytes / s), GB/s."""
     x = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
@@ -319,25 +330,30 @@ def main(argv=None) -> int:
         achieved = pf / (avg_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
                 "frac": round(achieved / MFMA_BF16_PEAK_TFS, 4)}
-    roof.update({"traffic": None, "kernel": args.probe, "avg_launch_ms": round(avg_ms, 4),
-                 "launches_timed": probe_n, "alg_bytes_per_launch": pb, "alg_flops_per_launch": pf})
+    roof.update({"traffic": measured_traffic(spec.name, args.probe), "kernel": args.probe,
+                 "avg_launch_ms": round(avg_ms, 4), "launches_timed": probe_n, "alg_bytes_per_launch": pb,
+                 "alg_flops_per_launch": pf})
 
     breakdown = None
     if args.breakdown:
+        # per step: event-bracketed time of every launch of the stage (a stage
+        # may be one launch per layer or one for all layers), its algorithmic
+        # bytes and flops over all layers
         breakdown = {}
+        reps = 10
         for st in ("qkv", "attention", "oproj", "gate_up", "down", "lm_head", "fusion", "kv_proj"):
-            nl = {"lm_head": 1, "fusion": 1}.get(st, spec.n_layers)
-            reps = 10
-            B_.probe_arm(wl.model, st, nl * reps)
+            B_.probe_arm(wl.model, st, 64 * reps)
             for _ in range(reps):
                 wl.step()
             ms, cnt, _ = B_.probe_read(wl.model)
             r_ = n * (blk - 1) if st == "lm_head" else n * blk
             b_, f_ = stage_work(spec, st, r_, keys)
-            per = ms / max(cnt, 1)
-            breakdown[st] = {"ms_per_launch": round(per, 4), "launches_per_step": nl,
-                             "GB_s": round(b_ / (per * 1e-3) / 1e9, 1),
-                             "TFLOP_s": round(f_ / (per * 1e-3) / 1e12, 2)}
+            per_layer = st not in ("lm_head", "fusion")
+            b_, f_ = (b_ * spec.n_layers, f_ * spec.n_layers) if per_layer else (b_, f_)
+            ms_step = ms / reps
+            breakdown[st] = {"us_per_step": round(ms_step * 1e3, 1), "launches_per_step": cnt // reps,
+                             "GB_s": round(b_ / (ms_step * 1e-3) / 1e9, 1),
+                             "TFLOP_s": round(f_ / (ms_step * 1e-3) / 1e12, 2)}
         log(f"breakdown: {json.dumps(breakdown)}")
 
     cpu = None
