@@ -5,12 +5,13 @@
 One *step* is one steady-state decode iteration of the drafter, every part of
 the hot path once, for every sequence of the workload:
 
-  1. dflash_fuse_ctx     fuse the target features of the B newly verified
-                         positions (the largest possible tau) and append them as
-                         injected K/V to every draft layer's cache;
-  2. dflash_draft_block  one block-diffusion pass over (anchor, B-1 masks)
-                         ending in the LM-head argmax;
-  3. dflash_accept_len   accepted-prefix scan against constructed target tokens.
+  1. dflash_step        fuse the target features of the B newly verified
+                         positions (the largest possible tau), append them as
+                         injected K/V to every draft layer's cache, and run one
+                         block-diffusion pass over (anchor, B-1 masks) ending in
+                         the LM-head argmax (--two-call: the same work as
+                         dflash_fuse_ctx followed by dflash_draft_block);
+  2. dflash_accept_len   accepted-prefix scan against constructed target tokens.
 
 Before each step the host rolls every context back by B positions (metadata
 only), so each step sees the same context length and does identical work.
@@ -108,8 +109,9 @@ def step_work(spec):
 # ----------------------------------------------------------------------------
 
 class Workload:
-    def __init__(self, spec, weights, torch, B_):
+    def __init__(self, spec, weights, torch, B_, two_call=False):
         self.spec, self.torch, self.B = spec, torch, B_
+        self.two_call = two_call
         I = _inputs()
         n, blk = spec.n_seqs, spec.block
         self.cfg = B_.Config.from_spec(spec, max_block=max(blk, 16))
@@ -152,8 +154,12 @@ class Workload:
         B_, s = self.B, self.spec
         for b, c in enumerate(self.base):
             self.ctx.truncate(b, c)
-        B_.fuse_ctx(self.model, self.ctx, self.step_feats, self.n_new, self.ws)
-        B_.draft_block(self.model, self.ctx, self.anchors, s.block, self.ws, draft=self.draft)
+        if self.two_call:
+            B_.fuse_ctx(self.model, self.ctx, self.step_feats, self.n_new, self.ws)
+            B_.draft_block(self.model, self.ctx, self.anchors, s.block, self.ws, draft=self.draft)
+        else:
+            B_.step(self.model, self.ctx, self.step_feats, self.n_new, self.anchors, s.block, self.ws,
+                    draft=self.draft)
         if hasattr(self, "target"):
             B_.accept_len(self.draft, self.target, s.block, self.accept, self.next_anchor)
 
@@ -266,6 +272,10 @@ def main(argv=None) -> int:
     ap.add_argument("--probe", default="lm_head", help="stage whose launches are timed for the roofline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--breakdown", action="store_true", help="also time every stage (extra passes)")
+    ap.add_argument("--two-call", action="store_true",
+                    help="step as dflash_fuse_ctx + dflash_draft_block instead of the fused dflash_step")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay the step as one captured HIP graph (identical steps, so identical work)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -291,24 +301,40 @@ def main(argv=None) -> int:
     copy_gbs = copy_bandwidth(torch)
     log(f"device copy bandwidth {copy_gbs:.0f} GB/s")
 
-    wl = Workload(spec, weights, torch, B_)
+    wl = Workload(spec, weights, torch, B_, two_call=args.two_call)
     log("workload resident; warming up")
     for _ in range(args.warmup):
         wl.step()
     torch.cuda.synchronize()
 
     n_launch = {"lm_head": 1, "fusion": 1}.get(args.probe, spec.n_layers)
-    B_.probe_arm(wl.model, args.probe, n_launch * args.steps)
+    run = wl.step
+    if args.graph:
+        # the probe's events are not captured: arm it after capture only for eager replays
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            wl.step()
+        torch.cuda.synchronize()
+        for _ in range(3):
+            g.replay()
+        run = g.replay
+    else:
+        B_.probe_arm(wl.model, args.probe, n_launch * args.steps)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     e0.record()
     for _ in range(args.steps):
-        wl.step()
+        run()
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     ms_step = e0.elapsed_time(e1) / args.steps
+    if args.graph:
+        # time the dominant kernel on eager steps right after the graph replays
+        B_.probe_arm(wl.model, args.probe, n_launch * args.steps)
+        for _ in range(args.steps):
+            wl.step()
     probe_ms, probe_n, probe_missed = B_.probe_read(wl.model)
     log(f"{args.steps} steps: {ms_step:.3f} ms/step (wall {wall * 1e3 / args.steps:.3f} ms/step)")
 
@@ -346,14 +372,17 @@ def main(argv=None) -> int:
             for _ in range(reps):
                 wl.step()
             ms, cnt, _ = B_.probe_read(wl.model)
+            if cnt == 0:  # e.g. the context K/V projection inside a fused dflash_step
+                breakdown[st] = {"us_per_step": 0.0, "launches_per_step": 0}
+                continue
             r_ = n * (blk - 1) if st == "lm_head" else n * blk
             b_, f_ = stage_work(spec, st, r_, keys)
             per_layer = st not in ("lm_head", "fusion")
             b_, f_ = (b_ * spec.n_layers, f_ * spec.n_layers) if per_layer else (b_, f_)
-            ms_step = ms / reps
-            breakdown[st] = {"us_per_step": round(ms_step * 1e3, 1), "launches_per_step": cnt // reps,
-                             "GB_s": round(b_ / (ms_step * 1e-3) / 1e9, 1),
-                             "TFLOP_s": round(f_ / (ms_step * 1e-3) / 1e12, 2)}
+            st_ms = ms / reps
+            breakdown[st] = {"us_per_step": round(st_ms * 1e3, 1), "launches_per_step": cnt // reps,
+                             "GB_s": round(b_ / (st_ms * 1e-3) / 1e9, 1),
+                             "TFLOP_s": round(f_ / (st_ms * 1e-3) / 1e12, 2)}
         log(f"breakdown: {json.dumps(breakdown)}")
 
     cpu = None
@@ -387,7 +416,8 @@ def main(argv=None) -> int:
                          f"{spec.n_q_heads}/{spec.n_kv_heads} heads x {spec.head_dim}, SwiGLU {spec.intermediate}, "
                          f"vocab {spec.vocab}, fusion {spec.fused_width}->{spec.hidden}; {n} sequence(s), "
                          f"context {spec.ctx_lens[0] if n == 1 else list(spec.ctx_lens)}, block {blk}; "
-                         f"step = append {blk} verified positions + draft pass + accept scan"),
+                         f"step = append {blk} verified positions + draft pass + accept scan"
+                         f"{' (two calls)' if args.two_call else ' (dflash_step)'}"),
             "global_batch": n,
             "block": blk,
             "seq_len": max(spec.ctx_lens),

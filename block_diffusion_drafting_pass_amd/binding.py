@@ -21,7 +21,7 @@ STATUS = {0: "DFLASH_OK", -1: "DFLASH_EINVAL", -2: "DFLASH_ESHAPE", -3: "DFLASH_
 # Every symbol include/dflash.h declares.
 EXPORTS = ("dflash_weight_count", "dflash_model_create", "dflash_model_destroy", "dflash_ctx_bytes",
            "dflash_ctx_create", "dflash_ctx_destroy", "dflash_ctx_length", "dflash_ctx_truncate",
-           "dflash_workspace_bytes", "dflash_fuse_ctx", "dflash_draft_block", "dflash_accept_len",
+           "dflash_workspace_bytes", "dflash_fuse_ctx", "dflash_draft_block", "dflash_step", "dflash_accept_len",
            "dflash_probe_arm", "dflash_probe_read", "dflash_status_str", "dflash_last_error")
 
 # Stages a measurement probe can bracket (dflash_stage in include/dflash.h).
@@ -82,6 +82,8 @@ def lib():
         L.dflash_fuse_ctx.restype = ctypes.c_int
         L.dflash_draft_block.argtypes = [vp, vp, vp, i32, vp, vp, vp, sz, vp]
         L.dflash_draft_block.restype = ctypes.c_int
+        L.dflash_step.argtypes = [vp, vp, vp, ctypes.POINTER(i32), vp, i32, vp, vp, vp, sz, vp]
+        L.dflash_step.restype = ctypes.c_int
         L.dflash_accept_len.argtypes = [vp, vp, i32, i32, vp, vp, vp]
         L.dflash_accept_len.restype = ctypes.c_int
         L.dflash_probe_arm.argtypes = [vp, ctypes.c_int, i32]
@@ -204,6 +206,18 @@ def draft_block(model: Model, ctx: Context, anchors, block: int, ws, draft=None,
         draft = torch.empty((ctx.n_seqs, block - 1), dtype=torch.int32, device=anchors.device)
     check(lib().dflash_draft_block(model.handle, ctx.handle, _ptr(anchors), block, _ptr(draft), _ptr(logits),
                                    _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    return draft
+
+
+def step(model: Model, ctx: Context, features, n_new: Sequence[int], anchors, block: int, ws, draft=None,
+         logits=None, stream=None):
+    """Append n_new verified positions per sequence and draft a block at the new lengths."""
+    import torch
+    if draft is None:
+        draft = torch.empty((ctx.n_seqs, block - 1), dtype=torch.int32, device=anchors.device)
+    arr = (ctypes.c_int32 * ctx.n_seqs)(*[int(v) for v in n_new])
+    check(lib().dflash_step(model.handle, ctx.handle, _ptr(features), arr, _ptr(anchors), block, _ptr(draft),
+                            _ptr(logits), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
     return draft
 
 

@@ -109,8 +109,8 @@ int ctx_layout(const dflash_config* c, int32_t n_seqs, const int64_t* cap, CtxLa
 
 struct WsLayout {
   int M = 0, Mp = 0, max_splits = 0, R = 0, Rp = 0;
-  size_t x = 0, a_hi = 0, a_lo = 0, b_hi = 0, b_lo = 0, q_hi = 0, q_lo = 0, part_o = 0, part_ml = 0,
-         amax = 0, part = 0, draft_end = 0;
+  size_t x = 0, a_hi = 0, a_lo = 0, qa_hi = 0, qa_lo = 0, b_hi = 0, b_lo = 0, q_hi = 0, q_lo = 0, part_o = 0,
+         part_ml = 0, amax = 0, part = 0, draft_end = 0;
   size_t h_hi = 0, h_lo = 0, part_f = 0, ingest_end = 0;
   size_t total() const { return std::max(draft_end, ingest_end); }
 };
@@ -133,21 +133,26 @@ WsLayout ws_layout(const dflash_config* c, int n_seqs, int block, int64_t max_ne
   size_t o = 0;
   auto take = [&](size_t bytes) { const size_t at = o; o += align_up(bytes); return at; };
   const size_t Mp = W.Mp, wa = std::max(H, QD);
+  // the q|k|v GEMM's rows: the block, plus appended positions on a fused step (<= 32 rows)
+  const size_t Mq = Mp <= 32 ? 32 : Mp;
   W.x = take(Mp * H * 4);
   W.a_hi = take(Mp * wa * 2);
   W.a_lo = take(Mp * wa * 2);
+  W.qa_hi = take(Mq * H * 2);
+  W.qa_lo = take(Mq * H * 2);
   W.b_hi = take(Mp * I * 2);
   W.b_lo = take(Mp * I * 2);
-  W.q_hi = take(Mp * QD * 2);
-  W.q_lo = take(Mp * QD * 2);
+  W.q_hi = take(Mq * QD * 2);
+  W.q_lo = take(Mq * QD * 2);
   W.part_o = take(attention_partial_bytes(n_seqs, c->n_q_heads, qtiles, W.max_splits, c->head_dim));
   W.part_ml = take(attention_ml_bytes(n_seqs, c->n_q_heads, qtiles, W.max_splits));
   W.amax = take((size_t)(c->vocab / 16) * Mp * 8);
   if (W.Mp <= 32) {
-    const int nqkv = (c->n_q_heads + 2 * c->n_kv_heads) * c->head_dim;
-    size_t pb = skinny_part_bytes(nqkv / 16, (int)H, W.Mp, nqkv);
+    const int nqkv = (c->n_q_heads + 2 * c->n_kv_heads) * c->head_dim, fw = c->n_target_layers * c->hidden;
+    size_t pb = skinny_part_bytes(nqkv / 16, (int)H, 32, nqkv);
     pb = std::max(pb, skinny_part_bytes((int)H / 16, (int)QD, W.Mp, (int)H));
     pb = std::max(pb, skinny_part_bytes((int)H / 16, (int)I, W.Mp, (int)H));
+    pb = std::max(pb, skinny_part_bytes((int)H / 16, fw, 32, (int)H));  // fusion on a fused step
     W.part = take(pb);
   }
   W.draft_end = o;
@@ -414,7 +419,7 @@ int dflash_fuse_ctx(const dflash_model* model, dflash_ctx* ctx, const void* feat
       const int kcf = skinny_plan(f.n_tiles, f.K, true).kc;
       model->probe.start(DFLASH_STAGE_FUSION, s);
       e = launch_gemm(f, st, Rp, s);
-      if (e == hipSuccess) e = launch_reduce_split(part_f, kcf, c.hidden, h_hi, h_lo, R, Rp, s);
+      if (e == hipSuccess) e = launch_reduce_split(part_f, kcf, Rp, c.hidden, h_hi, h_lo, R, Rp, s);
       model->probe.stop(DFLASH_STAGE_FUSION, s);
       if (e != hipSuccess) return hip_fail(e, "fuse_ctx: fusion GEMM");
       const int lg = kv_group(&c);
@@ -494,27 +499,31 @@ int dflash_fuse_ctx(const dflash_model* model, dflash_ctx* ctx, const void* feat
   return DFLASH_OK;
 }
 
-int dflash_draft_block(const dflash_model* model, const dflash_ctx* ctx, const int32_t* anchors, int32_t block,
-                       int32_t* draft, float* logits, void* ws, size_t ws_bytes, dflash_stream stream) {
-  if (!model || !ctx) return fail(DFLASH_EINVAL, "model or ctx is NULL");
-  if (!same_config(model->cfg, ctx->cfg)) return fail(DFLASH_ESHAPE, "ctx was created for another configuration");
-  const dflash_config& c = model->cfg;
-  if (block < 2 || block > c.max_block) return fail(DFLASH_EINVAL, "block %d outside [2, %d]", block, c.max_block);
-  if (!anchors || !draft) return fail(DFLASH_EINVAL, "anchors or draft is NULL");
-  if (!aligned(anchors, 4) || !aligned(draft, 4) || (logits && !aligned(logits, 4)))
-    return fail(DFLASH_EALIGN, "anchors, draft and logits must be 4-byte aligned");
-  if (!ws) return fail(DFLASH_EINVAL, "workspace is NULL");
-  if (!aligned(ws, kAlign)) return fail(DFLASH_EALIGN, "workspace is not 256-byte aligned");
-  const int n = ctx->n_seqs;
-  const WsLayout W = ws_layout(&c, n, block, 0);
-  if (ws_bytes < W.draft_end)
-    return fail(DFLASH_EWORKSPACE, "workspace holds %zu bytes, %zu needed", ws_bytes, W.draft_end);
+}  // extern "C"
 
-  hipStream_t s = (hipStream_t)stream;
-  char* wsb = (char*)ws;
+namespace {
+
+// Verified positions appended inside a draft pass (dflash_step): their fused
+// features ride as extra rows of every layer's q|k|v GEMM, which reads the
+// same W_k / W_v the separate context projection would.
+struct Append {
+  const u16* features = nullptr;  // [R][n_target_layers * hidden] bf16
+  int R = 0;
+  const int32_t* n_new = nullptr;  // host [n_seqs]
+  const int64_t* old_len = nullptr;
+};
+
+// The draft pass over block positions lens[b] .. lens[b] + block - 1.
+int draft_impl(const dflash_model* model, const dflash_ctx* ctx, const int64_t* lens, const int32_t* anchors,
+               int block, int32_t* draft, float* logits, char* wsb, const WsLayout& W, hipStream_t s,
+               const Append* ap) {
+  const dflash_config& c = model->cfg;
+  const int n = ctx->n_seqs;
   float* x = (float*)(wsb + W.x);
   u16* a_hi = (u16*)(wsb + W.a_hi);
   u16* a_lo = (u16*)(wsb + W.a_lo);
+  u16* qa_hi = (u16*)(wsb + W.qa_hi);
+  u16* qa_lo = (u16*)(wsb + W.qa_lo);
   u16* b_hi = (u16*)(wsb + W.b_hi);
   u16* b_lo = (u16*)(wsb + W.b_lo);
   u16* q_hi = (u16*)(wsb + W.q_hi);
@@ -524,19 +533,35 @@ int dflash_draft_block(const dflash_model* model, const dflash_ctx* ctx, const i
   unsigned long long* amax = (unsigned long long*)(wsb + W.amax);
   float* part = (float*)(wsb + W.part);
   const int M = W.M, Mp = W.Mp, H = c.hidden, QD = c.n_q_heads * c.head_dim, I = c.intermediate;
+  const int R = ap ? ap->R : 0;
+  const int Mq = M + R, Mqp = rows_pad(Mq);  // rows of the q|k|v GEMM
 
-  SeqTable st;
+  SeqTable st;  // block rows
   memset(&st, 0, sizeof(st));
   st.n = n;
   for (int b = 0; b < n; ++b) {
     st.row_start[b] = b * block;
-    st.pos_base[b] = (int32_t)ctx->len[b];
+    st.pos_base[b] = (int32_t)lens[b];
     st.slot_base[b] = (int32_t)ctx->L.slot_base[b];
   }
-  st.row_start[n] = n * block;
+  st.row_start[n] = M;
+  SeqTable sq = st;  // block rows, then the appended rows of each sequence at their own positions
+  if (ap) {
+    int e = n, off = M;
+    for (int b = 0; b < n; ++b) {
+      if (ap->n_new[b] == 0) continue;
+      sq.row_start[e] = off;
+      sq.pos_base[e] = (int32_t)ap->old_len[b];
+      sq.slot_base[e] = (int32_t)ctx->L.slot_base[b];
+      off += ap->n_new[b];
+      ++e;
+    }
+    sq.n = e;
+    sq.row_start[e] = off;
+  }
   int max_tiles = 1;
   for (int b = 0; b < n; ++b)
-    max_tiles = std::max<int>(max_tiles, (int)((ctx->len[b] + block + kTileKeys - 1) / kTileKeys));
+    max_tiles = std::max<int>(max_tiles, (int)((lens[b] + block + kTileKeys - 1) / kTileKeys));
   const int splits = std::min(W.max_splits, attention_splits(n * c.n_kv_heads, max_tiles));
 
   auto base_args = [&](const u16* ah, const u16* al, int lda, int K, int n_tiles, int epi, int map) {
@@ -545,7 +570,7 @@ int dflash_draft_block(const dflash_model* model, const dflash_ctx* ctx, const i
     g.a_hi = ah;
     g.a_lo = al;
     g.lda = lda;
-    g.a_rows = Mp;
+    g.a_rows = M;
     g.K = K;
     g.n_tiles = n_tiles;
     g.epi = epi;
@@ -564,19 +589,52 @@ int dflash_draft_block(const dflash_model* model, const dflash_ctx* ctx, const i
   const int kc_qkv = skinny_plan(nqkv / 16, H, true).kc;
   const int kc_o = skinny_plan(H / 16, QD, true).kc;
   const int kc_d = skinny_plan(H / 16, I, true).kc;
+  // the q|k|v GEMM reads its own A planes (block rows, then appended rows)
+  u16* qin_hi = skinny ? qa_hi : a_hi;
+  u16* qin_lo = skinny ? qa_lo : a_lo;
+  hipError_t e;
 
-  hipError_t e = launch_resid_norm(x, nullptr, 0, anchors, model->embed, block, c.mask_token_id, c.vocab,
-                                   model->layers[0].attn_norm, a_hi, a_lo, H, M, Mp, c.rms_eps, s);
+  if (ap) {
+    // fused target features of the appended rows -> rows M .. M+R-1 of the q|k|v input
+    const int fw = c.n_target_layers * H, Rp = rows_pad(R);
+    GemmArgs f;
+    memset(&f, 0, sizeof(f));
+    f.a_hi = ap->features;
+    f.lda = fw;
+    f.a_rows = R;
+    f.K = fw;
+    f.n_tiles = H / 16;
+    f.w.w0 = model->w_fc;
+    f.map = MAP_PLAIN;
+    f.epi = EPI_PARTIAL;
+    f.ep.M = R;
+    f.ep.Mp = Rp;
+    f.ep.out_f32 = part;
+    f.ep.ldo = H;
+    const int kcf = skinny_plan(f.n_tiles, f.K, true).kc;
+    model->probe.start(DFLASH_STAGE_FUSION, s);
+    e = launch_gemm(f, st, Rp, s);
+    if (e == hipSuccess)
+      e = launch_reduce_split(part, kcf, Rp, H, qa_hi + (size_t)M * H, qa_lo + (size_t)M * H, R, R, s);
+    model->probe.stop(DFLASH_STAGE_FUSION, s);
+    if (e != hipSuccess) return hip_fail(e, "step: fusion GEMM");
+  }
+
+  e = launch_resid_norm(x, nullptr, 0, 0, anchors, model->embed, block, c.mask_token_id, c.vocab,
+                        model->layers[0].attn_norm, qin_hi, qin_lo, H, M, M, c.rms_eps, s);
   if (e != hipSuccess) return hip_fail(e, "draft_block: embed + attention norm");
   for (int l = 0; l < c.n_layers; ++l) {
     const LayerW& Lw = model->layers[l];
     GemmArgs g;
     if (skinny) {
-      g = base_args(a_hi, a_lo, H, H, nqkv / 16, EPI_PARTIAL, MAP_QKV);
+      g = base_args(qin_hi, qin_lo, H, H, nqkv / 16, EPI_PARTIAL, MAP_QKV);
+      g.a_rows = Mq;
+      g.ep.M = Mq;
+      g.ep.Mp = Mqp;
       g.ep.out_f32 = part;
       g.ep.ldo = nqkv;
     } else {
-      g = base_args(a_hi, a_lo, H, H, nqkv / 16, EPI_QKV, MAP_ROPE);
+      g = base_args(qin_hi, qin_lo, H, H, nqkv / 16, EPI_QKV, MAP_ROPE);
       g.ep.out_hi = q_hi;
       g.ep.out_lo = q_lo;
       g.ep.ldh = QD;
@@ -593,10 +651,10 @@ int dflash_draft_block(const dflash_model* model, const dflash_ctx* ctx, const i
     g.ep.n_kv = c.n_kv_heads;
     g.ep.head_dim = c.head_dim;
     model->probe.start(DFLASH_STAGE_QKV, s);
-    e = launch_gemm(g, st, Mp, s);
+    e = launch_gemm(g, st, skinny ? Mqp : Mp, s);
     if (e == hipSuccess && skinny)
-      e = launch_qkv_finish(part, kc_qkv, M, Mp, c.n_q_heads, c.n_kv_heads, c.head_dim, ctx->rope_cos(),
-                            ctx->rope_sin(), q_hi, q_lo, ctx->kv_cache(l), ctx->kv_tiles(), st, s);
+      e = launch_qkv_finish(part, kc_qkv, Mq, Mqp, c.n_q_heads, c.n_kv_heads, c.head_dim, ctx->rope_cos(),
+                            ctx->rope_sin(), q_hi, q_lo, ctx->kv_cache(l), ctx->kv_tiles(), sq, s);
     model->probe.stop(DFLASH_STAGE_QKV, s);
     if (e != hipSuccess) return hip_fail(e, "draft_block: QKV projection");
 
@@ -615,8 +673,8 @@ int dflash_draft_block(const dflash_model* model, const dflash_ctx* ctx, const i
     model->probe.stop(DFLASH_STAGE_OPROJ, s);
     if (e != hipSuccess) return hip_fail(e, "draft_block: output projection");
 
-    e = launch_resid_norm(x, skinny ? part : nullptr, skinny ? kc_o : 0, nullptr, nullptr, block, 0, c.vocab,
-                          Lw.mlp_norm, a_hi, a_lo, H, M, Mp, c.rms_eps, s);
+    e = launch_resid_norm(x, skinny ? part : nullptr, skinny ? kc_o : 0, Mp, nullptr, nullptr, block, 0, c.vocab,
+                          Lw.mlp_norm, a_hi, a_lo, H, M, M, c.rms_eps, s);
     if (e != hipSuccess) return hip_fail(e, "draft_block: MLP norm");
 
     g = base_args(a_hi, a_lo, H, H, I / 8, EPI_SWIGLU, MAP_SWIGLU);
@@ -639,9 +697,10 @@ int dflash_draft_block(const dflash_model* model, const dflash_ctx* ctx, const i
     model->probe.stop(DFLASH_STAGE_DOWN, s);
     if (e != hipSuccess) return hip_fail(e, "draft_block: down projection");
 
-    const u16* next_gain = l + 1 < c.n_layers ? model->layers[l + 1].attn_norm : model->final_norm;
-    e = launch_resid_norm(x, skinny ? part : nullptr, skinny ? kc_d : 0, nullptr, nullptr, block, 0, c.vocab,
-                          next_gain, a_hi, a_lo, H, M, Mp, c.rms_eps, s);
+    const bool last = l + 1 == c.n_layers;
+    const u16* next_gain = last ? model->final_norm : model->layers[l + 1].attn_norm;
+    e = launch_resid_norm(x, skinny ? part : nullptr, skinny ? kc_d : 0, Mp, nullptr, nullptr, block, 0, c.vocab,
+                          next_gain, last ? a_hi : qin_hi, last ? a_lo : qin_lo, H, M, M, c.rms_eps, s);
     if (e != hipSuccess) return hip_fail(e, "draft_block: residual + norm");
   }
   GemmArgs g = base_args(a_hi, a_lo, H, H, c.vocab / 16, EPI_ARGMAX, MAP_PLAIN);
@@ -656,6 +715,75 @@ int dflash_draft_block(const dflash_model* model, const dflash_ctx* ctx, const i
   if (e != hipSuccess) return hip_fail(e, "draft_block: LM head");
   e = launch_argmax_reduce(amax, argmax_parts(c.vocab / 16, Mp), Mp, n, block, draft, s);
   if (e != hipSuccess) return hip_fail(e, "draft_block: argmax");
+  return DFLASH_OK;
+}
+
+int check_draft_args(const dflash_model* model, const dflash_ctx* ctx, const int32_t* anchors, int32_t block,
+                     int32_t* draft, float* logits, void* ws) {
+  if (!model || !ctx) return fail(DFLASH_EINVAL, "model or ctx is NULL");
+  if (!same_config(model->cfg, ctx->cfg)) return fail(DFLASH_ESHAPE, "ctx was created for another configuration");
+  const dflash_config& c = model->cfg;
+  if (block < 2 || block > c.max_block) return fail(DFLASH_EINVAL, "block %d outside [2, %d]", block, c.max_block);
+  if (!anchors || !draft) return fail(DFLASH_EINVAL, "anchors or draft is NULL");
+  if (!aligned(anchors, 4) || !aligned(draft, 4) || (logits && !aligned(logits, 4)))
+    return fail(DFLASH_EALIGN, "anchors, draft and logits must be 4-byte aligned");
+  if (!ws) return fail(DFLASH_EINVAL, "workspace is NULL");
+  if (!aligned(ws, kAlign)) return fail(DFLASH_EALIGN, "workspace is not 256-byte aligned");
+  return DFLASH_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dflash_draft_block(const dflash_model* model, const dflash_ctx* ctx, const int32_t* anchors, int32_t block,
+                       int32_t* draft, float* logits, void* ws, size_t ws_bytes, dflash_stream stream) {
+  int rc = check_draft_args(model, ctx, anchors, block, draft, logits, ws);
+  if (rc) return rc;
+  const WsLayout W = ws_layout(&model->cfg, ctx->n_seqs, block, 0);
+  if (ws_bytes < W.draft_end)
+    return fail(DFLASH_EWORKSPACE, "workspace holds %zu bytes, %zu needed", ws_bytes, W.draft_end);
+  return draft_impl(model, ctx, ctx->len.data(), anchors, block, draft, logits, (char*)ws, W, (hipStream_t)stream,
+                    nullptr);
+}
+
+int dflash_step(const dflash_model* model, dflash_ctx* ctx, const void* features, const int32_t* n_new,
+                const int32_t* anchors, int32_t block, int32_t* draft, float* logits, void* ws, size_t ws_bytes,
+                dflash_stream stream) {
+  int rc = check_draft_args(model, ctx, anchors, block, draft, logits, ws);
+  if (rc) return rc;
+  if (!n_new) return fail(DFLASH_EINVAL, "n_new is NULL");
+  const dflash_config& c = model->cfg;
+  const int n = ctx->n_seqs;
+  int64_t total = 0;
+  for (int b = 0; b < n; ++b) {
+    if (n_new[b] < 0) return fail(DFLASH_EINVAL, "n_new[%d] < 0", b);
+    if (ctx->len[b] + n_new[b] > ctx->cap[b])
+      return fail(DFLASH_ECAPACITY, "sequence %d: length %lld + %d exceeds capacity %lld", b,
+                  (long long)ctx->len[b], n_new[b], (long long)ctx->cap[b]);
+    total += n_new[b];
+  }
+  if (total > 0 && !features) return fail(DFLASH_EINVAL, "features is NULL");
+  if (total > 0 && !aligned(features, 16)) return fail(DFLASH_EALIGN, "features is not 16-byte aligned");
+  const WsLayout W = ws_layout(&c, n, block, total);
+  if (ws_bytes < W.total()) return fail(DFLASH_EWORKSPACE, "workspace holds %zu bytes, %zu needed", ws_bytes, W.total());
+  const int M = n * block;
+  if (total == 0 || M > 32 || M + total > 32) {
+    // too many rows for one fused weight sweep: append, then draft
+    rc = dflash_fuse_ctx(model, ctx, features, n_new, ws, ws_bytes, stream);
+    if (rc) return rc;
+    return dflash_draft_block(model, ctx, anchors, block, draft, logits, ws, ws_bytes, stream);
+  }
+  std::vector<int64_t> lens(n);
+  for (int b = 0; b < n; ++b) lens[b] = ctx->len[b] + n_new[b];
+  Append ap;
+  ap.features = (const u16*)features;
+  ap.R = (int)total;
+  ap.n_new = n_new;
+  ap.old_len = ctx->len.data();
+  rc = draft_impl(model, ctx, lens.data(), anchors, block, draft, logits, (char*)ws, W, (hipStream_t)stream, &ap);
+  if (rc) return rc;
+  ctx->len = lens;
   return DFLASH_OK;
 }
 

@@ -100,14 +100,16 @@ constexpr int kMaxKc = 16;       // most K chunks a skinny GEMM is split into
 hipError_t launch_gemm(const GemmArgs& g, const SeqTable& st, int Mp, hipStream_t s);
 
 // x[row] = E[token] (token: anchor for block row 0, the mask id otherwise), or
-// x[row] += sum over kc of part[kc][row] (fixed kc order); then
-// out = hi/lo(gain * x / sqrt(mean(x^2) + eps)).  Rows M..Mp-1 of out are zero.
-hipError_t launch_resid_norm(float* x, const float* part, int kc, const int32_t* anchors, const u16* embed,
-                             int block, int mask_id, int vocab, const u16* gain, u16* out_hi, u16* out_lo,
-                             int H, int M, int Mp, float eps, hipStream_t s);
-// out[row][j] = hi/lo(sum over kc of part[kc][row][j]) for rows < M, zero for M..Mp-1.
-hipError_t launch_reduce_split(const float* part, int kc, int N, u16* out_hi, u16* out_lo, int M, int Mp,
-                               hipStream_t s);
+// x[row] += sum over kc of part[kc][row] (fixed kc order; part_rows = the
+// partials' row stride per chunk); then out = hi/lo(gain * x / sqrt(mean(x^2)
+// + eps)) for rows < M.  Rows M..out_rows-1 of out are zero.
+hipError_t launch_resid_norm(float* x, const float* part, int kc, int part_rows, const int32_t* anchors,
+                             const u16* embed, int block, int mask_id, int vocab, const u16* gain, u16* out_hi,
+                             u16* out_lo, int H, int M, int out_rows, float eps, hipStream_t s);
+// out[row][j] = hi/lo(sum over kc of part[kc][row][j]) for rows < M (part_rows:
+// the partials' row stride per chunk); rows M..out_rows-1 of out are zero.
+hipError_t launch_reduce_split(const float* part, int kc, int part_rows, int N, u16* out_hi, u16* out_lo, int M,
+                               int out_rows, hipStream_t s);
 // Reduce q|k|v partials [kc][Mp][(n_q + 2 n_kv) d]; RoPE on q and k at each
 // row's position; q -> q_hi/lo [row][n_q d]; k, v -> the layer's cache slots.
 hipError_t launch_qkv_finish(const float* part, int kc, int M, int Mp, int n_q, int n_kv, int head_dim,

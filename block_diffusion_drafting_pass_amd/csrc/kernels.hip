@@ -723,10 +723,10 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pa
 // re-reads only the x elements it wrote itself.  Rows M..Mp-1 of the planes
 // are zero.
 __global__ __launch_bounds__(1024) void k_resid_norm(float* __restrict__ x, const float* __restrict__ part,
-                                                     int kc, const int32_t* __restrict__ anchors,
+                                                     int kc, int part_rows, const int32_t* __restrict__ anchors,
                                                      const u16* __restrict__ E, int block, int mask_id, int vocab,
                                                      const u16* __restrict__ gain, u16* __restrict__ out_hi,
-                                                     u16* __restrict__ out_lo, int H, int M, int Mp, float eps) {
+                                                     u16* __restrict__ out_lo, int H, int M, float eps) {
   const int row = blockIdx.x, tid = threadIdx.x;
   u16* oh = out_hi + (size_t)row * H;
   u16* ol = out_lo + (size_t)row * H;
@@ -755,7 +755,7 @@ __global__ __launch_bounds__(1024) void k_resid_norm(float* __restrict__ x, cons
       f32x4 p[kMaxKc];
 #pragma unroll
       for (int q = 0; q < kMaxKc; ++q)
-        if (q < kc) p[q] = *reinterpret_cast<const f32x4*>(part + ((size_t)q * Mp + row) * H + j);
+        if (q < kc) p[q] = *reinterpret_cast<const f32x4*>(part + ((size_t)q * part_rows + row) * H + j);
 #pragma unroll
       for (int q = 0; q < kMaxKc; ++q)
         if (q < kc) v += p[q];
@@ -787,17 +787,17 @@ __global__ __launch_bounds__(1024) void k_resid_norm(float* __restrict__ x, cons
   }
 }
 
-// out[row][j] = hi/lo(sum_{q < kc} part[q][row][j]); rows M..Mp-1 are zero.
-__global__ __launch_bounds__(256) void k_reduce_split(const float* __restrict__ part, int kc, int N,
+// out[row][j] = hi/lo(sum_{q < kc} part[q][row][j]); rows M..out_rows-1 are zero.
+__global__ __launch_bounds__(256) void k_reduce_split(const float* __restrict__ part, int kc, int part_rows, int N,
                                                       u16* __restrict__ out_hi, u16* __restrict__ out_lo, int M,
-                                                      int Mp) {
+                                                      int out_rows) {
   const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (size_t)Mp * N) return;
+  if (idx >= (size_t)out_rows * N) return;
   const int row = (int)(idx / N);
   u16 h = 0, l = 0;
   if (row < M) {
     float s = 0.f;
-    for (int q = 0; q < kc; ++q) s += part[(size_t)q * Mp * N + idx];
+    for (int q = 0; q < kc; ++q) s += part[(size_t)q * part_rows * N + idx];
     split_pair(s, h, l);
   }
   out_hi[idx] = h;
@@ -958,20 +958,20 @@ __global__ __launch_bounds__(256) void k_accept(const int32_t* __restrict__ draf
 // launchers
 // ---------------------------------------------------------------------------
 
-hipError_t launch_resid_norm(float* x, const float* part, int kc, const int32_t* anchors, const u16* embed,
-                             int block, int mask_id, int vocab, const u16* gain, u16* out_hi, u16* out_lo,
-                             int H, int M, int Mp, float eps, hipStream_t s) {
-  if (kc > kMaxKc) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_resid_norm, dim3(Mp), dim3(1024), 0, s, x, part, kc, anchors, embed, block, mask_id, vocab,
-                     gain, out_hi, out_lo, H, M, Mp, eps);
+hipError_t launch_resid_norm(float* x, const float* part, int kc, int part_rows, const int32_t* anchors,
+                             const u16* embed, int block, int mask_id, int vocab, const u16* gain, u16* out_hi,
+                             u16* out_lo, int H, int M, int out_rows, float eps, hipStream_t s) {
+  if (kc > kMaxKc || out_rows < M) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_resid_norm, dim3(out_rows), dim3(1024), 0, s, x, part, kc, part_rows, anchors, embed, block,
+                     mask_id, vocab, gain, out_hi, out_lo, H, M, eps);
   return hipGetLastError();
 }
 
-hipError_t launch_reduce_split(const float* part, int kc, int N, u16* out_hi, u16* out_lo, int M, int Mp,
-                               hipStream_t s) {
-  const size_t total = (size_t)Mp * N;
-  hipLaunchKernelGGL(k_reduce_split, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, part, kc, N, out_hi,
-                     out_lo, M, Mp);
+hipError_t launch_reduce_split(const float* part, int kc, int part_rows, int N, u16* out_hi, u16* out_lo, int M,
+                               int out_rows, hipStream_t s) {
+  const size_t total = (size_t)out_rows * N;
+  hipLaunchKernelGGL(k_reduce_split, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, part, kc, part_rows, N,
+                     out_hi, out_lo, M, out_rows);
   return hipGetLastError();
 }
 

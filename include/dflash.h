@@ -157,6 +157,21 @@ int dflash_draft_block(const dflash_model* model, const dflash_ctx* ctx, const i
                        int32_t block, int32_t* draft, float* logits, void* ws, size_t ws_bytes,
                        dflash_stream stream);
 
+/* One steady-state decode iteration in a single call: append n_new[b]
+ * verified positions to each sequence (as dflash_fuse_ctx) and then draft a
+ * block at the new lengths (as dflash_draft_block).  When the block rows and
+ * the appended rows together number at most 32, the appended positions ride
+ * as extra rows of every layer's q|k|v projection, which reads the W_k and
+ * W_v the separate context projection would read again, and the K/V
+ * projection pass of dflash_fuse_ctx disappears (the DFlash paper's Fig. 2
+ * cache receives the same values up to float32 summation order).  Otherwise
+ * the two calls run one after the other.  Arguments as for the two calls;
+ * the workspace must hold dflash_workspace_bytes(model, n_seqs, block,
+ * sum n_new).  Lengths advance only if every launch was enqueued. */
+int dflash_step(const dflash_model* model, dflash_ctx* ctx, const void* features, const int32_t* n_new,
+                const int32_t* anchors, int32_t block, int32_t* draft, float* logits, void* ws, size_t ws_bytes,
+                dflash_stream stream);
+
 /* Greedy verification (atlas summary, "Key results": temperature 0; metric:
  * acceptance length tau).  draft: device int32 [n_seqs][block-1] for block
  * positions 1..block-1; target: device int32 [n_seqs][block], the target's

@@ -209,3 +209,78 @@ def test_q8_ragged_b32(q8):
     lens = I.spec("q8b_l3_b32_ragged").ctx_lens
     seqs = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 3})
     _q8_case(q8, "q8b_l3_b32_ragged", seqs=seqs, label="3-layer ragged B32")
+
+
+# ----------------------------------------------------------------------------
+# dflash_step: append + draft in one call (fused weight sweep when <= 32 rows)
+# ----------------------------------------------------------------------------
+
+def _step_case(spec, w, dev_w, base_lens, n_new, block, label, two_call_check=True):
+    """Ingest base_lens, then dflash_step(n_new) vs the oracle (fuse then draft) and
+    vs the two-call GPU path on a second context."""
+    import torch
+    spec = spec.with_(ctx_lens=tuple(base_lens), block=block)
+    cap = [b + k + 8 for b, k in zip(base_lens, n_new)]
+    run = GpuRun(spec, dev_w, capacity=cap, max_new=sum(base_lens) + sum(n_new), max_block=32)
+    run2 = GpuRun(spec, dev_w, capacity=cap, max_new=sum(base_lens) + sum(n_new), max_block=32)
+    feats = [I.gen_features(spec, 1, b, c + k) for b, (c, k) in enumerate(zip(base_lens, n_new))]
+    run.ingest([f[:c] for f, c in zip(feats, base_lens)])
+    run2.ingest([f[:c] for f, c in zip(feats, base_lens)])
+    newrows = [f[c:] for f, c in zip(feats, base_lens)]
+    nonempty = [r for r in newrows if r.shape[0]]
+    dev_new = (torch.from_numpy(np.ascontiguousarray(np.concatenate(nonempty, 0)).view(np.int16)).cuda()
+               .view(torch.bfloat16) if nonempty else None)
+    anchors = I.gen_anchors(spec, 2)
+    a = torch.from_numpy(anchors).cuda()
+    n = len(base_lens)
+    lg = torch.empty((n, block - 1, spec.vocab), dtype=torch.float32, device="cuda")
+    d = B.step(run.model, run.ctx, dev_new, n_new, a, block, run.ws, logits=lg)
+    torch.cuda.synchronize()
+    assert run.ctx.lengths() == [c + k for c, k in zip(base_lens, n_new)]
+    model = O.OracleModel.from_spec(spec, w)
+    octx = O.OracleContext(model, n)
+    for b in range(n):
+        O.fuse_ctx(model, octx, b, feats[b])
+    ref = O.draft_block(model, octx, anchors, block)
+    gl, gd = lg.cpu().numpy(), d.cpu().numpy()
+    assert_parity(gl, gd, ref, label)
+    if two_call_check:
+        B.fuse_ctx(run2.model, run2.ctx, dev_new, n_new, run2.ws)
+        lg2 = torch.empty_like(lg)
+        B.draft_block(run2.model, run2.ctx, a, block, run2.ws, logits=lg2)
+        torch.cuda.synchronize()
+        diff = float(np.max(np.abs(lg2.cpu().numpy() - gl)))
+        say(f"{label}: step vs fuse+draft max-abs logit diff {diff:.2e}")
+        assert diff <= 1e-3, f"{label}: fused step differs from the two-call path by {diff}"
+    return run
+
+
+@pytest.mark.parametrize("base,new,block,label", [
+    ((112,), (16,), 16, "one seq, 16+16 rows fused"),
+    ((40, 9), (3, 5), 4, "two seqs ragged, fused"),
+    ((30, 0, 17), (0, 7, 1), 8, "three seqs with empty appends, fused"),
+    ((64,), (1,), 16, "single appended row"),
+    ((64, 10), (20, 5), 16, "57 rows: append then draft"),
+])
+def test_step_tiny(torch_cuda, base, new, block, label):
+    spec = I.spec("tiny")
+    w = I.gen_weights(spec, seed=7, std=0.05)
+    _step_case(spec, w, B.upload_weights(spec, w), base, new, block, label)
+
+
+def test_step_capacity_error_leaves_lengths(torch_cuda):
+    spec = I.spec("tiny").with_(ctx_lens=(10,))
+    w = I.gen_weights(spec, seed=0)
+    run = GpuRun(spec, B.upload_weights(spec, w), capacity=[12], max_new=40)
+    run.ingest(_feats(spec, 1, [10]))
+    feats = torch_cuda.zeros((3, spec.fused_width), dtype=torch_cuda.bfloat16, device="cuda")
+    a = torch_cuda.zeros(1, dtype=torch_cuda.int32, device="cuda")
+    with pytest.raises(B.DFlashError) as e:
+        B.step(run.model, run.ctx, feats, [3], a, 16, run.ws)
+    assert e.value.name == "DFLASH_ECAPACITY"
+    assert run.ctx.lengths() == [10]
+
+
+def test_step_q8_ctx1024(q8):
+    spec5, w, dev = q8
+    _step_case(spec5, w, dev, (1008,), (16,), 16, "5-layer step ctx 1008+16")
