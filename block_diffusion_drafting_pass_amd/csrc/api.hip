@@ -34,14 +34,11 @@ int hip_fail(hipError_t e, const char* where) {
 }
 
 constexpr size_t kAlign = 256;
-constexpr int kIngestChunk = 4096;  // rows of one fusion / K-V projection pass
+constexpr int kIngestChunk = 1024;  // rows of one fusion / K-V projection pass
 
 size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-// Padded row count: the skinny GEMM works on 16-row groups (up to 32 rows),
-// the tiled GEMM on 64-row tiles.
-int rows_pad(int m) { return m <= 32 ? (m + 15) / 16 * 16 : (m + 63) / 64 * 64; }
 
 struct LayerW {
   const u16 *attn_norm, *wq, *wk, *wv, *wo, *mlp_norm, *wgate, *wup, *wdown;
@@ -115,9 +112,9 @@ struct WsLayout {
   size_t total() const { return std::max(draft_end, ingest_end); }
 };
 
-// fp32 bytes of the K-chunk partial sums of one skinny GEMM (rows padded to Mp).
-size_t skinny_part_bytes(int n_tiles, int K, int Mp, int N) {
-  return (size_t)skinny_plan(n_tiles, K, true).kc * Mp * N * sizeof(float);
+// fp32 bytes of the K-chunk partial sums of one GEMM over Mp padded rows.
+size_t part_bytes(int n_tiles, int K, int Mp, int N) {
+  return (size_t)gemm_plan(n_tiles, K, Mp, true).kc * Mp * N * sizeof(float);
 }
 
 // Layers covered by one all-layer K/V projection launch.
@@ -147,12 +144,14 @@ WsLayout ws_layout(const dflash_config* c, int n_seqs, int block, int64_t max_ne
   W.part_o = take(attention_partial_bytes(n_seqs, c->n_q_heads, qtiles, W.max_splits, c->head_dim));
   W.part_ml = take(attention_ml_bytes(n_seqs, c->n_q_heads, qtiles, W.max_splits));
   W.amax = take((size_t)(c->vocab / 16) * Mp * 8);
-  if (W.Mp <= 32) {
+  {
     const int nqkv = (c->n_q_heads + 2 * c->n_kv_heads) * c->head_dim, fw = c->n_target_layers * c->hidden;
-    size_t pb = skinny_part_bytes(nqkv / 16, (int)H, 32, nqkv);
-    pb = std::max(pb, skinny_part_bytes((int)H / 16, (int)QD, W.Mp, (int)H));
-    pb = std::max(pb, skinny_part_bytes((int)H / 16, (int)I, W.Mp, (int)H));
-    pb = std::max(pb, skinny_part_bytes((int)H / 16, fw, 32, (int)H));  // fusion on a fused step
+    size_t pb = part_bytes(nqkv / 16, (int)H, (int)Mq, nqkv);
+    pb = std::max(pb, part_bytes((int)H / 16, (int)QD, W.Mp, (int)H));
+    pb = std::max(pb, part_bytes((int)H / 16, (int)I, W.Mp, (int)H));
+    if (W.Mp <= 32)
+      for (int r = 16; r <= 32; r += 16)  // fusion of the appended rows on a fused step
+        pb = std::max(pb, part_bytes((int)H / 16, fw, r, (int)H));
     W.part = take(pb);
   }
   W.draft_end = o;
@@ -162,11 +161,14 @@ WsLayout ws_layout(const dflash_config* c, int n_seqs, int block, int64_t max_ne
   W.h_hi = take((size_t)W.Rp * H * 2);
   W.h_lo = take((size_t)W.Rp * H * 2);
   if (W.R > 0) {
-    // a chunk of at most 32 rows takes the skinny path with K-chunk partials
+    // every chunk row count up to Rp (the last chunk may be shorter and split
+    // K further), and every layer-group size (the last group may be smaller)
     const int fw = c->n_target_layers * c->hidden, kd2 = 2 * c->n_kv_heads * c->head_dim;
-    size_t pb = skinny_part_bytes((int)H / 16, fw, 32, (int)H);
-    for (int nl = 1; nl <= kv_group(c); ++nl)  // the last layer group may be smaller
-      pb = std::max(pb, skinny_part_bytes(nl * kd2 / 16, (int)H, 32, nl * kd2));
+    size_t pb = 0;
+    for (int r = 16; r <= W.Rp; r = r < 32 ? r + 16 : (r == 32 ? 128 : r + 128)) {
+      pb = std::max(pb, part_bytes((int)H / 16, fw, r, (int)H));
+      for (int nl = 1; nl <= kv_group(c); ++nl) pb = std::max(pb, part_bytes(nl * kd2 / 16, (int)H, r, nl * kd2));
+    }
     W.part_f = take(pb);
   }
   W.ingest_end = o;
@@ -397,6 +399,9 @@ int dflash_fuse_ctx(const dflash_model* model, dflash_ctx* ctx, const void* feat
     st.n = n;
     st.row_start[n] = R;
 
+    // fusion GEMM -> K-chunk partials -> h (hi/lo); then every layer's
+    // W_k / W_v on h in one GEMM per layer group -> partials -> RoPE and the
+    // cache write.
     GemmArgs f;
     memset(&f, 0, sizeof(f));
     f.a_hi = (const u16*)features + (size_t)r0 * fw;
@@ -407,90 +412,46 @@ int dflash_fuse_ctx(const dflash_model* model, dflash_ctx* ctx, const void* feat
     f.n_tiles = c.hidden / 16;
     f.w.w0 = model->w_fc;
     f.map = MAP_PLAIN;
+    f.epi = EPI_PARTIAL;
     f.ep.M = R;
     f.ep.Mp = Rp;
-    hipError_t e;
-    if (Rp <= 32) {
-      // few rows: weight-streaming GEMMs with K-chunk partials, then small
-      // kernels that sum the chunks in order and finish each output
-      f.epi = EPI_PARTIAL;
-      f.ep.out_f32 = part_f;
-      f.ep.ldo = c.hidden;
-      const int kcf = skinny_plan(f.n_tiles, f.K, true).kc;
-      model->probe.start(DFLASH_STAGE_FUSION, s);
-      e = launch_gemm(f, st, Rp, s);
-      if (e == hipSuccess) e = launch_reduce_split(part_f, kcf, Rp, c.hidden, h_hi, h_lo, R, Rp, s);
-      model->probe.stop(DFLASH_STAGE_FUSION, s);
-      if (e != hipSuccess) return hip_fail(e, "fuse_ctx: fusion GEMM");
-      const int lg = kv_group(&c);
-      for (int l0 = 0; l0 < c.n_layers; l0 += lg) {
-        const int nl = std::min(lg, c.n_layers - l0);
-        GemmArgs g;
-        memset(&g, 0, sizeof(g));
-        g.a_hi = h_hi;
-        g.a_lo = h_lo;
-        g.lda = c.hidden;
-        g.a_rows = Rp;
-        g.K = c.hidden;
-        g.n_tiles = nl * 2 * c.n_kv_heads * c.head_dim / 16;
-        for (int j = 0; j < nl; ++j) {
-          g.w.wk[j] = model->layers[l0 + j].wk;
-          g.w.wv[j] = model->layers[l0 + j].wv;
-        }
-        g.map = MAP_KVL;
-        g.epi = EPI_PARTIAL;
-        g.ep.M = R;
-        g.ep.Mp = Rp;
-        g.ep.n_kv = c.n_kv_heads;
-        g.ep.head_dim = c.head_dim;
-        g.ep.out_f32 = part_f;
-        g.ep.ldo = g.n_tiles * 16;
-        const int kck = skinny_plan(g.n_tiles, g.K, true).kc;
-        model->probe.start(DFLASH_STAGE_KV_PROJ, s);
-        e = launch_gemm(g, st, Rp, s);
-        if (e == hipSuccess)
-          e = launch_kv_finish(part_f, kck, R, Rp, nl, c.n_kv_heads, c.head_dim, ctx->rope_cos(), ctx->rope_sin(),
-                               ctx->kv_cache(l0), ctx->L.layer_bytes / sizeof(u16), ctx->kv_tiles(), st, s);
-        model->probe.stop(DFLASH_STAGE_KV_PROJ, s);
-        if (e != hipSuccess) return hip_fail(e, "fuse_ctx: K/V projection");
-      }
-      continue;
-    }
-    f.epi = EPI_SPLIT;
-    f.ep.out_hi = h_hi;
-    f.ep.out_lo = h_lo;
-    f.ep.ldh = c.hidden;
+    f.ep.out_f32 = part_f;
+    f.ep.ldo = c.hidden;
+    const int kcf = gemm_plan(f.n_tiles, f.K, Rp, true).kc;
     model->probe.start(DFLASH_STAGE_FUSION, s);
-    e = launch_gemm(f, st, Rp, s);
+    hipError_t e = launch_gemm(f, st, Rp, s);
+    if (e == hipSuccess) e = launch_reduce_split(part_f, kcf, Rp, c.hidden, h_hi, h_lo, R, Rp, s);
     model->probe.stop(DFLASH_STAGE_FUSION, s);
     if (e != hipSuccess) return hip_fail(e, "fuse_ctx: fusion GEMM");
-
-    for (int l = 0; l < c.n_layers; ++l) {
+    const int lg = kv_group(&c);
+    for (int l0 = 0; l0 < c.n_layers; l0 += lg) {
+      const int nl = std::min(lg, c.n_layers - l0);
       GemmArgs g;
       memset(&g, 0, sizeof(g));
       g.a_hi = h_hi;
       g.a_lo = h_lo;
       g.lda = c.hidden;
-      g.a_rows = Rp;
+      g.a_rows = R;
       g.K = c.hidden;
-      g.n_tiles = 2 * c.n_kv_heads * c.head_dim / 16;
-      g.w.w0 = model->layers[l].wq;
-      g.w.w1 = model->layers[l].wk;
-      g.w.w2 = model->layers[l].wv;
-      g.map = MAP_ROPE;
-      g.epi = EPI_QKV;
+      g.n_tiles = nl * 2 * c.n_kv_heads * c.head_dim / 16;
+      for (int j = 0; j < nl; ++j) {
+        g.w.wk[j] = model->layers[l0 + j].wk;
+        g.w.wv[j] = model->layers[l0 + j].wv;
+      }
+      g.map = MAP_KVL;
+      g.epi = EPI_PARTIAL;
       g.ep.M = R;
       g.ep.Mp = Rp;
-      g.ep.n_q = c.n_q_heads;
       g.ep.n_kv = c.n_kv_heads;
       g.ep.head_dim = c.head_dim;
-      g.ep.head0 = c.n_q_heads;
-      g.ep.rope_cos = ctx->rope_cos();
-      g.ep.rope_sin = ctx->rope_sin();
-      g.ep.kv_cache = ctx->kv_cache(l);
-      g.ep.kv_tiles = ctx->kv_tiles();
+      g.ep.out_f32 = part_f;
+      g.ep.ldo = g.n_tiles * 16;
+      const int kck = gemm_plan(g.n_tiles, g.K, Rp, true).kc;
       model->probe.start(DFLASH_STAGE_KV_PROJ, s);
       e = launch_gemm(g, st, Rp, s);
+      if (e == hipSuccess)
+        e = launch_kv_finish(part_f, kck, R, Rp, nl, c.n_kv_heads, c.head_dim, ctx->rope_cos(), ctx->rope_sin(),
+                             ctx->kv_cache(l0), ctx->L.layer_bytes / sizeof(u16), ctx->kv_tiles(), st, s);
       model->probe.stop(DFLASH_STAGE_KV_PROJ, s);
       if (e != hipSuccess) return hip_fail(e, "fuse_ctx: K/V projection");
     }
@@ -580,18 +541,16 @@ int draft_impl(const dflash_model* model, const dflash_ctx* ctx, const int64_t* 
     return g;
   };
 
-  // Few rows (<= 32): weight-streaming GEMMs; the narrow ones split K over
-  // workgroups into partials that the following small kernel sums in order
-  // (residual + RMSNorm, or RoPE + cache write).  Many rows: tiled GEMMs that
-  // apply residual / RoPE epilogues directly.
-  const bool skinny = Mp <= 32;
+  // The q|k|v, O and down GEMMs (and the fusion) may split K over
+  // workgroups; the kernel that follows each sums the chunk partials in order
+  // (RoPE + cache write, residual + RMSNorm, hi/lo split).
   const int nqkv = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
-  const int kc_qkv = skinny_plan(nqkv / 16, H, true).kc;
-  const int kc_o = skinny_plan(H / 16, QD, true).kc;
-  const int kc_d = skinny_plan(H / 16, I, true).kc;
+  const int kc_qkv = gemm_plan(nqkv / 16, H, Mqp, true).kc;
+  const int kc_o = gemm_plan(H / 16, QD, Mp, true).kc;
+  const int kc_d = gemm_plan(H / 16, I, Mp, true).kc;
   // the q|k|v GEMM reads its own A planes (block rows, then appended rows)
-  u16* qin_hi = skinny ? qa_hi : a_hi;
-  u16* qin_lo = skinny ? qa_lo : a_lo;
+  u16* qin_hi = qa_hi;
+  u16* qin_lo = qa_lo;
   hipError_t e;
 
   if (ap) {
@@ -611,7 +570,7 @@ int draft_impl(const dflash_model* model, const dflash_ctx* ctx, const int64_t* 
     f.ep.Mp = Rp;
     f.ep.out_f32 = part;
     f.ep.ldo = H;
-    const int kcf = skinny_plan(f.n_tiles, f.K, true).kc;
+    const int kcf = gemm_plan(f.n_tiles, f.K, Rp, true).kc;
     model->probe.start(DFLASH_STAGE_FUSION, s);
     e = launch_gemm(f, st, Rp, s);
     if (e == hipSuccess)
@@ -625,25 +584,12 @@ int draft_impl(const dflash_model* model, const dflash_ctx* ctx, const int64_t* 
   if (e != hipSuccess) return hip_fail(e, "draft_block: embed + attention norm");
   for (int l = 0; l < c.n_layers; ++l) {
     const LayerW& Lw = model->layers[l];
-    GemmArgs g;
-    if (skinny) {
-      g = base_args(qin_hi, qin_lo, H, H, nqkv / 16, EPI_PARTIAL, MAP_QKV);
-      g.a_rows = Mq;
-      g.ep.M = Mq;
-      g.ep.Mp = Mqp;
-      g.ep.out_f32 = part;
-      g.ep.ldo = nqkv;
-    } else {
-      g = base_args(qin_hi, qin_lo, H, H, nqkv / 16, EPI_QKV, MAP_ROPE);
-      g.ep.out_hi = q_hi;
-      g.ep.out_lo = q_lo;
-      g.ep.ldh = QD;
-      g.ep.head0 = 0;
-      g.ep.rope_cos = ctx->rope_cos();
-      g.ep.rope_sin = ctx->rope_sin();
-      g.ep.kv_cache = ctx->kv_cache(l);
-      g.ep.kv_tiles = ctx->kv_tiles();
-    }
+    GemmArgs g = base_args(qin_hi, qin_lo, H, H, nqkv / 16, EPI_PARTIAL, MAP_QKV);
+    g.a_rows = Mq;
+    g.ep.M = Mq;
+    g.ep.Mp = Mqp;
+    g.ep.out_f32 = part;
+    g.ep.ldo = nqkv;
     g.w.w0 = Lw.wq;
     g.w.w1 = Lw.wk;
     g.w.w2 = Lw.wv;
@@ -651,8 +597,8 @@ int draft_impl(const dflash_model* model, const dflash_ctx* ctx, const int64_t* 
     g.ep.n_kv = c.n_kv_heads;
     g.ep.head_dim = c.head_dim;
     model->probe.start(DFLASH_STAGE_QKV, s);
-    e = launch_gemm(g, st, skinny ? Mqp : Mp, s);
-    if (e == hipSuccess && skinny)
+    e = launch_gemm(g, st, Mqp, s);
+    if (e == hipSuccess)
       e = launch_qkv_finish(part, kc_qkv, Mq, Mqp, c.n_q_heads, c.n_kv_heads, c.head_dim, ctx->rope_cos(),
                             ctx->rope_sin(), q_hi, q_lo, ctx->kv_cache(l), ctx->kv_tiles(), sq, s);
     model->probe.stop(DFLASH_STAGE_QKV, s);
@@ -664,16 +610,16 @@ int draft_impl(const dflash_model* model, const dflash_ctx* ctx, const int64_t* 
     model->probe.stop(DFLASH_STAGE_ATTENTION, s);
     if (e != hipSuccess) return hip_fail(e, "draft_block: attention");
 
-    g = base_args(a_hi, a_lo, QD, QD, H / 16, skinny ? EPI_PARTIAL : EPI_RESID, MAP_PLAIN);
+    g = base_args(a_hi, a_lo, QD, QD, H / 16, EPI_PARTIAL, MAP_PLAIN);
     g.w.w0 = Lw.wo;
-    g.ep.out_f32 = skinny ? part : x;
+    g.ep.out_f32 = part;
     g.ep.ldo = H;
     model->probe.start(DFLASH_STAGE_OPROJ, s);
     e = launch_gemm(g, st, Mp, s);
     model->probe.stop(DFLASH_STAGE_OPROJ, s);
     if (e != hipSuccess) return hip_fail(e, "draft_block: output projection");
 
-    e = launch_resid_norm(x, skinny ? part : nullptr, skinny ? kc_o : 0, Mp, nullptr, nullptr, block, 0, c.vocab,
+    e = launch_resid_norm(x, part, kc_o, Mp, nullptr, nullptr, block, 0, c.vocab,
                           Lw.mlp_norm, a_hi, a_lo, H, M, M, c.rms_eps, s);
     if (e != hipSuccess) return hip_fail(e, "draft_block: MLP norm");
 
@@ -688,9 +634,9 @@ int draft_impl(const dflash_model* model, const dflash_ctx* ctx, const int64_t* 
     model->probe.stop(DFLASH_STAGE_GATE_UP, s);
     if (e != hipSuccess) return hip_fail(e, "draft_block: gate/up projection");
 
-    g = base_args(b_hi, b_lo, I, I, H / 16, skinny ? EPI_PARTIAL : EPI_RESID, MAP_PLAIN);
+    g = base_args(b_hi, b_lo, I, I, H / 16, EPI_PARTIAL, MAP_PLAIN);
     g.w.w0 = Lw.wdown;
-    g.ep.out_f32 = skinny ? part : x;
+    g.ep.out_f32 = part;
     g.ep.ldo = H;
     model->probe.start(DFLASH_STAGE_DOWN, s);
     e = launch_gemm(g, st, Mp, s);
@@ -699,7 +645,7 @@ int draft_impl(const dflash_model* model, const dflash_ctx* ctx, const int64_t* 
 
     const bool last = l + 1 == c.n_layers;
     const u16* next_gain = last ? model->final_norm : model->layers[l + 1].attn_norm;
-    e = launch_resid_norm(x, skinny ? part : nullptr, skinny ? kc_d : 0, Mp, nullptr, nullptr, block, 0, c.vocab,
+    e = launch_resid_norm(x, part, kc_d, Mp, nullptr, nullptr, block, 0, c.vocab,
                           next_gain, last ? a_hi : qin_hi, last ? a_lo : qin_lo, H, M, M, c.rms_eps, s);
     if (e != hipSuccess) return hip_fail(e, "draft_block: residual + norm");
   }

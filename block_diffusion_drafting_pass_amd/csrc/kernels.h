@@ -25,21 +25,16 @@ struct SeqTable {
 // Weight-row maps: which weight row feeds column c (0..15) of 16-wide tile t.
 enum MapKind : int {
   MAP_PLAIN = 0,   // row 16 t + c of w0
-  MAP_ROPE = 1,    // head-structured [q | k | v]: cols c and c^8 are a RoPE pair
-  MAP_SWIGLU = 2,  // c < 8: row 8 t + c of w0 (gate); c >= 8: row 8 t + c - 8 of w1 (up)
-  MAP_QKV = 3,     // row 16 t + c of the stacked [w0; w1; w2] (q rows, k rows, v rows)
-  MAP_KVL = 4,     // row 16 t + c of the stacked [wk_0; wv_0; wk_1; wv_1; ...] of all layers
+  MAP_SWIGLU = 1,  // c < 8: row 8 t + c of w0 (gate); c >= 8: row 8 t + c - 8 of w1 (up)
+  MAP_QKV = 2,     // row 16 t + c of the stacked [w0; w1; w2] (q rows, k rows, v rows)
+  MAP_KVL = 3,     // row 16 t + c of the stacked [wk_0; wv_0; wk_1; wv_1; ...] of all layers
 };
 
 // Epilogues applied to a finished 16x16 fp32 tile.
 enum EpiKind : int {
-  EPI_F32 = 0,      // out_f32[row][16 t + c] = y
-  EPI_SPLIT = 1,    // out_hi/lo[row][16 t + c] = hi/lo(y)
-  EPI_RESID = 2,    // out_f32[row][16 t + c] += y   (residual stream)
-  EPI_SWIGLU = 3,   // out_hi/lo[row][8 t + c] = hi/lo(silu(gate) * up)
-  EPI_QKV = 4,      // RoPE(q), RoPE(k), v -> q workspace and the layer's K/V cache
-  EPI_ARGMAX = 5,   // per-row (max, lowest index) partial over the tile, optional logits
-  EPI_PARTIAL = 6,  // out_f32[kc][row][16 t + c] = y (one K chunk's share; rows < Mp)
+  EPI_SWIGLU = 0,   // out_hi/lo[row][8 t + c] = hi/lo(silu(gate) * up)
+  EPI_ARGMAX = 1,   // per-row (max, lowest index) key over the tile, optional logits
+  EPI_PARTIAL = 2,  // out_f32[kc][row][16 t + c] = y (K chunk kc's share; rows < M)
 };
 
 struct WeightSeg {
@@ -53,19 +48,15 @@ struct WeightSeg {
 struct EpiParams {
   int M;          // valid rows
   int Mp;         // padded rows (plane stride of split outputs, row stride of partials)
-  // EPI_F32 / EPI_RESID / EPI_PARTIAL
+  // EPI_PARTIAL
   float* out_f32;
   int ldo;
-  // EPI_SPLIT / EPI_SWIGLU / q of EPI_QKV
+  // EPI_SWIGLU
   u16* out_hi;
   u16* out_lo;
   int ldh;
-  // EPI_QKV (and MAP_ROPE / MAP_QKV / MAP_KVL)
-  int n_q, n_kv, head_dim, head0;
-  const float* rope_cos;  // [pos][head_dim/2]
-  const float* rope_sin;
-  u16* kv_cache;    // one layer's injected K/V cache, tiled (see kv_tile_offset)
-  int64_t kv_tiles; // 64-slot tiles per kv head (all sequences)
+  // MAP_QKV / MAP_KVL
+  int n_q, n_kv, head_dim;
   // EPI_ARGMAX: per-row argmax keys of each column tile (many-row GEMM) or of
   // each workgroup (few-row GEMM), [part][Mp]
   unsigned long long* amax_part;
@@ -87,15 +78,19 @@ struct GemmArgs {
   EpiParams ep;
 };
 
-// Launch shape of the skinny (<= 32 rows) weight-streaming GEMM for a given
-// problem: nc column tiles per wave, kc K chunks across workgroups (kc > 1
-// only with EPI_PARTIAL).
-struct SkinnyPlan {
+// Launch shape of a GEMM over Mp padded rows: few rows (Mp <= 32) take the
+// weight-streaming kernel with nc column tiles per wave; many rows (Mp a
+// multiple of 128) the LDS-tiled one.  kc K chunks across workgroups (kc > 1
+// only with EPI_PARTIAL).  The same function sizes the partial buffers.
+struct GemmPlan {
   int nc, kc;
 };
-SkinnyPlan skinny_plan(int n_tiles, int K, bool may_split);
-constexpr int kSkinnyWaves = 4;  // waves per workgroup, splitting each K chunk
-constexpr int kMaxKc = 16;       // most K chunks a skinny GEMM is split into
+GemmPlan gemm_plan(int n_tiles, int K, int Mp, bool may_split);
+constexpr int kSkinnyWaves = 4;  // waves per workgroup of the few-row GEMM
+constexpr int kMaxKc = 16;       // most K chunks a GEMM is split into
+// Padded row count of a GEMM operand: 16-row groups up to 32 rows (few-row
+// kernel), else whole 128-row tiles.
+inline int rows_pad(int m) { return m <= 32 ? (m + 15) / 16 * 16 : (m + 127) / 128 * 128; }
 
 hipError_t launch_gemm(const GemmArgs& g, const SeqTable& st, int Mp, hipStream_t s);
 

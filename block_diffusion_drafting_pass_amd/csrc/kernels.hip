@@ -110,19 +110,10 @@ __device__ __forceinline__ const u16* weight_row(const WeightSeg& w, const EpiPa
     if (r < qd + kd) return w.w1 + (size_t)(r - qd) * K;
     return w.w2 + (size_t)(r - qd - kd) * K;
   }
-  if (MAP == MAP_KVL) {
-    const int kd = ep.n_kv * ep.head_dim, r = tile * 16 + c;
-    const int l = r / (2 * kd), rr = r % (2 * kd);
-    return rr < kd ? w.wk[l] + (size_t)rr * K : w.wv[l] + (size_t)(rr - kd) * K;
-  }
-  // MAP_ROPE: head hh of [q heads | k heads | v heads]; the tile holds the
-  // eight RoPE pairs (j, j + d/2), j = j0 .. j0+7, in columns c and c + 8.
-  const int d = ep.head_dim, tph = d / 16;
-  const int hh = ep.head0 + tile / tph, j0 = (tile % tph) * 8;
-  const int r = (c < 8) ? (j0 + c) : (d / 2 + j0 + (c - 8));
-  if (hh < ep.n_q) return w.w0 + (size_t)(hh * d + r) * K;
-  if (hh < ep.n_q + ep.n_kv) return w.w1 + (size_t)((hh - ep.n_q) * d + r) * K;
-  return w.w2 + (size_t)((hh - ep.n_q - ep.n_kv) * d + r) * K;
+  // MAP_KVL
+  const int kd = ep.n_kv * ep.head_dim, r = tile * 16 + c;
+  const int l = r / (2 * kd), rr = r % (2 * kd);
+  return rr < kd ? w.wk[l] + (size_t)rr * K : w.wv[l] + (size_t)(rr - kd) * K;
 }
 
 // Position of a row and its injected-cache element address helpers.
@@ -140,26 +131,14 @@ __device__ __forceinline__ u16* kv_v_elem(u16* cache, int gk, int64_t slot, int6
 template <int EPI>
 __device__ __forceinline__ void epilogue(const EpiParams& ep, const SeqTable& st, int tile, int r0,
                                          f32x4 v, int lane, int kc) {
+  (void)st;
   const int c = lane & 15, g = lane >> 4;
-  if (EPI == EPI_F32 || EPI == EPI_RESID || EPI == EPI_SPLIT || EPI == EPI_PARTIAL) {
+  if (EPI == EPI_PARTIAL) {
     const int col = tile * 16 + c;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = r0 + 4 * g + i;
-      if (EPI == EPI_F32) {
-        if (row < ep.M) ep.out_f32[(size_t)row * ep.ldo + col] = v[i];
-      } else if (EPI == EPI_RESID) {
-        if (row < ep.M) ep.out_f32[(size_t)row * ep.ldo + col] += v[i];
-      } else if (EPI == EPI_PARTIAL) {
-        if (row < ep.M) ep.out_f32[((size_t)kc * ep.Mp + row) * ep.ldo + col] = v[i];
-      } else {
-        if (row < ep.Mp) {
-          u16 h = 0, l = 0;
-          if (row < ep.M) split_pair(v[i], h, l);
-          ep.out_hi[(size_t)row * ep.ldh + col] = h;
-          ep.out_lo[(size_t)row * ep.ldh + col] = l;
-        }
-      }
+      if (row < ep.M) ep.out_f32[((size_t)kc * ep.Mp + row) * ep.ldo + col] = v[i];
     }
   } else if (EPI == EPI_SWIGLU) {
 #pragma unroll
@@ -175,44 +154,6 @@ __device__ __forceinline__ void epilogue(const EpiParams& ep, const SeqTable& st
         const size_t o = (size_t)row * ep.ldh + tile * 8 + c;
         ep.out_hi[o] = h;
         ep.out_lo[o] = l;
-      }
-    }
-  } else if (EPI == EPI_QKV) {
-    const int d = ep.head_dim, tph = d / 16, half = d / 2;
-    const int hh = ep.head0 + tile / tph;
-    const int jj = (tile % tph) * 8 + (c & 7);
-    const int dcol = (c < 8) ? jj : half + jj;
-    const bool rope = hh < ep.n_q + ep.n_kv;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float partner = shfl_xor_f(v[i], 8);
-      const int row = r0 + 4 * g + i;
-      if (row >= ep.M) continue;
-      const int b = seq_of_row(st, row);
-      const int pos = st.pos_base[b] + (row - st.row_start[b]);
-      float val = v[i];
-      if (rope) {
-        const float cs = ep.rope_cos[(size_t)pos * half + jj];
-        const float sn = ep.rope_sin[(size_t)pos * half + jj];
-        val = (c < 8) ? (v[i] * cs - partner * sn) : (v[i] * cs + partner * sn);
-      }
-      u16 h, l;
-      split_pair(val, h, l);
-      if (hh < ep.n_q) {
-        const size_t o = (size_t)row * ep.ldh + hh * d + dcol;
-        ep.out_hi[o] = h;
-        ep.out_lo[o] = l;
-      } else {
-        const int64_t slot = st.slot_base[b] + pos;
-        if (hh < ep.n_q + ep.n_kv) {
-          u16* p = kv_k_elem(ep.kv_cache, hh - ep.n_q, slot, ep.kv_tiles, d, dcol);
-          p[0] = h;
-          p[kTileKeys * d] = l;
-        } else {
-          u16* p = kv_v_elem(ep.kv_cache, hh - ep.n_q - ep.n_kv, slot, ep.kv_tiles, d, dcol);
-          p[0] = h;
-          p[kTileKeys * d] = l;
-        }
       }
     }
   } else if (EPI == EPI_ARGMAX) {
@@ -369,100 +310,123 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void k_skinny(GemmArgs ga, SeqTa
 }
 
 // ---------------------------------------------------------------------------
-// LDS-tiled GEMM for many rows (M a multiple of 64): 64x64 output tile per
-// workgroup of four waves (2x2, each 32x32 = 2x2 MFMA tiles), k staged in
-// 64-wide slabs through padded LDS, the next slab's global loads in flight
-// while the current one is multiplied.
+// Many-row GEMM (M a multiple of 128): 128 x 256 output tile per workgroup
+// of eight waves (2 x 4, each 64 x 64 = 4 x 4 MFMA tiles), over K chunk kc
+// of gridDim / (mt nt) chunks.  K runs in 64-wide slabs through two LDS
+// buffers: while the waves multiply slab k out of one buffer, slab k+1's
+// global loads are in flight in registers and land in the other buffer, so
+// one barrier per slab suffices.  LDS rows are 128 bytes; 16-byte chunk c of
+// row r sits at c ^ ((r >> 1) & 7), which puts the 16 rows one fragment
+// read touches in distinct bank groups.  Workgroup ids run over the row
+// tiles first, so the row tiles that share a weight tile are dispatched
+// together and reuse it from L2.  A last column tile past n_tiles reads a
+// valid weight row and skips its epilogue.  Epilogues are the per-16x16-tile
+// ones above.
 // ---------------------------------------------------------------------------
 
-template <int EPI, int MAP, bool SPLIT>
-__global__ __launch_bounds__(256) void k_gemm_tiled(GemmArgs ga, SeqTable st) {
-  constexpr int BK = 64, LDS_STRIDE = BK + 8;
-  constexpr int NP = SPLIT ? 2 : 1;
-  __shared__ u16 sA[NP][64][LDS_STRIDE];
-  __shared__ u16 sW[64][LDS_STRIDE];
+constexpr int kBigBM = 128, kBigBN = 256, kBigBK = 64;
 
+__device__ __forceinline__ int big_swz(int row, int ch) { return row * 8 + (ch ^ ((row >> 1) & 7)); }
+
+template <int EPI, int MAP, bool SPLIT>
+__global__ __launch_bounds__(512) void k_gemm_big(GemmArgs ga, SeqTable st, int mt, int kcn) {
+  constexpr int BM = kBigBM, BN = kBigBN, BK = kBigBK, NP = SPLIT ? 2 : 1;
+  constexpr int ACH = BM * 8, WCH = BN * 8;        // 16-byte chunks per A plane / W slab
+  constexpr int STAGE = NP * ACH + WCH;             // chunks per LDS buffer
+  constexpr int AP = ACH / 512, WP = WCH / 512;     // chunks each thread stages per A plane / W
+  extern __shared__ u32x4 smem[];
+
+  const int bid = blockIdx.x, m_t = bid % mt, kc = (bid / mt) % kcn, n_t = bid / (mt * kcn);
+  const int row0 = m_t * BM, tile0 = n_t * (BN / 16);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 15, g = lane >> 4;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int tile0 = blockIdx.x * 4;
-  const int row0 = blockIdx.y * 64;
-  const int K = ga.K;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int K = ga.K, kspan = K / kcn, kbase = kc * kspan;
 
-  // global -> register staging: each thread moves two 16-byte chunks per operand plane
-  const u16* gA[NP][2];
-  bool av[2];
-  const u16* gW[2];
-  int ldr[2], ldk[2];
+  const u16* gA[NP][AP];
+  bool av[AP];
+  int ar[AP], ac[AP];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int q = tid + 256 * j;
-    ldr[j] = q >> 3;
-    ldk[j] = (q & 7) * 8;
-    const int arow = row0 + ldr[j];
-    av[j] = arow < ga.a_rows;
-    gA[0][j] = ga.a_hi + (size_t)arow * ga.lda + ldk[j];
-    if (SPLIT) gA[NP - 1][j] = ga.a_lo + (size_t)arow * ga.lda + ldk[j];
-    gW[j] = weight_row<MAP>(ga.w, ga.ep, tile0 + (ldr[j] >> 4), ldr[j] & 15, K) + ldk[j];
+  for (int q = 0; q < AP; ++q) {
+    const int idx = tid + 512 * q;
+    ar[q] = idx >> 3;
+    ac[q] = idx & 7;
+    const int arow = row0 + ar[q];
+    av[q] = arow < ga.a_rows;
+    gA[0][q] = ga.a_hi + (size_t)arow * ga.lda + kbase + ac[q] * 8;
+    if (SPLIT) gA[NP - 1][q] = ga.a_lo + (size_t)arow * ga.lda + kbase + ac[q] * 8;
   }
-  u32x4 rA[NP][2], rW[2];
-  auto load_slab = [&](int k0) {
+  const u16* gW[WP];
+  int wr[WP], wc[WP];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+  for (int q = 0; q < WP; ++q) {
+    const int idx = tid + 512 * q;
+    wr[q] = idx >> 3;
+    wc[q] = idx & 7;
+    const int tile = min(tile0 + (wr[q] >> 4), ga.n_tiles - 1);
+    gW[q] = weight_row<MAP>(ga.w, ga.ep, tile, wr[q] & 15, K) + kbase + wc[q] * 8;
+  }
+  u32x4 rA[NP][AP], rW[WP];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int q = 0; q < AP; ++q)
 #pragma unroll
       for (int p = 0; p < NP; ++p)
-        rA[p][j] = av[j] ? *reinterpret_cast<const u32x4*>(gA[p][j] + k0) : u32x4{0u, 0u, 0u, 0u};
-      rW[j] = *reinterpret_cast<const u32x4*>(gW[j] + k0);
-    }
+        rA[p][q] = av[q] ? *reinterpret_cast<const u32x4*>(gA[p][q] + k0) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int q = 0; q < WP; ++q) rW[q] = *reinterpret_cast<const u32x4*>(gW[q] + k0);
   };
-  auto store_slab = [&]() {
+  auto store = [&](int buf) {
+    u32x4* S = smem + buf * STAGE;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int q = 0; q < AP; ++q)
 #pragma unroll
-      for (int p = 0; p < NP; ++p) *reinterpret_cast<u32x4*>(&sA[p][ldr[j]][ldk[j]]) = rA[p][j];
-      *reinterpret_cast<u32x4*>(&sW[ldr[j]][ldk[j]]) = rW[j];
-    }
+      for (int p = 0; p < NP; ++p) S[p * ACH + big_swz(ar[q], ac[q])] = rA[p][q];
+#pragma unroll
+    for (int q = 0; q < WP; ++q) S[NP * ACH + big_swz(wr[q], wc[q])] = rW[q];
   };
 
-  f32x4 acc[2][2];
+  f32x4 acc[4][4];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = K / BK;
-  load_slab(0);
-  store_slab();
+  const int nk = kspan / BK;
+  load(0);
+  store(0);
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) load_slab((kt + 1) * BK);
+    const bool more = kt + 1 < nk;
+    if (more) load((kt + 1) * BK);
+    const u32x4* S = smem + (kt & 1) * STAGE;
 #pragma unroll
     for (int ks = 0; ks < BK / 32; ++ks) {
-      bf16x8 wf[2];
+      const int ch = ks * 4 + g;
+      bf16x8 wf[4];
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
-        wf[ct] = *reinterpret_cast<const bf16x8*>(&sW[wn * 32 + ct * 16 + c][ks * 32 + g * 8]);
+      for (int ct = 0; ct < 4; ++ct)
+        wf[ct] = __builtin_bit_cast(bf16x8, S[NP * ACH + big_swz(wn * 64 + ct * 16 + c, ch)]);
 #pragma unroll
-      for (int rg = 0; rg < 2; ++rg) {
+      for (int rg = 0; rg < 4; ++rg) {
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sA[p][wm * 32 + rg * 16 + c][ks * 32 + g * 8]);
+          const bf16x8 a = __builtin_bit_cast(bf16x8, S[p * ACH + big_swz(wm * 64 + rg * 16 + c, ch)]);
 #pragma unroll
-          for (int ct = 0; ct < 2; ++ct) acc[rg][ct] = mfma(a, wf[ct], acc[rg][ct]);
+          for (int ct = 0; ct < 4; ++ct) acc[rg][ct] = mfma(a, wf[ct], acc[rg][ct]);
         }
       }
     }
+    if (more) store((kt + 1) & 1);
     __syncthreads();
-    if (kt + 1 < nk) {
-      store_slab();
-      __syncthreads();
-    }
   }
 #pragma unroll
-  for (int rg = 0; rg < 2; ++rg)
+  for (int ct = 0; ct < 4; ++ct) {
+    const int tile = tile0 + wn * 4 + ct;
+    if (tile >= ga.n_tiles) break;  // uniform over the wave
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
-      epilogue<EPI>(ga.ep, st, tile0 + wn * 2 + ct, row0 + wm * 32 + rg * 16, acc[rg][ct], lane, 0);
+    for (int rg = 0; rg < 4; ++rg) epilogue<EPI>(ga.ep, st, tile, row0 + wm * 64 + rg * 16, acc[rg][ct], lane, kc);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -993,20 +957,28 @@ hipError_t launch_kv_finish(const float* part, int kc, int M, int Mp, int n_laye
   return hipGetLastError();
 }
 
-SkinnyPlan skinny_plan(int n_tiles, int K, bool may_split) {
-  SkinnyPlan p;
-  p.nc = (n_tiles % 8 == 0 && n_tiles >= 1024) ? 8 : (n_tiles % 4 == 0 ? 4 : (n_tiles % 2 == 0 ? 2 : 1));
+GemmPlan gemm_plan(int n_tiles, int K, int Mp, bool may_split) {
+  GemmPlan p;
   p.kc = 1;
-  if (may_split) {
-    const int waves = n_tiles / p.nc * kSkinnyWaves;
-    const int chunk = kSkinnyWaves * 64;  // K granularity of one chunk: 64 per wave
-    while (p.kc * 2 <= kMaxKc && p.kc * 2 * waves <= 3072 && K % (p.kc * 2 * chunk) == 0) p.kc *= 2;
+  if (Mp <= 32) {
+    p.nc = (n_tiles % 8 == 0 && n_tiles >= 1024) ? 8 : (n_tiles % 4 == 0 ? 4 : (n_tiles % 2 == 0 ? 2 : 1));
+    if (may_split) {
+      const int waves = n_tiles / p.nc * kSkinnyWaves;
+      const int chunk = kSkinnyWaves * 64;  // K granularity of one chunk: 64 per wave
+      while (p.kc * 2 <= kMaxKc && p.kc * 2 * waves <= 3072 && K % (p.kc * 2 * chunk) == 0) p.kc *= 2;
+    }
+  } else {
+    p.nc = kBigBN / 16;
+    if (may_split) {  // aim for about two workgroups per CU
+      const int wgs = (Mp / kBigBM) * ((n_tiles + p.nc - 1) / p.nc);
+      while (p.kc * 2 <= kMaxKc && p.kc * 2 * wgs <= 512 && K % (p.kc * 2 * kBigBK) == 0) p.kc *= 2;
+    }
   }
   return p;
 }
 
 template <int EPI, int MAP, bool SPLIT, int RG>
-static hipError_t skinny_nc(const GemmArgs& g, const SeqTable& st, const SkinnyPlan& p, hipStream_t s) {
+static hipError_t skinny_nc(const GemmArgs& g, const SeqTable& st, const GemmPlan& p, hipStream_t s) {
   const dim3 grid(g.n_tiles / p.nc, p.kc), blk(kSkinnyWaves * 64);
   switch (p.nc) {
     case 8: hipLaunchKernelGGL((k_skinny<EPI, MAP, 8, RG, SPLIT>), grid, blk, 0, s, g, st); break;
@@ -1019,30 +991,29 @@ static hipError_t skinny_nc(const GemmArgs& g, const SeqTable& st, const SkinnyP
 
 template <int EPI, int MAP, bool SPLIT>
 static hipError_t gemm_dispatch(const GemmArgs& g, const SeqTable& st, int Mp, hipStream_t s) {
+  const GemmPlan p = gemm_plan(g.n_tiles, g.K, Mp, EPI == EPI_PARTIAL);
   if (Mp <= 32) {
-    if (g.K % (kSkinnyWaves * 64)) return hipErrorInvalidValue;
-    const SkinnyPlan p = skinny_plan(g.n_tiles, g.K, EPI == EPI_PARTIAL);
+    if (g.K % (kSkinnyWaves * 64) || Mp % 16) return hipErrorInvalidValue;
     return Mp <= 16 ? skinny_nc<EPI, MAP, SPLIT, 1>(g, st, p, s) : skinny_nc<EPI, MAP, SPLIT, 2>(g, st, p, s);
   }
-  if constexpr (EPI == EPI_PARTIAL || MAP == MAP_QKV || MAP == MAP_KVL) {
-    return hipErrorInvalidValue;  // many-row GEMMs apply their epilogue directly
-  } else {
-    if (g.n_tiles % 4 || g.K % 64) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((k_gemm_tiled<EPI, MAP, SPLIT>), dim3(g.n_tiles / 4, Mp / 64), dim3(256), 0, s, g, st);
-    return hipGetLastError();
+  if (Mp % kBigBM || g.K % (p.kc * kBigBK)) return hipErrorInvalidValue;
+  constexpr int NP = SPLIT ? 2 : 1;
+  const int lds = 2 * (NP * kBigBM + kBigBN) * kBigBK * 2;  // bytes: two buffers of A planes + W
+  static bool attr_set = false;  // the dynamic-LDS limit is raised once per instantiation
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute((const void*)k_gemm_big<EPI, MAP, SPLIT>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
   }
+  const int mt = Mp / kBigBM, nt = (g.n_tiles + p.nc - 1) / p.nc;
+  hipLaunchKernelGGL((k_gemm_big<EPI, MAP, SPLIT>), dim3(mt * p.kc * nt), dim3(512), lds, s, g, st, mt, p.kc);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm(const GemmArgs& g, const SeqTable& st, int Mp, hipStream_t s) {
   const bool split = g.a_lo != nullptr;
   switch (g.epi) {
-    case EPI_SPLIT:
-      return split ? gemm_dispatch<EPI_SPLIT, MAP_PLAIN, true>(g, st, Mp, s)
-                   : gemm_dispatch<EPI_SPLIT, MAP_PLAIN, false>(g, st, Mp, s);
-    case EPI_QKV:
-      return gemm_dispatch<EPI_QKV, MAP_ROPE, true>(g, st, Mp, s);
-    case EPI_RESID:
-      return gemm_dispatch<EPI_RESID, MAP_PLAIN, true>(g, st, Mp, s);
     case EPI_SWIGLU:
       return gemm_dispatch<EPI_SWIGLU, MAP_SWIGLU, true>(g, st, Mp, s);
     case EPI_ARGMAX:
@@ -1115,7 +1086,7 @@ hipError_t launch_attention(const u16* q_hi, const u16* q_lo, const u16* kv_cach
 }
 
 int argmax_parts(int n_tiles, int Mp) {
-  return Mp <= 32 ? n_tiles / skinny_plan(n_tiles, 0, false).nc : n_tiles;
+  return Mp <= 32 ? n_tiles / gemm_plan(n_tiles, 0, Mp, false).nc : n_tiles;
 }
 
 hipError_t launch_argmax_reduce(const unsigned long long* part, int n_parts, int Mp, int n_seqs,

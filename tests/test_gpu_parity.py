@@ -118,6 +118,9 @@ def test_tiny_config(torch_cuda):
     ((50,), 2, 0.1, 0.05, "block 2"),
     ((128,), 16, 0.1, 0.05, "gain jitter"),
     ((300,) * 5, 32, 0.0, 0.03, "five seqs B32 M160"),
+    ((20, 5, 0, 33, 64, 7, 100, 12), 16, 0.0, 0.05, "eight seqs M128 big tiles"),
+    (tuple(range(3, 3 + 16 * 13, 13)), 16, 0.1, 0.05, "sixteen seqs M256 big tiles"),
+    ((130, 64, 200, 9), 32, 0.0, 0.05, "four seqs B32 M128 big tiles"),
 ])
 def test_tiny_variants(torch_cuda, lens, block, jitter, std, label):
     _tiny_case(I.spec("tiny"), lens, block, jitter=jitter, std=std, label=label)
