@@ -13,6 +13,10 @@ the hot path once, for every sequence of the workload:
                          dflash_fuse_ctx followed by dflash_draft_block);
   2. dflash_accept_len   accepted-prefix scan against constructed target tokens.
 
+--denoise-steps S > 1 adds S - 1 further passes over the block
+(dflash_draft_refine, each fed the previous pass's drafts), the multi-step
+alternative that the block size / steps efficiency trade-off compares against.
+
 Before each step the host rolls every context back by B positions (metadata
 only), so each step sees the same context length and does identical work.
 Inputs are seeded synthetic tensors already resident in HBM.  The default
@@ -83,6 +87,22 @@ def stage_work(spec, stage: str, rows: int, ctx_keys: int = 0):
     raise KeyError(stage)
 
 
+def pass_work(spec):
+    """Algorithmic (bytes, flops) of one further draft pass over the block
+    (no appended rows): layers, attention over context + block, LM head."""
+    B, n, L = spec.block, spec.n_seqs, spec.n_layers
+    M = n * B
+    keys = sum(c + B for c in spec.ctx_lens)
+    by, fl = stage_work(spec, "lm_head", n * (B - 1))
+    for st in ("qkv", "oproj", "gate_up", "down"):
+        b, f = stage_work(spec, st, M)
+        by, fl = by + L * b, fl + L * f
+    b, f = stage_work(spec, "attention", M, keys)
+    by, fl = by + L * b, fl + L * f
+    by += L * 2 * spec.hidden * 2 + spec.hidden * 2
+    return by, fl
+
+
 def step_work(spec):
     """Algorithmic (bytes, flops) of one step (append B + draft + accept)."""
     B, n, L = spec.block, spec.n_seqs, spec.n_layers
@@ -109,9 +129,10 @@ def step_work(spec):
 # ----------------------------------------------------------------------------
 
 class Workload:
-    def __init__(self, spec, weights, torch, B_, two_call=False):
+    def __init__(self, spec, weights, torch, B_, two_call=False, denoise_steps=1):
         self.spec, self.torch, self.B = spec, torch, B_
         self.two_call = two_call
+        self.denoise_steps = denoise_steps
         I = _inputs()
         n, blk = spec.n_seqs, spec.block
         self.cfg = B_.Config.from_spec(spec, max_block=max(blk, 16))
@@ -160,6 +181,9 @@ class Workload:
         else:
             B_.step(self.model, self.ctx, self.step_feats, self.n_new, self.anchors, s.block, self.ws,
                     draft=self.draft)
+        if self.denoise_steps > 1:
+            B_.draft_refine(self.model, self.ctx, self.anchors, s.block, self.denoise_steps - 1, self.ws,
+                            init_tokens=self.draft, draft=self.draft)
         if hasattr(self, "target"):
             B_.accept_len(self.draft, self.target, s.block, self.accept, self.next_anchor)
 
@@ -274,6 +298,8 @@ def main(argv=None) -> int:
     ap.add_argument("--breakdown", action="store_true", help="also time every stage (extra passes)")
     ap.add_argument("--two-call", action="store_true",
                     help="step as dflash_fuse_ctx + dflash_draft_block instead of the fused dflash_step")
+    ap.add_argument("--denoise-steps", type=int, default=1,
+                    help="draft passes per block (1 = the single-pass drafter)")
     ap.add_argument("--graph", action="store_true",
                     help="replay the step as one captured HIP graph (identical steps, so identical work)")
     args = ap.parse_args(argv)
@@ -301,13 +327,17 @@ def main(argv=None) -> int:
     copy_gbs = copy_bandwidth(torch)
     log(f"device copy bandwidth {copy_gbs:.0f} GB/s")
 
-    wl = Workload(spec, weights, torch, B_, two_call=args.two_call)
+    S = args.denoise_steps
+    if S < 1 or S > 65:
+        print("--denoise-steps must be in [1, 65]", file=sys.stderr)
+        return 2
+    wl = Workload(spec, weights, torch, B_, two_call=args.two_call, denoise_steps=S)
     log("workload resident; warming up")
     for _ in range(args.warmup):
         wl.step()
     torch.cuda.synchronize()
 
-    n_launch = {"lm_head": 1, "fusion": 1}.get(args.probe, spec.n_layers)
+    n_launch = {"lm_head": S, "fusion": 1}.get(args.probe, spec.n_layers * S)
     run = wl.step
     if args.graph:
         # the probe's events are not captured: arm it after capture only for eager replays
@@ -341,6 +371,9 @@ def main(argv=None) -> int:
     n, blk = spec.n_seqs, spec.block
     draft_tok_s = n * (blk - 1) / (ms_step * 1e-3)
     by, fl = step_work(spec)
+    if S > 1:
+        pb_, pf_ = pass_work(spec)
+        by, fl = by + (S - 1) * pb_, fl + (S - 1) * pf_
 
     rows = n * (blk - 1) if args.probe == "lm_head" else n * blk
     keys = sum(c + blk for c in spec.ctx_lens)
@@ -368,7 +401,7 @@ def main(argv=None) -> int:
         breakdown = {}
         reps = 10
         for st in ("qkv", "attention", "oproj", "gate_up", "down", "lm_head", "fusion", "kv_proj"):
-            B_.probe_arm(wl.model, st, 64 * reps)
+            B_.probe_arm(wl.model, st, 64 * S * reps)
             for _ in range(reps):
                 wl.step()
             ms, cnt, _ = B_.probe_read(wl.model)
@@ -379,6 +412,8 @@ def main(argv=None) -> int:
             b_, f_ = stage_work(spec, st, r_, keys)
             per_layer = st not in ("lm_head", "fusion")
             b_, f_ = (b_ * spec.n_layers, f_ * spec.n_layers) if per_layer else (b_, f_)
+            if st not in ("fusion", "kv_proj"):  # once per pass
+                b_, f_ = b_ * S, f_ * S
             st_ms = ms / reps
             breakdown[st] = {"us_per_step": round(st_ms * 1e3, 1), "launches_per_step": cnt // reps,
                              "GB_s": round(b_ / (st_ms * 1e-3) / 1e9, 1),
@@ -417,9 +452,11 @@ def main(argv=None) -> int:
                          f"vocab {spec.vocab}, fusion {spec.fused_width}->{spec.hidden}; {n} sequence(s), "
                          f"context {spec.ctx_lens[0] if n == 1 else list(spec.ctx_lens)}, block {blk}; "
                          f"step = append {blk} verified positions + draft pass + accept scan"
-                         f"{' (two calls)' if args.two_call else ' (dflash_step)'}"),
+                         f"{' (two calls)' if args.two_call else ' (dflash_step)'}"
+                         f"{f' + {S - 1} refinement pass(es)' if S > 1 else ''}"),
             "global_batch": n,
             "block": blk,
+            "denoise_steps": S,
             "seq_len": max(spec.ctx_lens),
             "parallelism": "single GPU",
         },

@@ -21,7 +21,7 @@ STATUS = {0: "DFLASH_OK", -1: "DFLASH_EINVAL", -2: "DFLASH_ESHAPE", -3: "DFLASH_
 # Every symbol include/dflash.h declares.
 EXPORTS = ("dflash_weight_count", "dflash_model_create", "dflash_model_destroy", "dflash_ctx_bytes",
            "dflash_ctx_create", "dflash_ctx_destroy", "dflash_ctx_length", "dflash_ctx_truncate",
-           "dflash_workspace_bytes", "dflash_fuse_ctx", "dflash_draft_block", "dflash_step", "dflash_accept_len",
+           "dflash_workspace_bytes", "dflash_fuse_ctx", "dflash_draft_block", "dflash_draft_refine", "dflash_step", "dflash_accept_len",
            "dflash_probe_arm", "dflash_probe_read", "dflash_status_str", "dflash_last_error")
 
 # Stages a measurement probe can bracket (dflash_stage in include/dflash.h).
@@ -82,6 +82,8 @@ def lib():
         L.dflash_fuse_ctx.restype = ctypes.c_int
         L.dflash_draft_block.argtypes = [vp, vp, vp, i32, vp, vp, vp, sz, vp]
         L.dflash_draft_block.restype = ctypes.c_int
+        L.dflash_draft_refine.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, vp, sz, vp]
+        L.dflash_draft_refine.restype = ctypes.c_int
         L.dflash_step.argtypes = [vp, vp, vp, ctypes.POINTER(i32), vp, i32, vp, vp, vp, sz, vp]
         L.dflash_step.restype = ctypes.c_int
         L.dflash_accept_len.argtypes = [vp, vp, i32, i32, vp, vp, vp]
@@ -206,6 +208,18 @@ def draft_block(model: Model, ctx: Context, anchors, block: int, ws, draft=None,
         draft = torch.empty((ctx.n_seqs, block - 1), dtype=torch.int32, device=anchors.device)
     check(lib().dflash_draft_block(model.handle, ctx.handle, _ptr(anchors), block, _ptr(draft), _ptr(logits),
                                    _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    return draft
+
+
+def draft_refine(model: Model, ctx: Context, anchors, block: int, n_steps: int, ws, init_tokens=None, draft=None,
+                 logits=None, stream=None):
+    """n_steps denoising passes; each later pass feeds the previous pass's drafts."""
+    import torch
+    if draft is None:
+        draft = torch.empty((ctx.n_seqs, block - 1), dtype=torch.int32, device=anchors.device)
+    check(lib().dflash_draft_refine(model.handle, ctx.handle, _ptr(anchors), _ptr(init_tokens), block, n_steps,
+                                    _ptr(draft), _ptr(logits), _ptr(ws), ws.numel() * ws.element_size(),
+                                    _stream(stream)))
     return draft
 
 

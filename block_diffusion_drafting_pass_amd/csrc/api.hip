@@ -475,9 +475,10 @@ struct Append {
 };
 
 // The draft pass over block positions lens[b] .. lens[b] + block - 1.
+// tokens: NULL (mask tokens) or device [n_seqs][block-1] tokens for rows 1..block-1.
 int draft_impl(const dflash_model* model, const dflash_ctx* ctx, const int64_t* lens, const int32_t* anchors,
-               int block, int32_t* draft, float* logits, char* wsb, const WsLayout& W, hipStream_t s,
-               const Append* ap) {
+               const int32_t* tokens, int block, int32_t* draft, float* logits, char* wsb, const WsLayout& W,
+               hipStream_t s, const Append* ap) {
   const dflash_config& c = model->cfg;
   const int n = ctx->n_seqs;
   float* x = (float*)(wsb + W.x);
@@ -579,7 +580,7 @@ int draft_impl(const dflash_model* model, const dflash_ctx* ctx, const int64_t* 
     if (e != hipSuccess) return hip_fail(e, "step: fusion GEMM");
   }
 
-  e = launch_resid_norm(x, nullptr, 0, 0, anchors, model->embed, block, c.mask_token_id, c.vocab,
+  e = launch_resid_norm(x, nullptr, 0, 0, anchors, tokens, model->embed, block, c.mask_token_id, c.vocab,
                         model->layers[0].attn_norm, qin_hi, qin_lo, H, M, M, c.rms_eps, s);
   if (e != hipSuccess) return hip_fail(e, "draft_block: embed + attention norm");
   for (int l = 0; l < c.n_layers; ++l) {
@@ -619,7 +620,7 @@ int draft_impl(const dflash_model* model, const dflash_ctx* ctx, const int64_t* 
     model->probe.stop(DFLASH_STAGE_OPROJ, s);
     if (e != hipSuccess) return hip_fail(e, "draft_block: output projection");
 
-    e = launch_resid_norm(x, part, kc_o, Mp, nullptr, nullptr, block, 0, c.vocab,
+    e = launch_resid_norm(x, part, kc_o, Mp, nullptr, nullptr, nullptr, block, 0, c.vocab,
                           Lw.mlp_norm, a_hi, a_lo, H, M, M, c.rms_eps, s);
     if (e != hipSuccess) return hip_fail(e, "draft_block: MLP norm");
 
@@ -645,7 +646,7 @@ int draft_impl(const dflash_model* model, const dflash_ctx* ctx, const int64_t* 
 
     const bool last = l + 1 == c.n_layers;
     const u16* next_gain = last ? model->final_norm : model->layers[l + 1].attn_norm;
-    e = launch_resid_norm(x, part, kc_d, Mp, nullptr, nullptr, block, 0, c.vocab,
+    e = launch_resid_norm(x, part, kc_d, Mp, nullptr, nullptr, nullptr, block, 0, c.vocab,
                           next_gain, last ? a_hi : qin_hi, last ? a_lo : qin_lo, H, M, M, c.rms_eps, s);
     if (e != hipSuccess) return hip_fail(e, "draft_block: residual + norm");
   }
@@ -689,8 +690,30 @@ int dflash_draft_block(const dflash_model* model, const dflash_ctx* ctx, const i
   const WsLayout W = ws_layout(&model->cfg, ctx->n_seqs, block, 0);
   if (ws_bytes < W.draft_end)
     return fail(DFLASH_EWORKSPACE, "workspace holds %zu bytes, %zu needed", ws_bytes, W.draft_end);
-  return draft_impl(model, ctx, ctx->len.data(), anchors, block, draft, logits, (char*)ws, W, (hipStream_t)stream,
-                    nullptr);
+  return draft_impl(model, ctx, ctx->len.data(), anchors, nullptr, block, draft, logits, (char*)ws, W,
+                    (hipStream_t)stream, nullptr);
+}
+
+int dflash_draft_refine(const dflash_model* model, const dflash_ctx* ctx, const int32_t* anchors,
+                        const int32_t* init_tokens, int32_t block, int32_t n_steps, int32_t* draft, float* logits,
+                        void* ws, size_t ws_bytes, dflash_stream stream) {
+  int rc = check_draft_args(model, ctx, anchors, block, draft, logits, ws);
+  if (rc) return rc;
+  if (n_steps < 1 || n_steps > 64) return fail(DFLASH_EINVAL, "n_steps %d outside [1, 64]", n_steps);
+  if (init_tokens && !aligned(init_tokens, 4)) return fail(DFLASH_EALIGN, "init_tokens must be 4-byte aligned");
+  const WsLayout W = ws_layout(&model->cfg, ctx->n_seqs, block, 0);
+  if (ws_bytes < W.draft_end)
+    return fail(DFLASH_EWORKSPACE, "workspace holds %zu bytes, %zu needed", ws_bytes, W.draft_end);
+  // each pass reads its tokens in its first kernel and writes draft in its
+  // last, so draft can carry the previous pass's drafts into the next pass
+  const int32_t* toks = init_tokens;
+  for (int step = 0; step < n_steps; ++step) {
+    rc = draft_impl(model, ctx, ctx->len.data(), anchors, toks, block, draft, step + 1 == n_steps ? logits : nullptr,
+                    (char*)ws, W, (hipStream_t)stream, nullptr);
+    if (rc) return rc;
+    toks = draft;
+  }
+  return DFLASH_OK;
 }
 
 int dflash_step(const dflash_model* model, dflash_ctx* ctx, const void* features, const int32_t* n_new,
@@ -727,7 +750,8 @@ int dflash_step(const dflash_model* model, dflash_ctx* ctx, const void* features
   ap.R = (int)total;
   ap.n_new = n_new;
   ap.old_len = ctx->len.data();
-  rc = draft_impl(model, ctx, lens.data(), anchors, block, draft, logits, (char*)ws, W, (hipStream_t)stream, &ap);
+  rc = draft_impl(model, ctx, lens.data(), anchors, nullptr, block, draft, logits, (char*)ws, W, (hipStream_t)stream,
+                  &ap);
   if (rc) return rc;
   ctx->len = lens;
   return DFLASH_OK;

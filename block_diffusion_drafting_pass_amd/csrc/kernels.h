@@ -94,13 +94,15 @@ inline int rows_pad(int m) { return m <= 32 ? (m + 15) / 16 * 16 : (m + 127) / 1
 
 hipError_t launch_gemm(const GemmArgs& g, const SeqTable& st, int Mp, hipStream_t s);
 
-// x[row] = E[token] (token: anchor for block row 0, the mask id otherwise), or
+// x[row] = E[token] (token: anchor for block row 0; for rows i >= 1 the mask
+// id, or block_tokens[seq][i-1] when given), or
 // x[row] += sum over kc of part[kc][row] (fixed kc order; part_rows = the
 // partials' row stride per chunk); then out = hi/lo(gain * x / sqrt(mean(x^2)
 // + eps)) for rows < M.  Rows M..out_rows-1 of out are zero.
 hipError_t launch_resid_norm(float* x, const float* part, int kc, int part_rows, const int32_t* anchors,
-                             const u16* embed, int block, int mask_id, int vocab, const u16* gain, u16* out_hi,
-                             u16* out_lo, int H, int M, int out_rows, float eps, hipStream_t s);
+                             const int32_t* block_tokens, const u16* embed, int block, int mask_id, int vocab,
+                             const u16* gain, u16* out_hi, u16* out_lo, int H, int M, int out_rows, float eps,
+                             hipStream_t s);
 // out[row][j] = hi/lo(sum over kc of part[kc][row][j]) for rows < M (part_rows:
 // the partials' row stride per chunk); rows M..out_rows-1 of out are zero.
 hipError_t launch_reduce_split(const float* part, int kc, int part_rows, int N, u16* out_hi, u16* out_lo, int M,

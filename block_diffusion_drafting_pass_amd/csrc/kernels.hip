@@ -688,6 +688,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pa
 // are zero.
 __global__ __launch_bounds__(1024) void k_resid_norm(float* __restrict__ x, const float* __restrict__ part,
                                                      int kc, int part_rows, const int32_t* __restrict__ anchors,
+                                                     const int32_t* __restrict__ block_tokens,
                                                      const u16* __restrict__ E, int block, int mask_id, int vocab,
                                                      const u16* __restrict__ gain, u16* __restrict__ out_hi,
                                                      u16* __restrict__ out_lo, int H, int M, float eps) {
@@ -704,7 +705,8 @@ __global__ __launch_bounds__(1024) void k_resid_norm(float* __restrict__ x, cons
   float* xr = x + (size_t)row * H;
   const u16* er = nullptr;
   if (E) {
-    int tok = (row % block == 0) ? anchors[row / block] : mask_id;
+    const int b = row / block, i = row % block;
+    int tok = i == 0 ? anchors[b] : (block_tokens ? block_tokens[b * (block - 1) + i - 1] : mask_id);
     tok = tok < 0 ? 0 : (tok >= vocab ? vocab - 1 : tok);
     er = E + (size_t)tok * H;
   }
@@ -923,11 +925,12 @@ __global__ __launch_bounds__(256) void k_accept(const int32_t* __restrict__ draf
 // ---------------------------------------------------------------------------
 
 hipError_t launch_resid_norm(float* x, const float* part, int kc, int part_rows, const int32_t* anchors,
-                             const u16* embed, int block, int mask_id, int vocab, const u16* gain, u16* out_hi,
-                             u16* out_lo, int H, int M, int out_rows, float eps, hipStream_t s) {
+                             const int32_t* block_tokens, const u16* embed, int block, int mask_id, int vocab,
+                             const u16* gain, u16* out_hi, u16* out_lo, int H, int M, int out_rows, float eps,
+                             hipStream_t s) {
   if (kc > kMaxKc || out_rows < M) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_resid_norm, dim3(out_rows), dim3(1024), 0, s, x, part, kc, part_rows, anchors, embed, block,
-                     mask_id, vocab, gain, out_hi, out_lo, H, M, eps);
+  hipLaunchKernelGGL(k_resid_norm, dim3(out_rows), dim3(1024), 0, s, x, part, kc, part_rows, anchors, block_tokens,
+                     embed, block, mask_id, vocab, gain, out_hi, out_lo, H, M, eps);
   return hipGetLastError();
 }
 

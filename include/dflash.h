@@ -157,6 +157,20 @@ int dflash_draft_block(const dflash_model* model, const dflash_ctx* ctx, const i
                        int32_t block, int32_t* draft, float* logits, void* ws, size_t ws_bytes,
                        dflash_stream stream);
 
+/* Several denoising passes over the block (forum post, section 1: a draft's
+ * efficiency is block size over diffusion steps times the acceptance rate;
+ * DFlash uses one step).  The pages do not state how a later step re-masks;
+ * this takes the plainest reading: pass 1 reads init_tokens (device int32
+ * [n_seqs][block-1] for positions 1..block-1, or NULL for mask tokens) and
+ * every later pass feeds the previous pass's drafts in their place.  draft
+ * and logits (NULL or as for dflash_draft_block) hold the last pass's result;
+ * init_tokens may alias draft.  n_steps = 1 with init_tokens = NULL is
+ * dflash_draft_block.  1 <= n_steps <= 64; other arguments as for
+ * dflash_draft_block. */
+int dflash_draft_refine(const dflash_model* model, const dflash_ctx* ctx, const int32_t* anchors,
+                        const int32_t* init_tokens, int32_t block, int32_t n_steps, int32_t* draft, float* logits,
+                        void* ws, size_t ws_bytes, dflash_stream stream);
+
 /* One steady-state decode iteration in a single call: append n_new[b]
  * verified positions to each sequence (as dflash_fuse_ctx) and then draft a
  * block at the new lengths (as dflash_draft_block).  When the block rows and

@@ -59,7 +59,7 @@ def _rope_head(vec: List[float], pos: int, theta: float) -> List[float]:
 
 
 def brute_draft(cfg, weights: Dict, features: Sequence, anchors: Sequence[int], block: int,
-                use_rope: bool = True):
+                use_rope: bool = True, block_tokens=None):
     """Full pipeline for tiny shapes: ingest each sequence's features as context,
     then draft one block per sequence.
 
@@ -102,7 +102,10 @@ def brute_draft(cfg, weights: Dict, features: Sequence, anchors: Sequence[int], 
                 ctxK[l][t] = heads_k
                 ctxV[l][t] = heads_v
 
-        toks = [int(anchor)] + [cfg.mask_token_id] * (block - 1)
+        if block_tokens is None:
+            toks = [int(anchor)] + [cfg.mask_token_id] * (block - 1)
+        else:
+            toks = [int(anchor)] + [int(t) for t in block_tokens[b]]
         x = [list(E[tk]) for tk in toks]
         for l in range(L):
             P = lay[l]

@@ -219,13 +219,16 @@ class DraftResult:
 
 
 def draft_block(model: OracleModel, ctx: OracleContext, anchors: np.ndarray, block: int,
-                use_rope: bool = True, seqs: Optional[List[int]] = None) -> DraftResult:
+                use_rope: bool = True, seqs: Optional[List[int]] = None,
+                block_tokens: Optional[np.ndarray] = None) -> DraftResult:
     """One block-diffusion draft pass over every sequence (or the listed ones).
 
     The block is the anchor token followed by B-1 mask tokens at positions
     c_b .. c_b+B-1; it runs through all draft layers in a single pass (forward
     post, section 1; atlas summary "Approach"), attending to [context K/V |
-    block K/V] with no mask.  Rows 1..B-1 are the drafts.
+    block K/V] with no mask.  Rows 1..B-1 are the drafts.  block_tokens
+    ([n_seqs][B-1], indexed like anchors) replaces the mask tokens of rows
+    1..B-1 when given (a refinement pass, see ``refine``).
     """
     m = model
     seqs = list(range(len(anchors))) if seqs is None else list(seqs)
@@ -234,6 +237,8 @@ def draft_block(model: OracleModel, ctx: OracleContext, anchors: np.ndarray, blo
     E = m.weights["embed"]
     toks = np.full((n, B), m.mask_token_id, dtype=np.int64)
     toks[:, 0] = np.asarray(anchors, dtype=np.int64)[seqs]
+    if block_tokens is not None:
+        toks[:, 1:] = np.asarray(block_tokens, dtype=np.int64)[seqs]
     x = bf16_to_f64(E[toks.reshape(-1)]).reshape(n, B, H)
     pos = [ctx.pos_offset + ctx.length(b) + np.arange(B) for b in seqs]
 
@@ -263,6 +268,23 @@ def draft_block(model: OracleModel, ctx: OracleContext, anchors: np.ndarray, blo
         logits[:, v0:v1] = y @ bf16_to_f64(E[v0:v1]).T
     logits = logits.reshape(n, B - 1, m.vocab)
     return DraftResult(logits=logits, drafts=argmax_lowest(logits), hidden=x)
+
+
+def refine(model: OracleModel, ctx: OracleContext, anchors: np.ndarray, block: int, steps: int,
+           init_tokens: Optional[np.ndarray] = None) -> List[DraftResult]:
+    """Several denoising passes over one block (forum post, section 1: the
+    efficiency of a draft is block size over diffusion steps times the
+    acceptance rate; one step is DFlash's default).  The pages do not state
+    how a later step re-masks; this takes the plainest reading: every pass
+    after the first feeds the previous pass's drafts in place of the mask
+    tokens.  Returns the result of every pass; the last one is the draft."""
+    out: List[DraftResult] = []
+    toks = init_tokens
+    for _ in range(steps):
+        r = draft_block(model, ctx, anchors, block, block_tokens=toks)
+        out.append(r)
+        toks = r.drafts
+    return out
 
 
 def accept_len(draft: np.ndarray, target: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:

@@ -287,3 +287,82 @@ def test_step_capacity_error_leaves_lengths(torch_cuda):
 def test_step_q8_ctx1024(q8):
     spec5, w, dev = q8
     _step_case(spec5, w, dev, (1008,), (16,), 16, "5-layer step ctx 1008+16")
+
+
+# ----------------------------------------------------------------------------
+# several denoising passes over one block (block tokens fed back)
+# ----------------------------------------------------------------------------
+
+def _refine_case(spec, w, dev_w, lens, block, label, steps=2):
+    """refine(1, tokens) vs the oracle pass over the same tokens; refine(steps) vs
+    chained single passes (bitwise) and vs the oracle pass over the GPU's
+    previous drafts."""
+    import torch
+    spec = spec.with_(ctx_lens=tuple(lens), block=block)
+    say(f"refine {label}: lens={lens} block={block} steps={steps}")
+    run = GpuRun(spec, dev_w, capacity=[c + 8 for c in lens], max_new=sum(lens))
+    feats = _feats(spec, 1, lens)
+    run.ingest(feats)
+    n = len(lens)
+    anchors = I.gen_anchors(spec, 2)
+    a = torch.from_numpy(anchors).cuda()
+    rng = np.random.default_rng(block * 7 + n)
+    init = rng.integers(0, spec.vocab, size=(n, block - 1)).astype(np.int32)
+    init[:, ::3] = spec.mask_token_id  # some positions stay masked
+    model = O.OracleModel.from_spec(spec, w)
+    octx = O.OracleContext(model, n)
+    for b in range(n):
+        O.fuse_ctx(model, octx, b, feats[b])
+
+    def gpu(n_steps, tokens):
+        lg = torch.empty((n, block - 1, spec.vocab), dtype=torch.float32, device="cuda")
+        t = None if tokens is None else torch.from_numpy(np.ascontiguousarray(tokens, np.int32)).cuda()
+        d = B.draft_refine(run.model, run.ctx, a, block, n_steps, run.ws, init_tokens=t, logits=lg)
+        torch.cuda.synchronize()
+        return d.cpu().numpy(), lg.cpu().numpy()
+
+    d1, l1 = gpu(1, init)
+    assert_parity(l1, d1, O.draft_block(model, octx, anchors, block, block_tokens=init), f"{label} pass 1")
+    d2, l2 = gpu(2, init)
+    d2c, l2c = gpu(1, d1)
+    assert np.array_equal(d2, d2c), f"{label}: two passes differ from chained single passes"
+    assert np.array_equal(l2.view(np.uint32), l2c.view(np.uint32)), f"{label}: logits not bitwise equal"
+    assert_parity(l2, d2, O.draft_block(model, octx, anchors, block, block_tokens=d1), f"{label} pass 2")
+    if steps > 2:
+        ds, ls = gpu(steps, None)
+        prev = None
+        for _ in range(steps - 1):
+            prev, _ = gpu(1, prev)
+        assert_parity(ls, ds, O.draft_block(model, octx, anchors, block, block_tokens=prev), f"{label} pass {steps}")
+    # masked start, one pass: identical to dflash_draft_block
+    dm, lm = gpu(1, None)
+    db, lb = run.draft(anchors, block)
+    assert np.array_equal(dm, db) and np.array_equal(lm.view(np.uint32), lb.view(np.uint32))
+
+
+@pytest.mark.parametrize("lens,block,steps,label", [
+    ((128,), 16, 3, "tiny B16 three passes"),
+    ((37, 5, 0), 8, 2, "ragged three seqs B8"),
+    ((64, 200), 32, 2, "B32 two seqs tiled"),
+    ((20, 5, 0, 33, 64, 7, 100, 12), 4, 2, "eight seqs B4"),
+])
+def test_refine_tiny(torch_cuda, lens, block, steps, label):
+    spec = I.spec("tiny")
+    w = I.gen_weights(spec, seed=3, std=0.05)
+    _refine_case(spec, w, B.upload_weights(spec, w), lens, block, label, steps=steps)
+
+
+def test_refine_rejects_bad_step_counts(torch_cuda):
+    spec = I.spec("tiny").with_(ctx_lens=(4,))
+    w = I.gen_weights(spec, seed=0)
+    run = GpuRun(spec, B.upload_weights(spec, w), capacity=[8], max_new=8)
+    a = torch_cuda.zeros(1, dtype=torch_cuda.int32, device="cuda")
+    for bad in (0, -1, 65):
+        with pytest.raises(B.DFlashError) as e:
+            B.draft_refine(run.model, run.ctx, a, 16, bad, run.ws)
+        assert e.value.name == "DFLASH_EINVAL"
+
+
+def test_refine_q8_ctx1024_b8(q8):
+    spec5, w, dev = q8
+    _refine_case(spec5, w, dev, (1024,), 8, "5-layer ctx1024 B8")

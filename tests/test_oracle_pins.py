@@ -343,3 +343,46 @@ def test_accept_len_closed_form_on_constructed_targets(name):
     # mean of min(K, B-1) for K ~ Geometric(0.15) from 0: sum_{k=1}^{B-1} 0.85^k
     mean = sum(0.85 ** k for k in range(1, spec.block))
     assert abs(acc.mean() - mean) < 0.25
+
+
+# ----------------------------------------------------------------------------
+# multi-step refinement (denoising steps > 1)
+# ----------------------------------------------------------------------------
+
+def test_block_tokens_pass_matches_brute_force():
+    """A pass with given block tokens in place of the masks, against the
+    independent scalar evaluation fed the same tokens."""
+    model, w = _model(MICRO, 3)
+    ctx, feats = _ingest(model, MICRO, 3)
+    anchors = I.gen_anchors(MICRO, 3)
+    rng = np.random.default_rng(11)
+    toks = rng.integers(0, MICRO.vocab, size=(len(anchors), MICRO.block - 1))
+    res = O.draft_block(model, ctx, anchors, MICRO.block, block_tokens=toks)
+    bl, bd = brute.brute_draft(MICRO, w, feats, anchors, MICRO.block, block_tokens=toks.tolist())
+    np.testing.assert_allclose(res.logits, np.array(bl), rtol=0, atol=1e-12)
+    assert res.drafts.tolist() == bd
+
+
+def test_refine_one_step_is_the_single_pass_and_chains_passes():
+    model, w = _model(MICRO, 4)
+    ctx, feats = _ingest(model, MICRO, 4)
+    anchors = I.gen_anchors(MICRO, 4)
+    single = O.draft_block(model, ctx, anchors, MICRO.block)
+    passes = O.refine(model, ctx, anchors, MICRO.block, 3)
+    np.testing.assert_array_equal(passes[0].logits, single.logits)
+    # each later pass is the brute-force pass fed the previous pass's drafts
+    for s in (1, 2):
+        bl, bd = brute.brute_draft(MICRO, w, feats, anchors, MICRO.block,
+                                   block_tokens=passes[s - 1].drafts.tolist())
+        np.testing.assert_allclose(passes[s].logits, np.array(bl), rtol=0, atol=1e-12)
+        assert passes[s].drafts.tolist() == bd
+
+
+def test_block_tokens_equal_to_masks_reproduce_the_masked_pass():
+    model, _ = _model(MICRO, 6)
+    ctx, _ = _ingest(model, MICRO, 6)
+    anchors = I.gen_anchors(MICRO, 6)
+    masks = np.full((len(anchors), MICRO.block - 1), MICRO.mask_token_id)
+    a = O.draft_block(model, ctx, anchors, MICRO.block)
+    b = O.draft_block(model, ctx, anchors, MICRO.block, block_tokens=masks)
+    np.testing.assert_array_equal(a.logits, b.logits)
