@@ -21,7 +21,7 @@ STATUS = {0: "DFLASH_OK", -1: "DFLASH_EINVAL", -2: "DFLASH_ESHAPE", -3: "DFLASH_
 # Every symbol include/dflash.h declares.
 EXPORTS = ("dflash_weight_count", "dflash_model_create", "dflash_model_destroy", "dflash_ctx_bytes",
            "dflash_ctx_create", "dflash_ctx_destroy", "dflash_ctx_length", "dflash_ctx_truncate",
-           "dflash_workspace_bytes", "dflash_fuse_ctx", "dflash_draft_block", "dflash_draft_refine", "dflash_step", "dflash_accept_len",
+           "dflash_workspace_bytes", "dflash_fuse_ctx", "dflash_draft_block", "dflash_draft_refine", "dflash_draft_anchored", "dflash_step", "dflash_accept_len",
            "dflash_probe_arm", "dflash_probe_read", "dflash_status_str", "dflash_last_error")
 
 # Stages a measurement probe can bracket (dflash_stage in include/dflash.h).
@@ -84,6 +84,9 @@ def lib():
         L.dflash_draft_block.restype = ctypes.c_int
         L.dflash_draft_refine.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, vp, sz, vp]
         L.dflash_draft_refine.restype = ctypes.c_int
+        L.dflash_draft_anchored.argtypes = [vp, vp, i32, ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_int64), vp, vp,
+                                            i32, vp, vp, vp, sz, vp]
+        L.dflash_draft_anchored.restype = ctypes.c_int
         L.dflash_step.argtypes = [vp, vp, vp, ctypes.POINTER(i32), vp, i32, vp, vp, vp, sz, vp]
         L.dflash_step.restype = ctypes.c_int
         L.dflash_accept_len.argtypes = [vp, vp, i32, i32, vp, vp, vp]
@@ -220,6 +223,24 @@ def draft_refine(model: Model, ctx: Context, anchors, block: int, n_steps: int, 
     check(lib().dflash_draft_refine(model.handle, ctx.handle, _ptr(anchors), _ptr(init_tokens), block, n_steps,
                                     _ptr(draft), _ptr(logits), _ptr(ws), ws.numel() * ws.element_size(),
                                     _stream(stream)))
+    return draft
+
+
+def draft_anchored(model: Model, ctx: Context, block_seq: Sequence[int], anchor_pos: Sequence[int], anchors,
+                   block: int, ws, block_tokens=None, draft=None, logits=None, stream=None):
+    """Blocks anchored at given positions of shared contexts (each sees its
+    sequence's context before its anchor, and itself)."""
+    import torch
+    n = len(block_seq)
+    if len(anchor_pos) != n:
+        raise ValueError("block_seq and anchor_pos differ in length")
+    if draft is None:
+        draft = torch.empty((n, block - 1), dtype=torch.int32, device=anchors.device)
+    seq_arr = (ctypes.c_int32 * n)(*[int(v) for v in block_seq])
+    pos_arr = (ctypes.c_int64 * n)(*[int(v) for v in anchor_pos])
+    check(lib().dflash_draft_anchored(model.handle, ctx.handle, n, seq_arr, pos_arr, _ptr(anchors),
+                                      _ptr(block_tokens), block, _ptr(draft), _ptr(logits), _ptr(ws),
+                                      ws.numel() * ws.element_size(), _stream(stream)))
     return draft
 
 

@@ -107,7 +107,7 @@ int ctx_layout(const dflash_config* c, int32_t n_seqs, const int64_t* cap, CtxLa
 struct WsLayout {
   int M = 0, Mp = 0, max_splits = 0, R = 0, Rp = 0;
   size_t x = 0, a_hi = 0, a_lo = 0, qa_hi = 0, qa_lo = 0, b_hi = 0, b_lo = 0, q_hi = 0, q_lo = 0, part_o = 0,
-         part_ml = 0, amax = 0, part = 0, draft_end = 0;
+         part_ml = 0, amax = 0, part = 0, bkv = 0, draft_end = 0;
   size_t h_hi = 0, h_lo = 0, part_f = 0, ingest_end = 0;
   size_t total() const { return std::max(draft_end, ingest_end); }
 };
@@ -154,6 +154,8 @@ WsLayout ws_layout(const dflash_config* c, int n_seqs, int block, int64_t max_ne
         pb = std::max(pb, part_bytes((int)H / 16, fw, r, (int)H));
     W.part = take(pb);
   }
+  // block K/V of anchored blocks: one cache-layout tile per block and kv head
+  W.bkv = take((size_t)c->n_kv_heads * n_seqs * 4 * kTileKeys * c->head_dim * sizeof(u16));
   W.draft_end = o;
   o = 0;
   W.R = (int)std::min<int64_t>(std::max<int64_t>(max_new, 0), kIngestChunk);
@@ -474,13 +476,37 @@ struct Append {
   const int64_t* old_len = nullptr;
 };
 
-// The draft pass over block positions lens[b] .. lens[b] + block - 1.
-// tokens: NULL (mask tokens) or device [n_seqs][block-1] tokens for rows 1..block-1.
-int draft_impl(const dflash_model* model, const dflash_ctx* ctx, const int64_t* lens, const int32_t* anchors,
+// The blocks one draft pass drafts: block b sits at positions pos[b] ..
+// pos[b] + block - 1 and sees the first pos[b] context keys of cache
+// sequence seq[b].  sep: the blocks' own K/V go to the workspace and the
+// cache is only read (several blocks may share a sequence); otherwise they
+// go to the cache head-room right after the context (one block per
+// sequence).
+struct Blocks {
+  int n = 0;
+  int64_t pos[kMaxSeqs];
+  int32_t seq[kMaxSeqs];
+  bool sep = false;
+};
+
+// One block per sequence at positions lens[b] ..
+Blocks seq_blocks(const dflash_ctx* ctx, const int64_t* lens) {
+  Blocks bk;
+  bk.n = ctx->n_seqs;
+  for (int b = 0; b < bk.n; ++b) {
+    bk.pos[b] = lens[b];
+    bk.seq[b] = b;
+  }
+  return bk;
+}
+
+// tokens: NULL (mask tokens) or device [n][block-1] tokens for rows 1..block-1.
+int draft_impl(const dflash_model* model, const dflash_ctx* ctx, const Blocks& bk, const int32_t* anchors,
                const int32_t* tokens, int block, int32_t* draft, float* logits, char* wsb, const WsLayout& W,
                hipStream_t s, const Append* ap) {
   const dflash_config& c = model->cfg;
-  const int n = ctx->n_seqs;
+  const int n = bk.n;
+  u16* bkv = (u16*)(wsb + W.bkv);
   float* x = (float*)(wsb + W.x);
   u16* a_hi = (u16*)(wsb + W.a_hi);
   u16* a_lo = (u16*)(wsb + W.a_lo);
@@ -503,11 +529,13 @@ int draft_impl(const dflash_model* model, const dflash_ctx* ctx, const int64_t* 
   st.n = n;
   for (int b = 0; b < n; ++b) {
     st.row_start[b] = b * block;
-    st.pos_base[b] = (int32_t)lens[b];
-    st.slot_base[b] = (int32_t)ctx->L.slot_base[b];
+    st.pos_base[b] = (int32_t)bk.pos[b];
+    st.slot_base[b] = (int32_t)ctx->L.slot_base[bk.seq[b]];
   }
   st.row_start[n] = M;
   SeqTable sq = st;  // block rows, then the appended rows of each sequence at their own positions
+  if (bk.sep)  // block b's row i -> slot b * kTileKeys + i of the workspace block area
+    for (int b = 0; b < n; ++b) sq.slot_base[b] = b * kTileKeys - (int32_t)bk.pos[b];
   if (ap) {
     int e = n, off = M;
     for (int b = 0; b < n; ++b) {
@@ -523,7 +551,8 @@ int draft_impl(const dflash_model* model, const dflash_ctx* ctx, const int64_t* 
   }
   int max_tiles = 1;
   for (int b = 0; b < n; ++b)
-    max_tiles = std::max<int>(max_tiles, (int)((lens[b] + block + kTileKeys - 1) / kTileKeys));
+    max_tiles = std::max<int>(max_tiles, bk.sep ? (int)((bk.pos[b] + kTileKeys - 1) / kTileKeys) + 1
+                                                : (int)((bk.pos[b] + block + kTileKeys - 1) / kTileKeys));
   const int splits = std::min(W.max_splits, attention_splits(n * c.n_kv_heads, max_tiles));
 
   auto base_args = [&](const u16* ah, const u16* al, int lda, int K, int n_tiles, int epi, int map) {
@@ -580,6 +609,10 @@ int draft_impl(const dflash_model* model, const dflash_ctx* ctx, const int64_t* 
     if (e != hipSuccess) return hip_fail(e, "step: fusion GEMM");
   }
 
+  if (bk.sep) {
+    e = launch_clear_block_pad(bkv, n, c.n_kv_heads, c.head_dim, block, s);
+    if (e != hipSuccess) return hip_fail(e, "draft: clear block K/V padding");
+  }
   e = launch_resid_norm(x, nullptr, 0, 0, anchors, tokens, model->embed, block, c.mask_token_id, c.vocab,
                         model->layers[0].attn_norm, qin_hi, qin_lo, H, M, M, c.rms_eps, s);
   if (e != hipSuccess) return hip_fail(e, "draft_block: embed + attention norm");
@@ -601,13 +634,14 @@ int draft_impl(const dflash_model* model, const dflash_ctx* ctx, const int64_t* 
     e = launch_gemm(g, st, Mqp, s);
     if (e == hipSuccess)
       e = launch_qkv_finish(part, kc_qkv, Mq, Mqp, c.n_q_heads, c.n_kv_heads, c.head_dim, ctx->rope_cos(),
-                            ctx->rope_sin(), q_hi, q_lo, ctx->kv_cache(l), ctx->kv_tiles(), sq, s);
+                            ctx->rope_sin(), q_hi, q_lo, bk.sep ? bkv : ctx->kv_cache(l),
+                            bk.sep ? (int64_t)n : ctx->kv_tiles(), sq, s);
     model->probe.stop(DFLASH_STAGE_QKV, s);
     if (e != hipSuccess) return hip_fail(e, "draft_block: QKV projection");
 
     model->probe.start(DFLASH_STAGE_ATTENTION, s);
-    e = launch_attention(q_hi, q_lo, ctx->kv_cache(l), ctx->kv_tiles(), part_o, part_ml, a_hi, a_lo, n, block,
-                         c.n_q_heads, c.n_kv_heads, c.head_dim, splits, st, s);
+    e = launch_attention(q_hi, q_lo, ctx->kv_cache(l), ctx->kv_tiles(), bk.sep ? bkv : nullptr, part_o, part_ml,
+                         a_hi, a_lo, n, block, c.n_q_heads, c.n_kv_heads, c.head_dim, splits, st, s);
     model->probe.stop(DFLASH_STAGE_ATTENTION, s);
     if (e != hipSuccess) return hip_fail(e, "draft_block: attention");
 
@@ -690,8 +724,8 @@ int dflash_draft_block(const dflash_model* model, const dflash_ctx* ctx, const i
   const WsLayout W = ws_layout(&model->cfg, ctx->n_seqs, block, 0);
   if (ws_bytes < W.draft_end)
     return fail(DFLASH_EWORKSPACE, "workspace holds %zu bytes, %zu needed", ws_bytes, W.draft_end);
-  return draft_impl(model, ctx, ctx->len.data(), anchors, nullptr, block, draft, logits, (char*)ws, W,
-                    (hipStream_t)stream, nullptr);
+  return draft_impl(model, ctx, seq_blocks(ctx, ctx->len.data()), anchors, nullptr, block, draft, logits, (char*)ws,
+                    W, (hipStream_t)stream, nullptr);
 }
 
 int dflash_draft_refine(const dflash_model* model, const dflash_ctx* ctx, const int32_t* anchors,
@@ -707,13 +741,42 @@ int dflash_draft_refine(const dflash_model* model, const dflash_ctx* ctx, const 
   // each pass reads its tokens in its first kernel and writes draft in its
   // last, so draft can carry the previous pass's drafts into the next pass
   const int32_t* toks = init_tokens;
+  const Blocks bk = seq_blocks(ctx, ctx->len.data());
   for (int step = 0; step < n_steps; ++step) {
-    rc = draft_impl(model, ctx, ctx->len.data(), anchors, toks, block, draft, step + 1 == n_steps ? logits : nullptr,
-                    (char*)ws, W, (hipStream_t)stream, nullptr);
+    rc = draft_impl(model, ctx, bk, anchors, toks, block, draft, step + 1 == n_steps ? logits : nullptr, (char*)ws, W,
+                    (hipStream_t)stream, nullptr);
     if (rc) return rc;
     toks = draft;
   }
   return DFLASH_OK;
+}
+
+int dflash_draft_anchored(const dflash_model* model, const dflash_ctx* ctx, int32_t n_blocks,
+                          const int32_t* block_seq, const int64_t* anchor_pos, const int32_t* anchors,
+                          const int32_t* block_tokens, int32_t block, int32_t* draft, float* logits, void* ws,
+                          size_t ws_bytes, dflash_stream stream) {
+  int rc = check_draft_args(model, ctx, anchors, block, draft, logits, ws);
+  if (rc) return rc;
+  if (n_blocks < 1 || n_blocks > kMaxSeqs) return fail(DFLASH_EINVAL, "n_blocks %d outside [1, %d]", n_blocks, kMaxSeqs);
+  if (!block_seq || !anchor_pos) return fail(DFLASH_EINVAL, "block_seq or anchor_pos is NULL");
+  if (block_tokens && !aligned(block_tokens, 4)) return fail(DFLASH_EALIGN, "block_tokens must be 4-byte aligned");
+  Blocks bk;
+  bk.n = n_blocks;
+  bk.sep = true;
+  for (int j = 0; j < n_blocks; ++j) {
+    const int32_t sq = block_seq[j];
+    if (sq < 0 || sq >= ctx->n_seqs) return fail(DFLASH_EINVAL, "block_seq[%d] = %d outside [0, %d)", j, sq, ctx->n_seqs);
+    if (anchor_pos[j] < 0 || anchor_pos[j] > ctx->len[sq])
+      return fail(DFLASH_EINVAL, "anchor_pos[%d] = %lld outside [0, %lld] (length of sequence %d)", j,
+                  (long long)anchor_pos[j], (long long)ctx->len[sq], sq);
+    bk.pos[j] = anchor_pos[j];
+    bk.seq[j] = sq;
+  }
+  const WsLayout W = ws_layout(&model->cfg, n_blocks, block, 0);
+  if (ws_bytes < W.draft_end)
+    return fail(DFLASH_EWORKSPACE, "workspace holds %zu bytes, %zu needed", ws_bytes, W.draft_end);
+  return draft_impl(model, ctx, bk, anchors, block_tokens, block, draft, logits, (char*)ws, W, (hipStream_t)stream,
+                    nullptr);
 }
 
 int dflash_step(const dflash_model* model, dflash_ctx* ctx, const void* features, const int32_t* n_new,
@@ -750,8 +813,8 @@ int dflash_step(const dflash_model* model, dflash_ctx* ctx, const void* features
   ap.R = (int)total;
   ap.n_new = n_new;
   ap.old_len = ctx->len.data();
-  rc = draft_impl(model, ctx, lens.data(), anchors, nullptr, block, draft, logits, (char*)ws, W, (hipStream_t)stream,
-                  &ap);
+  rc = draft_impl(model, ctx, seq_blocks(ctx, lens.data()), anchors, nullptr, block, draft, logits, (char*)ws, W,
+                  (hipStream_t)stream, &ap);
   if (rc) return rc;
   ctx->len = lens;
   return DFLASH_OK;

@@ -118,9 +118,19 @@ hipError_t launch_qkv_finish(const float* part, int kc, int M, int Mp, int n_q, 
 hipError_t launch_kv_finish(const float* part, int kc, int M, int Mp, int n_layers, int n_kv, int head_dim,
                             const float* rope_cos, const float* rope_sin, u16* kv_cache0, size_t layer_stride,
                             int64_t kv_tiles, const SeqTable& st, hipStream_t s);
+// Block queries of sequence b (rows row_start[b] ..) against pos_base[b]
+// context keys from its cache slots (slot_base[b] ..) and the block's own
+// keys.  blk_kv null: the block keys follow the context keys in the cache;
+// otherwise they are tile b of blk_kv (n_seqs tiles per kv head), and the
+// cache is only read.
 hipError_t launch_attention(const u16* q_hi, const u16* q_lo, const u16* kv_cache, int64_t kv_tiles,
-                            float* part_o, float* part_ml, u16* o_hi, u16* o_lo, int n_seqs, int block,
-                            int n_q, int n_kv, int head_dim, int splits, const SeqTable& st, hipStream_t s);
+                            const u16* blk_kv, float* part_o, float* part_ml, u16* o_hi, u16* o_lo, int n_seqs,
+                            int block, int n_q, int n_kv, int head_dim, int splits, const SeqTable& st,
+                            hipStream_t s);
+// Zero slots block .. kTileKeys-1 of the n_blocks x n_kv block tiles of a
+// separate block K/V area (slots the block never writes; attention masks
+// them, and zeros keep 0 * value finite).
+hipError_t launch_clear_block_pad(u16* blk_kv, int n_blocks, int n_kv, int head_dim, int block, hipStream_t s);
 // draft[b][i-1] from the largest key of block row i over n_parts partial keys.
 hipError_t launch_argmax_reduce(const unsigned long long* part, int n_parts, int Mp, int n_seqs,
                                 int block, int32_t* draft, hipStream_t s);

@@ -445,6 +445,9 @@ __global__ __launch_bounds__(512) void k_gemm_big(GemmArgs ga, SeqTable st, int 
 // key tile kt (0 or 1) is key 8 (rho / 4) + 4 kt + rho % 4 of the half, so
 // lane group q ends up holding keys 8q .. 8q+7 — exactly one B fragment.
 // fp32 x fp32 products are taken as hi*hi + hi*lo + lo*hi.
+// The keys are either [context | block] in the cache, or (anchored blocks
+// that share a context) the context prefix in the cache followed by one
+// tile of the block's own keys kept apart in the workspace.
 // With one split the result is normalised and written directly; otherwise
 // partial (m, l, O) go to a workspace and the merge kernel combines them in
 // split order.
@@ -472,6 +475,7 @@ template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) void k_attn_tiles(const u16* __restrict__ q_hi,
                                                          const u16* __restrict__ q_lo,
                                                          const u16* __restrict__ kv, int64_t kv_tiles,
+                                                         const u16* __restrict__ bkv, int bkv_tiles,
                                                          float* __restrict__ part_o,
                                                          float* __restrict__ part_ml,
                                                          u16* __restrict__ o_hi, u16* __restrict__ o_lo,
@@ -494,12 +498,18 @@ __global__ __launch_bounds__(NW * 64) void k_attn_tiles(const u16* __restrict__ 
   const bool comp = wave < G * qtiles;
   const int h = gkv * G + wave % G, qt = wave / G;
 
-  const int n_keys = st.pos_base[b] + block;
-  const int ntile = (n_keys + kTileKeys - 1) / kTileKeys;
+  // keys in the cache (context, plus the block when it sits there), then
+  // with a separate block area one more tile holding the block's keys
+  const bool sep = bkv != nullptr;
+  const int n_keys = st.pos_base[b] + (sep ? 0 : block);
+  const int ctiles = (n_keys + kTileKeys - 1) / kTileKeys;
+  const int ntile = ctiles + (sep ? 1 : 0);
   const int tps = (ntile + splits - 1) / splits;
   const int t0 = s * tps, t1 = min(ntile, t0 + tps);
   const u32x4* src = reinterpret_cast<const u32x4*>(
       kv + kv_tile_offset(gkv, st.slot_base[b] / kTileKeys, kv_tiles, D));
+  const u32x4* bsrc = sep ? reinterpret_cast<const u32x4*>(bkv + kv_tile_offset(gkv, b, bkv_tiles, D)) : nullptr;
+  auto tile_ptr = [&](int t) { return t < ctiles ? src + (size_t)t * TILE_CH : bsrc; };
 
   const int qi = qt * 16 + c;
   const bool qvalid = comp && qi < block;
@@ -518,8 +528,9 @@ __global__ __launch_bounds__(NW * 64) void k_attn_tiles(const u16* __restrict__ 
 
   u32x4 stage[CPT];
   if (t0 < t1) {
+    const u32x4* tp = tile_ptr(t0);
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) stage[j] = src[(size_t)t0 * TILE_CH + tid + j * NT];
+    for (int j = 0; j < CPT; ++j) stage[j] = tp[tid + j * NT];
   }
   for (int t = t0; t < t1; ++t) {
     __syncthreads();
@@ -527,8 +538,9 @@ __global__ __launch_bounds__(NW * 64) void k_attn_tiles(const u16* __restrict__ 
     for (int j = 0; j < CPT; ++j) lds[lds_chunk<D>(tid + j * NT)] = stage[j];
     __syncthreads();
     if (t + 1 < t1) {
+      const u32x4* tp = tile_ptr(t + 1);
 #pragma unroll
-      for (int j = 0; j < CPT; ++j) stage[j] = src[(size_t)(t + 1) * TILE_CH + tid + j * NT];
+      for (int j = 0; j < CPT; ++j) stage[j] = tp[tid + j * NT];
     }
     if (!comp) continue;
 
@@ -550,7 +562,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn_tiles(const u16* __restrict__ 
           sacc[hf][kt] = mfma(kl, qh[ds], sacc[hf][kt]);
         }
       }
-    const int kbase = t * kTileKeys;
+    const int lim = t < ctiles ? n_keys - t * kTileKeys : block;  // valid keys of this tile
     float sv[16];
     float mx = -INFINITY;
 #pragma unroll
@@ -559,8 +571,8 @@ __global__ __launch_bounds__(NW * 64) void k_attn_tiles(const u16* __restrict__ 
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int key = kbase + hf * 32 + 8 * g + 4 * kt + i;
-          const float x = key < n_keys ? sacc[hf][kt][i] * scale : -INFINITY;
+          const int key = hf * 32 + 8 * g + 4 * kt + i;
+          const float x = key < lim ? sacc[hf][kt][i] * scale : -INFINITY;
           sv[hf * 8 + kt * 4 + i] = x;
           mx = fmaxf(mx, x);
         }
@@ -1051,21 +1063,23 @@ size_t attention_ml_bytes(int n_seqs, int n_q, int qtiles, int splits) {
 
 template <int D>
 static hipError_t attention_dispatch(const u16* q_hi, const u16* q_lo, const u16* kv, int64_t kv_tiles,
-                                     float* part_o, float* part_ml, u16* o_hi, u16* o_lo, int n_seqs,
+                                     const u16* bkv, float* part_o, float* part_ml, u16* o_hi, u16* o_lo, int n_seqs,
                                      int block, int n_q, int n_kv, int splits, const SeqTable& st,
                                      hipStream_t s) {
   const int units = (n_q / n_kv) * ((block + 15) / 16);
   const float scale = (float)(1.0 / sqrt((double)D));
   const dim3 grid(n_seqs * n_kv * splits);
   if (units <= 4)
-    hipLaunchKernelGGL((k_attn_tiles<D, 4>), grid, dim3(256), 0, s, q_hi, q_lo, kv, kv_tiles, part_o, part_ml,
+    hipLaunchKernelGGL((k_attn_tiles<D, 4>), grid, dim3(256), 0, s, q_hi, q_lo, kv, kv_tiles, bkv, n_seqs,
+                       part_o, part_ml,
                        o_hi, o_lo, block, n_q, n_kv, splits, scale, st);
   else if (units <= 8)
-    hipLaunchKernelGGL((k_attn_tiles<D, 8>), grid, dim3(512), 0, s, q_hi, q_lo, kv, kv_tiles, part_o, part_ml,
+    hipLaunchKernelGGL((k_attn_tiles<D, 8>), grid, dim3(512), 0, s, q_hi, q_lo, kv, kv_tiles, bkv, n_seqs,
+                       part_o, part_ml,
                        o_hi, o_lo, block, n_q, n_kv, splits, scale, st);
   else if (units <= 16)
-    hipLaunchKernelGGL((k_attn_tiles<D, 16>), grid, dim3(1024), 0, s, q_hi, q_lo, kv, kv_tiles, part_o,
-                       part_ml, o_hi, o_lo, block, n_q, n_kv, splits, scale, st);
+    hipLaunchKernelGGL((k_attn_tiles<D, 16>), grid, dim3(1024), 0, s, q_hi, q_lo, kv, kv_tiles, bkv, n_seqs,
+                       part_o, part_ml, o_hi, o_lo, block, n_q, n_kv, splits, scale, st);
   else
     return hipErrorInvalidValue;
   if (splits > 1) {
@@ -1077,19 +1091,42 @@ static hipError_t attention_dispatch(const u16* q_hi, const u16* q_lo, const u16
 }
 
 hipError_t launch_attention(const u16* q_hi, const u16* q_lo, const u16* kv_cache, int64_t kv_tiles,
-                            float* part_o, float* part_ml, u16* o_hi, u16* o_lo, int n_seqs, int block,
-                            int n_q, int n_kv, int head_dim, int splits, const SeqTable& st, hipStream_t s) {
+                            const u16* blk_kv, float* part_o, float* part_ml, u16* o_hi, u16* o_lo, int n_seqs,
+                            int block, int n_q, int n_kv, int head_dim, int splits, const SeqTable& st,
+                            hipStream_t s) {
+  if (block > kTileKeys) return hipErrorInvalidValue;
   if (head_dim == 128)
-    return attention_dispatch<128>(q_hi, q_lo, kv_cache, kv_tiles, part_o, part_ml, o_hi, o_lo, n_seqs, block,
-                                   n_q, n_kv, splits, st, s);
+    return attention_dispatch<128>(q_hi, q_lo, kv_cache, kv_tiles, blk_kv, part_o, part_ml, o_hi, o_lo, n_seqs,
+                                   block, n_q, n_kv, splits, st, s);
   if (head_dim == 64)
-    return attention_dispatch<64>(q_hi, q_lo, kv_cache, kv_tiles, part_o, part_ml, o_hi, o_lo, n_seqs, block, n_q,
-                                  n_kv, splits, st, s);
+    return attention_dispatch<64>(q_hi, q_lo, kv_cache, kv_tiles, blk_kv, part_o, part_ml, o_hi, o_lo, n_seqs,
+                                  block, n_q, n_kv, splits, st, s);
   return hipErrorInvalidValue;
 }
 
 int argmax_parts(int n_tiles, int Mp) {
   return Mp <= 32 ? n_tiles / gemm_plan(n_tiles, 0, Mp, false).nc : n_tiles;
+}
+
+// One workgroup per block tile; thread t covers slot-major elements of the
+// pad slots of all four planes.
+__global__ __launch_bounds__(256) void k_clear_block_pad(u16* __restrict__ bkv, int d, int block) {
+  u16* tile = bkv + (size_t)blockIdx.x * 4 * kTileKeys * d;
+  const int pad = kTileKeys - block, per = pad * d;  // pad elements per plane
+  for (int e = threadIdx.x; e < 4 * per; e += 256) {
+    const int plane = e / per, w = e % per;
+    const int slot = block + w / d, col = w % d;
+    // K planes [slot][d]; V planes [d][slot]
+    const size_t off = plane < 2 ? (size_t)slot * d + col : (size_t)col * kTileKeys + slot;
+    tile[(size_t)plane * kTileKeys * d + off] = 0;
+  }
+}
+
+hipError_t launch_clear_block_pad(u16* blk_kv, int n_blocks, int n_kv, int head_dim, int block, hipStream_t s) {
+  if (block > kTileKeys || n_blocks < 1) return hipErrorInvalidValue;
+  if (block == kTileKeys) return hipSuccess;
+  hipLaunchKernelGGL(k_clear_block_pad, dim3(n_blocks * n_kv), dim3(256), 0, s, blk_kv, head_dim, block);
+  return hipGetLastError();
 }
 
 hipError_t launch_argmax_reduce(const unsigned long long* part, int n_parts, int Mp, int n_seqs,

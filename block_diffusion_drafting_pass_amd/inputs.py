@@ -229,3 +229,16 @@ def make_targets(draft: np.ndarray, K: np.ndarray, r: np.ndarray, bonus: np.ndar
         t[b, k:bm1] = (draft[b, k:] + r[b, k:]) % vocab
         t[b, bm1] = bonus[b]
     return t
+
+
+def gen_train_anchors(seq_len: int, n_blocks: int, block: int, seed: int, prompt_len: int = 0) -> np.ndarray:
+    """Anchor positions of ``n_blocks`` non-overlapping blocks inside the
+    response part [prompt_len, seq_len) of a training sequence, uniform over
+    all such placements, sorted.  Each block [a, a + block) lies inside the
+    sequence."""
+    free = seq_len - prompt_len - n_blocks * block
+    if free < 0:
+        raise ValueError("blocks do not fit in the response")
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed, spawn_key=(5,))))
+    c = np.sort(rng.choice(free + n_blocks, size=n_blocks, replace=False))
+    return (prompt_len + c + np.arange(n_blocks) * (block - 1)).astype(np.int64)

@@ -126,7 +126,8 @@ int dflash_ctx_truncate(dflash_ctx* ctx, int32_t seq, int64_t new_len);
 
 /* Workspace bytes for dflash_draft_block over all sequences of a context
  * with n_seqs sequences at block size `block`, and for dflash_fuse_ctx calls
- * appending up to max_new_tokens positions in total. */
+ * appending up to max_new_tokens positions in total.  With n_seqs = n the
+ * same size serves dflash_draft_anchored over up to n blocks. */
 size_t dflash_workspace_bytes(const dflash_model* model, int32_t n_seqs, int32_t block,
                               int64_t max_new_tokens);
 
@@ -170,6 +171,31 @@ int dflash_draft_block(const dflash_model* model, const dflash_ctx* ctx, const i
 int dflash_draft_refine(const dflash_model* model, const dflash_ctx* ctx, const int32_t* anchors,
                         const int32_t* init_tokens, int32_t block, int32_t n_steps, int32_t* draft, float* logits,
                         void* ws, size_t ws_bytes, dflash_stream stream);
+
+/* Draft many blocks anchored at given positions of shared contexts: the
+ * forward of the paper's training attention (Fig. 4: the target's context
+ * features condition the drafter, and masked blocks start at randomly
+ * sampled clean anchor tokens; atlas summary "Approach": random anchor-token
+ * block sampling).  Block j sits at positions anchor_pos[j] ..
+ * anchor_pos[j] + block - 1 of sequence block_seq[j]; its queries see that
+ * sequence's injected context keys at positions < anchor_pos[j] and the
+ * block's own keys, bidirectionally, and nothing of any other block; so a
+ * block at anchor_pos[j] = length drafts exactly as dflash_draft_block would.
+ *   n_blocks      1 .. 128
+ *   block_seq     host int32 [n_blocks], each in [0, n_seqs of ctx)
+ *   anchor_pos    host int64 [n_blocks], each in [0, length of its sequence]
+ *   anchors       device int32 [n_blocks]: the token at each anchor position
+ *   block_tokens  device int32 [n_blocks][block-1] for positions 1..block-1,
+ *                 or NULL for mask tokens
+ *   draft, logits device [n_blocks][block-1] (logits: [..][vocab] or NULL)
+ * The context is only read: blocks may overlap one another and the context.
+ * The workspace must hold dflash_workspace_bytes(model, n_blocks, block, 0)
+ * bytes.  Errors as for dflash_draft_block, plus DFLASH_EINVAL for a block
+ * index or anchor position out of range. */
+int dflash_draft_anchored(const dflash_model* model, const dflash_ctx* ctx, int32_t n_blocks,
+                          const int32_t* block_seq, const int64_t* anchor_pos, const int32_t* anchors,
+                          const int32_t* block_tokens, int32_t block, int32_t* draft, float* logits, void* ws,
+                          size_t ws_bytes, dflash_stream stream);
 
 /* One steady-state decode iteration in a single call: append n_new[b]
  * verified positions to each sequence (as dflash_fuse_ctx) and then draft a

@@ -117,6 +117,25 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, return_probs: bool = 
     return (o, probs) if return_probs else o
 
 
+def masked_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, allowed: np.ndarray) -> np.ndarray:
+    """GQA attention where query r sees key s only if allowed[r][s].
+
+    Same as ``attention`` over the allowed keys of each row: scores of the
+    other keys are left out of the softmax.  Every row must allow at least
+    one key.  q: [R][n_q][d], k, v: [S][n_kv][d], allowed: [R][S] bool.
+    """
+    R, n_q, d = q.shape
+    n_kv = k.shape[1]
+    allowed = np.asarray(allowed, dtype=bool)
+    assert allowed.shape == (R, k.shape[0]) and np.all(allowed.any(axis=1))
+    o = np.empty_like(q)
+    for h in range(n_q):
+        g = (h * n_kv) // n_q
+        s = np.where(allowed, (q[:, h, :] @ k[:, g, :].T) / np.sqrt(d), -np.inf)
+        o[:, h, :] = softmax_rows(s) @ v[:, g, :]
+    return o
+
+
 def argmax_lowest(x: np.ndarray) -> np.ndarray:
     """Index of the maximum along the last axis; ties go to the lowest index."""
     return np.argmax(x, axis=-1)
@@ -285,6 +304,69 @@ def refine(model: OracleModel, ctx: OracleContext, anchors: np.ndarray, block: i
         out.append(r)
         toks = r.drafts
     return out
+
+
+def draft_anchored(model: OracleModel, ctx: OracleContext, block_seq, anchor_pos, anchors: np.ndarray,
+                   block: int, block_tokens: Optional[np.ndarray] = None) -> DraftResult:
+    """Forward of the training attention (paper Fig. 4; atlas summary
+    "Approach": random anchor-token block sampling).
+
+    Each training sequence's target features are injected as context for
+    all of its positions.  Block j starts at the clean anchor token at
+    position anchor_pos[j] of sequence block_seq[j], followed by B-1 mask
+    tokens (or block_tokens[j]), at positions anchor_pos[j] ..
+    anchor_pos[j]+B-1.  All blocks of a sequence go through each layer
+    together, in one attention over [the sequence's context keys | every
+    block's keys] under a block-sparse mask: a query of block j sees the
+    context keys at positions < anchor_pos[j] (what has been verified when
+    that block is drafted at inference) and the keys of block j, and nothing
+    else.  Rows 1..B-1 of each block are its drafts.
+    """
+    m = model
+    block_seq = np.asarray(block_seq, dtype=np.int64)
+    anchor_pos = np.asarray(anchor_pos, dtype=np.int64)
+    n, B, H = len(block_seq), int(block), m.hidden
+    nq, nkv, d = m.n_q_heads, m.n_kv_heads, m.head_dim
+    E = m.weights["embed"]
+    toks = np.full((n, B), m.mask_token_id, dtype=np.int64)
+    toks[:, 0] = np.asarray(anchors, dtype=np.int64)
+    if block_tokens is not None:
+        toks[:, 1:] = np.asarray(block_tokens, dtype=np.int64)
+    x = bf16_to_f64(E[toks.reshape(-1)]).reshape(n, B, H)
+    pos = [ctx.pos_offset + int(anchor_pos[j]) + np.arange(B) for j in range(n)]
+
+    for l in range(m.n_layers):
+        u = rms_norm(x, m.lw(l, "attn_norm"), m.rms_eps)
+        q = (u @ m.lw(l, "wq").T).reshape(n, B, nq, d)
+        k = (u @ m.lw(l, "wk").T).reshape(n, B, nkv, d)
+        v = (u @ m.lw(l, "wv").T).reshape(n, B, nkv, d)
+        q = np.stack([apply_rope(q[j], pos[j], m.rope_theta) for j in range(n)])
+        k = np.stack([apply_rope(k[j], pos[j], m.rope_theta) for j in range(n)])
+        o = np.empty((n, B, nq, d))
+        for sq in sorted(set(block_seq.tolist())):
+            J = np.nonzero(block_seq == sq)[0]
+            T = ctx.length(sq)
+            keys = np.concatenate([ctx.k[sq][l]] + [k[j] for j in J], axis=0)
+            vals = np.concatenate([ctx.v[sq][l]] + [v[j] for j in J], axis=0)
+            allowed = np.zeros((len(J) * B, T + len(J) * B), dtype=bool)
+            for jj, j in enumerate(J):
+                rows = slice(jj * B, (jj + 1) * B)
+                allowed[rows, : anchor_pos[j]] = True
+                allowed[rows, T + jj * B: T + (jj + 1) * B] = True
+            oj = masked_attention(np.concatenate([q[j] for j in J], axis=0), keys, vals, allowed)
+            o[J] = oj.reshape(len(J), B, nq, d)
+        x = x + o.reshape(n, B, nq * d) @ m.lw(l, "wo").T
+        w = rms_norm(x, m.lw(l, "mlp_norm"), m.rms_eps)
+        a = silu(w @ m.lw(l, "wgate").T) * (w @ m.lw(l, "wup").T)
+        x = x + a @ m.lw(l, "wdown").T
+
+    y = rms_norm(x[:, 1:, :], m.w("final_norm"), m.rms_eps).reshape(n * (B - 1), H)
+    logits = np.empty((n * (B - 1), m.vocab))
+    for v0 in range(0, m.vocab, _LM_SLAB):
+        v1 = min(m.vocab, v0 + _LM_SLAB)
+        logits[:, v0:v1] = y @ bf16_to_f64(E[v0:v1]).T
+    logits = logits.reshape(n, B - 1, m.vocab)
+    return DraftResult(logits=logits, drafts=argmax_lowest(logits), hidden=x)
 
 
 def accept_len(draft: np.ndarray, target: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:

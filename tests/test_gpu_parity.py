@@ -366,3 +366,95 @@ def test_refine_rejects_bad_step_counts(torch_cuda):
 def test_refine_q8_ctx1024_b8(q8):
     spec5, w, dev = q8
     _refine_case(spec5, w, dev, (1024,), 8, "5-layer ctx1024 B8")
+
+
+# ----------------------------------------------------------------------------
+# anchored blocks over shared contexts (training-attention forward)
+# ----------------------------------------------------------------------------
+
+def _anchored_case(spec, w, dev_w, lens, bseq, apos, block, label, tokens=False, check_blocks=None):
+    import torch
+    spec = spec.with_(ctx_lens=tuple(lens), block=block)
+    n = len(bseq)
+    say(f"anchored {label}: lens={lens} blocks={n} block={block}")
+    run = GpuRun(spec, dev_w, capacity=[c + 8 for c in lens], max_new=sum(lens))
+    feats = _feats(spec, 1, lens)
+    run.ingest(feats)
+    ws = B.workspace(run.model, n, block, 0)
+    rng = np.random.default_rng(n * 31 + block)
+    anchors = rng.integers(0, spec.vocab - 1, size=n).astype(np.int32)
+    toks = None
+    if tokens:
+        toks = rng.integers(0, spec.vocab, size=(n, block - 1)).astype(np.int32)
+        toks[:, 1::2] = spec.mask_token_id
+    lg = torch.empty((n, block - 1, spec.vocab), dtype=torch.float32, device="cuda")
+    d = B.draft_anchored(run.model, run.ctx, bseq, apos, torch.from_numpy(anchors).cuda(), block, ws,
+                         block_tokens=None if toks is None else torch.from_numpy(toks).cuda(), logits=lg)
+    torch.cuda.synchronize()
+    assert run.ctx.lengths() == list(lens)
+    sel = list(range(n)) if check_blocks is None else check_blocks
+    model = O.OracleModel.from_spec(spec, w)
+    octx = O.OracleContext(model, len(lens))
+    for b in sorted({bseq[j] for j in sel}):
+        O.fuse_ctx(model, octx, b, feats[b])
+    ref = O.draft_anchored(model, octx, [bseq[j] for j in sel], [apos[j] for j in sel], anchors[sel], block,
+                           block_tokens=None if toks is None else toks[sel])
+    assert_parity(lg.cpu().numpy()[sel], d.cpu().numpy()[sel], ref, label)
+    return run, d
+
+
+@pytest.mark.parametrize("lens,bseq,apos,block,tokens,label", [
+    ((100, 40), [0, 0, 1, 0, 1, 0, 0, 1], [0, 37, 40, 100, 0, 64, 63, 17], 16, False, "eight blocks M128"),
+    ((50,), [0, 0, 0], [10, 12, 50], 4, True, "overlapping B4 with tokens"),
+    ((130, 3, 70), [2, 0, 1, 0], [70, 129, 3, 65], 8, False, "three seqs B8 skinny"),
+    ((300,), [0] * 16, list(range(0, 300, 19)), 32, False, "sixteen blocks B32 M512"),
+    ((0, 5), [0, 1], [0, 5], 16, False, "empty context"),
+])
+def test_anchored_tiny(torch_cuda, lens, bseq, apos, block, tokens, label):
+    spec = I.spec("tiny")
+    w = I.gen_weights(spec, seed=9, std=0.05)
+    _anchored_case(spec, w, B.upload_weights(spec, w), lens, bseq, apos, block, label, tokens=tokens)
+
+
+def test_anchored_leaves_the_context_unchanged(torch_cuda):
+    """Anchored blocks only read the cache: a later draft_block is bitwise unchanged."""
+    import torch
+    spec = I.spec("tiny").with_(ctx_lens=(90,))
+    w = I.gen_weights(spec, seed=2, std=0.05)
+    run = GpuRun(spec, B.upload_weights(spec, w), capacity=[100], max_new=90)
+    run.ingest(_feats(spec, 1, [90]))
+    anchors = I.gen_anchors(spec, 2)
+    d0, l0 = run.draft(anchors, 16)
+    ws = B.workspace(run.model, 4, 16, 0)
+    a = torch.zeros(4, dtype=torch.int32, device="cuda")
+    B.draft_anchored(run.model, run.ctx, [0, 0, 0, 0], [0, 30, 60, 90], a, 16, ws)
+    torch.cuda.synchronize()
+    d1, l1 = run.draft(anchors, 16)
+    assert np.array_equal(d0, d1) and np.array_equal(l0.view(np.uint32), l1.view(np.uint32))
+
+
+def test_anchored_rejects_bad_blocks(torch_cuda):
+    import torch
+    spec = I.spec("tiny").with_(ctx_lens=(10, 4))
+    w = I.gen_weights(spec, seed=0)
+    run = GpuRun(spec, B.upload_weights(spec, w), capacity=[16, 16], max_new=14)
+    run.ingest(_feats(spec, 1, [10, 4]))
+    ws = B.workspace(run.model, 2, 16, 0)
+    a = torch.zeros(2, dtype=torch.int32, device="cuda")
+    for bseq, apos in (([0, 2], [1, 1]), ([0, 1], [1, 5]), ([0, -1], [0, 0]), ([0, 1], [-1, 0])):
+        with pytest.raises(B.DFlashError) as e:
+            B.draft_anchored(run.model, run.ctx, bseq, apos, a, 16, ws)
+        assert e.value.name == "DFLASH_EINVAL", (bseq, apos)
+    small = B.workspace(run.model, 1, 16, 0)
+    with pytest.raises(B.DFlashError) as e:
+        B.draft_anchored(run.model, run.ctx, [0, 1], [1, 1], a, 16, small)
+    assert e.value.name == "DFLASH_EWORKSPACE"
+
+
+def test_anchored_q8_ctx1024(q8):
+    """The 5-layer drafter over one 1024-position context with 16 blocks of 16
+    (M = 256): the training-attention forward at the bench shapes."""
+    spec5, w, dev = q8
+    apos = [int(v) for v in I.gen_train_anchors(1024, 16, 16, seed=3)]
+    _anchored_case(spec5, w, dev, (1024,), [0] * 16, apos, 16, "5-layer ctx1024 16 blocks",
+                   check_blocks=[0, 7, 15])

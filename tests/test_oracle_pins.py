@@ -386,3 +386,102 @@ def test_block_tokens_equal_to_masks_reproduce_the_masked_pass():
     a = O.draft_block(model, ctx, anchors, MICRO.block)
     b = O.draft_block(model, ctx, anchors, MICRO.block, block_tokens=masks)
     np.testing.assert_array_equal(a.logits, b.logits)
+
+
+# ----------------------------------------------------------------------------
+# anchored blocks over shared contexts (the training attention of Fig. 4)
+# ----------------------------------------------------------------------------
+
+SMALL = I.DraftSpec("small", n_layers=2, hidden=32, n_q_heads=4, n_kv_heads=2, head_dim=8,
+                    intermediate=48, vocab=64, n_target_layers=2, block=4, ctx_lens=(23, 9))
+
+
+def _anchored_case(spec, seed):
+    model, w = _model(spec, seed)
+    ctx, feats = _ingest(model, spec, seed)
+    rng = np.random.default_rng(seed)
+    lens = spec.ctx_lens
+    # several blocks per sequence, anchors at 0, interior positions and the end
+    block_seq = [0, 0, 0, 1, 1, 0, 1]
+    anchor_pos = [0, 7, lens[0], 0, lens[1], 16, 4]
+    anchors = rng.integers(0, spec.vocab - 1, size=len(block_seq))
+    return model, w, ctx, feats, block_seq, anchor_pos, anchors
+
+
+@pytest.mark.parametrize("seed", [0, 3])
+def test_anchored_equals_inference_on_the_prefix(seed):
+    """Each anchored block drafts exactly what inference drafts at that anchor:
+    a fresh context holding only the first anchor_pos features."""
+    spec = SMALL
+    model, w, ctx, feats, bseq, apos, anchors = _anchored_case(spec, seed)
+    res = O.draft_anchored(model, ctx, bseq, apos, anchors, spec.block)
+    for j, (sq, a) in enumerate(zip(bseq, apos)):
+        one = O.OracleContext(model, 1)
+        O.fuse_ctx(model, one, 0, feats[sq][:a])
+        ref = O.draft_block(model, one, np.array([anchors[j]]), spec.block)
+        np.testing.assert_allclose(res.logits[j], ref.logits[0], rtol=0, atol=1e-12)
+
+
+def test_anchored_matches_scalar_brute_force():
+    spec = MICRO.with_(ctx_lens=(5, 3))
+    model, w = _model(spec, 2)
+    ctx, feats = _ingest(model, spec, 2)
+    bseq, apos, anchors = [0, 0, 1, 0], [2, 5, 1, 0], np.array([3, 9, 14, 0])
+    res = O.draft_anchored(model, ctx, bseq, apos, anchors, spec.block)
+    for j, (sq, a) in enumerate(zip(bseq, apos)):
+        bl, _ = brute.brute_draft(spec, w, [feats[sq][:a]], [anchors[j]], spec.block)
+        np.testing.assert_allclose(res.logits[j], np.array(bl[0]), rtol=0, atol=1e-12)
+
+
+def test_anchored_matches_packed_sdpa_formulation():
+    from tests.torch_cpu_ref import torch_anchored
+    spec = SMALL
+    model, w, ctx, feats, bseq, apos, anchors = _anchored_case(spec, 1)
+    res = O.draft_anchored(model, ctx, bseq, apos, anchors, spec.block)
+    tl, td = torch_anchored(spec, w, feats, bseq, apos, anchors, spec.block)
+    np.testing.assert_allclose(res.logits, tl, rtol=0, atol=1e-10)
+
+
+def test_anchored_block_sees_only_its_prefix_and_itself():
+    spec = SMALL
+    model, w, ctx, feats, bseq, apos, anchors = _anchored_case(spec, 4)
+    base = O.draft_anchored(model, ctx, bseq, apos, anchors, spec.block)
+    # features at or after a block's anchor, and other blocks' tokens, change nothing for it
+    j = 1  # sequence 0, anchor 7
+    f2 = [f.copy() for f in feats]
+    f2[0][apos[j]:] = I.gen_features(spec, 77, 0, len(feats[0]))[apos[j]:]
+    ctx2 = O.OracleContext(model, 2)
+    for b in range(2):
+        O.fuse_ctx(model, ctx2, b, f2[b])
+    toks = np.full((len(bseq), spec.block - 1), spec.mask_token_id)
+    toks[0] = [1, 2, 3]
+    toks[2] = [5, 6, 7]
+    r2 = O.draft_anchored(model, ctx2, bseq, apos, anchors, spec.block, block_tokens=toks)
+    np.testing.assert_allclose(r2.logits[j], base.logits[j], rtol=0, atol=1e-12)
+    # ... while a feature before the anchor does
+    f3 = [f.copy() for f in feats]
+    f3[0][apos[j] - 1] = I.gen_features(spec, 78, 0, len(feats[0]))[apos[j] - 1]
+    ctx3 = O.OracleContext(model, 2)
+    for b in range(2):
+        O.fuse_ctx(model, ctx3, b, f3[b])
+    r3 = O.draft_anchored(model, ctx3, bseq, apos, anchors, spec.block)
+    assert np.max(np.abs(r3.logits[j] - base.logits[j])) > 1e-6
+
+
+def test_masked_attention_reduces_to_attention_on_the_allowed_keys():
+    rng = np.random.default_rng(5)
+    q, k, v = rng.normal(size=(6, 4, 8)), rng.normal(size=(11, 2, 8)), rng.normal(size=(11, 2, 8))
+    np.testing.assert_allclose(O.masked_attention(q, k, v, np.ones((6, 11), bool)), O.attention(q, k, v),
+                               rtol=0, atol=1e-14)
+    keep = np.array([0, 3, 4, 9])
+    allowed = np.zeros((6, 11), bool)
+    allowed[:, keep] = True
+    np.testing.assert_allclose(O.masked_attention(q, k, v, allowed), O.attention(q, k[keep], v[keep]),
+                               rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("seq_len,n,blk,prompt", [(1024, 16, 16, 0), (64, 4, 16, 0), (4096, 64, 16, 1024), (40, 3, 8, 10)])
+def test_train_anchor_placement_is_valid(seq_len, n, blk, prompt):
+    a = I.gen_train_anchors(seq_len, n, blk, seed=1, prompt_len=prompt)
+    assert len(a) == n and a[0] >= prompt and a[-1] + blk <= seq_len
+    assert np.all(np.diff(a) >= blk)

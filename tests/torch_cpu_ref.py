@@ -70,3 +70,56 @@ def torch_draft(cfg, weights, features, anchors, block, use_rope=True):
         out_logits.append(F.linear(y, W["embed"]).numpy())
     logits = np.stack(out_logits)
     return logits, logits.argmax(-1)
+
+
+def torch_anchored(cfg, weights, features, block_seq, anchor_pos, anchors, block):
+    """Anchored blocks (training attention) as one packed sequence: every
+    sequence's context rows, then every block's rows, through each layer in a
+    single SDPA call whose boolean mask lets a row of block j see its own
+    block and the rows of sequence block_seq[j]'s context before
+    anchor_pos[j].  Context positions are keys only: their K/V come from the
+    target features, not from a layer input.  Returns (logits [n][B-1][V],
+    drafts)."""
+    nq, nkv, d, H = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.hidden
+    W = {k: _t(v) for k, v in weights.items()}
+    eps = cfg.rms_eps
+    n = len(block_seq)
+    lens = [len(f) for f in features]
+    starts = np.concatenate([[0], np.cumsum(lens)]).astype(int)
+    C = int(starts[-1])
+    # context K/V of every sequence, packed: rows starts[s] .. starts[s+1]
+    fe = torch.cat([_t(f) if len(f) else torch.zeros(0, cfg.n_target_layers * H, dtype=torch.float64)
+                    for f in features], 0)
+    h = F.linear(fe, W["w_fc"])
+    ctx_pos = torch.cat([torch.arange(c) for c in lens]) if C else torch.zeros(0, dtype=torch.long)
+    toks = torch.full((n, block), cfg.mask_token_id, dtype=torch.long)
+    toks[:, 0] = torch.as_tensor(np.asarray(anchors, dtype=np.int64))
+    x = W["embed"][toks.reshape(-1)]                     # [n*B][H]
+    blk_pos = torch.cat([torch.arange(int(a), int(a) + block) for a in anchor_pos])
+    R = n * block
+    mask = torch.zeros(R, C + R, dtype=torch.bool)
+    for j in range(n):
+        rows = slice(j * block, (j + 1) * block)
+        s0 = int(starts[int(block_seq[j])])
+        mask[rows, s0: s0 + int(anchor_pos[j])] = True
+        mask[rows, C + j * block: C + (j + 1) * block] = True
+    for l in range(cfg.n_layers):
+        p = f"layers.{l}."
+        ck = F.linear(h, W[p + "wk"]).view(C, nkv, d).transpose(0, 1)
+        cv = F.linear(h, W[p + "wv"]).view(C, nkv, d).transpose(0, 1)
+        ck = _rope_complex(ck, ctx_pos, cfg.rope_theta)
+        u = F.rms_norm(x, (H,), weight=W[p + "attn_norm"], eps=eps)
+        q = _rope_complex(F.linear(u, W[p + "wq"]).view(R, nq, d).transpose(0, 1), blk_pos, cfg.rope_theta)
+        k = _rope_complex(F.linear(u, W[p + "wk"]).view(R, nkv, d).transpose(0, 1), blk_pos, cfg.rope_theta)
+        v = F.linear(u, W[p + "wv"]).view(R, nkv, d).transpose(0, 1)
+        keys = torch.cat([ck, k], dim=1)
+        vals = torch.cat([cv, v], dim=1)
+        o = F.scaled_dot_product_attention(q[None], keys[None], vals[None], attn_mask=mask[None, None],
+                                           enable_gqa=(nq != nkv))[0]
+        x = x + F.linear(o.transpose(0, 1).reshape(R, nq * d), W[p + "wo"])
+        w = F.rms_norm(x, (H,), weight=W[p + "mlp_norm"], eps=eps)
+        x = x + F.linear(F.silu(F.linear(w, W[p + "wgate"])) * F.linear(w, W[p + "wup"]), W[p + "wdown"])
+    x = x.view(n, block, H)
+    y = F.rms_norm(x[:, 1:], (H,), weight=W["final_norm"], eps=eps)
+    logits = F.linear(y, W["embed"]).numpy()
+    return logits, logits.argmax(-1)
