@@ -13,6 +13,12 @@ the hot path once, for every sequence of the workload:
                          dflash_fuse_ctx followed by dflash_draft_block);
   2. dflash_accept_len   accepted-prefix scan against constructed target tokens.
 
+A training-forward workload (e.g. --workload q8b_train4x4096) instead
+times the forward of the training attention: one step ingests every
+training sequence's target features as injected context (dflash_fuse_ctx)
+and drafts all of its anchored blocks (dflash_draft_anchored), each block
+seeing the context before its anchor and itself.
+
 --denoise-steps S > 1 adds S - 1 further passes over the block
 (dflash_draft_refine, each fed the previous pass's drafts), the multi-step
 alternative that the block size / steps efficiency trade-off compares against.
@@ -199,6 +205,102 @@ class Workload:
         return d.cpu().numpy(), lg.cpu().numpy()
 
 
+class TrainWorkload:
+    """Training-attention forward: every sequence's full context ingested,
+    then train_blocks anchored blocks per sequence drafted in one call."""
+
+    def __init__(self, spec, weights, torch, B_):
+        self.spec, self.torch, self.B = spec, torch, B_
+        I = _inputs()
+        blk = spec.block
+        self.denoise_steps = 1
+        self.bseq, self.apos = [], []
+        for b, T in enumerate(spec.ctx_lens):
+            a = I.gen_train_anchors(T, spec.train_blocks, blk, seed=10 + b, prompt_len=spec.prompt_len)
+            self.bseq += [b] * len(a)
+            self.apos += [int(v) for v in a]
+        self.n_blocks = len(self.bseq)
+        self.cfg = B_.Config.from_spec(spec, max_block=max(blk, 16))
+        self.model = B_.Model(self.cfg, B_.upload_weights(spec, weights))
+        self.ctx = B_.Context(self.model, list(spec.ctx_lens))
+        self.ws = B_.workspace(self.model, max(self.n_blocks, spec.n_seqs), blk, sum(spec.ctx_lens))
+        self.host_feats = [I.gen_features(spec, 1, b, c) for b, c in enumerate(spec.ctx_lens)]
+        self.feats = torch.from_numpy(np.ascontiguousarray(np.concatenate(self.host_feats, 0)).view(np.int16)) \
+            .cuda().view(torch.bfloat16)
+        rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(6, spawn_key=(9,))))
+        self.anchor_tok = rng.integers(0, spec.vocab - 1, size=self.n_blocks).astype(np.int32)
+        self.anchors = torch.from_numpy(self.anchor_tok).cuda()
+        self.draft = torch.empty((self.n_blocks, blk - 1), dtype=torch.int32, device="cuda")
+        self.n_new = list(spec.ctx_lens)
+
+    def step(self, logits=None):
+        B_, s = self.B, self.spec
+        for b in range(s.n_seqs):
+            self.ctx.truncate(b, 0)
+        B_.fuse_ctx(self.model, self.ctx, self.feats, self.n_new, self.ws)
+        B_.draft_anchored(self.model, self.ctx, self.bseq, self.apos, self.anchors, s.block, self.ws,
+                          draft=self.draft, logits=logits)
+
+    def logits(self, blocks):
+        t = self.torch
+        lg = t.empty((self.n_blocks, self.spec.block - 1, self.spec.vocab), dtype=t.float32, device="cuda")
+        self.step(logits=lg)
+        t.cuda.synchronize()
+        out = lg[blocks].cpu().numpy(), self.draft[blocks].cpu().numpy()
+        del lg
+        return out
+
+
+def _decode_rows(wl, stage: str) -> int:
+    """Activation rows of one launch of `stage` (per layer for layer stages)."""
+    s = wl.spec
+    n = wl.n_blocks if isinstance(wl, TrainWorkload) else s.n_seqs
+    if stage == "lm_head":
+        return n * (s.block - 1)
+    if stage in ("fusion", "kv_proj") and isinstance(wl, TrainWorkload):
+        return sum(s.ctx_lens)
+    return n * s.block
+
+
+def stage_total(wl, stage: str):
+    """Algorithmic (bytes, flops) of every launch of `stage` in one step."""
+    s = wl.spec
+    S = wl.denoise_steps
+    rows = _decode_rows(wl, stage)
+    if stage == "attention":
+        if isinstance(wl, TrainWorkload):
+            # the shared context is read once (bytes); each block attends to
+            # its prefix and itself (flops)
+            kb = sum(s.ctx_lens) + wl.n_blocks * s.block
+            kf = sum(a + s.block for a in wl.apos)
+        else:
+            kb = kf = sum(c + s.block for c in s.ctx_lens)
+        b, _ = stage_work(s, "attention", rows, kb)
+        _, f = stage_work(s, "attention", rows, kf)
+    else:
+        b, f = stage_work(s, stage, rows)
+    if stage not in ("lm_head", "fusion"):
+        b, f = b * s.n_layers, f * s.n_layers
+    if stage not in ("fusion", "kv_proj"):
+        b, f = b * S, f * S
+    return b, f
+
+
+def train_step_work(wl):
+    """Algorithmic (bytes, flops) of one training-forward step: ingest of every
+    position (fusion + all layers' K/V), then the anchored pass."""
+    by = fl = 0
+    for st in ("fusion", "kv_proj", "qkv", "oproj", "gate_up", "down", "attention", "lm_head"):
+        b, f = stage_total(wl, st)
+        if st in ("qkv", "kv_proj"):
+            # W_k / W_v bytes are shared by the ingest and the block pass
+            b = b if st == "qkv" else 0
+        by, fl = by + b, fl + f
+    s = wl.spec
+    by += s.n_layers * 2 * s.hidden * 2 + s.hidden * 2
+    return by, fl
+
+
 def measured_traffic(workload: str, stage: str):
     """HBM bytes per launch of `stage` from the committed rocprofv3 counter
     summary for this workload, if there is one and the kernel sources have not
@@ -284,6 +386,37 @@ def cpu_baseline(spec, weights, ws_target_s=10.0, max_reps=3):
     }, res
 
 
+def cpu_baseline_train(spec, weights, wl, n_blk=2):
+    """The oracle on sequence 0 of a training-forward workload: its ingest,
+    then n_blk of its anchored blocks, extrapolated to all of its blocks."""
+    from oracle import dflash_oracle as O
+    I = _inputs()
+    sub = spec.with_(ctx_lens=spec.ctx_lens[:1])
+    model = O.OracleModel.from_spec(sub, weights)
+    ctx = O.OracleContext(model, 1)
+    T, blk = spec.ctx_lens[0], spec.block
+    t0 = time.perf_counter()
+    O.fuse_ctx(model, ctx, 0, I.gen_features(spec, 1, 0, T))
+    t_ing = time.perf_counter() - t0
+    log(f"oracle ingest of {T} positions: {t_ing:.1f} s")
+    sel = [j for j in range(wl.n_blocks) if wl.bseq[j] == 0][:n_blk]
+    t0 = time.perf_counter()
+    res = O.draft_anchored(model, ctx, [0] * len(sel), [wl.apos[j] for j in sel], wl.anchor_tok[sel], blk)
+    t_blk = time.perf_counter() - t0
+    log(f"oracle anchored pass over {len(sel)} blocks: {t_blk:.1f} s")
+    per_seq = t_ing + spec.train_blocks / len(sel) * t_blk
+    return {
+        "value": spec.train_blocks * (blk - 1) / per_seq,
+        "unit": "drafted positions/s",
+        "cores": blas_threads(),
+        "kind": "oracle",
+        "sample": (f"sequence 0: ingest of {T} positions ({t_ing:.1f} s) and {len(sel)} of its "
+                   f"{spec.train_blocks} anchored blocks ({t_blk:.1f} s), extrapolated to all its blocks; numpy "
+                   f"float64; {len(os.sched_getaffinity(0))} host CPUs visible, "
+                   f"{platform.processor() or platform.machine()}"),
+    }, res, sel
+
+
 # ----------------------------------------------------------------------------
 
 def main(argv=None) -> int:
@@ -331,13 +464,18 @@ def main(argv=None) -> int:
     if S < 1 or S > 65:
         print("--denoise-steps must be in [1, 65]", file=sys.stderr)
         return 2
-    wl = Workload(spec, weights, torch, B_, two_call=args.two_call, denoise_steps=S)
+    train = spec.train_blocks > 0
+    if train and (S > 1 or args.two_call):
+        print("--denoise-steps and --two-call apply to decode workloads only", file=sys.stderr)
+        return 2
+    wl = TrainWorkload(spec, weights, torch, B_) if train else \
+        Workload(spec, weights, torch, B_, two_call=args.two_call, denoise_steps=S)
     log("workload resident; warming up")
     for _ in range(args.warmup):
         wl.step()
     torch.cuda.synchronize()
 
-    n_launch = {"lm_head": S, "fusion": 1}.get(args.probe, spec.n_layers * S)
+    n_launch = 64 * S if train else {"lm_head": S, "fusion": 1}.get(args.probe, spec.n_layers * S)
     run = wl.step
     if args.graph:
         # the probe's events are not captured: arm it after capture only for eager replays
@@ -369,15 +507,21 @@ def main(argv=None) -> int:
     log(f"{args.steps} steps: {ms_step:.3f} ms/step (wall {wall * 1e3 / args.steps:.3f} ms/step)")
 
     n, blk = spec.n_seqs, spec.block
-    draft_tok_s = n * (blk - 1) / (ms_step * 1e-3)
-    by, fl = step_work(spec)
-    if S > 1:
-        pb_, pf_ = pass_work(spec)
-        by, fl = by + (S - 1) * pb_, fl + (S - 1) * pf_
+    n_units = wl.n_blocks if train else n
+    draft_tok_s = n_units * (blk - 1) / (ms_step * 1e-3)
+    if train:
+        by, fl = train_step_work(wl)
+    else:
+        by, fl = step_work(spec)
+        if S > 1:
+            pb_, pf_ = pass_work(spec)
+            by, fl = by + (S - 1) * pb_, fl + (S - 1) * pf_
 
-    rows = n * (blk - 1) if args.probe == "lm_head" else n * blk
-    keys = sum(c + blk for c in spec.ctx_lens)
-    pb, pf = stage_work(spec, args.probe, rows, keys)
+    # the probed stage's algorithmic work per launch: its per-step total over
+    # the launches one step makes
+    tb, tf = stage_total(wl, args.probe)
+    per_step = max(probe_n, 1) / args.steps
+    pb, pf = tb / per_step, tf / per_step
     avg_ms = probe_ms / max(probe_n, 1)
     ai = pf / pb
     ridge = MFMA_BF16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9)
@@ -408,12 +552,7 @@ def main(argv=None) -> int:
             if cnt == 0:  # e.g. the context K/V projection inside a fused dflash_step
                 breakdown[st] = {"us_per_step": 0.0, "launches_per_step": 0}
                 continue
-            r_ = n * (blk - 1) if st == "lm_head" else n * blk
-            b_, f_ = stage_work(spec, st, r_, keys)
-            per_layer = st not in ("lm_head", "fusion")
-            b_, f_ = (b_ * spec.n_layers, f_ * spec.n_layers) if per_layer else (b_, f_)
-            if st not in ("fusion", "kv_proj"):  # once per pass
-                b_, f_ = b_ * S, f_ * S
+            b_, f_ = stage_total(wl, st)
             st_ms = ms / reps
             breakdown[st] = {"us_per_step": round(st_ms * 1e3, 1), "launches_per_step": cnt // reps,
                              "GB_s": round(b_ / (st_ms * 1e-3) / 1e9, 1),
@@ -422,7 +561,17 @@ def main(argv=None) -> int:
 
     cpu = None
     parity = None
-    if not args.no_cpu:
+    if not args.no_cpu and train:
+        log("timing the CPU oracle on the host cores")
+        cpu, ref, sel = cpu_baseline_train(spec, weights, wl)
+        lg_gpu, d_gpu = wl.logits(sel)
+        from oracle import dflash_oracle as O
+        sure = O.top2_gap(ref.logits) > 0.05
+        parity = {"blocks": sel, "max_abs_logit_err": float(np.max(np.abs(lg_gpu - ref.logits))),
+                  "drafts_equal_on_decided_rows": bool(np.all((d_gpu == ref.drafts)[sure])),
+                  "decided_rows": int(sure.sum())}
+        log(f"parity vs oracle (sequence 0, blocks {sel}): {parity}")
+    elif not args.no_cpu:
         d_gpu, lg_gpu = wl.logits()
         log("timing the CPU oracle on the host cores")
         cpu, ref = cpu_baseline(spec, weights)
@@ -433,10 +582,28 @@ def main(argv=None) -> int:
                   "decided_rows": int(sure.sum())}
         log(f"parity vs oracle (sequence 0): {parity}")
 
+    if train:
+        metric = (f"training-attention forward: drafted positions/sec ({spec.train_blocks} anchored blocks of "
+                  f"{blk} per sequence), {spec.n_layers}-layer, {n} x {spec.ctx_lens[0]} context")
+        workload = (f"{spec.name}: {spec.n_layers}-layer drafter, hidden {spec.hidden}, "
+                    f"{spec.n_q_heads}/{spec.n_kv_heads} heads x {spec.head_dim}, SwiGLU {spec.intermediate}, "
+                    f"vocab {spec.vocab}, fusion {spec.fused_width}->{spec.hidden}; {n} training sequence(s) of "
+                    f"{list(spec.ctx_lens)} positions (prompt {spec.prompt_len}), {wl.n_blocks} anchored blocks "
+                    f"of {blk}; step = ingest every position + one anchored draft pass (dflash_fuse_ctx + "
+                    f"dflash_draft_anchored)")
+    else:
+        metric = METRIC
+        workload = (f"{spec.name}: {spec.n_layers}-layer drafter, hidden {spec.hidden}, "
+                    f"{spec.n_q_heads}/{spec.n_kv_heads} heads x {spec.head_dim}, SwiGLU {spec.intermediate}, "
+                    f"vocab {spec.vocab}, fusion {spec.fused_width}->{spec.hidden}; {n} sequence(s), "
+                    f"context {spec.ctx_lens[0] if n == 1 else list(spec.ctx_lens)}, block {blk}; "
+                    f"step = append {blk} verified positions + draft pass + accept scan"
+                    f"{' (two calls)' if args.two_call else ' (dflash_step)'}"
+                    f"{f' + {S - 1} refinement pass(es)' if S > 1 else ''}")
     out = {
-        "metric": METRIC,
+        "metric": metric,
         "value": round(draft_tok_s, 1),
-        "unit": "draft tokens/s",
+        "unit": "drafted positions/s" if train else "draft tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -447,20 +614,14 @@ def main(argv=None) -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": (f"{spec.name}: {spec.n_layers}-layer drafter, hidden {spec.hidden}, "
-                         f"{spec.n_q_heads}/{spec.n_kv_heads} heads x {spec.head_dim}, SwiGLU {spec.intermediate}, "
-                         f"vocab {spec.vocab}, fusion {spec.fused_width}->{spec.hidden}; {n} sequence(s), "
-                         f"context {spec.ctx_lens[0] if n == 1 else list(spec.ctx_lens)}, block {blk}; "
-                         f"step = append {blk} verified positions + draft pass + accept scan"
-                         f"{' (two calls)' if args.two_call else ' (dflash_step)'}"
-                         f"{f' + {S - 1} refinement pass(es)' if S > 1 else ''}"),
-            "global_batch": n,
+            "workload": workload,
+            "global_batch": n_units if train else n,
             "block": blk,
             "denoise_steps": S,
             "seq_len": max(spec.ctx_lens),
             "parallelism": "single GPU",
         },
-        "blocks_per_s": round(n / (ms_step * 1e-3), 1),
+        "blocks_per_s": round(n_units / (ms_step * 1e-3), 1),
         "step_alg_bytes": by,
         "step_alg_flops": fl,
         "step_hbm_frac": round(by / (ms_step * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),

@@ -52,6 +52,10 @@ class DraftSpec:
     rms_eps: float = 1e-6
     rope_theta: float = 1e6
     geometric_p: float = 0.15
+    # training-forward workloads: anchored blocks per sequence, placed in the
+    # response part after prompt_len positions (0: a decode workload)
+    train_blocks: int = 0
+    prompt_len: int = 0
 
     @property
     def mask_token_id(self) -> int:
@@ -91,6 +95,10 @@ SPECS: Dict[str, DraftSpec] = {
     # 3-layer drafter, block 32, eight sequences with ragged contexts in [512, 4096].
     "q8b_l3_b32_ragged": DraftSpec("q8b_l3_b32_ragged", n_layers=3, block=32,
                                    ctx_lens=_ragged_lens(20260205, 8, 512, 4096), **_Q8),
+    # Training-attention forward: 4 sequences of 4096 positions (1024 prompt,
+    # 3072 response), 32 anchored blocks of 16 in each response.
+    "q8b_train4x4096": DraftSpec("q8b_train4x4096", n_layers=5, block=16, ctx_lens=(4096,) * 4,
+                                 train_blocks=32, prompt_len=1024, **_Q8),
 }
 
 
