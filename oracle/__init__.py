@@ -9,4 +9,7 @@ holds none of the method's arithmetic).
 * ``dflash_oracle`` — the draft pass as a plain numpy float64 function.
 * ``brute``         — an independent scalar-loop evaluation for tiny shapes,
                       used to pin ``dflash_oracle``.
+* ``sampling``      — sampled drafts (temperature > 0) and lossless
+                      verification, with the Philox4x64-10 generator both
+                      sides implement.
 """
