@@ -19,6 +19,11 @@ training sequence's target features as injected context (dflash_fuse_ctx)
 and drafts all of its anchored blocks (dflash_draft_anchored), each block
 seeing the context before its anchor and itself.
 
+--temperature T > 0 samples the drafts instead (dflash_step_sample, which
+also writes the drafter's logits) and verifies them losslessly against
+resident synthetic target logits (dflash_verify_sample) in place of the
+greedy scan.
+
 --denoise-steps S > 1 adds S - 1 further passes over the block
 (dflash_draft_refine, each fed the previous pass's drafts), the multi-step
 alternative that the block size / steps efficiency trade-off compares against.
@@ -135,10 +140,11 @@ def step_work(spec):
 # ----------------------------------------------------------------------------
 
 class Workload:
-    def __init__(self, spec, weights, torch, B_, two_call=False, denoise_steps=1):
+    def __init__(self, spec, weights, torch, B_, two_call=False, denoise_steps=1, temperature=0.0):
         self.spec, self.torch, self.B = spec, torch, B_
         self.two_call = two_call
         self.denoise_steps = denoise_steps
+        self.temperature = temperature
         I = _inputs()
         n, blk = spec.n_seqs, spec.block
         self.cfg = B_.Config.from_spec(spec, max_block=max(blk, 16))
@@ -158,10 +164,24 @@ class Workload:
         self.accept = torch.empty(n, dtype=torch.int32, device="cuda")
         self.next_anchor = torch.empty(n, dtype=torch.int32, device="cuda")
         self.n_new = [blk] * n
+        if temperature > 0:
+            # the drafter's logits (q) and resident target logits (p): the
+            # first pass's q plus N(0, 1/2) noise for the draft positions, and
+            # N(0, 1) logits for the position after the block
+            self.q_logits = torch.empty((n, blk - 1, spec.vocab), dtype=torch.float32, device="cuda")
+            self.verify_ws = torch.empty(max(1, int(B_.lib().dflash_verify_workspace_bytes(n, blk))),
+                                         dtype=torch.uint8, device="cuda")
+            self.p_logits = torch.empty((n, blk, spec.vocab), dtype=torch.float32, device="cuda")
         # target tokens: the first pass's drafts with a Geometric(p)-stopped
         # matched prefix, then uniformly random different tokens
         self.step()
         torch.cuda.synchronize()
+        if temperature > 0:
+            rng = np.random.default_rng(8)
+            q = self.q_logits.cpu().numpy()
+            p = np.concatenate([q + rng.normal(scale=0.5, size=q.shape).astype(np.float32),
+                                rng.normal(size=(n, 1, spec.vocab)).astype(np.float32)], axis=1)
+            self.p_logits.copy_(torch.from_numpy(p))
         K, r, bonus = I.gen_accept_construction(spec, 4)
         self.K = K
         tgt = I.make_targets(self.draft.cpu().numpy(), K, r, bonus, spec.vocab)
@@ -181,6 +201,13 @@ class Workload:
         B_, s = self.B, self.spec
         for b, c in enumerate(self.base):
             self.ctx.truncate(b, c)
+        if self.temperature > 0:
+            B_.step_sample(self.model, self.ctx, self.step_feats, self.n_new, self.anchors, s.block,
+                           self.temperature, 1234, self.ws, draft=self.draft, logits=self.q_logits)
+            if hasattr(self, "target"):
+                B_.verify_sample(self.draft, self.q_logits, self.p_logits, s.block, self.temperature, 1234,
+                                 ws=self.verify_ws, accept=self.accept, next_token=self.next_anchor)
+            return
         if self.two_call:
             B_.fuse_ctx(self.model, self.ctx, self.step_feats, self.n_new, self.ws)
             B_.draft_block(self.model, self.ctx, self.anchors, s.block, self.ws, draft=self.draft)
@@ -433,6 +460,8 @@ def main(argv=None) -> int:
                     help="step as dflash_fuse_ctx + dflash_draft_block instead of the fused dflash_step")
     ap.add_argument("--denoise-steps", type=int, default=1,
                     help="draft passes per block (1 = the single-pass drafter)")
+    ap.add_argument("--temperature", type=float, default=0.0,
+                    help="sampled drafts at this temperature, verified losslessly (0 = greedy)")
     ap.add_argument("--graph", action="store_true",
                     help="replay the step as one captured HIP graph (identical steps, so identical work)")
     args = ap.parse_args(argv)
@@ -465,11 +494,14 @@ def main(argv=None) -> int:
         print("--denoise-steps must be in [1, 65]", file=sys.stderr)
         return 2
     train = spec.train_blocks > 0
-    if train and (S > 1 or args.two_call):
-        print("--denoise-steps and --two-call apply to decode workloads only", file=sys.stderr)
+    if train and (S > 1 or args.two_call or args.temperature > 0):
+        print("--denoise-steps, --two-call and --temperature apply to decode workloads only", file=sys.stderr)
+        return 2
+    if args.temperature > 0 and (S > 1 or args.two_call):
+        print("--temperature combines with neither --denoise-steps nor --two-call", file=sys.stderr)
         return 2
     wl = TrainWorkload(spec, weights, torch, B_) if train else \
-        Workload(spec, weights, torch, B_, two_call=args.two_call, denoise_steps=S)
+        Workload(spec, weights, torch, B_, two_call=args.two_call, denoise_steps=S, temperature=args.temperature)
     log("workload resident; warming up")
     for _ in range(args.warmup):
         wl.step()
@@ -599,7 +631,8 @@ def main(argv=None) -> int:
                     f"context {spec.ctx_lens[0] if n == 1 else list(spec.ctx_lens)}, block {blk}; "
                     f"step = append {blk} verified positions + draft pass + accept scan"
                     f"{' (two calls)' if args.two_call else ' (dflash_step)'}"
-                    f"{f' + {S - 1} refinement pass(es)' if S > 1 else ''}")
+                    f"{f' + {S - 1} refinement pass(es)' if S > 1 else ''}"
+                    f"{f'; drafts sampled at temperature {args.temperature} and verified losslessly' if args.temperature > 0 else ''}")
     out = {
         "metric": metric,
         "value": round(draft_tok_s, 1),
@@ -618,6 +651,7 @@ def main(argv=None) -> int:
             "global_batch": n_units if train else n,
             "block": blk,
             "denoise_steps": S,
+            "temperature": args.temperature,
             "seq_len": max(spec.ctx_lens),
             "parallelism": "single GPU",
         },

@@ -21,7 +21,8 @@ STATUS = {0: "DFLASH_OK", -1: "DFLASH_EINVAL", -2: "DFLASH_ESHAPE", -3: "DFLASH_
 # Every symbol include/dflash.h declares.
 EXPORTS = ("dflash_weight_count", "dflash_model_create", "dflash_model_destroy", "dflash_ctx_bytes",
            "dflash_ctx_create", "dflash_ctx_destroy", "dflash_ctx_length", "dflash_ctx_truncate",
-           "dflash_workspace_bytes", "dflash_fuse_ctx", "dflash_draft_block", "dflash_draft_refine", "dflash_draft_anchored", "dflash_step", "dflash_accept_len",
+           "dflash_workspace_bytes", "dflash_fuse_ctx", "dflash_draft_block", "dflash_draft_refine", "dflash_draft_anchored", "dflash_draft_sample",
+    "dflash_verify_workspace_bytes", "dflash_verify_sample", "dflash_step", "dflash_step_sample", "dflash_accept_len",
            "dflash_probe_arm", "dflash_probe_read", "dflash_status_str", "dflash_last_error")
 
 # Stages a measurement probe can bracket (dflash_stage in include/dflash.h).
@@ -87,6 +88,15 @@ def lib():
         L.dflash_draft_anchored.argtypes = [vp, vp, i32, ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_int64), vp, vp,
                                             i32, vp, vp, vp, sz, vp]
         L.dflash_draft_anchored.restype = ctypes.c_int
+        sp = ctypes.POINTER(Sampling)
+        L.dflash_draft_sample.argtypes = [vp, vp, vp, i32, sp, vp, vp, vp, sz, vp]
+        L.dflash_draft_sample.restype = ctypes.c_int
+        L.dflash_step_sample.argtypes = [vp, vp, vp, ctypes.POINTER(i32), vp, i32, sp, vp, vp, vp, sz, vp]
+        L.dflash_step_sample.restype = ctypes.c_int
+        L.dflash_verify_workspace_bytes.argtypes = [i32, i32]
+        L.dflash_verify_workspace_bytes.restype = sz
+        L.dflash_verify_sample.argtypes = [vp, vp, vp, i32, i32, i32, sp, vp, vp, vp, sz, vp]
+        L.dflash_verify_sample.restype = ctypes.c_int
         L.dflash_step.argtypes = [vp, vp, vp, ctypes.POINTER(i32), vp, i32, vp, vp, vp, sz, vp]
         L.dflash_step.restype = ctypes.c_int
         L.dflash_accept_len.argtypes = [vp, vp, i32, i32, vp, vp, vp]
@@ -244,6 +254,43 @@ def draft_anchored(model: Model, ctx: Context, block_seq: Sequence[int], anchor_
     return draft
 
 
+class Sampling(ctypes.Structure):
+    """dflash_sampling: temperature (> 0) and the seed of the random numbers."""
+    _fields_ = [("temperature", ctypes.c_double), ("seed", ctypes.c_uint64)]
+
+
+def draft_sample(model: Model, ctx: Context, anchors, block: int, temperature: float, seed: int, ws, draft=None,
+                 logits=None, stream=None):
+    """Sampled drafts (softmax(logits / temperature) by the Gumbel-max rule)."""
+    import torch
+    if draft is None:
+        draft = torch.empty((ctx.n_seqs, block - 1), dtype=torch.int32, device=anchors.device)
+    sp = Sampling(float(temperature), int(seed) & ((1 << 64) - 1))
+    check(lib().dflash_draft_sample(model.handle, ctx.handle, _ptr(anchors), block, ctypes.byref(sp), _ptr(draft),
+                                    _ptr(logits), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    return draft
+
+
+def verify_sample(draft, draft_logits, target_logits, block: int, temperature: float, seed: int, ws=None,
+                  accept=None, next_token=None, stream=None):
+    """Lossless verification of sampled blocks; returns (accept, next_token)."""
+    import torch
+    n = draft.shape[0]
+    vocab = target_logits.shape[-1]
+    dev = draft.device
+    if accept is None:
+        accept = torch.empty(n, dtype=torch.int32, device=dev)
+    if next_token is None:
+        next_token = torch.empty(n, dtype=torch.int32, device=dev)
+    if ws is None:
+        ws = torch.empty(max(1, int(lib().dflash_verify_workspace_bytes(n, block))), dtype=torch.uint8, device=dev)
+    sp = Sampling(float(temperature), int(seed) & ((1 << 64) - 1))
+    check(lib().dflash_verify_sample(_ptr(draft), _ptr(draft_logits), _ptr(target_logits), n, block, vocab,
+                                     ctypes.byref(sp), _ptr(accept), _ptr(next_token), _ptr(ws),
+                                     ws.numel() * ws.element_size(), _stream(stream)))
+    return accept, next_token
+
+
 def step(model: Model, ctx: Context, features, n_new: Sequence[int], anchors, block: int, ws, draft=None,
          logits=None, stream=None):
     """Append n_new verified positions per sequence and draft a block at the new lengths."""
@@ -253,6 +300,20 @@ def step(model: Model, ctx: Context, features, n_new: Sequence[int], anchors, bl
     arr = (ctypes.c_int32 * ctx.n_seqs)(*[int(v) for v in n_new])
     check(lib().dflash_step(model.handle, ctx.handle, _ptr(features), arr, _ptr(anchors), block, _ptr(draft),
                             _ptr(logits), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    return draft
+
+
+def step_sample(model: Model, ctx: Context, features, n_new: Sequence[int], anchors, block: int, temperature: float,
+                seed: int, ws, draft=None, logits=None, stream=None):
+    """dflash_step with sampled drafts."""
+    import torch
+    if draft is None:
+        draft = torch.empty((ctx.n_seqs, block - 1), dtype=torch.int32, device=anchors.device)
+    arr = (ctypes.c_int32 * ctx.n_seqs)(*[int(v) for v in n_new])
+    sp = Sampling(float(temperature), int(seed) & ((1 << 64) - 1))
+    check(lib().dflash_step_sample(model.handle, ctx.handle, _ptr(features), arr, _ptr(anchors), block,
+                                   ctypes.byref(sp), _ptr(draft), _ptr(logits), _ptr(ws),
+                                   ws.numel() * ws.element_size(), _stream(stream)))
     return draft
 
 

@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 #include <new>
 #include <string>
 #include <vector>
@@ -501,9 +502,10 @@ Blocks seq_blocks(const dflash_ctx* ctx, const int64_t* lens) {
 }
 
 // tokens: NULL (mask tokens) or device [n][block-1] tokens for rows 1..block-1.
+// smp: NULL (greedy drafts) or the sampling parameters of sampled drafts.
 int draft_impl(const dflash_model* model, const dflash_ctx* ctx, const Blocks& bk, const int32_t* anchors,
                const int32_t* tokens, int block, int32_t* draft, float* logits, char* wsb, const WsLayout& W,
-               hipStream_t s, const Append* ap) {
+               hipStream_t s, const Append* ap, const dflash_sampling* smp = nullptr) {
   const dflash_config& c = model->cfg;
   const int n = bk.n;
   u16* bkv = (u16*)(wsb + W.bkv);
@@ -690,6 +692,10 @@ int draft_impl(const dflash_model* model, const dflash_ctx* ctx, const Blocks& b
   g.ep.logits = logits;
   g.ep.vocab = c.vocab;
   g.ep.block = block;
+  if (smp) {
+    g.ep.temp = smp->temperature;
+    g.ep.seed = smp->seed;
+  }
   model->probe.start(DFLASH_STAGE_LM_HEAD, s);
   e = launch_gemm(g, st, Mp, s);
   model->probe.stop(DFLASH_STAGE_LM_HEAD, s);
@@ -713,6 +719,13 @@ int check_draft_args(const dflash_model* model, const dflash_ctx* ctx, const int
   return DFLASH_OK;
 }
 
+int check_sampling(const dflash_sampling* sp) {
+  if (!sp) return fail(DFLASH_EINVAL, "sampling parameters are NULL");
+  if (!(sp->temperature > 0.0) || !std::isfinite(sp->temperature) || sp->temperature > 1e6)
+    return fail(DFLASH_EINVAL, "temperature %g outside (0, 1e6]", sp->temperature);
+  return DFLASH_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -726,6 +739,19 @@ int dflash_draft_block(const dflash_model* model, const dflash_ctx* ctx, const i
     return fail(DFLASH_EWORKSPACE, "workspace holds %zu bytes, %zu needed", ws_bytes, W.draft_end);
   return draft_impl(model, ctx, seq_blocks(ctx, ctx->len.data()), anchors, nullptr, block, draft, logits, (char*)ws,
                     W, (hipStream_t)stream, nullptr);
+}
+
+int dflash_draft_sample(const dflash_model* model, const dflash_ctx* ctx, const int32_t* anchors, int32_t block,
+                        const dflash_sampling* sampling, int32_t* draft, float* logits, void* ws, size_t ws_bytes,
+                        dflash_stream stream) {
+  int rc = check_draft_args(model, ctx, anchors, block, draft, logits, ws);
+  if (rc) return rc;
+  if ((rc = check_sampling(sampling))) return rc;
+  const WsLayout W = ws_layout(&model->cfg, ctx->n_seqs, block, 0);
+  if (ws_bytes < W.draft_end)
+    return fail(DFLASH_EWORKSPACE, "workspace holds %zu bytes, %zu needed", ws_bytes, W.draft_end);
+  return draft_impl(model, ctx, seq_blocks(ctx, ctx->len.data()), anchors, nullptr, block, draft, logits, (char*)ws,
+                    W, (hipStream_t)stream, nullptr, sampling);
 }
 
 int dflash_draft_refine(const dflash_model* model, const dflash_ctx* ctx, const int32_t* anchors,
@@ -779,11 +805,16 @@ int dflash_draft_anchored(const dflash_model* model, const dflash_ctx* ctx, int3
                     nullptr);
 }
 
-int dflash_step(const dflash_model* model, dflash_ctx* ctx, const void* features, const int32_t* n_new,
-                const int32_t* anchors, int32_t block, int32_t* draft, float* logits, void* ws, size_t ws_bytes,
-                dflash_stream stream) {
+}  // extern "C"
+
+namespace {
+
+int step_impl(const dflash_model* model, dflash_ctx* ctx, const void* features, const int32_t* n_new,
+              const int32_t* anchors, int32_t block, const dflash_sampling* smp, int32_t* draft, float* logits,
+              void* ws, size_t ws_bytes, dflash_stream stream) {
   int rc = check_draft_args(model, ctx, anchors, block, draft, logits, ws);
   if (rc) return rc;
+  if (smp && (rc = check_sampling(smp))) return rc;
   if (!n_new) return fail(DFLASH_EINVAL, "n_new is NULL");
   const dflash_config& c = model->cfg;
   const int n = ctx->n_seqs;
@@ -804,7 +835,8 @@ int dflash_step(const dflash_model* model, dflash_ctx* ctx, const void* features
     // too many rows for one fused weight sweep: append, then draft
     rc = dflash_fuse_ctx(model, ctx, features, n_new, ws, ws_bytes, stream);
     if (rc) return rc;
-    return dflash_draft_block(model, ctx, anchors, block, draft, logits, ws, ws_bytes, stream);
+    return smp ? dflash_draft_sample(model, ctx, anchors, block, smp, draft, logits, ws, ws_bytes, stream)
+               : dflash_draft_block(model, ctx, anchors, block, draft, logits, ws, ws_bytes, stream);
   }
   std::vector<int64_t> lens(n);
   for (int b = 0; b < n; ++b) lens[b] = ctx->len[b] + n_new[b];
@@ -814,10 +846,54 @@ int dflash_step(const dflash_model* model, dflash_ctx* ctx, const void* features
   ap.n_new = n_new;
   ap.old_len = ctx->len.data();
   rc = draft_impl(model, ctx, seq_blocks(ctx, lens.data()), anchors, nullptr, block, draft, logits, (char*)ws, W,
-                  (hipStream_t)stream, &ap);
+                  (hipStream_t)stream, &ap, smp);
   if (rc) return rc;
   ctx->len = lens;
   return DFLASH_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dflash_step(const dflash_model* model, dflash_ctx* ctx, const void* features, const int32_t* n_new,
+                const int32_t* anchors, int32_t block, int32_t* draft, float* logits, void* ws, size_t ws_bytes,
+                dflash_stream stream) {
+  return step_impl(model, ctx, features, n_new, anchors, block, nullptr, draft, logits, ws, ws_bytes, stream);
+}
+
+int dflash_step_sample(const dflash_model* model, dflash_ctx* ctx, const void* features, const int32_t* n_new,
+                       const int32_t* anchors, int32_t block, const dflash_sampling* sampling, int32_t* draft,
+                       float* logits, void* ws, size_t ws_bytes, dflash_stream stream) {
+  if (!sampling) return fail(DFLASH_EINVAL, "sampling parameters are NULL");
+  return step_impl(model, ctx, features, n_new, anchors, block, sampling, draft, logits, ws, ws_bytes, stream);
+}
+
+size_t dflash_verify_workspace_bytes(int32_t n_seqs, int32_t block) {
+  if (n_seqs < 0 || block < 2) return 0;
+  return align_up((size_t)n_seqs * block * 2 * sizeof(int32_t)) + kAlign;
+}
+
+int dflash_verify_sample(const int32_t* draft, const float* draft_logits, const float* target_logits, int32_t n_seqs,
+                         int32_t block, int32_t vocab, const dflash_sampling* sampling, int32_t* accept,
+                         int32_t* next_token, void* ws, size_t ws_bytes, dflash_stream stream) {
+  int rc = check_sampling(sampling);
+  if (rc) return rc;
+  if (n_seqs < 0) return fail(DFLASH_EINVAL, "n_seqs %d < 0", n_seqs);
+  if (block < 2 || block > 1024) return fail(DFLASH_EINVAL, "block %d outside [2, 1024]", block);
+  if (vocab < 1) return fail(DFLASH_EINVAL, "vocab %d < 1", vocab);
+  if (n_seqs == 0) return DFLASH_OK;
+  if (!draft || !draft_logits || !target_logits || !accept || !next_token || !ws)
+    return fail(DFLASH_EINVAL, "a pointer argument is NULL");
+  if (!aligned(draft, 4) || !aligned(draft_logits, 4) || !aligned(target_logits, 4) || !aligned(accept, 4) ||
+      !aligned(next_token, 4) || !aligned(ws, 4))
+    return fail(DFLASH_EALIGN, "arguments must be 4-byte aligned");
+  const size_t need = (size_t)n_seqs * block * 2 * sizeof(int32_t);
+  if (ws_bytes < need) return fail(DFLASH_EWORKSPACE, "workspace holds %zu bytes, %zu needed", ws_bytes, need);
+  const hipError_t e = launch_verify_sample(draft, draft_logits, target_logits, n_seqs, block, vocab,
+                                            sampling->temperature, sampling->seed, (int32_t*)ws, accept, next_token,
+                                            (hipStream_t)stream);
+  return e == hipSuccess ? DFLASH_OK : hip_fail(e, "verify_sample");
 }
 
 int dflash_probe_arm(dflash_model* model, int stage, int32_t max_launches) {

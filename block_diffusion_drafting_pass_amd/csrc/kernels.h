@@ -63,7 +63,14 @@ struct EpiParams {
   float* logits;                  // [n_seqs][block-1][vocab] or null
   int vocab;
   int block;
+  // sampled drafts: temp > 0 replaces each logit l of draft row i of block b
+  // by l / temp + G, G the Gumbel number of (seed, b, i, column)
+  double temp;
+  unsigned long long seed;
 };
+
+// Random-number purposes (the key's second word).
+constexpr unsigned long long kPurposeDraft = 1, kPurposeAccept = 2, kPurposeResidual = 3;
 
 struct GemmArgs {
   const u16* a_hi;   // A rows (bf16); with split A this is the hi plane
@@ -138,6 +145,12 @@ hipError_t launch_argmax_reduce(const unsigned long long* part, int n_parts, int
 int argmax_parts(int n_tiles, int Mp);
 hipError_t launch_accept(const int32_t* draft, const int32_t* target, int n, int block,
                          int32_t* accept, int32_t* next_anchor, hipStream_t s);
+// Lossless verification of sampled blocks at temperature temp (fp64): per
+// (sequence, position) the keep test and the residual / bonus sample into
+// pos [n][block][2], then the per-sequence scan into accept / next_token.
+hipError_t launch_verify_sample(const int32_t* draft, const float* q_logits, const float* p_logits, int n,
+                                int block, int vocab, double temp, unsigned long long seed, int32_t* pos,
+                                int32_t* accept, int32_t* next_token, hipStream_t s);
 
 // Injected K/V cache layout of one layer.  Slots are grouped in tiles of
 // kTileKeys; tile t of kv head g is one contiguous block of four planes:

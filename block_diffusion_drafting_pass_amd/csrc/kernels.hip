@@ -91,9 +91,43 @@ __device__ __forceinline__ u64 argmax_key(float v, int col) {
   return ((u64)o << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)col);
 }
 
-// ---------------------------------------------------------------------------
-// weight-row maps and epilogues (shared by both GEMM kernels)
-// ---------------------------------------------------------------------------
+// Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds, each
+// multiplying words 0 and 2 by the round constants and mixing the 128-bit
+// products' halves with words 1 and 3 and the key, which is then advanced by
+// the Weyl constants.  Only word 0 of the output block is used.
+__device__ __forceinline__ u64 philox_w0(u64 c0, u64 c1, u64 c2, u64 c3, u64 k0, u64 k1) {
+  constexpr u64 M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  constexpr u64 W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const u64 hi0 = __umul64hi(M0, c0), lo0 = M0 * c0;
+    const u64 hi1 = __umul64hi(M1, c2), lo1 = M1 * c2;
+    c0 = hi1 ^ c1 ^ k0;
+    c1 = lo1;
+    c2 = hi0 ^ c3 ^ k1;
+    c3 = lo0;
+    k0 += W0;
+    k1 += W1;
+  }
+  return c0;
+}
+
+// Uniform number in (0, 1) of (seed, purpose, block b, position i, index v):
+// the top 53 bits of Philox word 0 of counter (v, i, b, 0), key (seed, purpose).
+__device__ __forceinline__ double philox_uniform(u64 seed, u64 purpose, int b, int i, int v) {
+  const u64 w = philox_w0((u64)v, (u64)i, (u64)b, 0ull, seed, purpose);
+  return ((double)(w >> 11) + 0.5) * 0x1.0p-53;
+}
+
+__device__ __forceinline__ double gumbel(double u) { return -log(-log(u)); }
+
+// The value whose per-row argmax is the draft: the logit itself (greedy), or
+// logit / temp + Gumbel noise (a sample from softmax(logits / temp)).
+__device__ __forceinline__ float draft_score(const EpiParams& ep, int row, int col, float v) {
+  if (ep.temp <= 0.0) return v;
+  const double g = gumbel(philox_uniform(ep.seed, kPurposeDraft, row / ep.block, row % ep.block, col));
+  return (float)((double)v / ep.temp + g);
+}
 
 // ---------------------------------------------------------------------------
 // weight-row maps and epilogues (shared by both GEMM kernels)
@@ -165,7 +199,7 @@ __device__ __forceinline__ void epilogue(const EpiParams& ep, const SeqTable& st
       const bool draft_row = row < ep.M && bi != 0;
       if (draft_row && ep.logits)
         ep.logits[((size_t)(row / ep.block) * (ep.block - 1) + (bi - 1)) * ep.vocab + col] = v[i];
-      u64 key = draft_row ? argmax_key(v[i], col) : 0ull;
+      u64 key = draft_row ? argmax_key(draft_score(ep, row, col, v[i]), col) : 0ull;
 #pragma unroll
       for (int m = 1; m < 16; m <<= 1) {
         const u64 o = shfl_xor_u64(key, m);
@@ -200,7 +234,7 @@ __device__ __forceinline__ void argmax_tail(const EpiParams& ep, int tile0, f32x
       const bool draft_row = row < ep.M && bi != 0;
       if (draft_row && ep.logits)
         ep.logits[((size_t)(row / ep.block) * (ep.block - 1) + (bi - 1)) * ep.vocab + col] = s[i];
-      u64 key = draft_row ? argmax_key(s[i], col) : 0ull;
+      u64 key = draft_row ? argmax_key(draft_score(ep, row, col, s[i]), col) : 0ull;
 #pragma unroll
       for (int m = 1; m < 16; m <<= 1) {
         const u64 o = shfl_xor_u64(key, m);
@@ -931,6 +965,129 @@ __global__ __launch_bounds__(256) void k_accept(const int32_t* __restrict__ draf
   if (next_anchor) next_anchor[b] = tg[k];
 }
 
+// ---------------------------------------------------------------------------
+// Lossless verification of sampled drafts (speculative sampling), fp64.
+// Workgroup (b, i) handles position i (1..B) of sequence b: the log
+// normalisers of p_i = softmax(P_i / T) and, for i < B, q_i = softmax(Q_i / T)
+// (one online max/sum pass), the keep test U q_i(x) < p_i(x) for the draft x,
+// and, where that test fails or at the bonus position i = B, the sample:
+// the largest log(max(0, p_i - q_i)) + G (residual) or P_B / T + G (bonus),
+// lowest index on ties.  A scan then takes the first rejected position.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ void lse_merge(double& m, double& s, double m2, double s2) {
+  if (m2 == -INFINITY) return;
+  if (m == -INFINITY) {
+    m = m2;
+    s = s2;
+    return;
+  }
+  const double mx = fmax(m, m2);
+  s = s * exp(m - mx) + s2 * exp(m2 - mx);
+  m = mx;
+}
+
+__device__ __forceinline__ void amax_merge(double& v, int& ix, double v2, int ix2) {
+  if (v2 > v || (v2 == v && ix2 < ix)) {
+    v = v2;
+    ix = ix2;
+  }
+}
+
+__global__ __launch_bounds__(1024) void k_verify_pos(const int32_t* __restrict__ draft,
+                                                     const float* __restrict__ ql, const float* __restrict__ pl,
+                                                     int block, int vocab, double temp, u64 seed,
+                                                     int32_t* __restrict__ pos) {
+  __shared__ double sm[4][16];
+  __shared__ int si[16];
+  __shared__ int keep_s;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = blockIdx.x / block, i = blockIdx.x % block + 1;
+  const bool bonus = i == block;
+  const float* P = pl + ((size_t)b * block + (i - 1)) * vocab;
+  const float* Q = bonus ? nullptr : ql + ((size_t)b * (block - 1) + (i - 1)) * vocab;
+  // log normalisers
+  double mp = -INFINITY, sp = 0.0, mq = -INFINITY, sq = 0.0;
+  for (int v = tid; v < vocab; v += 1024) {
+    lse_merge(mp, sp, (double)P[v] / temp, 1.0);
+    if (!bonus) lse_merge(mq, sq, (double)Q[v] / temp, 1.0);
+  }
+  for (int o = 32; o >= 1; o >>= 1) {
+    lse_merge(mp, sp, __shfl_xor(mp, o, 64), __shfl_xor(sp, o, 64));
+    lse_merge(mq, sq, __shfl_xor(mq, o, 64), __shfl_xor(sq, o, 64));
+  }
+  if (lane == 0) {
+    sm[0][wave] = mp;
+    sm[1][wave] = sp;
+    sm[2][wave] = mq;
+    sm[3][wave] = sq;
+  }
+  __syncthreads();
+  mp = sm[0][0], sp = sm[1][0], mq = sm[2][0], sq = sm[3][0];
+  for (int w = 1; w < 16; ++w) {
+    lse_merge(mp, sp, sm[0][w], sm[1][w]);
+    lse_merge(mq, sq, sm[2][w], sm[3][w]);
+  }
+  const double lzp = mp + log(sp), lzq = bonus ? 0.0 : mq + log(sq);
+  if (tid == 0) {
+    int keep = 0;
+    if (!bonus) {
+      const int x = min(max(draft[(size_t)b * (block - 1) + (i - 1)], 0), vocab - 1);
+      const double px = exp((double)P[x] / temp - lzp), qx = exp((double)Q[x] / temp - lzq);
+      keep = philox_uniform(seed, kPurposeAccept, b, i, 0) * qx < px;
+    }
+    keep_s = keep;
+  }
+  __syncthreads();
+  int32_t* out = pos + ((size_t)b * block + (i - 1)) * 2;
+  if (keep_s) {
+    if (tid == 0) {
+      out[0] = 1;
+      out[1] = -1;
+    }
+    return;
+  }
+  double best = -INFINITY;
+  int bi = vocab;
+  for (int v = tid; v < vocab; v += 1024) {
+    double sc;
+    if (bonus) {
+      sc = (double)P[v] / temp;
+    } else {
+      const double r = exp((double)P[v] / temp - lzp) - exp((double)Q[v] / temp - lzq);
+      sc = r > 0.0 ? log(r) : -INFINITY;
+    }
+    if (sc == -INFINITY) continue;
+    sc += gumbel(philox_uniform(seed, kPurposeResidual, b, i, v));
+    amax_merge(best, bi, sc, v);
+  }
+  for (int o = 32; o >= 1; o >>= 1) amax_merge(best, bi, __shfl_xor(best, o, 64), __shfl_xor(bi, o, 64));
+  __syncthreads();
+  if (lane == 0) {
+    sm[0][wave] = best;
+    si[wave] = bi;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    best = sm[0][0];
+    bi = si[0];
+    for (int w = 1; w < 16; ++w) amax_merge(best, bi, sm[0][w], si[w]);
+    out[0] = bonus ? 1 : 0;
+    out[1] = bi < vocab ? bi : 0;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_verify_scan(const int32_t* __restrict__ pos, int n, int block,
+                                                     int32_t* __restrict__ accept, int32_t* __restrict__ next_token) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= n) return;
+  const int32_t* p = pos + (size_t)b * block * 2;
+  int k = 0;
+  while (k < block - 1 && p[2 * k]) ++k;
+  accept[b] = k;
+  next_token[b] = p[2 * k + 1];
+}
+
 
 // ---------------------------------------------------------------------------
 // launchers
@@ -1133,6 +1290,16 @@ hipError_t launch_argmax_reduce(const unsigned long long* part, int n_parts, int
                                 int block, int32_t* draft, hipStream_t s) {
   hipLaunchKernelGGL(k_argmax_reduce, dim3(n_seqs * (block - 1)), dim3(256), 0, s, part, n_parts, Mp,
                      block, draft);
+  return hipGetLastError();
+}
+
+hipError_t launch_verify_sample(const int32_t* draft, const float* q_logits, const float* p_logits, int n,
+                                int block, int vocab, double temp, unsigned long long seed, int32_t* pos,
+                                int32_t* accept, int32_t* next_token, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_verify_pos, dim3(n * block), dim3(1024), 0, s, draft, q_logits, p_logits, block, vocab, temp,
+                     seed, pos);
+  hipLaunchKernelGGL(k_verify_scan, dim3((n + 255) / 256), dim3(256), 0, s, pos, n, block, accept, next_token);
   return hipGetLastError();
 }
 

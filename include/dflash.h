@@ -158,6 +158,52 @@ int dflash_draft_block(const dflash_model* model, const dflash_ctx* ctx, const i
                        int32_t block, int32_t* draft, float* logits, void* ws, size_t ws_bytes,
                        dflash_stream stream);
 
+/* Sampling parameters of sampled drafts and of their verification.  The
+ * random numbers are a pure function of (seed, purpose, block index b,
+ * position i, vocabulary index v): word 0 of Philox4x64-10 (Salmon et al.,
+ * SC'11) at counter (v, i, b, 0) and key (seed, purpose), its top 53 bits
+ * mapped to (0, 1).  Use a fresh seed for every drafted block. */
+typedef struct {
+  double temperature; /* > 0 (at most 1e6); temperature 0 is dflash_draft_block */
+  uint64_t seed;
+} dflash_sampling;
+
+/* dflash_draft_block with sampled drafts: position i of block b takes the
+ * token with the largest logit / T + G, G = -log(-log(U)) its Gumbel number
+ * (purpose 1), i.e. a sample from softmax(logits / T).  The pages evaluate
+ * greedy drafts only (atlas summary, "Key results": temperature 0); this is
+ * the sampled counterpart that lossless verification needs.  logits (NULL or
+ * as for dflash_draft_block) receives the raw logits, the q that
+ * dflash_verify_sample takes.  Other arguments and errors as for
+ * dflash_draft_block, plus DFLASH_EINVAL for a NULL or out-of-range
+ * `sampling`. */
+int dflash_draft_sample(const dflash_model* model, const dflash_ctx* ctx, const int32_t* anchors, int32_t block,
+                        const dflash_sampling* sampling, int32_t* draft, float* logits, void* ws, size_t ws_bytes,
+                        dflash_stream stream);
+
+/* Lossless verification of sampled blocks (the paper, Introduction:
+ * speculative decoding verifies the drafts with the target and is lossless;
+ * the rule is standard speculative sampling).  For each sequence b, in
+ * position order i = 1..block-1, draft x is kept when
+ * U(seed, 2, b, i, 0) * q_i(x) < p_i(x), with q_i = softmax(draft_logits / T)
+ * and p_i = softmax(target_logits / T); at the first position where it is
+ * not, next_token[b] is the largest log(max(0, p_i - q_i)) + G (purpose 3)
+ * and accept[b] = i - 1; when every draft is kept, next_token[b] is the
+ * largest target_logits[block-1] / T + G at position block (purpose 3) and
+ * accept[b] = block - 1.  Arithmetic is fp64.
+ *   draft          device int32 [n_seqs][block-1] (clamped into [0, vocab))
+ *   draft_logits   device fp32 [n_seqs][block-1][vocab]
+ *   target_logits  device fp32 [n_seqs][block][vocab]; row i-1 is the
+ *                  target's distribution for position i
+ *   accept, next_token  device int32 [n_seqs]
+ *   ws             device scratch of dflash_verify_workspace_bytes() bytes
+ * Errors: DFLASH_EINVAL (NULL pointer, bad sizes or sampling),
+ * DFLASH_EALIGN, DFLASH_EWORKSPACE, DFLASH_EHIP. */
+size_t dflash_verify_workspace_bytes(int32_t n_seqs, int32_t block);
+int dflash_verify_sample(const int32_t* draft, const float* draft_logits, const float* target_logits, int32_t n_seqs,
+                         int32_t block, int32_t vocab, const dflash_sampling* sampling, int32_t* accept,
+                         int32_t* next_token, void* ws, size_t ws_bytes, dflash_stream stream);
+
 /* Several denoising passes over the block (forum post, section 1: a draft's
  * efficiency is block size over diffusion steps times the acceptance rate;
  * DFlash uses one step).  The pages do not state how a later step re-masks;
@@ -211,6 +257,11 @@ int dflash_draft_anchored(const dflash_model* model, const dflash_ctx* ctx, int3
 int dflash_step(const dflash_model* model, dflash_ctx* ctx, const void* features, const int32_t* n_new,
                 const int32_t* anchors, int32_t block, int32_t* draft, float* logits, void* ws, size_t ws_bytes,
                 dflash_stream stream);
+
+/* dflash_step with sampled drafts (as dflash_draft_sample). */
+int dflash_step_sample(const dflash_model* model, dflash_ctx* ctx, const void* features, const int32_t* n_new,
+                       const int32_t* anchors, int32_t block, const dflash_sampling* sampling, int32_t* draft,
+                       float* logits, void* ws, size_t ws_bytes, dflash_stream stream);
 
 /* Greedy verification (atlas summary, "Key results": temperature 0; metric:
  * acceptance length tau).  draft: device int32 [n_seqs][block-1] for block

@@ -195,3 +195,40 @@ def test_model_create_rejects_wide_gqa_groups():
     ptrs = (ctypes.c_void_p * n)(*([0x10000] * n))
     h = ctypes.c_void_p()
     assert _err(L.dflash_model_create(ctypes.byref(cfg), ptrs, ctypes.byref(h))) == "DFLASH_EUNSUPPORTED"
+
+
+def test_verify_sample_validation_without_device_calls():
+    L = _lib()
+    sp = B.Sampling(0.8, 42)
+    assert L.dflash_verify_workspace_bytes(4, 16) >= 4 * 16 * 2 * 4
+    assert L.dflash_verify_workspace_bytes(4, 1) == 0
+    fake = ctypes.c_void_p(0x100000)
+    acc = ctypes.c_void_p(0x200000)
+    # zero sequences: nothing to do, no device call
+    assert L.dflash_verify_sample(None, None, None, 0, 16, 4096, ctypes.byref(sp), None, None, None, 0, None) == 0
+    for bad_t in (0.0, -1.0, float("inf"), float("nan"), 2e6):
+        bad = B.Sampling(bad_t, 1)
+        assert _err(L.dflash_verify_sample(fake, fake, fake, 1, 16, 4096, ctypes.byref(bad), acc, acc, fake, 1 << 20,
+                                           None)) == "DFLASH_EINVAL", bad_t
+    assert _err(L.dflash_verify_sample(fake, fake, fake, 1, 16, 4096, None, acc, acc, fake, 1 << 20,
+                                       None)) == "DFLASH_EINVAL"
+    assert _err(L.dflash_verify_sample(fake, None, fake, 1, 16, 4096, ctypes.byref(sp), acc, acc, fake, 1 << 20,
+                                       None)) == "DFLASH_EINVAL"
+    assert _err(L.dflash_verify_sample(fake, fake, fake, 1, 1, 4096, ctypes.byref(sp), acc, acc, fake, 1 << 20,
+                                       None)) == "DFLASH_EINVAL"
+    assert _err(L.dflash_verify_sample(fake, fake, fake, 2, 16, 4096, ctypes.byref(sp), acc, acc, fake, 64,
+                                       None)) == "DFLASH_EWORKSPACE"
+    assert _err(L.dflash_verify_sample(ctypes.c_void_p(0x100002), fake, fake, 1, 16, 4096, ctypes.byref(sp), acc,
+                                       acc, fake, 1 << 20, None)) == "DFLASH_EALIGN"
+
+
+def test_sampled_draft_validation_without_context():
+    L = _lib()
+    cfg, m = _fake_model()
+    sp = B.Sampling(1.0, 0)
+    fake = ctypes.c_void_p(0x100000)
+    assert _err(L.dflash_draft_sample(m, None, fake, 16, ctypes.byref(sp), fake, None, fake, 1 << 30,
+                                      None)) == "DFLASH_EINVAL"
+    assert _err(L.dflash_step_sample(m, None, None, None, fake, 16, None, fake, None, fake, 1 << 30,
+                                     None)) == "DFLASH_EINVAL"
+    L.dflash_model_destroy(m)

@@ -14,7 +14,7 @@ import pytest
 from block_diffusion_drafting_pass_amd import binding as B
 from block_diffusion_drafting_pass_amd import inputs as I
 from oracle import dflash_oracle as O
-from tests.gpu_harness import GpuRun, accept_check, assert_parity, oracle_run, say
+from tests.gpu_harness import LOGIT_TOL, GpuRun, accept_check, assert_parity, oracle_run, say
 
 pytestmark = pytest.mark.gpu
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -458,3 +458,149 @@ def test_anchored_q8_ctx1024(q8):
     apos = [int(v) for v in I.gen_train_anchors(1024, 16, 16, seed=3)]
     _anchored_case(spec5, w, dev, (1024,), [0] * 16, apos, 16, "5-layer ctx1024 16 blocks",
                    check_blocks=[0, 7, 15])
+
+
+# ----------------------------------------------------------------------------
+# sampled drafts (temperature > 0) and lossless verification
+# ----------------------------------------------------------------------------
+
+def _check_sampled(gpu_logits, gpu_drafts, ref_logits, T, seed, label, n_check=None):
+    """GPU sampled drafts vs the oracle's Gumbel-max samples of the oracle's
+    logits (equal wherever the top-2 perturbed-score gap > GAP / T), and vs
+    the same rule applied to the GPU's own logits (its pick must be the
+    largest score up to float32 rounding of that score)."""
+    from oracle import sampling as S
+    n, bm1, V = ref_logits.shape
+    sure = checked = 0
+    for b in range(n if n_check is None else n_check):
+        for i in range(1, bm1 + 1):
+            ref_sc = S.sample_scores(ref_logits[b, i - 1], T, seed, b, i)
+            top2 = np.sort(ref_sc)[-2:]
+            if top2[1] - top2[0] > 0.05 / T:
+                sure += 1
+                assert gpu_drafts[b, i - 1] == int(np.argmax(ref_sc)), f"{label}: seq {b} pos {i} differs"
+            own = S.sample_scores(gpu_logits[b, i - 1].astype(np.float64), T, seed, b, i)
+            x = int(gpu_drafts[b, i - 1])
+            assert own[x] >= own.max() - 1e-5 * max(1.0, abs(own.max())), f"{label}: seq {b} pos {i} not the max"
+            checked += 1
+    say(f"{label}: sampled drafts checked on {checked} positions ({sure} decided by the oracle)")
+
+
+@pytest.mark.parametrize("lens,block,T,seed,label", [
+    ((128,), 16, 1.0, 1, "tiny T1"),
+    ((128,), 16, 0.6, 77, "tiny T0.6"),
+    ((37, 5, 0), 4, 1.4, 5, "ragged B4 T1.4"),
+    ((20, 5, 0, 33, 64, 7, 100, 12), 16, 0.8, 9, "eight seqs M128 T0.8"),
+])
+def test_sampled_draft_tiny(torch_cuda, lens, block, T, seed, label):
+    import torch
+    spec = I.spec("tiny").with_(ctx_lens=tuple(lens), block=block)
+    w = I.gen_weights(spec, seed=3, std=0.05)
+    run = GpuRun(spec, B.upload_weights(spec, w), capacity=[c + 8 for c in lens], max_new=sum(lens))
+    feats = _feats(spec, 1, lens)
+    run.ingest(feats)
+    anchors = I.gen_anchors(spec, 2)
+    a = torch.from_numpy(anchors).cuda()
+    n = len(lens)
+    lg = torch.empty((n, block - 1, spec.vocab), dtype=torch.float32, device="cuda")
+    d = B.draft_sample(run.model, run.ctx, a, block, T, seed, run.ws, logits=lg)
+    torch.cuda.synchronize()
+    gl, gd = lg.cpu().numpy(), d.cpu().numpy()
+    ref = oracle_run(spec, w, feats, anchors, block)
+    err = float(np.max(np.abs(gl - ref.logits)))
+    assert err <= LOGIT_TOL, f"{label}: logits error {err}"
+    _check_sampled(gl, gd, ref.logits, T, seed, label)
+    # the same seed gives the same drafts; another seed other drafts
+    d2 = B.draft_sample(run.model, run.ctx, a, block, T, seed, run.ws)
+    d3 = B.draft_sample(run.model, run.ctx, a, block, T, seed + 1, run.ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(d2.cpu().numpy(), gd)
+    assert not np.array_equal(d3.cpu().numpy(), gd)
+
+
+def test_sampled_step_matches_two_calls(torch_cuda):
+    import torch
+    spec = I.spec("tiny").with_(ctx_lens=(112,), block=16)
+    w = I.gen_weights(spec, seed=7, std=0.05)
+    dev_w = B.upload_weights(spec, w)
+    feats = _feats(spec, 1, [128])[0]
+    runs = [GpuRun(spec, dev_w, capacity=[140], max_new=128) for _ in range(2)]
+    for r in runs:
+        r.ingest([feats[:112]])
+    new = torch.from_numpy(np.ascontiguousarray(feats[112:]).view(np.int16)).cuda().view(torch.bfloat16)
+    a = torch.from_numpy(I.gen_anchors(spec, 2)).cuda()
+    lg1 = torch.empty((1, 15, spec.vocab), dtype=torch.float32, device="cuda")
+    lg2 = torch.empty_like(lg1)
+    d1 = B.step_sample(runs[0].model, runs[0].ctx, new, [16], a, 16, 0.9, 123, runs[0].ws, logits=lg1)
+    B.fuse_ctx(runs[1].model, runs[1].ctx, new, [16], runs[1].ws)
+    d2 = B.draft_sample(runs[1].model, runs[1].ctx, a, 16, 0.9, 123, runs[1].ws, logits=lg2)
+    torch.cuda.synchronize()
+    model = O.OracleModel.from_spec(spec, w)
+    octx = O.OracleContext(model, 1)
+    O.fuse_ctx(model, octx, 0, feats)
+    ref = O.draft_block(model, octx, I.gen_anchors(spec, 2), 16)
+    _check_sampled(lg1.cpu().numpy(), d1.cpu().numpy(), ref.logits, 0.9, 123, "sampled step")
+    _check_sampled(lg2.cpu().numpy(), d2.cpu().numpy(), ref.logits, 0.9, 123, "sampled two calls")
+    assert runs[0].ctx.lengths() == [128]
+
+
+def test_sampled_draft_q8_ctx1024(q8):
+    import torch
+    spec5, w, dev = q8
+    lens = (1024,)
+    spec = spec5.with_(ctx_lens=lens)
+    run = GpuRun(spec, dev, capacity=[1100], max_new=1024)
+    feats = _feats(spec, 1, lens)
+    run.ingest(feats)
+    anchors = I.gen_anchors(spec, 2)
+    lg = torch.empty((1, 15, spec.vocab), dtype=torch.float32, device="cuda")
+    d = B.draft_sample(run.model, run.ctx, torch.from_numpy(anchors).cuda(), 16, 0.7, 2026, run.ws, logits=lg)
+    torch.cuda.synchronize()
+    ref = oracle_run(spec, w, feats, anchors, 16)
+    gl = lg.cpu().numpy()
+    assert float(np.max(np.abs(gl - ref.logits))) <= LOGIT_TOL
+    _check_sampled(gl, d.cpu().numpy(), ref.logits, 0.7, 2026, "5-layer sampled T0.7")
+
+
+def _verify_case(n, block, V, T, seed, scale, label, qp_same=False):
+    import torch
+    from oracle import sampling as S
+    rng = np.random.default_rng(seed)
+    q = (rng.normal(size=(n, block - 1, V)) * scale).astype(np.float32)
+    p = (rng.normal(size=(n, block, V)) * scale).astype(np.float32)
+    if qp_same:
+        p[:, : block - 1] = q
+    # drafts: mostly the likely tokens under q, some arbitrary
+    draft = np.argmax(q + rng.gumbel(size=q.shape) * T, axis=-1).astype(np.int32)
+    draft[:, ::5] = rng.integers(0, V, size=draft[:, ::5].shape)
+    acc_ref, nxt_ref = S.verify_sampled(draft, q, p, T, seed)
+    margins = S.accept_margins(draft, q, p, T, seed)
+    dq, dp, dd = (torch.from_numpy(x).cuda() for x in (q, p, draft))
+    acc, nxt = B.verify_sample(dd, dq, dp, block, T, seed)
+    torch.cuda.synchronize()
+    acc, nxt = acc.cpu().numpy(), nxt.cpu().numpy()
+    checked = 0
+    for b in range(n):
+        if np.min(margins[b, : acc_ref[b] + 1 if acc_ref[b] < block - 1 else block - 1]) < 1e-9:
+            continue  # a decision within rounding of its threshold
+        checked += 1
+        assert (acc[b], nxt[b]) == (acc_ref[b], nxt_ref[b]), f"{label}: seq {b}: {(acc[b], nxt[b])} vs " \
+                                                             f"{(acc_ref[b], nxt_ref[b])}"
+    say(f"{label}: accept {acc.tolist()[:12]} ... ({checked}/{n} sequences compared)")
+    assert checked >= n - 1
+    return acc, nxt
+
+
+@pytest.mark.parametrize("n,block,V,T,seed,scale,label", [
+    (24, 16, 4096, 1.0, 1, 2.0, "V4096 T1"),
+    (16, 4, 4096, 0.5, 2, 3.0, "B4 T0.5"),
+    (8, 32, 1000, 1.5, 3, 1.0, "B32 V1000"),
+    (2, 16, 151936, 0.8, 4, 3.0, "full vocab"),
+])
+def test_verify_sample_matches_oracle(torch_cuda, n, block, V, T, seed, scale, label):
+    _verify_case(n, block, V, T, seed, scale, label)
+
+
+def test_verify_sample_keeps_everything_when_draft_equals_target(torch_cuda):
+    acc, _ = _verify_case(8, 16, 2048, 1.0, 5, 2.0, "q equals p", qp_same=True)
+    assert np.all(acc == 15)
