@@ -169,7 +169,7 @@ class Workload:
             # first pass's q plus N(0, 1/2) noise for the draft positions, and
             # N(0, 1) logits for the position after the block
             self.q_logits = torch.empty((n, blk - 1, spec.vocab), dtype=torch.float32, device="cuda")
-            self.verify_ws = torch.empty(max(1, int(B_.lib().dflash_verify_workspace_bytes(n, blk))),
+            self.verify_ws = torch.empty(max(1, int(B_.lib().dflash_verify_workspace_bytes(n, blk, spec.vocab))),
                                          dtype=torch.uint8, device="cuda")
             self.p_logits = torch.empty((n, blk, spec.vocab), dtype=torch.float32, device="cuda")
         # target tokens: the first pass's drafts with a Geometric(p)-stopped

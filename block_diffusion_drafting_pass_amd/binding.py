@@ -93,7 +93,7 @@ def lib():
         L.dflash_draft_sample.restype = ctypes.c_int
         L.dflash_step_sample.argtypes = [vp, vp, vp, ctypes.POINTER(i32), vp, i32, sp, vp, vp, vp, sz, vp]
         L.dflash_step_sample.restype = ctypes.c_int
-        L.dflash_verify_workspace_bytes.argtypes = [i32, i32]
+        L.dflash_verify_workspace_bytes.argtypes = [i32, i32, i32]
         L.dflash_verify_workspace_bytes.restype = sz
         L.dflash_verify_sample.argtypes = [vp, vp, vp, i32, i32, i32, sp, vp, vp, vp, sz, vp]
         L.dflash_verify_sample.restype = ctypes.c_int
@@ -283,7 +283,8 @@ def verify_sample(draft, draft_logits, target_logits, block: int, temperature: f
     if next_token is None:
         next_token = torch.empty(n, dtype=torch.int32, device=dev)
     if ws is None:
-        ws = torch.empty(max(1, int(lib().dflash_verify_workspace_bytes(n, block))), dtype=torch.uint8, device=dev)
+        ws = torch.empty(max(1, int(lib().dflash_verify_workspace_bytes(n, block, vocab))), dtype=torch.uint8,
+                         device=dev)
     sp = Sampling(float(temperature), int(seed) & ((1 << 64) - 1))
     check(lib().dflash_verify_sample(_ptr(draft), _ptr(draft_logits), _ptr(target_logits), n, block, vocab,
                                      ctypes.byref(sp), _ptr(accept), _ptr(next_token), _ptr(ws),

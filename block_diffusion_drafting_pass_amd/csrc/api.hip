@@ -869,9 +869,9 @@ int dflash_step_sample(const dflash_model* model, dflash_ctx* ctx, const void* f
   return step_impl(model, ctx, features, n_new, anchors, block, sampling, draft, logits, ws, ws_bytes, stream);
 }
 
-size_t dflash_verify_workspace_bytes(int32_t n_seqs, int32_t block) {
-  if (n_seqs < 0 || block < 2) return 0;
-  return align_up((size_t)n_seqs * block * 2 * sizeof(int32_t)) + kAlign;
+size_t dflash_verify_workspace_bytes(int32_t n_seqs, int32_t block, int32_t vocab) {
+  if (n_seqs < 0 || block < 2 || block > 1024 || vocab < 1) return 0;
+  return align_up(verify_scratch_bytes(n_seqs, block, vocab));
 }
 
 int dflash_verify_sample(const int32_t* draft, const float* draft_logits, const float* target_logits, int32_t n_seqs,
@@ -886,12 +886,13 @@ int dflash_verify_sample(const int32_t* draft, const float* draft_logits, const 
   if (!draft || !draft_logits || !target_logits || !accept || !next_token || !ws)
     return fail(DFLASH_EINVAL, "a pointer argument is NULL");
   if (!aligned(draft, 4) || !aligned(draft_logits, 4) || !aligned(target_logits, 4) || !aligned(accept, 4) ||
-      !aligned(next_token, 4) || !aligned(ws, 4))
-    return fail(DFLASH_EALIGN, "arguments must be 4-byte aligned");
-  const size_t need = (size_t)n_seqs * block * 2 * sizeof(int32_t);
+      !aligned(next_token, 4))
+    return fail(DFLASH_EALIGN, "arrays must be 4-byte aligned");
+  if (!aligned(ws, 16)) return fail(DFLASH_EALIGN, "workspace must be 16-byte aligned");  // fp64 partials
+  const size_t need = verify_scratch_bytes(n_seqs, block, vocab);
   if (ws_bytes < need) return fail(DFLASH_EWORKSPACE, "workspace holds %zu bytes, %zu needed", ws_bytes, need);
   const hipError_t e = launch_verify_sample(draft, draft_logits, target_logits, n_seqs, block, vocab,
-                                            sampling->temperature, sampling->seed, (int32_t*)ws, accept, next_token,
+                                            sampling->temperature, sampling->seed, ws, accept, next_token,
                                             (hipStream_t)stream);
   return e == hipSuccess ? DFLASH_OK : hip_fail(e, "verify_sample");
 }

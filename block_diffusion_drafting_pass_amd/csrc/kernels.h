@@ -145,11 +145,16 @@ hipError_t launch_argmax_reduce(const unsigned long long* part, int n_parts, int
 int argmax_parts(int n_tiles, int Mp);
 hipError_t launch_accept(const int32_t* draft, const int32_t* target, int n, int block,
                          int32_t* accept, int32_t* next_anchor, hipStream_t s);
-// Lossless verification of sampled blocks at temperature temp (fp64): per
-// (sequence, position) the keep test and the residual / bonus sample into
-// pos [n][block][2], then the per-sequence scan into accept / next_token.
+// Lossless verification of sampled blocks at temperature temp (fp64), with
+// the vocabulary cut into verify_chunks(vocab) chunks: chunked log
+// normalisers, then the keep tests, the first failing position and the
+// residual / bonus sample, into accept / next_token.  scratch: 8-byte
+// aligned, verify_scratch_bytes() bytes.
+constexpr int kVerifyMaxChunks = 64;    // chunks of the log-normaliser pass
+constexpr int kVerifyMaxRChunks = 256;  // chunks of the residual / bonus sampling pass
+size_t verify_scratch_bytes(int n, int block, int vocab);
 hipError_t launch_verify_sample(const int32_t* draft, const float* q_logits, const float* p_logits, int n,
-                                int block, int vocab, double temp, unsigned long long seed, int32_t* pos,
+                                int block, int vocab, double temp, unsigned long long seed, void* scratch,
                                 int32_t* accept, int32_t* next_token, hipStream_t s);
 
 // Injected K/V cache layout of one layer.  Slots are grouped in tiles of

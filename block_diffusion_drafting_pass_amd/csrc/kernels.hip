@@ -15,6 +15,8 @@
 // as A and B use the same one, which every kernel here does by construction.
 #include <math.h>
 
+#include <algorithm>
+
 #include "kernels.h"
 
 namespace dflash {
@@ -967,14 +969,18 @@ __global__ __launch_bounds__(256) void k_accept(const int32_t* __restrict__ draf
 
 // ---------------------------------------------------------------------------
 // Lossless verification of sampled drafts (speculative sampling), fp64.
-// Workgroup (b, i) handles position i (1..B) of sequence b: the log
-// normalisers of p_i = softmax(P_i / T) and, for i < B, q_i = softmax(Q_i / T)
-// (one online max/sum pass), the keep test U q_i(x) < p_i(x) for the draft x,
-// and, where that test fails or at the bonus position i = B, the sample:
-// the largest log(max(0, p_i - q_i)) + G (residual) or P_B / T + G (bonus),
-// lowest index on ties.  A scan then takes the first rejected position.
+// The vocabulary is cut into C chunks.  k_verify_lse: workgroup (b, i, c)
+// forms the online (max, sum of exp) of P_i / T and, for draft positions
+// i < B, Q_i / T over chunk c.  k_verify_sample: workgroup (b, c) merges the
+// chunk partials of every position in chunk order into the log normalisers,
+// takes the keep test U q_i(x) < p_i(x) of each draft x, finds the first
+// position k that fails (or the bonus position B), and forms the largest
+// log(max(0, p_k - q_k)) + G (or P_B / T + G) over its own, finer sampling
+// chunk, lowest index on ties.  k_verify_final: per sequence, the largest of
+// the chunk candidates, in chunk order.
 // ---------------------------------------------------------------------------
 
+// (m, s) += the values represented by (m2, s2): s counts exp(value - m).
 __device__ __forceinline__ void lse_merge(double& m, double& s, double m2, double s2) {
   if (m2 == -INFINITY) return;
   if (m == -INFINITY) {
@@ -982,9 +988,12 @@ __device__ __forceinline__ void lse_merge(double& m, double& s, double m2, doubl
     s = s2;
     return;
   }
-  const double mx = fmax(m, m2);
-  s = s * exp(m - mx) + s2 * exp(m2 - mx);
-  m = mx;
+  if (m2 > m) {
+    s = s * exp(m - m2) + s2;
+    m = m2;
+  } else {
+    s += s2 * exp(m2 - m);
+  }
 }
 
 __device__ __forceinline__ void amax_merge(double& v, int& ix, double v2, int ix2) {
@@ -994,98 +1003,175 @@ __device__ __forceinline__ void amax_merge(double& v, int& ix, double v2, int ix
   }
 }
 
-__global__ __launch_bounds__(1024) void k_verify_pos(const int32_t* __restrict__ draft,
-                                                     const float* __restrict__ ql, const float* __restrict__ pl,
-                                                     int block, int vocab, double temp, u64 seed,
-                                                     int32_t* __restrict__ pos) {
-  __shared__ double sm[4][16];
-  __shared__ int si[16];
-  __shared__ int keep_s;
+int verify_chunks(int vocab) { return std::min(kVerifyMaxChunks, std::max(1, (vocab + 4095) / 4096)); }
+int verify_rchunks(int vocab) { return std::min(kVerifyMaxRChunks, std::max(1, (vocab + 511) / 512)); }
+
+// Chunk partial of the log normalisers: (max, sum) of P / T and of Q / T.
+struct Lse4 {
+  double mp, sp, mq, sq;
+};
+
+__device__ __forceinline__ double wave_max(double v) {
+  for (int o = 32; o >= 1; o >>= 1) v = fmax(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ double wave_sum(double v) {
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Workgroup (b, i, c): (max, sum of exp(x - max)) of x = P_i / T and, for
+// i < B, Q_i / T over vocabulary chunk c (two passes; the chunk stays in
+// L2 between them).
+__global__ __launch_bounds__(256) void k_verify_lse(const float* __restrict__ ql, const float* __restrict__ pl,
+                                                    int block, int vocab, int chunks, double inv_t,
+                                                    Lse4* __restrict__ part) {
+  __shared__ double sm[2][4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int b = blockIdx.x / block, i = blockIdx.x % block + 1;
-  const bool bonus = i == block;
-  const float* P = pl + ((size_t)b * block + (i - 1)) * vocab;
-  const float* Q = bonus ? nullptr : ql + ((size_t)b * (block - 1) + (i - 1)) * vocab;
-  // log normalisers
-  double mp = -INFINITY, sp = 0.0, mq = -INFINITY, sq = 0.0;
-  for (int v = tid; v < vocab; v += 1024) {
-    lse_merge(mp, sp, (double)P[v] / temp, 1.0);
-    if (!bonus) lse_merge(mq, sq, (double)Q[v] / temp, 1.0);
+  const int c = blockIdx.x % chunks, bi = blockIdx.x / chunks;  // bi = b * block + (i - 1)
+  const int b = bi / block, i = bi % block + 1;
+  const bool has_q = i < block;
+  const float* P = pl + (size_t)bi * vocab;
+  const float* Q = has_q ? ql + ((size_t)b * (block - 1) + (i - 1)) * vocab : pl + (size_t)bi * vocab;
+  const int per = (vocab + chunks - 1) / chunks, v0 = c * per, v1 = min(vocab, v0 + per);
+  double mp = -INFINITY, mq = -INFINITY;
+  for (int v = v0 + tid; v < v1; v += 256) {
+    mp = fmax(mp, (double)P[v]);
+    mq = fmax(mq, (double)Q[v]);
   }
-  for (int o = 32; o >= 1; o >>= 1) {
-    lse_merge(mp, sp, __shfl_xor(mp, o, 64), __shfl_xor(sp, o, 64));
-    lse_merge(mq, sq, __shfl_xor(mq, o, 64), __shfl_xor(sq, o, 64));
-  }
+  mp = wave_max(mp);
+  mq = wave_max(mq);
   if (lane == 0) {
     sm[0][wave] = mp;
-    sm[1][wave] = sp;
-    sm[2][wave] = mq;
-    sm[3][wave] = sq;
+    sm[1][wave] = mq;
   }
   __syncthreads();
-  mp = sm[0][0], sp = sm[1][0], mq = sm[2][0], sq = sm[3][0];
-  for (int w = 1; w < 16; ++w) {
-    lse_merge(mp, sp, sm[0][w], sm[1][w]);
-    lse_merge(mq, sq, sm[2][w], sm[3][w]);
-  }
-  const double lzp = mp + log(sp), lzq = bonus ? 0.0 : mq + log(sq);
-  if (tid == 0) {
-    int keep = 0;
-    if (!bonus) {
-      const int x = min(max(draft[(size_t)b * (block - 1) + (i - 1)], 0), vocab - 1);
-      const double px = exp((double)P[x] / temp - lzp), qx = exp((double)Q[x] / temp - lzq);
-      keep = philox_uniform(seed, kPurposeAccept, b, i, 0) * qx < px;
-    }
-    keep_s = keep;
-  }
+  mp = fmax(fmax(sm[0][0], sm[0][1]), fmax(sm[0][2], sm[0][3])) * inv_t;
+  mq = fmax(fmax(sm[1][0], sm[1][1]), fmax(sm[1][2], sm[1][3])) * inv_t;
   __syncthreads();
-  int32_t* out = pos + ((size_t)b * block + (i - 1)) * 2;
-  if (keep_s) {
-    if (tid == 0) {
-      out[0] = 1;
-      out[1] = -1;
+  double sp = 0.0, sq = 0.0;
+  if (v0 < v1) {
+    for (int v = v0 + tid; v < v1; v += 256) {
+      sp += exp((double)P[v] * inv_t - mp);
+      sq += exp((double)Q[v] * inv_t - mq);
     }
-    return;
   }
-  double best = -INFINITY;
-  int bi = vocab;
-  for (int v = tid; v < vocab; v += 1024) {
-    double sc;
-    if (bonus) {
-      sc = (double)P[v] / temp;
-    } else {
-      const double r = exp((double)P[v] / temp - lzp) - exp((double)Q[v] / temp - lzq);
-      sc = r > 0.0 ? log(r) : -INFINITY;
-    }
-    if (sc == -INFINITY) continue;
-    sc += gumbel(philox_uniform(seed, kPurposeResidual, b, i, v));
-    amax_merge(best, bi, sc, v);
-  }
-  for (int o = 32; o >= 1; o >>= 1) amax_merge(best, bi, __shfl_xor(best, o, 64), __shfl_xor(bi, o, 64));
-  __syncthreads();
+  sp = wave_sum(sp);
+  sq = wave_sum(sq);
   if (lane == 0) {
-    sm[0][wave] = best;
-    si[wave] = bi;
+    sm[0][wave] = sp;
+    sm[1][wave] = sq;
   }
   __syncthreads();
   if (tid == 0) {
-    best = sm[0][0];
-    bi = si[0];
-    for (int w = 1; w < 16; ++w) amax_merge(best, bi, sm[0][w], si[w]);
-    out[0] = bonus ? 1 : 0;
-    out[1] = bi < vocab ? bi : 0;
+    sp = (sm[0][0] + sm[0][1]) + (sm[0][2] + sm[0][3]);
+    sq = (sm[1][0] + sm[1][1]) + (sm[1][2] + sm[1][3]);
+    part[(size_t)bi * chunks + c] = has_q ? Lse4{mp, sp, mq, sq} : Lse4{mp, sp, -INFINITY, 0.0};
   }
 }
 
-__global__ __launch_bounds__(256) void k_verify_scan(const int32_t* __restrict__ pos, int n, int block,
-                                                     int32_t* __restrict__ accept, int32_t* __restrict__ next_token) {
-  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+// Log normalisers of position bi from its chunk partials, by one wave
+// (chunks <= 64: lane c holds chunk c; a fixed shuffle tree merges them).
+__device__ __forceinline__ void verify_lz_wave(const Lse4* part, int bi, int chunks, int lane, double& lzp,
+                                               double& lzq) {
+  double mp = -INFINITY, sp = 0.0, mq = -INFINITY, sq = 0.0;
+  if (lane < chunks) {
+    const Lse4 t = part[(size_t)bi * chunks + lane];
+    mp = t.mp, sp = t.sp, mq = t.mq, sq = t.sq;
+  }
+  for (int o = 32; o >= 1; o >>= 1) {
+    const double a = __shfl_xor(mp, o, 64), bs = __shfl_xor(sp, o, 64);
+    const double cq = __shfl_xor(mq, o, 64), ds = __shfl_xor(sq, o, 64);
+    lse_merge(mp, sp, a, bs);
+    lse_merge(mq, sq, cq, ds);
+  }
+  lzp = mp + log(sp);
+  lzq = mq + log(sq);
+}
+
+__global__ __launch_bounds__(256) void k_verify_sample(const int32_t* __restrict__ draft,
+                                                       const float* __restrict__ ql, const float* __restrict__ pl,
+                                                       int block, int vocab, int chunks, int rchunks, double inv_t,
+                                                       u64 seed, const Lse4* __restrict__ part,
+                                                       double* __restrict__ cand_v, int* __restrict__ cand_i,
+                                                       int32_t* __restrict__ accept) {
+  __shared__ int keep[1024];
+  __shared__ double lz_s[1024][2];
+  __shared__ double sv[4];
+  __shared__ int si[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = blockIdx.x % rchunks, b = blockIdx.x / rchunks;  // c: this workgroup's sampling chunk
+  // keep test of every draft position, one wave per position
+  for (int i = 1 + wave; i < block; i += 4) {
+    const int bi = b * block + (i - 1);
+    double lzp, lzq;
+    verify_lz_wave(part, bi, chunks, lane, lzp, lzq);
+    if (lane == 0) {
+      const int x = min(max(draft[(size_t)b * (block - 1) + (i - 1)], 0), vocab - 1);
+      const double px = exp((double)pl[(size_t)bi * vocab + x] * inv_t - lzp);
+      const double qx = exp((double)ql[((size_t)b * (block - 1) + (i - 1)) * vocab + x] * inv_t - lzq);
+      keep[i] = philox_uniform(seed, kPurposeAccept, b, i, 0) * qx < px;
+      lz_s[i][0] = lzp;
+      lz_s[i][1] = lzq;
+    }
+  }
+  __syncthreads();
+  int k = 1;
+  while (k < block && keep[k]) ++k;  // first rejected position, or block (bonus)
+  if (tid == 0 && c == 0) accept[b] = k - 1;
+  const bool bonus = k == block;
+  const float* P = pl + ((size_t)b * block + (k - 1)) * vocab;
+  const float* Q = bonus ? nullptr : ql + ((size_t)b * (block - 1) + (k - 1)) * vocab;
+  const double lzp = bonus ? 0.0 : lz_s[k][0], lzq = bonus ? 0.0 : lz_s[k][1];
+  const int per = (vocab + rchunks - 1) / rchunks, v0 = c * per, v1 = min(vocab, v0 + per);
+  double best = -INFINITY;
+  int bix = vocab;
+  for (int v = v0 + tid; v < v1; v += 256) {
+    double sc;
+    if (bonus) {
+      sc = (double)P[v] * inv_t;
+    } else {
+      const double r = exp((double)P[v] * inv_t - lzp) - exp((double)Q[v] * inv_t - lzq);
+      sc = r > 0.0 ? log(r) : -INFINITY;
+    }
+    if (sc == -INFINITY) continue;
+    sc += gumbel(philox_uniform(seed, kPurposeResidual, b, k, v));
+    amax_merge(best, bix, sc, v);
+  }
+  for (int o = 32; o >= 1; o >>= 1) {
+    const double ov = __shfl_xor(best, o, 64);
+    const int oi = __shfl_xor(bix, o, 64);
+    amax_merge(best, bix, ov, oi);
+  }
+  if (lane == 0) {
+    sv[wave] = best;
+    si[wave] = bix;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    best = sv[0];
+    bix = si[0];
+    for (int w = 1; w < 4; ++w) amax_merge(best, bix, sv[w], si[w]);
+    cand_v[(size_t)b * rchunks + c] = best;
+    cand_i[(size_t)b * rchunks + c] = bix;
+  }
+}
+
+// One wave per sequence: the largest chunk candidate (lowest index on ties).
+__global__ __launch_bounds__(256) void k_verify_final(const double* __restrict__ cand_v,
+                                                      const int* __restrict__ cand_i, int n, int chunks,
+                                                      int vocab, int32_t* __restrict__ next_token) {
+  const int lane = threadIdx.x & 63, b = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (b >= n) return;
-  const int32_t* p = pos + (size_t)b * block * 2;
-  int k = 0;
-  while (k < block - 1 && p[2 * k]) ++k;
-  accept[b] = k;
-  next_token[b] = p[2 * k + 1];
+  double best = -INFINITY;
+  int bix = vocab;
+  for (int c = lane; c < chunks; c += 64) amax_merge(best, bix, cand_v[(size_t)b * chunks + c], cand_i[(size_t)b * chunks + c]);
+  for (int o = 32; o >= 1; o >>= 1) {
+    const double ov = __shfl_xor(best, o, 64);
+    const int oi = __shfl_xor(bix, o, 64);
+    amax_merge(best, bix, ov, oi);
+  }
+  if (lane == 0) next_token[b] = bix < vocab ? bix : 0;
 }
 
 
@@ -1293,13 +1379,27 @@ hipError_t launch_argmax_reduce(const unsigned long long* part, int n_parts, int
   return hipGetLastError();
 }
 
+size_t verify_scratch_bytes(int n, int block, int vocab) {
+  const size_t C = verify_chunks(vocab), CR = verify_rchunks(vocab);
+  const size_t lse = (size_t)n * block * C * sizeof(Lse4);
+  return lse + (size_t)n * CR * (sizeof(double) + sizeof(int)) + 64;
+}
+
 hipError_t launch_verify_sample(const int32_t* draft, const float* q_logits, const float* p_logits, int n,
-                                int block, int vocab, double temp, unsigned long long seed, int32_t* pos,
+                                int block, int vocab, double temp, unsigned long long seed, void* scratch,
                                 int32_t* accept, int32_t* next_token, hipStream_t s) {
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_verify_pos, dim3(n * block), dim3(1024), 0, s, draft, q_logits, p_logits, block, vocab, temp,
-                     seed, pos);
-  hipLaunchKernelGGL(k_verify_scan, dim3((n + 255) / 256), dim3(256), 0, s, pos, n, block, accept, next_token);
+  if (block < 2 || block > 1024) return hipErrorInvalidValue;
+  const int C = verify_chunks(vocab), CR = verify_rchunks(vocab);
+  Lse4* part = (Lse4*)scratch;
+  double* cand_v = (double*)(part + (size_t)n * block * C);
+  int* cand_i = (int*)(cand_v + (size_t)n * CR);
+  const double inv_t = 1.0 / temp;
+  hipLaunchKernelGGL(k_verify_lse, dim3(n * block * C), dim3(256), 0, s, q_logits, p_logits, block, vocab, C, inv_t,
+                     part);
+  hipLaunchKernelGGL(k_verify_sample, dim3(n * CR), dim3(256), 0, s, draft, q_logits, p_logits, block, vocab, C,
+                     CR, inv_t, seed, part, cand_v, cand_i, accept);
+  hipLaunchKernelGGL(k_verify_final, dim3((n + 3) / 4), dim3(256), 0, s, cand_v, cand_i, n, CR, vocab, next_token);
   return hipGetLastError();
 }
 

@@ -196,10 +196,12 @@ int dflash_draft_sample(const dflash_model* model, const dflash_ctx* ctx, const 
  *   target_logits  device fp32 [n_seqs][block][vocab]; row i-1 is the
  *                  target's distribution for position i
  *   accept, next_token  device int32 [n_seqs]
- *   ws             device scratch of dflash_verify_workspace_bytes() bytes
+ *   ws             device scratch, 16-byte aligned, of
+ *                  dflash_verify_workspace_bytes(n_seqs, block, vocab) bytes
+ *                  (0 for bad sizes)
  * Errors: DFLASH_EINVAL (NULL pointer, bad sizes or sampling),
  * DFLASH_EALIGN, DFLASH_EWORKSPACE, DFLASH_EHIP. */
-size_t dflash_verify_workspace_bytes(int32_t n_seqs, int32_t block);
+size_t dflash_verify_workspace_bytes(int32_t n_seqs, int32_t block, int32_t vocab);
 int dflash_verify_sample(const int32_t* draft, const float* draft_logits, const float* target_logits, int32_t n_seqs,
                          int32_t block, int32_t vocab, const dflash_sampling* sampling, int32_t* accept,
                          int32_t* next_token, void* ws, size_t ws_bytes, dflash_stream stream);

@@ -200,8 +200,9 @@ def test_model_create_rejects_wide_gqa_groups():
 def test_verify_sample_validation_without_device_calls():
     L = _lib()
     sp = B.Sampling(0.8, 42)
-    assert L.dflash_verify_workspace_bytes(4, 16) >= 4 * 16 * 2 * 4
-    assert L.dflash_verify_workspace_bytes(4, 1) == 0
+    assert L.dflash_verify_workspace_bytes(4, 16, 4096) >= 4 * 16 * 32
+    assert L.dflash_verify_workspace_bytes(4, 1, 4096) == 0
+    assert L.dflash_verify_workspace_bytes(4, 16, 0) == 0
     fake = ctypes.c_void_p(0x100000)
     acc = ctypes.c_void_p(0x200000)
     # zero sequences: nothing to do, no device call
