@@ -346,30 +346,39 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void k_skinny(GemmArgs ga, SeqTa
 }
 
 // ---------------------------------------------------------------------------
-// Many-row GEMM (M a multiple of 128): 128 x 256 output tile per workgroup
-// of eight waves (2 x 4, each 64 x 64 = 4 x 4 MFMA tiles), over K chunk kc
-// of gridDim / (mt nt) chunks.  K runs in 64-wide slabs through two LDS
-// buffers: while the waves multiply slab k out of one buffer, slab k+1's
-// global loads are in flight in registers and land in the other buffer, so
-// one barrier per slab suffices.  LDS rows are 128 bytes; 16-byte chunk c of
-// row r sits at c ^ ((r >> 1) & 7), which puts the 16 rows one fragment
-// read touches in distinct bank groups.  Workgroup ids run over the row
+// Many-row GEMM (M a multiple of 128): BM x 256 output tile per workgroup
+// of BM / 16 waves (BM / 64 x 4, each 64 x 64 = 4 x 4 MFMA tiles), over K
+// chunk kc of gridDim / (mt nt) chunks.  K runs in BK-wide slabs through
+// two LDS buffers: while the waves multiply slab k out of one buffer, slab
+// k+1's global loads are in flight in registers and land in the other
+// buffer, so one barrier per slab suffices.  LDS rows are 2 BK bytes;
+// 16-byte chunk c of row r sits at c ^ ((r >> 1) & (BK / 8 - 1)), which
+// spreads the rows one fragment read touches over the bank groups.  The
+// shape (BM, BK) is picked per launch (big_cfg): 128 / 32 (64 KB of LDS,
+// two workgroups per CU) for split-K launches and wide grids; 128 / 64
+// (128 KB, one per CU, so a small grid spreads over the CUs) for small
+// grids; 256 / 32 (96 KB, 16 waves) for the widest argmax launches.  Workgroup ids run over the row
 // tiles first, so the row tiles that share a weight tile are dispatched
 // together and reuse it from L2.  A last column tile past n_tiles reads a
 // valid weight row and skips its epilogue.  Epilogues are the per-16x16-tile
 // ones above.
 // ---------------------------------------------------------------------------
 
-constexpr int kBigBM = 128, kBigBN = 256, kBigBK = 64;
+constexpr int kBigBN = 256;
 
-__device__ __forceinline__ int big_swz(int row, int ch) { return row * 8 + (ch ^ ((row >> 1) & 7)); }
+template <int BK>
+__device__ __forceinline__ int big_swz(int row, int ch) {
+  constexpr int CPR = BK / 8;  // 16-byte chunks per row
+  return row * CPR + (ch ^ ((row >> 1) & (CPR - 1)));
+}
 
-template <int EPI, int MAP, bool SPLIT>
-__global__ __launch_bounds__(512) void k_gemm_big(GemmArgs ga, SeqTable st, int mt, int kcn) {
-  constexpr int BM = kBigBM, BN = kBigBN, BK = kBigBK, NP = SPLIT ? 2 : 1;
-  constexpr int ACH = BM * 8, WCH = BN * 8;        // 16-byte chunks per A plane / W slab
+template <int EPI, int MAP, bool SPLIT, int BM, int BK>
+__global__ __launch_bounds__(BM * 4) void k_gemm_big(GemmArgs ga, SeqTable st, int mt, int kcn) {
+  constexpr int BN = kBigBN, NP = SPLIT ? 2 : 1, NT = BM * 4, CPR = BK / 8;
+  constexpr int ACH = BM * CPR, WCH = BN * CPR;     // 16-byte chunks per A plane / W slab
   constexpr int STAGE = NP * ACH + WCH;             // chunks per LDS buffer
-  constexpr int AP = ACH / 512, WP = WCH / 512;     // chunks each thread stages per A plane / W
+  constexpr int AP = ACH / NT, WP = WCH / NT;       // chunks each thread stages per A plane / W
+  static_assert(ACH % NT == 0 && WCH % NT == 0, "staging must split evenly over the threads");
   extern __shared__ u32x4 smem[];
 
   const int bid = blockIdx.x, m_t = bid % mt, kc = (bid / mt) % kcn, n_t = bid / (mt * kcn);
@@ -384,9 +393,9 @@ __global__ __launch_bounds__(512) void k_gemm_big(GemmArgs ga, SeqTable st, int 
   int ar[AP], ac[AP];
 #pragma unroll
   for (int q = 0; q < AP; ++q) {
-    const int idx = tid + 512 * q;
-    ar[q] = idx >> 3;
-    ac[q] = idx & 7;
+    const int idx = tid + NT * q;
+    ar[q] = idx / CPR;
+    ac[q] = idx % CPR;
     const int arow = row0 + ar[q];
     av[q] = arow < ga.a_rows;
     gA[0][q] = ga.a_hi + (size_t)arow * ga.lda + kbase + ac[q] * 8;
@@ -396,9 +405,9 @@ __global__ __launch_bounds__(512) void k_gemm_big(GemmArgs ga, SeqTable st, int 
   int wr[WP], wc[WP];
 #pragma unroll
   for (int q = 0; q < WP; ++q) {
-    const int idx = tid + 512 * q;
-    wr[q] = idx >> 3;
-    wc[q] = idx & 7;
+    const int idx = tid + NT * q;
+    wr[q] = idx / CPR;
+    wc[q] = idx % CPR;
     const int tile = min(tile0 + (wr[q] >> 4), ga.n_tiles - 1);
     gW[q] = weight_row<MAP>(ga.w, ga.ep, tile, wr[q] & 15, K) + kbase + wc[q] * 8;
   }
@@ -417,9 +426,9 @@ __global__ __launch_bounds__(512) void k_gemm_big(GemmArgs ga, SeqTable st, int 
 #pragma unroll
     for (int q = 0; q < AP; ++q)
 #pragma unroll
-      for (int p = 0; p < NP; ++p) S[p * ACH + big_swz(ar[q], ac[q])] = rA[p][q];
+      for (int p = 0; p < NP; ++p) S[p * ACH + big_swz<BK>(ar[q], ac[q])] = rA[p][q];
 #pragma unroll
-    for (int q = 0; q < WP; ++q) S[NP * ACH + big_swz(wr[q], wc[q])] = rW[q];
+    for (int q = 0; q < WP; ++q) S[NP * ACH + big_swz<BK>(wr[q], wc[q])] = rW[q];
   };
 
   f32x4 acc[4][4];
@@ -442,12 +451,12 @@ __global__ __launch_bounds__(512) void k_gemm_big(GemmArgs ga, SeqTable st, int 
       bf16x8 wf[4];
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct)
-        wf[ct] = __builtin_bit_cast(bf16x8, S[NP * ACH + big_swz(wn * 64 + ct * 16 + c, ch)]);
+        wf[ct] = __builtin_bit_cast(bf16x8, S[NP * ACH + big_swz<BK>(wn * 64 + ct * 16 + c, ch)]);
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
-          const bf16x8 a = __builtin_bit_cast(bf16x8, S[p * ACH + big_swz(wm * 64 + rg * 16 + c, ch)]);
+          const bf16x8 a = __builtin_bit_cast(bf16x8, S[p * ACH + big_swz<BK>(wm * 64 + rg * 16 + c, ch)]);
 #pragma unroll
           for (int ct = 0; ct < 4; ++ct) acc[rg][ct] = mfma(a, wf[ct], acc[rg][ct]);
         }
@@ -1215,6 +1224,19 @@ hipError_t launch_kv_finish(const float* part, int kc, int M, int Mp, int n_laye
   return hipGetLastError();
 }
 
+// Tile shape of a many-row GEMM launch (see k_gemm_big): split-K launches
+// take 128 / 32; otherwise the widest argmax launches take 256 / 32, and the
+// rest 128 / 32 on a wide grid or 128 / 64 on a grid smaller than the CUs.
+struct BigCfg {
+  int bm, bk;
+};
+static BigCfg big_cfg(int epi, int Mp, int n_tiles) {
+  const int nt = (n_tiles + kBigBN / 16 - 1) / (kBigBN / 16);
+  if (epi == EPI_PARTIAL) return {128, 32};
+  if (epi == EPI_ARGMAX) return (Mp % 256 == 0 && (Mp / 256) * nt >= 1024) ? BigCfg{256, 32} : BigCfg{128, 64};
+  return (Mp / 128) * nt >= 256 ? BigCfg{128, 32} : BigCfg{128, 64};
+}
+
 GemmPlan gemm_plan(int n_tiles, int K, int Mp, bool may_split) {
   GemmPlan p;
   p.kc = 1;
@@ -1227,9 +1249,9 @@ GemmPlan gemm_plan(int n_tiles, int K, int Mp, bool may_split) {
     }
   } else {
     p.nc = kBigBN / 16;
-    if (may_split) {  // aim for about two workgroups per CU
-      const int wgs = (Mp / kBigBM) * ((n_tiles + p.nc - 1) / p.nc);
-      while (p.kc * 2 <= kMaxKc && p.kc * 2 * wgs <= 512 && K % (p.kc * 2 * kBigBK) == 0) p.kc *= 2;
+    if (may_split) {  // split-K launches are 128 / 32: aim for about two workgroups per CU
+      const int wgs = (Mp / 128) * ((n_tiles + p.nc - 1) / p.nc);
+      while (p.kc * 2 <= kMaxKc && p.kc * 2 * wgs <= 512 && K % (p.kc * 2 * 32) == 0) p.kc *= 2;
     }
   }
   return p;
@@ -1247,6 +1269,24 @@ static hipError_t skinny_nc(const GemmArgs& g, const SeqTable& st, const GemmPla
   return hipGetLastError();
 }
 
+template <int EPI, int MAP, bool SPLIT, int BM, int BK>
+static hipError_t big_launch(const GemmArgs& g, const SeqTable& st, int Mp, const GemmPlan& p, hipStream_t s) {
+  if (Mp % BM || g.K % (p.kc * BK)) return hipErrorInvalidValue;
+  constexpr int NP = SPLIT ? 2 : 1;
+  constexpr int lds = 2 * (NP * BM + kBigBN) * BK * 2;  // bytes: two buffers of A planes + W
+  static bool attr_set = false;  // the dynamic-LDS limit is raised once per instantiation
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute((const void*)k_gemm_big<EPI, MAP, SPLIT, BM, BK>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int mt = Mp / BM, nt = (g.n_tiles + p.nc - 1) / p.nc;
+  hipLaunchKernelGGL((k_gemm_big<EPI, MAP, SPLIT, BM, BK>), dim3(mt * p.kc * nt), dim3(BM * 4), lds, s, g, st, mt,
+                     p.kc);
+  return hipGetLastError();
+}
+
 template <int EPI, int MAP, bool SPLIT>
 static hipError_t gemm_dispatch(const GemmArgs& g, const SeqTable& st, int Mp, hipStream_t s) {
   const GemmPlan p = gemm_plan(g.n_tiles, g.K, Mp, EPI == EPI_PARTIAL);
@@ -1254,19 +1294,17 @@ static hipError_t gemm_dispatch(const GemmArgs& g, const SeqTable& st, int Mp, h
     if (g.K % (kSkinnyWaves * 64) || Mp % 16) return hipErrorInvalidValue;
     return Mp <= 16 ? skinny_nc<EPI, MAP, SPLIT, 1>(g, st, p, s) : skinny_nc<EPI, MAP, SPLIT, 2>(g, st, p, s);
   }
-  if (Mp % kBigBM || g.K % (p.kc * kBigBK)) return hipErrorInvalidValue;
-  constexpr int NP = SPLIT ? 2 : 1;
-  const int lds = 2 * (NP * kBigBM + kBigBN) * kBigBK * 2;  // bytes: two buffers of A planes + W
-  static bool attr_set = false;  // the dynamic-LDS limit is raised once per instantiation
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute((const void*)k_gemm_big<EPI, MAP, SPLIT>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
+  if (Mp % 128) return hipErrorInvalidValue;
+  const BigCfg cf = big_cfg(EPI, Mp, g.n_tiles);
+  if constexpr (EPI == EPI_PARTIAL) {
+    return big_launch<EPI, MAP, SPLIT, 128, 32>(g, st, Mp, p, s);
+  } else {
+    if constexpr (EPI == EPI_ARGMAX) {
+      if (cf.bm == 256) return big_launch<EPI, MAP, SPLIT, 256, 32>(g, st, Mp, p, s);
+    }
+    return cf.bk == 32 ? big_launch<EPI, MAP, SPLIT, 128, 32>(g, st, Mp, p, s)
+                       : big_launch<EPI, MAP, SPLIT, 128, 64>(g, st, Mp, p, s);
   }
-  const int mt = Mp / kBigBM, nt = (g.n_tiles + p.nc - 1) / p.nc;
-  hipLaunchKernelGGL((k_gemm_big<EPI, MAP, SPLIT>), dim3(mt * p.kc * nt), dim3(512), lds, s, g, st, mt, p.kc);
-  return hipGetLastError();
 }
 
 hipError_t launch_gemm(const GemmArgs& g, const SeqTable& st, int Mp, hipStream_t s) {
