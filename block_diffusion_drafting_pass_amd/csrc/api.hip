@@ -622,6 +622,7 @@ int draft_impl(const dflash_model* model, const dflash_ctx* ctx, const Blocks& b
     const LayerW& Lw = model->layers[l];
     GemmArgs g = base_args(qin_hi, qin_lo, H, H, nqkv / 16, EPI_PARTIAL, MAP_QKV);
     g.a_rows = Mq;
+    g.q_rows = R > 0 ? M : 0;  // appended rows need only their K / V
     g.ep.M = Mq;
     g.ep.Mp = Mqp;
     g.ep.out_f32 = part;

@@ -79,6 +79,7 @@ struct GemmArgs {
   int a_rows;        // rows of A that exist in memory; others read as zero
   int K;
   int n_tiles;       // 16-wide output tiles in the mapped column space
+  int q_rows;        // MAP_QKV: rows >= q_rows need no q columns (appended context rows); 0: all do
   WeightSeg w;
   int map;
   int epi;

@@ -290,6 +290,11 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void k_skinny(GemmArgs ga, SeqTa
   for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
     for (int j = 0; j < NC; ++j) acc[rg][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // row groups that need none of this workgroup's columns (appended context
+  // rows against q columns) skip their products; their partials stay zero
+  int rg_end = RG;
+  if (MAP == MAP_QKV && RG > 1 && ga.q_rows > 0 && (tile0 + NC) * 16 <= ga.ep.n_q * ga.ep.head_dim)
+    rg_end = (ga.q_rows + 15) / 16;
 
   bf16x8 wf[U][NC];
 #pragma unroll
@@ -309,6 +314,7 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void k_skinny(GemmArgs ga, SeqTa
     for (int u = 0; u < U; ++u) {
 #pragma unroll
       for (int rg = 0; rg < RG; ++rg) {
+        if (rg >= rg_end) break;  // uniform over the workgroup
         const bf16x8 a = ld_frag(ah[rg] + k + u * 32);
 #pragma unroll
         for (int j = 0; j < NC; ++j) acc[rg][j] = mfma(a, wf[u][j], acc[rg][j]);
