@@ -604,3 +604,80 @@ def test_verify_sample_matches_oracle(torch_cuda, n, block, V, T, seed, scale, l
 def test_verify_sample_keeps_everything_when_draft_equals_target(torch_cuda):
     acc, _ = _verify_case(8, 16, 2048, 1.0, 5, 2.0, "q equals p", qp_same=True)
     assert np.all(acc == 15)
+
+
+# ----------------------------------------------------------------------------
+# the decode step captured once as a HIP graph and replayed
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("sampled,base,n_new", [
+    (False, (112,), (16,)),       # fused: 16 block rows + 16 appended rows in one sweep
+    (True, (112,), (16,)),
+    (False, (100, 40), (8, 8)),   # 48 rows: append, then draft
+    (True, (100, 40), (8, 8)),
+])
+def test_step_graph_replays_match_eager(torch_cuda, sampled, base, n_new):
+    """dflash_step (greedy or sampled) + the accept scan captured in a graph:
+    three replays, with eager work and synchronisation between them, each
+    bitwise equal to the eager step.  The host rolls the context back before
+    each replay, so every replay appends to the same slots."""
+    torch = torch_cuda
+    n = len(base)
+    spec = I.spec("tiny").with_(ctx_lens=tuple(base), block=16)
+    w = I.gen_weights(spec, seed=5, std=0.05)
+    dev_w = B.upload_weights(spec, w)
+    cap = [b + k + 16 for b, k in zip(base, n_new)]
+    run = GpuRun(spec, dev_w, capacity=cap, max_new=sum(base) + sum(n_new), max_block=32)
+    other = GpuRun(spec, dev_w, capacity=cap, max_new=sum(base) + sum(n_new), max_block=32)
+    feats = _feats(spec, 1, [b + k for b, k in zip(base, n_new)])
+    run.ingest([f[:b] for f, b in zip(feats, base)])
+    other.ingest([f[:b] for f, b in zip(feats, base)])
+    new = torch.from_numpy(np.ascontiguousarray(np.concatenate([f[b:] for f, b in zip(feats, base)])).view(np.int16)) \
+        .cuda().view(torch.bfloat16)
+    a = torch.from_numpy(I.gen_anchors(spec, 2)).cuda()
+    draft = torch.empty((n, 15), dtype=torch.int32, device="cuda")
+    logits = torch.empty((n, 15, spec.vocab), dtype=torch.float32, device="cuda")
+    rng = np.random.default_rng(3)
+    target = torch.from_numpy(rng.integers(0, spec.vocab, size=(n, 16)).astype(np.int32)).cuda()
+    acc = torch.empty(n, dtype=torch.int32, device="cuda")
+    nxt = torch.empty(n, dtype=torch.int32, device="cuda")
+
+    def step():
+        if sampled:
+            B.step_sample(run.model, run.ctx, new, list(n_new), a, 16, 0.8, 77, run.ws, draft=draft, logits=logits)
+        else:
+            B.step(run.model, run.ctx, new, list(n_new), a, 16, run.ws, draft=draft, logits=logits)
+        B.accept_len(draft, target, 16, acc, nxt)
+
+    def rollback():
+        for b, c in enumerate(base):
+            run.ctx.truncate(b, c)
+
+    step()
+    torch.cuda.synchronize()
+    ref = (draft.cpu().numpy().copy(), logits.cpu().numpy().copy(), acc.cpu().numpy().copy(),
+           nxt.cpu().numpy().copy())
+    rollback()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        draft.fill_(-1)
+        logits.zero_()
+        rollback()
+        g.replay()
+        torch.cuda.synchronize()
+        got = (draft.cpu().numpy(), logits.cpu().numpy(), acc.cpu().numpy(), nxt.cpu().numpy())
+        for x, y in zip(got, ref):
+            assert np.array_equal(x.view(np.uint32) if x.dtype == np.float32 else x,
+                                  y.view(np.uint32) if y.dtype == np.float32 else y), f"replay {rep} differs"
+        # eager work on another context between replays
+        B.draft_block(other.model, other.ctx, a, 16, other.ws)
+        torch.cuda.synchronize()
+    assert run.ctx.lengths() == list(base)
+    say(f"graph replays equal the eager step (sampled={sampled}, base={base})")
