@@ -353,17 +353,18 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void k_skinny(GemmArgs ga, SeqTa
 
 // ---------------------------------------------------------------------------
 // Many-row GEMM (M a multiple of 128): BM x 256 output tile per workgroup
-// of BM / 16 waves (BM / 64 x 4, each 64 x 64 = 4 x 4 MFMA tiles), over K
-// chunk kc of gridDim / (mt nt) chunks.  K runs in BK-wide slabs through
+// of BM / 64 x WN waves, each 64 rows x 256 / WN columns (4 x 16 / WN MFMA
+// tiles), over K chunk kc of gridDim / (mt nt) chunks.  K runs in BK-wide slabs through
 // two LDS buffers: while the waves multiply slab k out of one buffer, slab
 // k+1's global loads are in flight in registers and land in the other
 // buffer, so one barrier per slab suffices.  LDS rows are 2 BK bytes;
 // 16-byte chunk c of row r sits at c ^ ((r >> 1) & (BK / 8 - 1)), which
 // spreads the rows one fragment read touches over the bank groups.  The
-// shape (BM, BK) is picked per launch (big_cfg): 128 / 32 (64 KB of LDS,
-// two workgroups per CU) for split-K launches and wide grids; 128 / 64
-// (128 KB, one per CU, so a small grid spreads over the CUs) for small
-// grids; 256 / 32 (96 KB, 16 waves) for the widest argmax launches.  Workgroup ids run over the row
+// shape (BM, BK, WN) is picked per launch (big_cfg): 128 / 32 / 2 (four
+// waves of 64 x 128, 64 KB of LDS, two workgroups per CU) for split-K
+// launches and wide grids; 128 / 64 / 4 (128 KB, one per CU, so a small grid
+// spreads over the CUs) for small grids; 256 / 32 / 4 (96 KB, 16 waves) for
+// the widest argmax launches.  Workgroup ids run over the row
 // tiles first, so the row tiles that share a weight tile are dispatched
 // together and reuse it from L2.  A last column tile past n_tiles reads a
 // valid weight row and skips its epilogue.  Epilogues are the per-16x16-tile
@@ -378,9 +379,10 @@ __device__ __forceinline__ int big_swz(int row, int ch) {
   return row * CPR + (ch ^ ((row >> 1) & (CPR - 1)));
 }
 
-template <int EPI, int MAP, bool SPLIT, int BM, int BK>
-__global__ __launch_bounds__(BM * 4) void k_gemm_big(GemmArgs ga, SeqTable st, int mt, int kcn) {
-  constexpr int BN = kBigBN, NP = SPLIT ? 2 : 1, NT = BM * 4, CPR = BK / 8;
+template <int EPI, int MAP, bool SPLIT, int BM, int BK, int WN>
+__global__ __launch_bounds__(BM / 64 * WN * 64) void k_gemm_big(GemmArgs ga, SeqTable st, int mt, int kcn) {
+  constexpr int BN = kBigBN, NP = SPLIT ? 2 : 1, NT = BM / 64 * WN * 64, CPR = BK / 8;
+  constexpr int TN = BN / WN / 16;  // 16-wide column tiles per wave (each wave: 64 rows x TN tiles)
   constexpr int ACH = BM * CPR, WCH = BN * CPR;     // 16-byte chunks per A plane / W slab
   constexpr int STAGE = NP * ACH + WCH;             // chunks per LDS buffer
   constexpr int AP = ACH / NT, WP = WCH / NT;       // chunks each thread stages per A plane / W
@@ -391,7 +393,7 @@ __global__ __launch_bounds__(BM * 4) void k_gemm_big(GemmArgs ga, SeqTable st, i
   const int row0 = m_t * BM, tile0 = n_t * (BN / 16);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 15, g = lane >> 4;
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wm = wave / WN, wn = wave % WN;
   const int K = ga.K, kspan = K / kcn, kbase = kc * kspan;
 
   const u16* gA[NP][AP];
@@ -437,11 +439,11 @@ __global__ __launch_bounds__(BM * 4) void k_gemm_big(GemmArgs ga, SeqTable st, i
     for (int q = 0; q < WP; ++q) S[NP * ACH + big_swz<BK>(wr[q], wc[q])] = rW[q];
   };
 
-  f32x4 acc[4][4];
+  f32x4 acc[4][TN];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < TN; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nk = kspan / BK;
   load(0);
@@ -454,17 +456,17 @@ __global__ __launch_bounds__(BM * 4) void k_gemm_big(GemmArgs ga, SeqTable st, i
 #pragma unroll
     for (int ks = 0; ks < BK / 32; ++ks) {
       const int ch = ks * 4 + g;
-      bf16x8 wf[4];
+      bf16x8 wf[TN];
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
-        wf[ct] = __builtin_bit_cast(bf16x8, S[NP * ACH + big_swz<BK>(wn * 64 + ct * 16 + c, ch)]);
+      for (int ct = 0; ct < TN; ++ct)
+        wf[ct] = __builtin_bit_cast(bf16x8, S[NP * ACH + big_swz<BK>(wn * TN * 16 + ct * 16 + c, ch)]);
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
           const bf16x8 a = __builtin_bit_cast(bf16x8, S[p * ACH + big_swz<BK>(wm * 64 + rg * 16 + c, ch)]);
 #pragma unroll
-          for (int ct = 0; ct < 4; ++ct) acc[rg][ct] = mfma(a, wf[ct], acc[rg][ct]);
+          for (int ct = 0; ct < TN; ++ct) acc[rg][ct] = mfma(a, wf[ct], acc[rg][ct]);
         }
       }
     }
@@ -472,8 +474,8 @@ __global__ __launch_bounds__(BM * 4) void k_gemm_big(GemmArgs ga, SeqTable st, i
     __syncthreads();
   }
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {
-    const int tile = tile0 + wn * 4 + ct;
+  for (int ct = 0; ct < TN; ++ct) {
+    const int tile = tile0 + wn * TN + ct;
     if (tile >= ga.n_tiles) break;  // uniform over the wave
 #pragma unroll
     for (int rg = 0; rg < 4; ++rg) epilogue<EPI>(ga.ep, st, tile, row0 + wm * 64 + rg * 16, acc[rg][ct], lane, kc);
@@ -1275,21 +1277,21 @@ static hipError_t skinny_nc(const GemmArgs& g, const SeqTable& st, const GemmPla
   return hipGetLastError();
 }
 
-template <int EPI, int MAP, bool SPLIT, int BM, int BK>
+template <int EPI, int MAP, bool SPLIT, int BM, int BK, int WN>
 static hipError_t big_launch(const GemmArgs& g, const SeqTable& st, int Mp, const GemmPlan& p, hipStream_t s) {
   if (Mp % BM || g.K % (p.kc * BK)) return hipErrorInvalidValue;
   constexpr int NP = SPLIT ? 2 : 1;
   constexpr int lds = 2 * (NP * BM + kBigBN) * BK * 2;  // bytes: two buffers of A planes + W
   static bool attr_set = false;  // the dynamic-LDS limit is raised once per instantiation
   if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute((const void*)k_gemm_big<EPI, MAP, SPLIT, BM, BK>,
+    const hipError_t e = hipFuncSetAttribute((const void*)k_gemm_big<EPI, MAP, SPLIT, BM, BK, WN>,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const int mt = Mp / BM, nt = (g.n_tiles + p.nc - 1) / p.nc;
-  hipLaunchKernelGGL((k_gemm_big<EPI, MAP, SPLIT, BM, BK>), dim3(mt * p.kc * nt), dim3(BM * 4), lds, s, g, st, mt,
-                     p.kc);
+  hipLaunchKernelGGL((k_gemm_big<EPI, MAP, SPLIT, BM, BK, WN>), dim3(mt * p.kc * nt), dim3(BM / 64 * WN * 64), lds, s,
+                     g, st, mt, p.kc);
   return hipGetLastError();
 }
 
@@ -1303,13 +1305,13 @@ static hipError_t gemm_dispatch(const GemmArgs& g, const SeqTable& st, int Mp, h
   if (Mp % 128) return hipErrorInvalidValue;
   const BigCfg cf = big_cfg(EPI, Mp, g.n_tiles);
   if constexpr (EPI == EPI_PARTIAL) {
-    return big_launch<EPI, MAP, SPLIT, 128, 32>(g, st, Mp, p, s);
+    return big_launch<EPI, MAP, SPLIT, 128, 32, 2>(g, st, Mp, p, s);
   } else {
     if constexpr (EPI == EPI_ARGMAX) {
-      if (cf.bm == 256) return big_launch<EPI, MAP, SPLIT, 256, 32>(g, st, Mp, p, s);
+      if (cf.bm == 256) return big_launch<EPI, MAP, SPLIT, 256, 32, 4>(g, st, Mp, p, s);
     }
-    return cf.bk == 32 ? big_launch<EPI, MAP, SPLIT, 128, 32>(g, st, Mp, p, s)
-                       : big_launch<EPI, MAP, SPLIT, 128, 64>(g, st, Mp, p, s);
+    return cf.bk == 32 ? big_launch<EPI, MAP, SPLIT, 128, 32, 4>(g, st, Mp, p, s)
+                       : big_launch<EPI, MAP, SPLIT, 128, 64, 4>(g, st, Mp, p, s);
   }
 }
 
