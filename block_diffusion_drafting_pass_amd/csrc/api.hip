@@ -584,6 +584,7 @@ int draft_impl(const dflash_model* model, const dflash_ctx* ctx, const Blocks& b
   u16* qin_hi = qa_hi;
   u16* qin_lo = qa_lo;
   hipError_t e;
+  int fus_kc = 0, fus_rows = 0;
 
   if (ap) {
     // fused target features of the appended rows -> rows M .. M+R-1 of the q|k|v input
@@ -602,11 +603,10 @@ int draft_impl(const dflash_model* model, const dflash_ctx* ctx, const Blocks& b
     f.ep.Mp = Rp;
     f.ep.out_f32 = part;
     f.ep.ldo = H;
-    const int kcf = gemm_plan(f.n_tiles, f.K, Rp, true).kc;
+    fus_kc = gemm_plan(f.n_tiles, f.K, Rp, true).kc;
+    fus_rows = Rp;
     model->probe.start(DFLASH_STAGE_FUSION, s);
     e = launch_gemm(f, st, Rp, s);
-    if (e == hipSuccess)
-      e = launch_reduce_split(part, kcf, Rp, H, qa_hi + (size_t)M * H, qa_lo + (size_t)M * H, R, R, s);
     model->probe.stop(DFLASH_STAGE_FUSION, s);
     if (e != hipSuccess) return hip_fail(e, "step: fusion GEMM");
   }
@@ -615,8 +615,11 @@ int draft_impl(const dflash_model* model, const dflash_ctx* ctx, const Blocks& b
     e = launch_clear_block_pad(bkv, n, c.n_kv_heads, c.head_dim, block, s);
     if (e != hipSuccess) return hip_fail(e, "draft: clear block K/V padding");
   }
-  e = launch_resid_norm(x, nullptr, 0, 0, anchors, tokens, model->embed, block, c.mask_token_id, c.vocab,
-                        model->layers[0].attn_norm, qin_hi, qin_lo, H, M, M, c.rms_eps, s);
+  // block embedding + first norm for rows < M; with appended rows the same
+  // launch sums their fusion partials into rows M .. M+R-1 of the q|k|v input
+  e = launch_resid_norm(x, ap ? part : nullptr, fus_kc, fus_rows, anchors, tokens, model->embed, block,
+                        c.mask_token_id, c.vocab, model->layers[0].attn_norm, qin_hi, qin_lo, H, M, M + R,
+                        c.rms_eps, s);
   if (e != hipSuccess) return hip_fail(e, "draft_block: embed + attention norm");
   for (int l = 0; l < c.n_layers; ++l) {
     const LayerW& Lw = model->layers[l];

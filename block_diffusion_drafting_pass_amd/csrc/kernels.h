@@ -106,7 +106,9 @@ hipError_t launch_gemm(const GemmArgs& g, const SeqTable& st, int Mp, hipStream_
 // id, or block_tokens[seq][i-1] when given), or
 // x[row] += sum over kc of part[kc][row] (fixed kc order; part_rows = the
 // partials' row stride per chunk); then out = hi/lo(gain * x / sqrt(mean(x^2)
-// + eps)) for rows < M.  Rows M..out_rows-1 of out are zero.
+// + eps)) for rows < M.  Rows M..out_rows-1 of out are zero, except in
+// embedding mode with part given: there they are appended rows, out[row] =
+// hi/lo(sum over kc of part[kc][row - M]) (no gain, no norm, x untouched).
 hipError_t launch_resid_norm(float* x, const float* part, int kc, int part_rows, const int32_t* anchors,
                              const int32_t* block_tokens, const u16* embed, int block, int mask_id, int vocab,
                              const u16* gain, u16* out_hi, u16* out_lo, int H, int M, int out_rows, float eps,

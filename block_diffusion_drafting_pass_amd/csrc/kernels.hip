@@ -760,6 +760,28 @@ __global__ __launch_bounds__(1024) void k_resid_norm(float* __restrict__ x, cons
   const int row = blockIdx.x, tid = threadIdx.x;
   u16* oh = out_hi + (size_t)row * H;
   u16* ol = out_lo + (size_t)row * H;
+  if (row >= M && E && part) {
+    // appended rows: their fused features, summed over the K chunks in order
+    const int r = row - M;
+    for (int j = tid * 4; j < H; j += 4096) {
+      f32x4 p[kMaxKc];
+#pragma unroll
+      for (int q = 0; q < kMaxKc; ++q)
+        if (q < kc) p[q] = *reinterpret_cast<const f32x4*>(part + ((size_t)q * part_rows + r) * H + j);
+      f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int q = 0; q < kMaxKc; ++q)
+        if (q < kc) v += p[q];
+      u16 hh[4], ll[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) split_pair(v[i], hh[i], ll[i]);
+      *reinterpret_cast<uint2*>(oh + j) =
+          make_uint2((uint32_t)hh[0] | ((uint32_t)hh[1] << 16), (uint32_t)hh[2] | ((uint32_t)hh[3] << 16));
+      *reinterpret_cast<uint2*>(ol + j) =
+          make_uint2((uint32_t)ll[0] | ((uint32_t)ll[1] << 16), (uint32_t)ll[2] | ((uint32_t)ll[3] << 16));
+    }
+    return;
+  }
   if (row >= M) {
     for (int j = tid * 4; j < H; j += 4096) {
       *reinterpret_cast<uint2*>(oh + j) = make_uint2(0u, 0u);
