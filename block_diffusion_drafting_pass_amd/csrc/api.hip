@@ -874,7 +874,7 @@ int dflash_step_sample(const dflash_model* model, dflash_ctx* ctx, const void* f
 }
 
 size_t dflash_verify_workspace_bytes(int32_t n_seqs, int32_t block, int32_t vocab) {
-  if (n_seqs < 0 || block < 2 || block > 1024 || vocab < 1) return 0;
+  if (n_seqs < 0 || block < 2 || block > 1024 || vocab < 1 || vocab > kVerifyMaxVocab) return 0;
   return align_up(verify_scratch_bytes(n_seqs, block, vocab));
 }
 
@@ -885,7 +885,8 @@ int dflash_verify_sample(const int32_t* draft, const float* draft_logits, const 
   if (rc) return rc;
   if (n_seqs < 0) return fail(DFLASH_EINVAL, "n_seqs %d < 0", n_seqs);
   if (block < 2 || block > 1024) return fail(DFLASH_EINVAL, "block %d outside [2, 1024]", block);
-  if (vocab < 1) return fail(DFLASH_EINVAL, "vocab %d < 1", vocab);
+  if (vocab < 1 || vocab > kVerifyMaxVocab)
+    return fail(DFLASH_EINVAL, "vocab %d outside [1, %d]", vocab, kVerifyMaxVocab);
   if (n_seqs == 0) return DFLASH_OK;
   if (!draft || !draft_logits || !target_logits || !accept || !next_token || !ws)
     return fail(DFLASH_EINVAL, "a pointer argument is NULL");

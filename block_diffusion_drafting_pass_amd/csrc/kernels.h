@@ -153,7 +153,8 @@ hipError_t launch_accept(const int32_t* draft, const int32_t* target, int n, int
 // normalisers, then the keep tests, the first failing position and the
 // residual / bonus sample, into accept / next_token.  scratch: 8-byte
 // aligned, verify_scratch_bytes() bytes.
-constexpr int kVerifyMaxChunks = 64;    // chunks of the log-normaliser pass
+constexpr int kVerifyMaxChunks = 64;    // chunks of the log-normaliser pass (at most 4096 entries each)
+constexpr int kVerifyMaxVocab = kVerifyMaxChunks * 4096;
 constexpr int kVerifyMaxRChunks = 256;  // chunks of the residual / bonus sampling pass
 size_t verify_scratch_bytes(int n, int block, int vocab);
 hipError_t launch_verify_sample(const int32_t* draft, const float* q_logits, const float* p_logits, int n,

@@ -1009,31 +1009,16 @@ __global__ __launch_bounds__(256) void k_accept(const int32_t* __restrict__ draf
 // ---------------------------------------------------------------------------
 // Lossless verification of sampled drafts (speculative sampling), fp64.
 // The vocabulary is cut into C chunks.  k_verify_lse: workgroup (b, i, c)
-// forms the online (max, sum of exp) of P_i / T and, for draft positions
-// i < B, Q_i / T over chunk c.  k_verify_sample: workgroup (b, c) merges the
-// chunk partials of every position in chunk order into the log normalisers,
-// takes the keep test U q_i(x) < p_i(x) of each draft x, finds the first
-// position k that fails (or the bonus position B), and forms the largest
-// log(max(0, p_k - q_k)) + G (or P_B / T + G) over its own, finer sampling
-// chunk, lowest index on ties.  k_verify_final: per sequence, the largest of
-// the chunk candidates, in chunk order.
+// forms (max, sum of exp) of P_i / T and, for draft positions i < B, of
+// Q_i / T over chunk c.  k_verify_keep: one workgroup per sequence, one
+// wave per position, merges each position's chunk partials into its log
+// normalisers,
+// takes the keep test U q_i(x) < p_i(x) of the draft x and finds the first
+// position k that fails (or the bonus position B).  k_verify_sample:
+// workgroup (b, c) forms the largest log(max(0, p_k - q_k)) + G (or
+// P_B / T + G) over its own, finer sampling chunk, lowest index on ties.
+// k_verify_final: per sequence, the largest of the chunk candidates.
 // ---------------------------------------------------------------------------
-
-// (m, s) += the values represented by (m2, s2): s counts exp(value - m).
-__device__ __forceinline__ void lse_merge(double& m, double& s, double m2, double s2) {
-  if (m2 == -INFINITY) return;
-  if (m == -INFINITY) {
-    m = m2;
-    s = s2;
-    return;
-  }
-  if (m2 > m) {
-    s = s * exp(m - m2) + s2;
-    m = m2;
-  } else {
-    s += s2 * exp(m2 - m);
-  }
-}
 
 __device__ __forceinline__ void amax_merge(double& v, int& ix, double v2, int ix2) {
   if (v2 > v || (v2 == v && ix2 < ix)) {
@@ -1060,26 +1045,35 @@ __device__ __forceinline__ double wave_sum(double v) {
 }
 
 // Workgroup (b, i, c): (max, sum of exp(x - max)) of x = P_i / T and, for
-// i < B, Q_i / T over vocabulary chunk c (two passes; the chunk stays in
-// L2 between them).
+// i < B, Q_i / T over vocabulary chunk c.  A chunk holds at most 4096
+// entries, so each thread loads its (at most 16) values of both rows at once
+// into registers and both passes run there.
 __global__ __launch_bounds__(256) void k_verify_lse(const float* __restrict__ ql, const float* __restrict__ pl,
                                                     int block, int vocab, int chunks, double inv_t,
                                                     Lse4* __restrict__ part) {
+  constexpr int PER = 16;  // values per thread and row: 16 x 256 >= 4096
   __shared__ double sm[2][4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = blockIdx.x % chunks, bi = blockIdx.x / chunks;  // bi = b * block + (i - 1)
   const int b = bi / block, i = bi % block + 1;
   const bool has_q = i < block;
   const float* P = pl + (size_t)bi * vocab;
-  const float* Q = has_q ? ql + ((size_t)b * (block - 1) + (i - 1)) * vocab : pl + (size_t)bi * vocab;
+  const float* Q = has_q ? ql + ((size_t)b * (block - 1) + (i - 1)) * vocab : P;
   const int per = (vocab + chunks - 1) / chunks, v0 = c * per, v1 = min(vocab, v0 + per);
-  double mp = -INFINITY, mq = -INFINITY;
-  for (int v = v0 + tid; v < v1; v += 256) {
-    mp = fmax(mp, (double)P[v]);
-    mq = fmax(mq, (double)Q[v]);
+  float pv[PER], qv[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int v = v0 + tid + u * 256;
+    pv[u] = v < v1 ? P[v] : -INFINITY;
+    qv[u] = v < v1 ? Q[v] : -INFINITY;
   }
-  mp = wave_max(mp);
-  mq = wave_max(mq);
+  float fp = -INFINITY, fq = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    fp = fmaxf(fp, pv[u]);
+    fq = fmaxf(fq, qv[u]);
+  }
+  double mp = wave_max((double)fp), mq = wave_max((double)fq);
   if (lane == 0) {
     sm[0][wave] = mp;
     sm[1][wave] = mq;
@@ -1090,9 +1084,10 @@ __global__ __launch_bounds__(256) void k_verify_lse(const float* __restrict__ ql
   __syncthreads();
   double sp = 0.0, sq = 0.0;
   if (v0 < v1) {
-    for (int v = v0 + tid; v < v1; v += 256) {
-      sp += exp((double)P[v] * inv_t - mp);
-      sq += exp((double)Q[v] * inv_t - mq);
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      if (pv[u] != -INFINITY) sp += exp((double)pv[u] * inv_t - mp);
+      if (qv[u] != -INFINITY) sq += exp((double)qv[u] * inv_t - mq);
     }
   }
   sp = wave_sum(sp);
@@ -1109,59 +1104,80 @@ __global__ __launch_bounds__(256) void k_verify_lse(const float* __restrict__ ql
   }
 }
 
-// Log normalisers of position bi from its chunk partials, by one wave
-// (chunks <= 64: lane c holds chunk c; a fixed shuffle tree merges them).
+// Log normalisers (log Z_p, log Z_q) of position bi from its chunk
+// partials, by one wave: lane c holds chunk c (chunks <= 64); the largest
+// chunk maximum first, then one exp per chunk, summed by a fixed shuffle tree.
 __device__ __forceinline__ void verify_lz_wave(const Lse4* part, int bi, int chunks, int lane, double& lzp,
                                                double& lzq) {
-  double mp = -INFINITY, sp = 0.0, mq = -INFINITY, sq = 0.0;
-  if (lane < chunks) {
-    const Lse4 t = part[(size_t)bi * chunks + lane];
-    mp = t.mp, sp = t.sp, mq = t.mq, sq = t.sq;
-  }
-  for (int o = 32; o >= 1; o >>= 1) {
-    const double a = __shfl_xor(mp, o, 64), bs = __shfl_xor(sp, o, 64);
-    const double cq = __shfl_xor(mq, o, 64), ds = __shfl_xor(sq, o, 64);
-    lse_merge(mp, sp, a, bs);
-    lse_merge(mq, sq, cq, ds);
-  }
+  Lse4 t{-INFINITY, 0.0, -INFINITY, 0.0};
+  if (lane < chunks) t = part[(size_t)bi * chunks + lane];
+  const double mp = wave_max(t.mp), mq = wave_max(t.mq);
+  const double sp = wave_sum(t.mp == -INFINITY ? 0.0 : t.sp * exp(t.mp - mp));
+  const double sq = wave_sum(t.mq == -INFINITY ? 0.0 : t.sq * exp(t.mq - mq));
   lzp = mp + log(sp);
   lzq = mq + log(sq);
 }
 
-__global__ __launch_bounds__(256) void k_verify_sample(const int32_t* __restrict__ draft,
-                                                       const float* __restrict__ ql, const float* __restrict__ pl,
-                                                       int block, int vocab, int chunks, int rchunks, double inv_t,
-                                                       u64 seed, const Lse4* __restrict__ part,
-                                                       double* __restrict__ cand_v, int* __restrict__ cand_i,
-                                                       int32_t* __restrict__ accept) {
+// Per verification record (per sequence): the first rejected position k
+// (block when every draft is kept) and the log normalisers at k.
+struct VerifyPos {
+  double lzp, lzq;
+  int k, pad;
+};
+
+// One workgroup of 16 waves per sequence: wave w handles draft positions
+// i = w + 1, w + 17, ...: its log normalisers and the keep test
+// U q_i(x) < p_i(x); then thread 0 takes the first failing position.
+__global__ __launch_bounds__(1024) void k_verify_keep(const int32_t* __restrict__ draft, const float* __restrict__ ql,
+                                                      const float* __restrict__ pl, int block, int vocab, int chunks,
+                                                      double inv_t, u64 seed, const Lse4* __restrict__ part,
+                                                      VerifyPos* __restrict__ vp, int32_t* __restrict__ accept) {
   __shared__ int keep[1024];
-  __shared__ double lz_s[1024][2];
-  __shared__ double sv[4];
-  __shared__ int si[4];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int c = blockIdx.x % rchunks, b = blockIdx.x / rchunks;  // c: this workgroup's sampling chunk
-  // keep test of every draft position, one wave per position
-  for (int i = 1 + wave; i < block; i += 4) {
+  __shared__ double lz[1024][2];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, b = blockIdx.x;
+  for (int i = 1 + wave; i < block; i += 16) {
     const int bi = b * block + (i - 1);
+    int x = 0;
+    if (lane == 0) x = min(max(draft[(size_t)b * (block - 1) + (i - 1)], 0), vocab - 1);
     double lzp, lzq;
     verify_lz_wave(part, bi, chunks, lane, lzp, lzq);
     if (lane == 0) {
-      const int x = min(max(draft[(size_t)b * (block - 1) + (i - 1)], 0), vocab - 1);
       const double px = exp((double)pl[(size_t)bi * vocab + x] * inv_t - lzp);
       const double qx = exp((double)ql[((size_t)b * (block - 1) + (i - 1)) * vocab + x] * inv_t - lzq);
       keep[i] = philox_uniform(seed, kPurposeAccept, b, i, 0) * qx < px;
-      lz_s[i][0] = lzp;
-      lz_s[i][1] = lzq;
+      lz[i][0] = lzp;
+      lz[i][1] = lzq;
     }
   }
   __syncthreads();
-  int k = 1;
-  while (k < block && keep[k]) ++k;  // first rejected position, or block (bonus)
-  if (tid == 0 && c == 0) accept[b] = k - 1;
+  if (threadIdx.x == 0) {
+    int k = 1;
+    while (k < block && keep[k]) ++k;  // first rejected position, or block (bonus)
+    VerifyPos r;
+    r.k = k;
+    r.pad = 0;
+    r.lzp = k < block ? lz[k][0] : 0.0;
+    r.lzq = k < block ? lz[k][1] : 0.0;
+    vp[b] = r;
+    accept[b] = k - 1;
+  }
+}
+
+// Workgroup (b, c): chunk c's largest log(max(0, p_k - q_k)) + G at the
+// first rejected position k, or P_B / T + G at the bonus position.
+__global__ __launch_bounds__(256) void k_verify_sample(const float* __restrict__ ql, const float* __restrict__ pl,
+                                                       int block, int vocab, int rchunks, double inv_t, u64 seed,
+                                                       const VerifyPos* __restrict__ vp,
+                                                       double* __restrict__ cand_v, int* __restrict__ cand_i) {
+  __shared__ double sv[4];
+  __shared__ int si[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = blockIdx.x % rchunks, b = blockIdx.x / rchunks;
+  const VerifyPos r = vp[b];
+  const int k = r.k;
   const bool bonus = k == block;
   const float* P = pl + ((size_t)b * block + (k - 1)) * vocab;
   const float* Q = bonus ? nullptr : ql + ((size_t)b * (block - 1) + (k - 1)) * vocab;
-  const double lzp = bonus ? 0.0 : lz_s[k][0], lzq = bonus ? 0.0 : lz_s[k][1];
   const int per = (vocab + rchunks - 1) / rchunks, v0 = c * per, v1 = min(vocab, v0 + per);
   double best = -INFINITY;
   int bix = vocab;
@@ -1170,8 +1186,8 @@ __global__ __launch_bounds__(256) void k_verify_sample(const int32_t* __restrict
     if (bonus) {
       sc = (double)P[v] * inv_t;
     } else {
-      const double r = exp((double)P[v] * inv_t - lzp) - exp((double)Q[v] * inv_t - lzq);
-      sc = r > 0.0 ? log(r) : -INFINITY;
+      const double d = exp((double)P[v] * inv_t - r.lzp) - exp((double)Q[v] * inv_t - r.lzq);
+      sc = d > 0.0 ? log(d) : -INFINITY;
     }
     if (sc == -INFINITY) continue;
     sc += gumbel(philox_uniform(seed, kPurposeResidual, b, k, v));
@@ -1450,23 +1466,26 @@ hipError_t launch_argmax_reduce(const unsigned long long* part, int n_parts, int
 size_t verify_scratch_bytes(int n, int block, int vocab) {
   const size_t C = verify_chunks(vocab), CR = verify_rchunks(vocab);
   const size_t lse = (size_t)n * block * C * sizeof(Lse4);
-  return lse + (size_t)n * CR * (sizeof(double) + sizeof(int)) + 64;
+  return lse + (size_t)n * sizeof(VerifyPos) + (size_t)n * CR * (sizeof(double) + sizeof(int)) + 64;
 }
 
 hipError_t launch_verify_sample(const int32_t* draft, const float* q_logits, const float* p_logits, int n,
                                 int block, int vocab, double temp, unsigned long long seed, void* scratch,
                                 int32_t* accept, int32_t* next_token, hipStream_t s) {
   if (n == 0) return hipSuccess;
-  if (block < 2 || block > 1024) return hipErrorInvalidValue;
+  if (block < 2 || block > 1024 || vocab < 1 || vocab > kVerifyMaxVocab) return hipErrorInvalidValue;
   const int C = verify_chunks(vocab), CR = verify_rchunks(vocab);
   Lse4* part = (Lse4*)scratch;
-  double* cand_v = (double*)(part + (size_t)n * block * C);
+  VerifyPos* vp = (VerifyPos*)(part + (size_t)n * block * C);
+  double* cand_v = (double*)(vp + n);
   int* cand_i = (int*)(cand_v + (size_t)n * CR);
   const double inv_t = 1.0 / temp;
   hipLaunchKernelGGL(k_verify_lse, dim3(n * block * C), dim3(256), 0, s, q_logits, p_logits, block, vocab, C, inv_t,
                      part);
-  hipLaunchKernelGGL(k_verify_sample, dim3(n * CR), dim3(256), 0, s, draft, q_logits, p_logits, block, vocab, C,
-                     CR, inv_t, seed, part, cand_v, cand_i, accept);
+  hipLaunchKernelGGL(k_verify_keep, dim3(n), dim3(1024), 0, s, draft, q_logits, p_logits, block, vocab, C, inv_t,
+                     seed, part, vp, accept);
+  hipLaunchKernelGGL(k_verify_sample, dim3(n * CR), dim3(256), 0, s, q_logits, p_logits, block, vocab, CR, inv_t,
+                     seed, vp, cand_v, cand_i);
   hipLaunchKernelGGL(k_verify_final, dim3((n + 3) / 4), dim3(256), 0, s, cand_v, cand_i, n, CR, vocab, next_token);
   return hipGetLastError();
 }

@@ -190,7 +190,8 @@ int dflash_draft_sample(const dflash_model* model, const dflash_ctx* ctx, const 
  * not, next_token[b] is the largest log(max(0, p_i - q_i)) + G (purpose 3)
  * and accept[b] = i - 1; when every draft is kept, next_token[b] is the
  * largest target_logits[block-1] / T + G at position block (purpose 3) and
- * accept[b] = block - 1.  Arithmetic is fp64.
+ * accept[b] = block - 1.  Arithmetic is fp64.  2 <= block <= 1024 and
+ * 1 <= vocab <= 262144.
  *   draft          device int32 [n_seqs][block-1] (clamped into [0, vocab))
  *   draft_logits   device fp32 [n_seqs][block-1][vocab]
  *   target_logits  device fp32 [n_seqs][block][vocab]; row i-1 is the

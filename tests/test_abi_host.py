@@ -203,8 +203,12 @@ def test_verify_sample_validation_without_device_calls():
     assert L.dflash_verify_workspace_bytes(4, 16, 4096) >= 4 * 16 * 32
     assert L.dflash_verify_workspace_bytes(4, 1, 4096) == 0
     assert L.dflash_verify_workspace_bytes(4, 16, 0) == 0
+    assert L.dflash_verify_workspace_bytes(4, 16, 262145) == 0
     fake = ctypes.c_void_p(0x100000)
     acc = ctypes.c_void_p(0x200000)
+    big = B.Sampling(1.0, 1)
+    assert _err(L.dflash_verify_sample(fake, fake, fake, 1, 16, 262145, ctypes.byref(big), acc, acc, fake, 1 << 30,
+                                       None)) == "DFLASH_EINVAL"
     # zero sequences: nothing to do, no device call
     assert L.dflash_verify_sample(None, None, None, 0, 16, 4096, ctypes.byref(sp), None, None, None, 0, None) == 0
     for bad_t in (0.0, -1.0, float("inf"), float("nan"), 2e6):
