@@ -96,8 +96,8 @@ __device__ __forceinline__ u64 argmax_key(float v, int col) {
 // Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds, each
 // multiplying words 0 and 2 by the round constants and mixing the 128-bit
 // products' halves with words 1 and 3 and the key, which is then advanced by
-// the Weyl constants.  Only word 0 of the output block is used.
-__device__ __forceinline__ u64 philox_w0(u64 c0, u64 c1, u64 c2, u64 c3, u64 k0, u64 k1) {
+// the Weyl constants.  Returns the four output words.
+__device__ __forceinline__ void philox4(u64 c0, u64 c1, u64 c2, u64 c3, u64 k0, u64 k1, u64 (&out)[4]) {
   constexpr u64 M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
   constexpr u64 W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
 #pragma unroll
@@ -111,24 +111,58 @@ __device__ __forceinline__ u64 philox_w0(u64 c0, u64 c1, u64 c2, u64 c3, u64 k0,
     k0 += W0;
     k1 += W1;
   }
-  return c0;
+  out[0] = c0;
+  out[1] = c1;
+  out[2] = c2;
+  out[3] = c3;
 }
 
+__device__ __forceinline__ double word_uniform(u64 w) { return ((double)(w >> 11) + 0.5) * 0x1.0p-53; }
+
 // Uniform number in (0, 1) of (seed, purpose, block b, position i, index v):
-// the top 53 bits of Philox word 0 of counter (v, i, b, 0), key (seed, purpose).
+// the top 53 bits of word i mod 4 of the Philox block at counter
+// (v, i div 4, b, 0), key (seed, purpose).
 __device__ __forceinline__ double philox_uniform(u64 seed, u64 purpose, int b, int i, int v) {
-  const u64 w = philox_w0((u64)v, (u64)i, (u64)b, 0ull, seed, purpose);
-  return ((double)(w >> 11) + 0.5) * 0x1.0p-53;
+  u64 w[4];
+  philox4((u64)v, (u64)(i >> 2), (u64)b, 0ull, seed, purpose, w);
+  return word_uniform(w[i & 3]);
 }
 
 __device__ __forceinline__ double gumbel(double u) { return -log(-log(u)); }
 
-// The value whose per-row argmax is the draft: the logit itself (greedy), or
-// logit / temp + Gumbel noise (a sample from softmax(logits / temp)).
-__device__ __forceinline__ float draft_score(const EpiParams& ep, int row, int col, float v) {
+// The same Gumbel number of word w in float32: -log(U) is formed from U for
+// U < 1/2 and as -log1p(-(1 - U)) above, with 1 - U exact from the integer,
+// so it keeps full relative precision where U is close to 1.
+__device__ __forceinline__ float gumbel_f32(u64 w) {
+  const u64 m = w >> 11;                                    // U = (m + 1/2) 2^-53
+  const double one_minus = ((double)((1ull << 53) - m) - 0.5) * 0x1.0p-53;
+  const float e = m < (1ull << 52) ? -logf((float)(((double)m + 0.5) * 0x1.0p-53))
+                                   : -log1pf(-(float)one_minus);
+  return -logf(e);
+}
+
+// The values whose per-row argmax are the drafts, for a lane's four rows
+// row0 .. row0 + 3 at one column: the logits themselves (greedy), or
+// logit / temp + Gumbel noise (a sample from softmax(logits / temp)), in
+// float32 like the logits; one Philox block serves the rows that share a
+// (block, position div 4).
+__device__ __forceinline__ f32x4 draft_scores(const EpiParams& ep, int row0, int col, f32x4 v) {
   if (ep.temp <= 0.0) return v;
-  const double g = gumbel(philox_uniform(ep.seed, kPurposeDraft, row / ep.block, row % ep.block, col));
-  return (float)((double)v / ep.temp + g);
+  const float inv_t = (float)(1.0 / ep.temp);
+  u64 w[4];
+  int cur = -1;
+  f32x4 out;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = row0 + i, b = row / ep.block, pos = row % ep.block;
+    const int key = b * 1024 + (pos >> 2);
+    if (key != cur) {
+      philox4((u64)col, (u64)(pos >> 2), (u64)b, 0ull, ep.seed, kPurposeDraft, w);
+      cur = key;
+    }
+    out[i] = v[i] * inv_t + gumbel_f32(w[pos & 3]);
+  }
+  return out;
 }
 
 // ---------------------------------------------------------------------------
@@ -194,6 +228,7 @@ __device__ __forceinline__ void epilogue(const EpiParams& ep, const SeqTable& st
     }
   } else if (EPI == EPI_ARGMAX) {
     const int col = tile * 16 + c;
+    const f32x4 sc = draft_scores(ep, r0 + 4 * g, col, v);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = r0 + 4 * g + i;
@@ -201,7 +236,7 @@ __device__ __forceinline__ void epilogue(const EpiParams& ep, const SeqTable& st
       const bool draft_row = row < ep.M && bi != 0;
       if (draft_row && ep.logits)
         ep.logits[((size_t)(row / ep.block) * (ep.block - 1) + (bi - 1)) * ep.vocab + col] = v[i];
-      u64 key = draft_row ? argmax_key(draft_score(ep, row, col, v[i]), col) : 0ull;
+      u64 key = draft_row ? argmax_key(sc[i], col) : 0ull;
 #pragma unroll
       for (int m = 1; m < 16; m <<= 1) {
         const u64 o = shfl_xor_u64(key, m);
@@ -229,6 +264,7 @@ __device__ __forceinline__ void argmax_tail(const EpiParams& ep, int tile0, f32x
 #pragma unroll
     for (int q = 1; q < KS; ++q) s += red[q][it][lane];
     const int col = (tile0 + it % NC) * 16 + c, r0 = (it / NC) * 16;
+    const f32x4 sc = draft_scores(ep, r0 + 4 * g, col, s);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = r0 + 4 * g + i;
@@ -236,7 +272,7 @@ __device__ __forceinline__ void argmax_tail(const EpiParams& ep, int tile0, f32x
       const bool draft_row = row < ep.M && bi != 0;
       if (draft_row && ep.logits)
         ep.logits[((size_t)(row / ep.block) * (ep.block - 1) + (bi - 1)) * ep.vocab + col] = s[i];
-      u64 key = draft_row ? argmax_key(draft_score(ep, row, col, s[i]), col) : 0ull;
+      u64 key = draft_row ? argmax_key(sc[i], col) : 0ull;
 #pragma unroll
       for (int m = 1; m < 16; m <<= 1) {
         const u64 o = shfl_xor_u64(key, m);

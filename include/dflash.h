@@ -160,9 +160,9 @@ int dflash_draft_block(const dflash_model* model, const dflash_ctx* ctx, const i
 
 /* Sampling parameters of sampled drafts and of their verification.  The
  * random numbers are a pure function of (seed, purpose, block index b,
- * position i, vocabulary index v): word 0 of Philox4x64-10 (Salmon et al.,
- * SC'11) at counter (v, i, b, 0) and key (seed, purpose), its top 53 bits
- * mapped to (0, 1).  Use a fresh seed for every drafted block. */
+ * position i, vocabulary index v): word i mod 4 of Philox4x64-10 (Salmon et
+ * al., SC'11) at counter (v, i div 4, b, 0) and key (seed, purpose), its top
+ * 53 bits mapped to (0, 1).  Use a fresh seed for every drafted block. */
 typedef struct {
   double temperature; /* > 0 (at most 1e6); temperature 0 is dflash_draft_block */
   uint64_t seed;

@@ -27,10 +27,12 @@ Moraes, Dror and Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC'11),
 each from that published definition:
 
     U(seed, purpose, b, i, v) = (w >> 11 + 1/2) * 2^-53,
-    w = word 0 of Philox4x64-10(counter (v, i, b, 0), key (seed, purpose)),
+    w = word (i mod 4) of Philox4x64-10(counter (v, i div 4, b, 0),
+                                        key (seed, purpose)),
 
 with b the block (sequence) index within a call, i the position in the block
-(1..B) and v the vocabulary index (0 where only one number is needed).
+(1..B) and v the vocabulary index (0 where only one number is needed); one
+generator block serves four consecutive positions of one index.
 Purposes: 1 draft sampling, 2 acceptance tests, 3 residual and bonus samples.
 Floating point is float64 throughout.
 """
@@ -80,8 +82,8 @@ def _mulhilo64(a: np.ndarray, m: int) -> Tuple[np.ndarray, np.ndarray]:
     return hi, lo
 
 
-def philox_word0(c0, c1, c2, c3, k0: int, k1: int) -> np.ndarray:
-    """Word 0 of Philox4x64-10 for arrays of counters (numpy, wrapping uint64)."""
+def philox_words(c0, c1, c2, c3, k0: int, k1: int):
+    """The four words of Philox4x64-10 for arrays of counters (numpy, wrapping uint64)."""
     x0, x1, x2, x3 = (np.asarray(c, dtype=np.uint64) for c in (c0, c1, c2, c3))
     x0, x1, x2, x3 = np.broadcast_arrays(x0, x1, x2, x3)
     ka, kb = np.uint64(k0 & _MASK64), np.uint64(k1 & _MASK64)
@@ -92,12 +94,12 @@ def philox_word0(c0, c1, c2, c3, k0: int, k1: int) -> np.ndarray:
             x0, x1, x2, x3 = hi1 ^ x1 ^ ka, lo1, hi0 ^ x3 ^ kb, lo0
             ka = ka + np.uint64(PHILOX_W0)
             kb = kb + np.uint64(PHILOX_W1)
-    return x0
+    return x0, x1, x2, x3
 
 
 def uniforms(seed: int, purpose: int, b: int, i: int, v) -> np.ndarray:
     """U(seed, purpose, b, i, v) in (0, 1) for an array of vocabulary indices v."""
-    w = philox_word0(np.asarray(v, dtype=np.uint64), i, b, 0, seed, purpose)
+    w = philox_words(np.asarray(v, dtype=np.uint64), i // 4, b, 0, seed, purpose)[i % 4]
     return ((w >> np.uint64(11)).astype(np.float64) + 0.5) * 2.0 ** -53
 
 

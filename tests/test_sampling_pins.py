@@ -41,13 +41,21 @@ def test_philox_matches_numpy_bit_generator(counter, key):
     assert S.philox4x64_10(counter, key) == _np_philox_at(counter, key)
 
 
-def test_vectorized_philox_word0_matches_scalar():
+def test_vectorized_philox_matches_scalar():
     rng = np.random.default_rng(0)
     c = rng.integers(0, 2 ** 63, size=(4, 64), dtype=np.uint64) * np.uint64(2) + np.uint64(1)
     k0, k1 = 0xFEDCBA9876543210, 3
-    w = S.philox_word0(c[0], c[1], c[2], c[3], k0, k1)
+    w = S.philox_words(c[0], c[1], c[2], c[3], k0, k1)
     for j in range(64):
-        assert int(w[j]) == S.philox4x64_10([int(c[r, j]) for r in range(4)], (k0, k1))[0]
+        assert tuple(int(w[q][j]) for q in range(4)) == S.philox4x64_10([int(c[r, j]) for r in range(4)], (k0, k1))
+
+
+def test_uniform_mapping_takes_one_word_per_position():
+    """U(seed, purpose, b, i, v) is word i mod 4 of the block at counter (v, i div 4, b, 0)."""
+    for i in (1, 2, 3, 4, 5, 15, 16):
+        words = S.philox4x64_10((7, i // 4, 3, 0), (99, 2))
+        u = S.uniforms(99, 2, 3, i, [7])[0]
+        assert u == ((words[i % 4] >> 11) + 0.5) * 2.0 ** -53
 
 
 def test_uniforms_are_in_the_open_unit_interval_and_uniform():
