@@ -19,6 +19,10 @@ training sequence's target features as injected context (dflash_fuse_ctx)
 and drafts all of its anchored blocks (dflash_draft_anchored), each block
 seeing the context before its anchor and itself.
 
+--phase ingest times the other phase of the method instead: every
+sequence's whole context ingested from its target features (the fusion map
+and every layer's injected K/V, dflash_fuse_ctx), in ingested positions/s.
+
 --temperature T > 0 samples the drafts instead (dflash_step_sample, which
 also writes the drafter's logits) and verifies them losslessly against
 resident synthetic target logits (dflash_verify_sample) in place of the
@@ -278,13 +282,46 @@ class TrainWorkload:
         return out
 
 
+class IngestWorkload:
+    """The ingest phase: every sequence's whole context ingested from its
+    target features (fusion + every layer's K/V into the cache) in one call."""
+
+    def __init__(self, spec, weights, torch, B_):
+        self.spec, self.torch, self.B = spec, torch, B_
+        I = _inputs()
+        self.denoise_steps = 1
+        self.cfg = B_.Config.from_spec(spec, max_block=max(spec.block, 16))
+        self.model = B_.Model(self.cfg, B_.upload_weights(spec, weights))
+        self.ctx = B_.Context(self.model, list(spec.ctx_lens))
+        self.ws = B_.workspace(self.model, spec.n_seqs, spec.block, sum(spec.ctx_lens))
+        packed = np.concatenate([I.gen_features(spec, 1, b, c) for b, c in enumerate(spec.ctx_lens)], axis=0)
+        self.feats = torch.from_numpy(np.ascontiguousarray(packed).view(np.int16)).cuda().view(torch.bfloat16)
+        del packed
+        self.n_new = list(spec.ctx_lens)
+
+    def step(self):
+        for b in range(self.spec.n_seqs):
+            self.ctx.truncate(b, 0)
+        self.B.fuse_ctx(self.model, self.ctx, self.feats, self.n_new, self.ws)
+
+
+def ingest_work(spec):
+    """Algorithmic (bytes, flops) of ingesting every context position: W_fc
+    and the features, every layer's W_k / W_v, the K/V written to the cache
+    (fp32-equivalent, 8 bytes per K and V element pair)."""
+    T, L = sum(spec.ctx_lens), spec.n_layers
+    fb, ff = stage_work(spec, "fusion", T)
+    kb, kf = stage_work(spec, "kv_proj", T)
+    return fb + L * kb + T * L * spec.n_kv_heads * spec.head_dim * 8, ff + L * kf
+
+
 def _decode_rows(wl, stage: str) -> int:
     """Activation rows of one launch of `stage` (per layer for layer stages)."""
     s = wl.spec
     n = wl.n_blocks if isinstance(wl, TrainWorkload) else s.n_seqs
     if stage == "lm_head":
         return n * (s.block - 1)
-    if stage in ("fusion", "kv_proj") and isinstance(wl, TrainWorkload):
+    if stage in ("fusion", "kv_proj") and isinstance(wl, (TrainWorkload, IngestWorkload)):
         return sum(s.ctx_lens)
     return n * s.block
 
@@ -413,6 +450,33 @@ def cpu_baseline(spec, weights, ws_target_s=10.0, max_reps=3):
     }, res
 
 
+def cpu_baseline_ingest(spec, weights, max_pos=512):
+    """The oracle's ingest of the first max_pos positions of sequence 0."""
+    from oracle import dflash_oracle as O
+    I = _inputs()
+    sub = spec.with_(ctx_lens=spec.ctx_lens[:1])
+    model = O.OracleModel.from_spec(sub, weights)
+    T = min(spec.ctx_lens[0], max_pos)
+    feats = I.gen_features(spec, 1, 0, T)
+    times = []
+    while len(times) < 3 and sum(times) < 10.0:
+        ctx = O.OracleContext(model, 1)
+        t0 = time.perf_counter()
+        O.fuse_ctx(model, ctx, 0, feats)
+        times.append(time.perf_counter() - t0)
+        log(f"oracle ingest of {T} positions: {times[-1]:.2f} s")
+    t = float(np.median(times))
+    return {
+        "value": T / t,
+        "unit": "ingested positions/s",
+        "cores": blas_threads(),
+        "kind": "oracle",
+        "sample": (f"{len(times)} oracle ingest(s) of the first {T} positions of sequence 0 (fusion + every layer's "
+                   f"K/V), numpy float64, median {t:.2f} s; {len(os.sched_getaffinity(0))} host CPUs visible, "
+                   f"{platform.processor() or platform.machine()}"),
+    }
+
+
 def cpu_baseline_train(spec, weights, wl, n_blk=2):
     """The oracle on sequence 0 of a training-forward workload: its ingest,
     then n_blk of its anchored blocks, extrapolated to all of its blocks."""
@@ -460,6 +524,8 @@ def main(argv=None) -> int:
                     help="step as dflash_fuse_ctx + dflash_draft_block instead of the fused dflash_step")
     ap.add_argument("--denoise-steps", type=int, default=1,
                     help="draft passes per block (1 = the single-pass drafter)")
+    ap.add_argument("--phase", choices=("decode", "ingest"), default="decode",
+                    help="decode: the draft step (default); ingest: whole-context ingest of every sequence")
     ap.add_argument("--temperature", type=float, default=0.0,
                     help="sampled drafts at this temperature, verified losslessly (0 = greedy)")
     ap.add_argument("--graph", action="store_true",
@@ -494,20 +560,32 @@ def main(argv=None) -> int:
         print("--denoise-steps must be in [1, 65]", file=sys.stderr)
         return 2
     train = spec.train_blocks > 0
+    ingest = args.phase == "ingest"
+    if ingest and (train or S > 1 or args.two_call or args.temperature > 0 or args.graph):
+        print("--phase ingest takes a decode workload and none of --denoise-steps, --two-call, --temperature, "
+              "--graph", file=sys.stderr)
+        return 2
+    if ingest and args.probe == "lm_head":
+        args.probe = "fusion"
     if train and (S > 1 or args.two_call or args.temperature > 0):
         print("--denoise-steps, --two-call and --temperature apply to decode workloads only", file=sys.stderr)
         return 2
     if args.temperature > 0 and (S > 1 or args.two_call):
         print("--temperature combines with neither --denoise-steps nor --two-call", file=sys.stderr)
         return 2
-    wl = TrainWorkload(spec, weights, torch, B_) if train else \
-        Workload(spec, weights, torch, B_, two_call=args.two_call, denoise_steps=S, temperature=args.temperature)
+    if ingest:
+        wl = IngestWorkload(spec, weights, torch, B_)
+    elif train:
+        wl = TrainWorkload(spec, weights, torch, B_)
+    else:
+        wl = Workload(spec, weights, torch, B_, two_call=args.two_call, denoise_steps=S,
+                      temperature=args.temperature)
     log("workload resident; warming up")
     for _ in range(args.warmup):
         wl.step()
     torch.cuda.synchronize()
 
-    n_launch = 64 * S if train else {"lm_head": S, "fusion": 1}.get(args.probe, spec.n_layers * S)
+    n_launch = 64 * S if (train or ingest) else {"lm_head": S, "fusion": 1}.get(args.probe, spec.n_layers * S)
     run = wl.step
     if args.graph:
         # the probe's events are not captured: arm it after capture only for eager replays
@@ -541,7 +619,10 @@ def main(argv=None) -> int:
     n, blk = spec.n_seqs, spec.block
     n_units = wl.n_blocks if train else n
     draft_tok_s = n_units * (blk - 1) / (ms_step * 1e-3)
-    if train:
+    if ingest:
+        draft_tok_s = sum(spec.ctx_lens) / (ms_step * 1e-3)
+        by, fl = ingest_work(spec)
+    elif train:
         by, fl = train_step_work(wl)
     else:
         by, fl = step_work(spec)
@@ -576,7 +657,8 @@ def main(argv=None) -> int:
         # bytes and flops over all layers
         breakdown = {}
         reps = 10
-        for st in ("qkv", "attention", "oproj", "gate_up", "down", "lm_head", "fusion", "kv_proj"):
+        for st in (("fusion", "kv_proj") if ingest else
+                   ("qkv", "attention", "oproj", "gate_up", "down", "lm_head", "fusion", "kv_proj")):
             B_.probe_arm(wl.model, st, 64 * S * reps)
             for _ in range(reps):
                 wl.step()
@@ -593,7 +675,10 @@ def main(argv=None) -> int:
 
     cpu = None
     parity = None
-    if not args.no_cpu and train:
+    if not args.no_cpu and ingest:
+        log("timing the CPU oracle on the host cores")
+        cpu = cpu_baseline_ingest(spec, weights)
+    elif not args.no_cpu and train:
         log("timing the CPU oracle on the host cores")
         cpu, ref, sel = cpu_baseline_train(spec, weights, wl)
         lg_gpu, d_gpu = wl.logits(sel)
@@ -614,7 +699,14 @@ def main(argv=None) -> int:
                   "decided_rows": int(sure.sum())}
         log(f"parity vs oracle (sequence 0): {parity}")
 
-    if train:
+    if ingest:
+        metric = (f"context ingest: positions/sec (fusion + {spec.n_layers} layers' injected K/V), "
+                  f"{n} x {spec.ctx_lens[0]} positions")
+        workload = (f"{spec.name}: {spec.n_layers}-layer drafter, hidden {spec.hidden}, {spec.n_kv_heads} kv heads x "
+                    f"{spec.head_dim}, fusion {spec.fused_width}->{spec.hidden}; {n} sequence(s) of "
+                    f"{list(spec.ctx_lens)[:4]}{'...' if n > 4 else ''} positions; step = ingest every position "
+                    f"(dflash_fuse_ctx)")
+    elif train:
         metric = (f"training-attention forward: drafted positions/sec ({spec.train_blocks} anchored blocks of "
                   f"{blk} per sequence), {spec.n_layers}-layer, {n} x {spec.ctx_lens[0]} context")
         workload = (f"{spec.name}: {spec.n_layers}-layer drafter, hidden {spec.hidden}, "
@@ -636,7 +728,7 @@ def main(argv=None) -> int:
     out = {
         "metric": metric,
         "value": round(draft_tok_s, 1),
-        "unit": "drafted positions/s" if train else "draft tokens/s",
+        "unit": "ingested positions/s" if ingest else ("drafted positions/s" if train else "draft tokens/s"),
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,

@@ -946,50 +946,73 @@ __global__ __launch_bounds__(256) void k_qkv_finish(const float* __restrict__ pa
   }
 }
 
-// One thread per (row, layer, kv head, pair j < d/2): the K pair with RoPE and
-// the V pair, summed over kc chunks, written to that layer's cache.
+// Workgroup (64-row block, layer, kv head): its rows' K pairs with RoPE and
+// V values, summed over kc chunks in order.  K goes to the cache row by row
+// (consecutive threads, consecutive dimensions); V, whose cache planes are
+// transposed ([d][slot]), goes through LDS so that each V-plane row receives
+// its 64 slots from consecutive threads.
+template <int D>
 __global__ __launch_bounds__(256) void k_kv_finish(const float* __restrict__ part, int kc, int M, int Mp,
-                                                   int n_layers, int n_kv, int d, const float* __restrict__ rc,
+                                                   int n_layers, int n_kv, const float* __restrict__ rc,
                                                    const float* __restrict__ rs, u16* __restrict__ kv0,
                                                    size_t layer_stride, int64_t kv_tiles, SeqTable st) {
-  const int half = d / 2, kd = n_kv * d, N = n_layers * 2 * kd;
-  const int idx = blockIdx.x * 256 + threadIdx.x;
-  if (idx >= M * n_layers * n_kv * half) return;
-  const int j = idx % half;
-  int t = idx / half;
-  const int gk = t % n_kv;
-  t /= n_kv;
-  const int l = t % n_layers, row = t / n_layers;
-  float k1 = 0.f, k2 = 0.f, v1 = 0.f, v2 = 0.f;
-  for (int q = 0; q < kc; ++q) {
-    const float* p = part + ((size_t)q * Mp + row) * N + l * 2 * kd + gk * d + j;
-    k1 += p[0];
-    k2 += p[half];
-    v1 += p[kd];
-    v2 += p[kd + half];
-  }
-  const int b = seq_of_row(st, row);
-  const int pos = st.pos_base[b] + (row - st.row_start[b]);
-  const float cs = rc[(size_t)pos * half + j], sn = rs[(size_t)pos * half + j];
-  const float r1 = k1 * cs - k2 * sn, r2 = k2 * cs + k1 * sn;
-  const int64_t slot = st.slot_base[b] + pos;
+  constexpr int HALF = D / 2, R = 64, RSTEP = 256 / HALF;
+  __shared__ u16 vh[D][R + 2], vl[D][R + 2];
+  __shared__ int64_t slot_s[R];
+  __shared__ int pos_s[R];
+  const int tid = threadIdx.x;
+  const int nblk = (M + R - 1) / R;
+  int t = blockIdx.x;
+  const int rb = t % nblk;
+  t /= nblk;
+  const int gk = t % n_kv, l = t / n_kv;
+  const int r0 = rb * R, kd = n_kv * D, N = n_layers * 2 * kd;
   u16* cache = kv0 + (size_t)l * layer_stride;
-  u16 h, lo;
-  u16* pk = kv_k_elem(cache, gk, slot, kv_tiles, d, j);
-  split_pair(r1, h, lo);
-  pk[0] = h;
-  pk[kTileKeys * d] = lo;
-  split_pair(r2, h, lo);
-  pk[half] = h;
-  pk[kTileKeys * d + half] = lo;
-  u16* pv = kv_v_elem(cache, gk, slot, kv_tiles, d, j);
-  u16* pv2 = kv_v_elem(cache, gk, slot, kv_tiles, d, j + half);
-  split_pair(v1, h, lo);
-  pv[0] = h;
-  pv[kTileKeys * d] = lo;
-  split_pair(v2, h, lo);
-  pv2[0] = h;
-  pv2[kTileKeys * d] = lo;
+  if (tid < R) {
+    const int row = r0 + tid;
+    if (row < M) {
+      const int b = seq_of_row(st, row);
+      const int pos = st.pos_base[b] + (row - st.row_start[b]);
+      pos_s[tid] = pos;
+      slot_s[tid] = st.slot_base[b] + pos;
+    }
+  }
+  __syncthreads();
+  const int j = tid % HALF;
+  for (int rr = tid / HALF; rr < R && r0 + rr < M; rr += RSTEP) {
+    const int row = r0 + rr;
+    float k1 = 0.f, k2 = 0.f, v1 = 0.f, v2 = 0.f;
+    for (int q = 0; q < kc; ++q) {
+      const float* p = part + ((size_t)q * Mp + row) * N + l * 2 * kd + gk * D + j;
+      k1 += p[0];
+      k2 += p[HALF];
+      v1 += p[kd];
+      v2 += p[kd + HALF];
+    }
+    const int pos = pos_s[rr];
+    const float cs = rc[(size_t)pos * HALF + j], sn = rs[(size_t)pos * HALF + j];
+    const float e1 = k1 * cs - k2 * sn, e2 = k2 * cs + k1 * sn;
+    u16 h, lo;
+    u16* pk = kv_k_elem(cache, gk, slot_s[rr], kv_tiles, D, j);
+    split_pair(e1, h, lo);
+    pk[0] = h;
+    pk[kTileKeys * D] = lo;
+    split_pair(e2, h, lo);
+    pk[HALF] = h;
+    pk[kTileKeys * D + HALF] = lo;
+    split_pair(v1, vh[j][rr], vl[j][rr]);
+    split_pair(v2, vh[j + HALF][rr], vl[j + HALF][rr]);
+  }
+  __syncthreads();
+  const int rr = tid % R;
+  if (r0 + rr < M) {
+    const int64_t slot = slot_s[rr];
+    for (int dd = tid / R; dd < D; dd += 256 / R) {
+      u16* pv = kv_v_elem(cache, gk, slot, kv_tiles, D, dd);
+      pv[0] = vh[dd][rr];
+      pv[kTileKeys * D] = vl[dd][rr];
+    }
+  }
 }
 
 // draft[b][i-1] = lowest column of the largest logit of block row i: the
@@ -1300,9 +1323,16 @@ hipError_t launch_qkv_finish(const float* part, int kc, int M, int Mp, int n_q, 
 hipError_t launch_kv_finish(const float* part, int kc, int M, int Mp, int n_layers, int n_kv, int head_dim,
                             const float* rope_cos, const float* rope_sin, u16* kv_cache0, size_t layer_stride,
                             int64_t kv_tiles, const SeqTable& st, hipStream_t s) {
-  const int total = M * n_layers * n_kv * (head_dim / 2);
-  hipLaunchKernelGGL(k_kv_finish, dim3((total + 255) / 256), dim3(256), 0, s, part, kc, M, Mp, n_layers, n_kv,
-                     head_dim, rope_cos, rope_sin, kv_cache0, layer_stride, kv_tiles, st);
+  if (M == 0) return hipSuccess;
+  const dim3 grid((M + 63) / 64 * n_layers * n_kv);
+  if (head_dim == 128)
+    hipLaunchKernelGGL(k_kv_finish<128>, grid, dim3(256), 0, s, part, kc, M, Mp, n_layers, n_kv, rope_cos, rope_sin,
+                       kv_cache0, layer_stride, kv_tiles, st);
+  else if (head_dim == 64)
+    hipLaunchKernelGGL(k_kv_finish<64>, grid, dim3(256), 0, s, part, kc, M, Mp, n_layers, n_kv, rope_cos, rope_sin,
+                       kv_cache0, layer_stride, kv_tiles, st);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
