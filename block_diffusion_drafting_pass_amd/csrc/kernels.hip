@@ -946,6 +946,82 @@ __global__ __launch_bounds__(256) void k_qkv_finish(const float* __restrict__ pa
   }
 }
 
+// Many-row form of k_qkv_finish: workgroup (64-row block, head) of the
+// q|k|v heads.  q and K are written row by row; V goes through LDS so that
+// each transposed V-plane row receives its slots from consecutive threads.
+template <int D>
+__global__ __launch_bounds__(256) void k_qkv_finish_blk(const float* __restrict__ part, int kc, int M, int Mp,
+                                                        int n_q, int n_kv, const float* __restrict__ rc,
+                                                        const float* __restrict__ rs, u16* __restrict__ q_hi,
+                                                        u16* __restrict__ q_lo, u16* __restrict__ kv,
+                                                        int64_t kv_tiles, SeqTable st) {
+  constexpr int HALF = D / 2, R = 64, RSTEP = 256 / HALF;
+  __shared__ u16 vh[D][R + 2], vl[D][R + 2];
+  __shared__ int64_t slot_s[R];
+  __shared__ int pos_s[R];
+  const int tid = threadIdx.x;
+  const int nh = n_q + 2 * n_kv, N = nh * D;
+  const int nblk = (M + R - 1) / R;
+  const int rb = blockIdx.x % nblk, hh = blockIdx.x / nblk;
+  const int r0 = rb * R;
+  const bool is_q = hh < n_q, is_k = !is_q && hh < n_q + n_kv;
+  if (tid < R) {
+    const int row = r0 + tid;
+    if (row < M) {
+      const int b = seq_of_row(st, row);
+      const int pos = st.pos_base[b] + (row - st.row_start[b]);
+      pos_s[tid] = pos;
+      slot_s[tid] = st.slot_base[b] + pos;
+    }
+  }
+  __syncthreads();
+  const int j = tid % HALF;
+  for (int rr = tid / HALF; rr < R && r0 + rr < M; rr += RSTEP) {
+    const int row = r0 + rr;
+    float a = 0.f, bv = 0.f;
+    for (int q = 0; q < kc; ++q) {
+      const float* p = part + ((size_t)q * Mp + row) * N + hh * D + j;
+      a += p[0];
+      bv += p[HALF];
+    }
+    if (!is_q && !is_k) {
+      split_pair(a, vh[j][rr], vl[j][rr]);
+      split_pair(bv, vh[j + HALF][rr], vl[j + HALF][rr]);
+      continue;
+    }
+    const int pos = pos_s[rr];
+    const float cs = rc[(size_t)pos * HALF + j], sn = rs[(size_t)pos * HALF + j];
+    const float a2 = a * cs - bv * sn, b2 = bv * cs + a * sn;
+    u16 ah, al, bh, bl;
+    split_pair(a2, ah, al);
+    split_pair(b2, bh, bl);
+    if (is_q) {
+      const size_t o = (size_t)row * (n_q * D) + hh * D + j;
+      q_hi[o] = ah;
+      q_lo[o] = al;
+      q_hi[o + HALF] = bh;
+      q_lo[o + HALF] = bl;
+    } else {
+      u16* p = kv_k_elem(kv, hh - n_q, slot_s[rr], kv_tiles, D, j);
+      p[0] = ah;
+      p[kTileKeys * D] = al;
+      p[HALF] = bh;
+      p[kTileKeys * D + HALF] = bl;
+    }
+  }
+  if (is_q || is_k) return;  // uniform over the workgroup
+  __syncthreads();
+  const int rr = tid % R;
+  if (r0 + rr < M) {
+    const int64_t slot = slot_s[rr];
+    for (int dd = tid / R; dd < D; dd += 256 / R) {
+      u16* pv = kv_v_elem(kv, hh - n_q - n_kv, slot, kv_tiles, D, dd);
+      pv[0] = vh[dd][rr];
+      pv[kTileKeys * D] = vl[dd][rr];
+    }
+  }
+}
+
 // Workgroup (64-row block, layer, kv head): its rows' K pairs with RoPE and
 // V values, summed over kc chunks in order.  K goes to the cache row by row
 // (consecutive threads, consecutive dimensions); V, whose cache planes are
@@ -1314,6 +1390,17 @@ hipError_t launch_reduce_split(const float* part, int kc, int part_rows, int N, 
 hipError_t launch_qkv_finish(const float* part, int kc, int M, int Mp, int n_q, int n_kv, int head_dim,
                              const float* rope_cos, const float* rope_sin, u16* q_hi, u16* q_lo,
                              u16* kv_cache, int64_t kv_tiles, const SeqTable& st, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  if (M >= 1024 && (head_dim == 128 || head_dim == 64)) {  // many rows: 64-row blocks per head
+    const dim3 grid((M + 63) / 64 * (n_q + 2 * n_kv));
+    if (head_dim == 128)
+      hipLaunchKernelGGL(k_qkv_finish_blk<128>, grid, dim3(256), 0, s, part, kc, M, Mp, n_q, n_kv, rope_cos,
+                         rope_sin, q_hi, q_lo, kv_cache, kv_tiles, st);
+    else
+      hipLaunchKernelGGL(k_qkv_finish_blk<64>, grid, dim3(256), 0, s, part, kc, M, Mp, n_q, n_kv, rope_cos,
+                         rope_sin, q_hi, q_lo, kv_cache, kv_tiles, st);
+    return hipGetLastError();
+  }
   const int total = M * (n_q + 2 * n_kv) * (head_dim / 2);
   hipLaunchKernelGGL(k_qkv_finish, dim3((total + 255) / 256), dim3(256), 0, s, part, kc, M, Mp, n_q, n_kv, head_dim,
                      rope_cos, rope_sin, q_hi, q_lo, kv_cache, kv_tiles, st);
