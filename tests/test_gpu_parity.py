@@ -681,3 +681,37 @@ def test_step_graph_replays_match_eager(torch_cuda, sampled, base, n_new):
         torch.cuda.synchronize()
     assert run.ctx.lengths() == list(base)
     say(f"graph replays equal the eager step (sampled={sampled}, base={base})")
+
+
+# ----------------------------------------------------------------------------
+# maximum sizes of one call
+# ----------------------------------------------------------------------------
+
+def test_max_sequences_per_call(torch_cuda):
+    """128 sequences (the most one call takes) at block 16: 2048 block rows on
+    the many-row path; the oracle checks a spread of sequences."""
+    spec = I.spec("tiny")
+    lens = tuple(int(v) for v in np.random.default_rng(11).integers(0, 200, size=128))
+    spec = spec.with_(ctx_lens=lens, block=16)
+    w = I.gen_weights(spec, seed=6, std=0.05)
+    run = GpuRun(spec, B.upload_weights(spec, w), capacity=[c + 8 for c in lens], max_new=sum(lens))
+    feats = _feats(spec, 1, lens)
+    run.ingest(feats)
+    anchors = I.gen_anchors(spec, 2)
+    drafts, logits = run.draft(anchors, 16)
+    seqs = [0, 1, 17, 63, 64, 100, 126, 127]
+    ref = oracle_run(spec, w, feats, anchors, 16, seqs=seqs)
+    assert_parity(logits[seqs], drafts[seqs], ref, "128 sequences")
+    accept_check(drafts[seqs], ref, spec.with_(ctx_lens=tuple(lens[s] for s in seqs)), 3, "128 sequences")
+
+
+def test_max_anchored_blocks_per_call(torch_cuda):
+    """128 anchored blocks of 16 over two shared contexts (2048 rows)."""
+    lens = (700, 300)
+    bseq = [0] * 80 + [1] * 48
+    rng = np.random.default_rng(12)
+    apos = [int(v) for v in rng.integers(0, 701, size=80)] + [int(v) for v in rng.integers(0, 301, size=48)]
+    spec = I.spec("tiny")
+    w = I.gen_weights(spec, seed=8, std=0.05)
+    _anchored_case(spec, w, B.upload_weights(spec, w), lens, bseq, apos, 16, "128 anchored blocks",
+                   check_blocks=[0, 5, 79, 80, 100, 127])
