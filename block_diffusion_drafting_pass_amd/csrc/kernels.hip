@@ -388,133 +388,161 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void k_skinny(GemmArgs ga, SeqTa
 }
 
 // ---------------------------------------------------------------------------
-// Many-row GEMM (M a multiple of 128): BM x 256 output tile per workgroup
-// of BM / 64 x WN waves, each 64 rows x 256 / WN columns (4 x 16 / WN MFMA
-// tiles), over K chunk kc of gridDim / (mt nt) chunks.  K runs in BK-wide slabs through
-// two LDS buffers: while the waves multiply slab k out of one buffer, slab
-// k+1's global loads are in flight in registers and land in the other
-// buffer, so one barrier per slab suffices.  LDS rows are 2 BK bytes;
-// 16-byte chunk c of row r sits at c ^ ((r >> 1) & (BK / 8 - 1)), which
-// spreads the rows one fragment read touches over the bank groups.  The
-// shape (BM, BK, WN) is picked per launch (big_cfg): 128 / 32 / 2 (four
-// waves of 64 x 128, 64 KB of LDS, two workgroups per CU) for split-K
-// launches and wide grids; 128 / 64 / 4 (128 KB, one per CU, so a small grid
-// spreads over the CUs) for small grids; 256 / 32 / 4 (96 KB, 16 waves) for
-// the widest argmax launches.  Workgroup ids run over the row
-// tiles first, so the row tiles that share a weight tile are dispatched
-// together and reuse it from L2.  A last column tile past n_tiles reads a
-// valid weight row and skips its epilogue.  Epilogues are the per-16x16-tile
-// ones above.
+// Many-row GEMM (M a multiple of 128): BM x 256 output tile per workgroup of
+// eight waves, each 64 rows x 256 / WN columns (4 x 16 / WN MFMA tiles), over
+// K chunk kc of gridDim / (mt nt) chunks.  K runs in 32-wide slabs; each
+// slab (the A planes' BM rows and the 256 weight rows) is copied by
+// global_load_lds (16 bytes per lane, 1 KB per wave instruction) straight
+// into one of S stage arrays in LDS, so S - 1 slabs are in flight without
+// holding registers.  Lane l of a wave's j-th copy writes physical 16-byte
+// chunk (wave IPW + j) 64 + l of the stage, i.e. chunk pc of LDS row r, and
+// loads the logical chunk pc ^ ((r >> 1) & 3) of that row (big_swz).  Per
+// slab: wait until this wave's copies of the slab have landed (vmcnt),
+// barrier (every wave's copies landed, every wave done with the previous
+// slab), issue slab kt + S - 1 into the stage slab kt - 1 used, multiply
+// slab kt.  A rows past a_rows read row a_rows - 1 (an output row depends
+// only on its own A row, and no epilogue consumes rows >= M); a last column
+// tile past n_tiles reads a valid weight row and skips its epilogue.
+// Workgroup ids are dealt round-robin over the eight XCDs; when their count
+// is a multiple of eight, id i takes logical tile (i % 8) (count / 8) + i / 8,
+// so the row tiles that share a weight tile run on one XCD and share its L2.
+// Logical tiles run over the row tiles first, then the K chunks, then the
+// column tiles.  Epilogues are the per-16x16-tile ones above.
 // ---------------------------------------------------------------------------
+
+// One 16-byte-per-lane global -> LDS copy: the wave's 64 lanes fill 1 KB at
+// LDS address lds (wave-uniform) + 16 lane.  Issued from asm so that the
+// compiler does not wait for every outstanding copy before each LDS read;
+// the kernel waits for its copies itself (wait_vmcnt) before the barrier
+// that publishes a stage.  The copy takes its LDS address from m0, which the
+// asm saves and restores (the compiler may keep a value there); one wait
+// state separates the m0 write from the copy that reads it.
+__device__ __forceinline__ void dma16(const void* src, const void* lds) {
+  const uint32_t addr = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(addr)
+      : "memory");
+}
+
+// s_waitcnt with vmcnt <= N and the other counters left alone (gfx9 field
+// layout: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
 
 constexpr int kBigBN = 256;
 
+// 16-byte chunk c of LDS row r (2 BK bytes per row) sits at chunk
+// c ^ ((r >> 1) & (BK / 8 - 1)) of the row, which spreads the 16 rows one
+// fragment read touches over the bank groups.
 template <int BK>
 __device__ __forceinline__ int big_swz(int row, int ch) {
   constexpr int CPR = BK / 8;  // 16-byte chunks per row
   return row * CPR + (ch ^ ((row >> 1) & (CPR - 1)));
 }
 
-template <int EPI, int MAP, bool SPLIT, int BM, int BK, int WN>
-__global__ __launch_bounds__(BM / 64 * WN * 64) void k_gemm_big(GemmArgs ga, SeqTable st, int mt, int kcn) {
-  constexpr int BN = kBigBN, NP = SPLIT ? 2 : 1, NT = BM / 64 * WN * 64, CPR = BK / 8;
-  constexpr int TN = BN / WN / 16;  // 16-wide column tiles per wave (each wave: 64 rows x TN tiles)
-  constexpr int ACH = BM * CPR, WCH = BN * CPR;     // 16-byte chunks per A plane / W slab
-  constexpr int STAGE = NP * ACH + WCH;             // chunks per LDS buffer
-  constexpr int AP = ACH / NT, WP = WCH / NT;       // chunks each thread stages per A plane / W
-  static_assert(ACH % NT == 0 && WCH % NT == 0, "staging must split evenly over the threads");
-  extern __shared__ u32x4 smem[];
+template <int EPI, int MAP, bool SPLIT, int BM, int WM, int WN, int S>
+__global__ __launch_bounds__(WM * WN * 64) void k_gemm_dl(GemmArgs ga, SeqTable st, int mt, int kcn) {
+  constexpr int BN = kBigBN, BK = 32, NP = SPLIT ? 2 : 1, NW = WM * WN, CPR = BK / 8;
+  constexpr int TM = BM / WM / 16, TN = BN / WN / 16;
+  constexpr int ACH = BM * CPR, WCH = BN * CPR, STAGE = NP * ACH + WCH;
+  constexpr int IPW = STAGE / 64 / NW;  // copies per wave per slab
+  static_assert(STAGE % (64 * NW) == 0 && ACH % 64 == 0, "a stage must split into whole wave copies");
+  static_assert(S >= 2 && S <= 4, "two to four stages");
+  __shared__ u32x4 st0[STAGE];
+  __shared__ u32x4 st1[STAGE];
+  __shared__ u32x4 st2[S > 2 ? STAGE : 1];
+  __shared__ u32x4 st3[S > 3 ? STAGE : 1];
 
-  const int bid = blockIdx.x, m_t = bid % mt, kc = (bid / mt) % kcn, n_t = bid / (mt * kcn);
+  const int nwg = gridDim.x;
+  const int bid = (nwg & 7) == 0 ? (int)(blockIdx.x & 7) * (nwg >> 3) + (int)(blockIdx.x >> 3) : (int)blockIdx.x;
+  const int m_t = bid % mt, kc = (bid / mt) % kcn, n_t = bid / (mt * kcn);
   const int row0 = m_t * BM, tile0 = n_t * (BN / 16);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 15, g = lane >> 4;
   const int wm = wave / WN, wn = wave % WN;
   const int K = ga.K, kspan = K / kcn, kbase = kc * kspan;
 
-  const u16* gA[NP][AP];
-  bool av[AP];
-  int ar[AP], ac[AP];
+  const u16* gp[IPW];
 #pragma unroll
-  for (int q = 0; q < AP; ++q) {
-    const int idx = tid + NT * q;
-    ar[q] = idx / CPR;
-    ac[q] = idx % CPR;
-    const int arow = row0 + ar[q];
-    av[q] = arow < ga.a_rows;
-    gA[0][q] = ga.a_hi + (size_t)arow * ga.lda + kbase + ac[q] * 8;
-    if (SPLIT) gA[NP - 1][q] = ga.a_lo + (size_t)arow * ga.lda + kbase + ac[q] * 8;
+  for (int j = 0; j < IPW; ++j) {
+    const int p = (wave * IPW + j) * 64 + lane;  // physical chunk of the stage
+    const int plane = p / ACH;                   // 0 .. NP-1: A planes; NP: weights
+    const int q = p - (plane < NP ? plane : NP) * ACH;
+    const int r = q / CPR, lc = (q % CPR) ^ ((r >> 1) & (CPR - 1));
+    if (plane < NP) {
+      const int arow = min(row0 + r, ga.a_rows - 1);
+      gp[j] = (plane == 0 ? ga.a_hi : ga.a_lo) + (size_t)arow * ga.lda + kbase + lc * 8;
+    } else {
+      const int tile = min(tile0 + (r >> 4), ga.n_tiles - 1);
+      gp[j] = weight_row<MAP>(ga.w, ga.ep, tile, r & 15, K) + kbase + lc * 8;
+    }
   }
-  const u16* gW[WP];
-  int wr[WP], wc[WP];
+  u32x4* const stg[4] = {st0, st1, st2, st3};
+  auto issue = [&](u32x4* sp, int k0) {
 #pragma unroll
-  for (int q = 0; q < WP; ++q) {
-    const int idx = tid + NT * q;
-    wr[q] = idx / CPR;
-    wc[q] = idx % CPR;
-    const int tile = min(tile0 + (wr[q] >> 4), ga.n_tiles - 1);
-    gW[q] = weight_row<MAP>(ga.w, ga.ep, tile, wr[q] & 15, K) + kbase + wc[q] * 8;
-  }
-  u32x4 rA[NP][AP], rW[WP];
-  auto load = [&](int k0) {
-#pragma unroll
-    for (int q = 0; q < AP; ++q)
-#pragma unroll
-      for (int p = 0; p < NP; ++p)
-        rA[p][q] = av[q] ? *reinterpret_cast<const u32x4*>(gA[p][q] + k0) : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int q = 0; q < WP; ++q) rW[q] = *reinterpret_cast<const u32x4*>(gW[q] + k0);
-  };
-  auto store = [&](int buf) {
-    u32x4* S = smem + buf * STAGE;
-#pragma unroll
-    for (int q = 0; q < AP; ++q)
-#pragma unroll
-      for (int p = 0; p < NP; ++p) S[p * ACH + big_swz<BK>(ar[q], ac[q])] = rA[p][q];
-#pragma unroll
-    for (int q = 0; q < WP; ++q) S[NP * ACH + big_swz<BK>(wr[q], wc[q])] = rW[q];
+    for (int j = 0; j < IPW; ++j) dma16(gp[j] + k0, sp + (wave * IPW + j) * 64);
   };
 
-  f32x4 acc[4][TN];
+  f32x4 acc[TM][TN];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < TM; ++a)
 #pragma unroll
     for (int b = 0; b < TN; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const u32x4* Sm) {
+    bf16x8 wf[TN];
+#pragma unroll
+    for (int ct = 0; ct < TN; ++ct)
+      wf[ct] = __builtin_bit_cast(bf16x8, Sm[NP * ACH + big_swz<BK>(wn * TN * 16 + ct * 16 + c, g)]);
+#pragma unroll
+    for (int rg = 0; rg < TM; ++rg)
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const bf16x8 a = __builtin_bit_cast(bf16x8, Sm[p * ACH + big_swz<BK>(wm * TM * 16 + rg * 16 + c, g)]);
+#pragma unroll
+        for (int ct = 0; ct < TN; ++ct) acc[rg][ct] = mfma(a, wf[ct], acc[rg][ct]);
+      }
+  };
 
   const int nk = kspan / BK;
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const bool more = kt + 1 < nk;
-    if (more) load((kt + 1) * BK);
-    const u32x4* S = smem + (kt & 1) * STAGE;
 #pragma unroll
-    for (int ks = 0; ks < BK / 32; ++ks) {
-      const int ch = ks * 4 + g;
-      bf16x8 wf[TN];
+  for (int s = 0; s < S - 1; ++s)
+    if (s < nk) issue(stg[s], s * BK);
+  for (int kt0 = 0; kt0 < nk; kt0 += S) {
 #pragma unroll
-      for (int ct = 0; ct < TN; ++ct)
-        wf[ct] = __builtin_bit_cast(bf16x8, S[NP * ACH + big_swz<BK>(wn * TN * 16 + ct * 16 + c, ch)]);
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-#pragma unroll
-        for (int p = 0; p < NP; ++p) {
-          const bf16x8 a = __builtin_bit_cast(bf16x8, S[p * ACH + big_swz<BK>(wm * 64 + rg * 16 + c, ch)]);
-#pragma unroll
-          for (int ct = 0; ct < TN; ++ct) acc[rg][ct] = mfma(a, wf[ct], acc[rg][ct]);
-        }
+    for (int s = 0; s < S; ++s) {
+      const int kt = kt0 + s;
+      if (kt < nk) {
+        // slab kt landed: the copies of the slabs issued after it may stay
+        // in flight (S - 2 of them while any remain to be issued)
+        if (kt + S - 2 < nk)
+          wait_vmcnt<(S - 2) * IPW>();
+        else
+          wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (kt + S - 1 < nk) issue(stg[(s + S - 1) % S], (kt + S - 1) * BK);
+        compute(stg[s]);
       }
     }
-    if (more) store((kt + 1) & 1);
-    __syncthreads();
   }
 #pragma unroll
   for (int ct = 0; ct < TN; ++ct) {
     const int tile = tile0 + wn * TN + ct;
     if (tile >= ga.n_tiles) break;  // uniform over the wave
 #pragma unroll
-    for (int rg = 0; rg < 4; ++rg) epilogue<EPI>(ga.ep, st, tile, row0 + wm * 64 + rg * 16, acc[rg][ct], lane, kc);
+    for (int rg = 0; rg < TM; ++rg)
+      epilogue<EPI>(ga.ep, st, tile, row0 + wm * TM * 16 + rg * 16, acc[rg][ct], lane, kc);
   }
 }
 
@@ -1423,19 +1451,6 @@ hipError_t launch_kv_finish(const float* part, int kc, int M, int Mp, int n_laye
   return hipGetLastError();
 }
 
-// Tile shape of a many-row GEMM launch (see k_gemm_big): split-K launches
-// take 128 / 32; otherwise the widest argmax launches take 256 / 32, and the
-// rest 128 / 32 on a wide grid or 128 / 64 on a grid smaller than the CUs.
-struct BigCfg {
-  int bm, bk;
-};
-static BigCfg big_cfg(int epi, int Mp, int n_tiles) {
-  const int nt = (n_tiles + kBigBN / 16 - 1) / (kBigBN / 16);
-  if (epi == EPI_PARTIAL) return {128, 32};
-  if (epi == EPI_ARGMAX) return (Mp % 256 == 0 && (Mp / 256) * nt >= 1024) ? BigCfg{256, 32} : BigCfg{128, 64};
-  return (Mp / 128) * nt >= 256 ? BigCfg{128, 32} : BigCfg{128, 64};
-}
-
 GemmPlan gemm_plan(int n_tiles, int K, int Mp, bool may_split) {
   GemmPlan p;
   p.kc = 1;
@@ -1448,7 +1463,7 @@ GemmPlan gemm_plan(int n_tiles, int K, int Mp, bool may_split) {
     }
   } else {
     p.nc = kBigBN / 16;
-    if (may_split) {  // split-K launches are 128 / 32: aim for about two workgroups per CU
+    if (may_split) {  // about 512 workgroups of 128-row tiles (256 of 256-row tiles)
       const int wgs = (Mp / 128) * ((n_tiles + p.nc - 1) / p.nc);
       while (p.kc * 2 <= kMaxKc && p.kc * 2 * wgs <= 512 && K % (p.kc * 2 * 32) == 0) p.kc *= 2;
     }
@@ -1468,22 +1483,25 @@ static hipError_t skinny_nc(const GemmArgs& g, const SeqTable& st, const GemmPla
   return hipGetLastError();
 }
 
-template <int EPI, int MAP, bool SPLIT, int BM, int BK, int WN>
-static hipError_t big_launch(const GemmArgs& g, const SeqTable& st, int Mp, const GemmPlan& p, hipStream_t s) {
-  if (Mp % BM || g.K % (p.kc * BK)) return hipErrorInvalidValue;
-  constexpr int NP = SPLIT ? 2 : 1;
-  constexpr int lds = 2 * (NP * BM + kBigBN) * BK * 2;  // bytes: two buffers of A planes + W
-  static bool attr_set = false;  // the dynamic-LDS limit is raised once per instantiation
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute((const void*)k_gemm_big<EPI, MAP, SPLIT, BM, BK, WN>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+template <int EPI, int MAP, bool SPLIT, int BM, int WM, int WN, int S>
+static hipError_t dl_launch(const GemmArgs& g, const SeqTable& st, int Mp, const GemmPlan& p, hipStream_t s) {
+  if (Mp % BM || g.K % (p.kc * 32) || g.a_rows < 1) return hipErrorInvalidValue;
   const int mt = Mp / BM, nt = (g.n_tiles + p.nc - 1) / p.nc;
-  hipLaunchKernelGGL((k_gemm_big<EPI, MAP, SPLIT, BM, BK, WN>), dim3(mt * p.kc * nt), dim3(BM / 64 * WN * 64), lds, s,
-                     g, st, mt, p.kc);
+  hipLaunchKernelGGL((k_gemm_dl<EPI, MAP, SPLIT, BM, WM, WN, S>), dim3(mt * p.kc * nt), dim3(WM * WN * 64), 0, s, g,
+                     st, mt, p.kc);
   return hipGetLastError();
+}
+
+// Direct-to-LDS many-row GEMM: 256-row tiles (eight waves of 64 x 128) when
+// the rows allow and the grid still covers the CUs, else 128-row tiles
+// (eight waves of 64 x 64); three stages of 48 KB with two A planes, four
+// stages otherwise.
+template <int EPI, int MAP, bool SPLIT>
+static hipError_t dl_dispatch(const GemmArgs& g, const SeqTable& st, int Mp, const GemmPlan& p, hipStream_t s) {
+  const int nt = (g.n_tiles + p.nc - 1) / p.nc;
+  if (Mp % 256 == 0 && (Mp / 256) * nt * p.kc >= 256)
+    return dl_launch<EPI, MAP, SPLIT, 256, 4, 2, SPLIT ? 3 : 4>(g, st, Mp, p, s);
+  return dl_launch<EPI, MAP, SPLIT, 128, 2, 4, 4>(g, st, Mp, p, s);
 }
 
 template <int EPI, int MAP, bool SPLIT>
@@ -1494,16 +1512,7 @@ static hipError_t gemm_dispatch(const GemmArgs& g, const SeqTable& st, int Mp, h
     return Mp <= 16 ? skinny_nc<EPI, MAP, SPLIT, 1>(g, st, p, s) : skinny_nc<EPI, MAP, SPLIT, 2>(g, st, p, s);
   }
   if (Mp % 128) return hipErrorInvalidValue;
-  const BigCfg cf = big_cfg(EPI, Mp, g.n_tiles);
-  if constexpr (EPI == EPI_PARTIAL) {
-    return big_launch<EPI, MAP, SPLIT, 128, 32, 2>(g, st, Mp, p, s);
-  } else {
-    if constexpr (EPI == EPI_ARGMAX) {
-      if (cf.bm == 256) return big_launch<EPI, MAP, SPLIT, 256, 32, 4>(g, st, Mp, p, s);
-    }
-    return cf.bk == 32 ? big_launch<EPI, MAP, SPLIT, 128, 32, 4>(g, st, Mp, p, s)
-                       : big_launch<EPI, MAP, SPLIT, 128, 64, 4>(g, st, Mp, p, s);
-  }
+  return dl_dispatch<EPI, MAP, SPLIT>(g, st, Mp, p, s);
 }
 
 hipError_t launch_gemm(const GemmArgs& g, const SeqTable& st, int Mp, hipStream_t s) {
