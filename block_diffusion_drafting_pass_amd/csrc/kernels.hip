@@ -389,7 +389,7 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void k_skinny(GemmArgs ga, SeqTa
 
 // ---------------------------------------------------------------------------
 // Many-row GEMM (M a multiple of 128): BM x 256 output tile per workgroup of
-// eight waves, each 64 rows x 256 / WN columns (4 x 16 / WN MFMA tiles), over
+// BM / 64 x WN waves, each 64 rows x 256 / WN columns (4 x 16 / WN MFMA tiles), over
 // K chunk kc of gridDim / (mt nt) chunks.  K runs in 32-wide slabs; each
 // slab (the A planes' BM rows and the 256 weight rows) is copied by
 // global_load_lds (16 bytes per lane, 1 KB per wave instruction) straight
@@ -1492,15 +1492,19 @@ static hipError_t dl_launch(const GemmArgs& g, const SeqTable& st, int Mp, const
   return hipGetLastError();
 }
 
-// Direct-to-LDS many-row GEMM: 256-row tiles (eight waves of 64 x 128) when
-// the rows allow and the grid still covers the CUs, else 128-row tiles
-// (eight waves of 64 x 64); three stages of 48 KB with two A planes, four
-// stages otherwise.
+// Tile shape per launch: 256-row tiles (sixteen waves of 64 x 64, three
+// stages, one workgroup per CU) when the rows allow and the grid still
+// covers the CUs; else 128-row tiles (eight waves of 64 x 64) with two
+// stages of at most 32 KB, so that two workgroups share a CU, when the grid
+// covers the CUs, and with four stages (one per CU) on a smaller grid, which
+// the dispatcher would otherwise pack two to a CU, leaving CUs idle (at 192
+// workgroups: 162 us with two stages, 138 us with four).
 template <int EPI, int MAP, bool SPLIT>
 static hipError_t dl_dispatch(const GemmArgs& g, const SeqTable& st, int Mp, const GemmPlan& p, hipStream_t s) {
   const int nt = (g.n_tiles + p.nc - 1) / p.nc;
   if (Mp % 256 == 0 && (Mp / 256) * nt * p.kc >= 256)
-    return dl_launch<EPI, MAP, SPLIT, 256, 4, 2, SPLIT ? 3 : 4>(g, st, Mp, p, s);
+    return dl_launch<EPI, MAP, SPLIT, 256, 4, 4, 3>(g, st, Mp, p, s);
+  if ((Mp / 128) * nt * p.kc >= 256) return dl_launch<EPI, MAP, SPLIT, 128, 2, 4, 2>(g, st, Mp, p, s);
   return dl_launch<EPI, MAP, SPLIT, 128, 2, 4, 4>(g, st, Mp, p, s);
 }
 
