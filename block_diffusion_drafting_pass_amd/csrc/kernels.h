@@ -87,11 +87,12 @@ struct GemmArgs {
 };
 
 // Launch shape of a GEMM over Mp padded rows: few rows (Mp <= 32) take the
-// weight-streaming kernel with nc column tiles per wave; many rows (Mp a
-// multiple of 128) the LDS-tiled one.  kc K chunks across workgroups (kc > 1
-// only with EPI_PARTIAL).  The same function sizes the partial buffers.
+// weight-streaming kernel with nc column tiles per wave and ks waves per
+// workgroup; many rows (Mp a multiple of 128) the LDS-tiled one.  kc K
+// chunks across workgroups (kc > 1 only with EPI_PARTIAL).  The same
+// function sizes the partial buffers.
 struct GemmPlan {
-  int nc, kc;
+  int nc, kc, ks;
 };
 GemmPlan gemm_plan(int n_tiles, int K, int Mp, bool may_split);
 constexpr int kSkinnyWaves = 4;  // waves per workgroup of the few-row GEMM
