@@ -127,7 +127,14 @@ WsLayout ws_layout(const dflash_config* c, int n_seqs, int block, int64_t max_ne
   W.M = n_seqs * block;
   W.Mp = rows_pad(W.M);
   const int qtiles = (block + 15) / 16;
-  W.max_splits = attention_max_splits(n_seqs * c->n_kv_heads);
+  // key splits of the attention pass: enough for one block per workgroup,
+  // and for anchored blocks grouped attention_group_size to a workgroup
+  // (fewer workgroups, so more splits)
+  {
+    const int gs = attention_group_size(c->n_q_heads, c->n_kv_heads, block);
+    W.max_splits = std::max(attention_max_splits(n_seqs * c->n_kv_heads),
+                            attention_max_splits((n_seqs + gs - 1) / gs * c->n_kv_heads));
+  }
   size_t o = 0;
   auto take = [&](size_t bytes) { const size_t at = o; o += align_up(bytes); return at; };
   const size_t Mp = W.Mp, wa = std::max(H, QD);
@@ -551,11 +558,41 @@ int draft_impl(const dflash_model* model, const dflash_ctx* ctx, const Blocks& b
     sq.n = e;
     sq.row_start[e] = off;
   }
-  int max_tiles = 1;
-  for (int b = 0; b < n; ++b)
-    max_tiles = std::max<int>(max_tiles, bk.sep ? (int)((bk.pos[b] + kTileKeys - 1) / kTileKeys) + 1
-                                                : (int)((bk.pos[b] + block + kTileKeys - 1) / kTileKeys));
-  const int splits = std::min(W.max_splits, attention_splits(n * c.n_kv_heads, max_tiles));
+  int max_tiles = 1, attn_units = n;
+  AttnGroups groups;
+  groups.n = 0;
+  if (bk.sep) {
+    // blocks of one sequence, in anchor order, share an attention workgroup
+    // (up to attention_group_size of them): each context tile is read once
+    // for the whole group
+    const int gs = attention_group_size(c.n_q_heads, c.n_kv_heads, block);
+    std::vector<int> order(n);
+    for (int b = 0; b < n; ++b) order[b] = b;
+    std::stable_sort(order.begin(), order.end(), [&](int u, int v) {
+      return bk.seq[u] != bk.seq[v] ? bk.seq[u] < bk.seq[v] : bk.pos[u] < bk.pos[v];
+    });
+    int fill = gs;
+    for (int i = 0; i < n; ++i) {
+      const int b = order[i];
+      if (fill == gs || bk.seq[groups.member[groups.n - 1][0]] != bk.seq[b]) {
+        for (int j = 0; j < kAttnGroup; ++j) groups.member[groups.n][j] = -1;
+        ++groups.n;
+        fill = 0;
+      }
+      groups.member[groups.n - 1][fill++] = (int16_t)b;
+    }
+    for (int g = 0; g < groups.n; ++g) {
+      int ct = 0, nb = 0;
+      for (int j = 0; j < kAttnGroup && groups.member[g][j] >= 0; ++j, ++nb)
+        ct = std::max<int>(ct, (int)((bk.pos[groups.member[g][j]] + kTileKeys - 1) / kTileKeys));
+      max_tiles = std::max(max_tiles, ct + nb);
+    }
+    attn_units = groups.n;
+  } else {
+    for (int b = 0; b < n; ++b)
+      max_tiles = std::max<int>(max_tiles, (int)((bk.pos[b] + block + kTileKeys - 1) / kTileKeys));
+  }
+  const int splits = std::min(W.max_splits, attention_splits(attn_units * c.n_kv_heads, max_tiles));
 
   auto base_args = [&](const u16* ah, const u16* al, int lda, int K, int n_tiles, int epi, int map) {
     GemmArgs g;
@@ -647,7 +684,7 @@ int draft_impl(const dflash_model* model, const dflash_ctx* ctx, const Blocks& b
 
     model->probe.start(DFLASH_STAGE_ATTENTION, s);
     e = launch_attention(q_hi, q_lo, ctx->kv_cache(l), ctx->kv_tiles(), bk.sep ? bkv : nullptr, part_o, part_ml,
-                         a_hi, a_lo, n, block, c.n_q_heads, c.n_kv_heads, c.head_dim, splits, st, s);
+                         a_hi, a_lo, n, block, c.n_q_heads, c.n_kv_heads, c.head_dim, splits, st, bk.sep ? &groups : nullptr, s);
     model->probe.stop(DFLASH_STAGE_ATTENTION, s);
     if (e != hipSuccess) return hip_fail(e, "draft_block: attention");
 

@@ -129,15 +129,30 @@ hipError_t launch_qkv_finish(const float* part, int kc, int M, int Mp, int n_q, 
 hipError_t launch_kv_finish(const float* part, int kc, int M, int Mp, int n_layers, int n_kv, int head_dim,
                             const float* rope_cos, const float* rope_sin, u16* kv_cache0, size_t layer_stride,
                             int64_t kv_tiles, const SeqTable& st, hipStream_t s);
+// Blocks that share one context and one attention workgroup: member[g][j]
+// is the j-th block of group g (-1 past the group's end).  Every member of a
+// group has the same slot_base (the same context); the group's workgroup
+// stages each context tile once for all of its members' query waves.
+constexpr int kAttnGroup = 4;
+struct AttnGroups {
+  int32_t n;
+  int16_t member[kMaxSeqs][kAttnGroup];
+};
+// Query heads one attention wave serves from each K / V fragment it reads
+// (grouped launches), and the most blocks one group may hold at this shape
+// (16 waves per workgroup).
+int attention_heads_per_wave(int n_q, int n_kv, bool grouped);
+int attention_group_size(int n_q, int n_kv, int block);
 // Block queries of sequence b (rows row_start[b] ..) against pos_base[b]
 // context keys from its cache slots (slot_base[b] ..) and the block's own
 // keys.  blk_kv null: the block keys follow the context keys in the cache;
 // otherwise they are tile b of blk_kv (n_seqs tiles per kv head), and the
-// cache is only read.
+// cache is only read.  groups (only with blk_kv): one workgroup per group of
+// blocks and kv head instead of per block and kv head.
 hipError_t launch_attention(const u16* q_hi, const u16* q_lo, const u16* kv_cache, int64_t kv_tiles,
                             const u16* blk_kv, float* part_o, float* part_ml, u16* o_hi, u16* o_lo, int n_seqs,
                             int block, int n_q, int n_kv, int head_dim, int splits, const SeqTable& st,
-                            hipStream_t s);
+                            const AttnGroups* groups, hipStream_t s);
 // Zero slots block .. kTileKeys-1 of the n_blocks x n_kv block tiles of a
 // separate block K/V area (slots the block never writes; attention masks
 // them, and zeros keep 0 * value finite).

@@ -16,6 +16,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "kernels.h"
 
@@ -30,9 +31,17 @@ typedef unsigned long long u64;
 // small helpers
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16, round to nearest even (one v_cvt_pk_bf16_f32; for every
+// finite input it equals rounding the bit pattern at bit 16 with ties to
+// even, denormals included).
+__device__ __forceinline__ uint32_t bf16_rne(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+// Two conversions in one instruction: a in the low half, b in the high half.
+__device__ __forceinline__ uint32_t bf16_rne2(float a, float b) {
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 __device__ __forceinline__ float bf16_val(uint32_t b) { return __uint_as_float(b << 16); }
 
@@ -42,6 +51,9 @@ __device__ __forceinline__ void split_pair(float x, u16& hi, u16& lo) {
   hi = (u16)h;
   lo = (u16)bf16_rne(x - bf16_val(h));
 }
+
+// 2^x on the hardware exponential unit (softmax weights: x <= 0; -inf -> 0).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ bf16x8 ld_frag(const u16* p) {
   return *reinterpret_cast<const bf16x8*>(p);
@@ -59,11 +71,8 @@ __device__ __forceinline__ void split_frag(const float* v, bf16x8& hi, bf16x8& l
   u32x4 h, l;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    u16 h0, l0, h1, l1;
-    split_pair(v[2 * j], h0, l0);
-    split_pair(v[2 * j + 1], h1, l1);
-    h[j] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-    l[j] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+    h[j] = bf16_rne2(v[2 * j], v[2 * j + 1]);
+    l[j] = bf16_rne2(v[2 * j] - bf16_val(h[j] & 0xFFFFu), v[2 * j + 1] - bf16_val(h[j] >> 16));
   }
   hi = __builtin_bit_cast(bf16x8, h);
   lo = __builtin_bit_cast(bf16x8, l);
@@ -549,10 +558,16 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_dl(GemmArgs ga, SeqTable 
 // ---------------------------------------------------------------------------
 // Attention over [injected context | block] keys.
 //
-// One workgroup per (sequence, kv head, key split).  Its waves are the query
-// units that read this kv head: (q head of the GQA group) x (16-row query
-// tile); at least four waves are launched so that a cache tile is staged by
-// enough threads (surplus waves only stage).  Each 64-key cache tile is
+// One workgroup per (sequence, kv head, key split), or with anchored blocks
+// that share a context per (group of blocks, kv head, key split).  Its waves
+// are the query units that read this kv head: (HPW q heads of the GQA group)
+// x (16-row query tile) x (block of the group); at least four waves are
+// launched so that a cache tile is staged by enough threads (surplus waves
+// only stage).  A group's blocks are sorted by anchor; its context tiles
+// are those of its longest prefix, and a wave skips tiles past its own
+// block's prefix.  Each K / V fragment a wave reads from LDS feeds all HPW
+// of its heads.  Softmax weights use the hardware base-2 exponential with
+// log2(e) folded into the argument.  Each 64-key cache tile is
 // copied once from HBM (contiguous, prefetched into registers while the
 // previous tile is used) into LDS, where every query unit of the group reads
 // it.  Per 32-key half a wave computes S^T = K Q^T with keys as MFMA rows, so
@@ -564,7 +579,8 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_dl(GemmArgs ga, SeqTable 
 // fp32 x fp32 products are taken as hi*hi + hi*lo + lo*hi.
 // The keys are either [context | block] in the cache, or (anchored blocks
 // that share a context) the context prefix in the cache followed by one
-// tile of the block's own keys kept apart in the workspace.
+// tile of the block's own keys kept apart in the workspace (for a group:
+// one such tile per member, after the shared context tiles).
 // With one split the result is normalised and written directly; otherwise
 // partial (m, l, O) go to a workspace and the merge kernel combines them in
 // split order.
@@ -588,7 +604,7 @@ __device__ __forceinline__ int lds_chunk(int cidx) {
   return plane * PL + drow * 8 + (ch ^ v_swz(drow));
 }
 
-template <int D, int NW>
+template <int D, int NW, bool GRP, int HPW>
 __global__ __launch_bounds__(NW * 64) void k_attn_tiles(const u16* __restrict__ q_hi,
                                                          const u16* __restrict__ q_lo,
                                                          const u16* __restrict__ kv, int64_t kv_tiles,
@@ -597,7 +613,8 @@ __global__ __launch_bounds__(NW * 64) void k_attn_tiles(const u16* __restrict__ 
                                                          float* __restrict__ part_ml,
                                                          u16* __restrict__ o_hi, u16* __restrict__ o_lo,
                                                          int block, int n_q, int n_kv, int splits,
-                                                         float scale, SeqTable st) {
+                                                         float scale, SeqTable st,
+                                                         std::conditional_t<GRP, AttnGroups, int> grp) {
   constexpr int CH = D / 8, PL = kTileKeys * CH;
   constexpr int TILE_CH = 4 * PL;  // 16-byte chunks per cache tile
   constexpr int NT = NW * 64;
@@ -610,38 +627,66 @@ __global__ __launch_bounds__(NW * 64) void k_attn_tiles(const u16* __restrict__ 
   const int c = lane & 15, g = lane >> 4;
   const int s = blockIdx.x % splits;
   const int pair = blockIdx.x / splits;
-  const int gkv = pair % n_kv, b = pair / n_kv;
-  const int G = n_q / n_kv, qtiles = (block + 15) / 16;
-  const bool comp = wave < G * qtiles;
-  const int h = gkv * G + wave % G, qt = wave / G;
+  const int gkv = pair % n_kv, unit = pair / n_kv;  // unit: the block, or the group of blocks
+  const int G = n_q / n_kv, HG = G / HPW, qtiles = (block + 15) / 16, upb = HG * qtiles;
+  const int mj = wave / upb, wu = wave % upb;  // this wave: member mj of the unit, query unit wu of its block
+  int nb = 1, b0 = unit, b = mj == 0 ? unit : -1;
+  if constexpr (GRP) {
+    nb = 0;
+#pragma unroll
+    for (int j = 0; j < kAttnGroup; ++j) nb += grp.member[unit][j] >= 0;
+    b0 = grp.member[unit][0];
+    b = mj < kAttnGroup ? grp.member[unit][mj] : -1;
+  }
+  const bool comp = b >= 0;
+  const int h0 = gkv * G + (wu % HG) * HPW, qt = wu / HG;  // this wave's heads h0 .. h0 + HPW - 1
 
-  // keys in the cache (context, plus the block when it sits there), then
-  // with a separate block area one more tile holding the block's keys
+  // context tiles in the cache (with the block's keys when they sit there),
+  // shared by the unit's blocks, then with a separate block area one tile
+  // of each member's own keys
   const bool sep = bkv != nullptr;
-  const int n_keys = st.pos_base[b] + (sep ? 0 : block);
-  const int ctiles = (n_keys + kTileKeys - 1) / kTileKeys;
-  const int ntile = ctiles + (sep ? 1 : 0);
+  int maxct = 0;
+  if constexpr (GRP) {
+    for (int j = 0; j < nb; ++j)
+      maxct = max(maxct, (st.pos_base[grp.member[unit][j]] + kTileKeys - 1) / kTileKeys);
+  } else {
+    maxct = (st.pos_base[unit] + (sep ? 0 : block) + kTileKeys - 1) / kTileKeys;
+  }
+  const int n_keys = comp ? st.pos_base[b] + (sep ? 0 : block) : 0;
+  const int ntile = maxct + (sep ? nb : 0);
   const int tps = (ntile + splits - 1) / splits;
   const int t0 = s * tps, t1 = min(ntile, t0 + tps);
   const u32x4* src = reinterpret_cast<const u32x4*>(
-      kv + kv_tile_offset(gkv, st.slot_base[b] / kTileKeys, kv_tiles, D));
-  const u32x4* bsrc = sep ? reinterpret_cast<const u32x4*>(bkv + kv_tile_offset(gkv, b, bkv_tiles, D)) : nullptr;
-  auto tile_ptr = [&](int t) { return t < ctiles ? src + (size_t)t * TILE_CH : bsrc; };
+      kv + kv_tile_offset(gkv, st.slot_base[b0] / kTileKeys, kv_tiles, D));
+  auto tile_ptr = [&](int t) -> const u32x4* {
+    if (t < maxct) return src + (size_t)t * TILE_CH;
+    int mb = unit;
+    if constexpr (GRP) mb = grp.member[unit][t - maxct];
+    return reinterpret_cast<const u32x4*>(bkv + kv_tile_offset(gkv, mb, bkv_tiles, D));
+  };
 
   const int qi = qt * 16 + c;
   const bool qvalid = comp && qi < block;
-  const size_t qrow = (size_t)(st.row_start[b] + qi);
-  const size_t qoff = qrow * (n_q * D) + h * D + g * 8;
-  bf16x8 qh[DS], ql[DS];
+  const size_t qrow = (size_t)(st.row_start[comp ? b : b0] + qi);
+  bf16x8 qh[HPW][DS], ql[HPW][DS];
 #pragma unroll
-  for (int ds = 0; ds < DS; ++ds) {
-    qh[ds] = qvalid ? ld_frag(q_hi + qoff + ds * 32) : zero_frag();
-    ql[ds] = qvalid ? ld_frag(q_lo + qoff + ds * 32) : zero_frag();
+  for (int hh = 0; hh < HPW; ++hh) {
+    const size_t qoff = qrow * (n_q * D) + (h0 + hh) * D + g * 8;
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      qh[hh][ds] = qvalid ? ld_frag(q_hi + qoff + ds * 32) : zero_frag();
+      ql[hh][ds] = qvalid ? ld_frag(q_lo + qoff + ds * 32) : zero_frag();
+    }
   }
-  f32x4 o[DT];
+  f32x4 o[HPW][DT];
+  float m[HPW], l[HPW];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, l = 0.f;
+  for (int hh = 0; hh < HPW; ++hh) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[hh][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m[hh] = -INFINITY;
+    l[hh] = 0.f;
+  }
 
   u32x4 stage[CPT];
   if (t0 < t1) {
@@ -660,13 +705,19 @@ __global__ __launch_bounds__(NW * 64) void k_attn_tiles(const u16* __restrict__ 
       for (int j = 0; j < CPT; ++j) stage[j] = tp[tid + j * NT];
     }
     if (!comp) continue;
+    // valid keys of this tile for this wave's block (none: the tile belongs
+    // to a longer member's prefix or is another member's block tile)
+    const int lim = t < maxct ? n_keys - t * kTileKeys : (t - maxct == mj ? block : 0);
+    if (lim <= 0) continue;  // uniform over the wave
 
-    f32x4 sacc[2][2];
+    // every K fragment read from LDS serves all HPW heads of the wave
+    f32x4 sacc[HPW][2][2];
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        sacc[hf][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int hh = 0; hh < HPW; ++hh) sacc[hh][hf][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
         const int key = hf * 32 + 8 * (c >> 2) + 4 * kt + (c & 3);
         const int sw = k_swz(key) & (CH - 1);
 #pragma unroll
@@ -674,80 +725,95 @@ __global__ __launch_bounds__(NW * 64) void k_attn_tiles(const u16* __restrict__ 
           const int ch = (ds * 4 + g) ^ sw;
           const bf16x8 kh = __builtin_bit_cast(bf16x8, lds[key * CH + ch]);
           const bf16x8 kl = __builtin_bit_cast(bf16x8, lds[PL + key * CH + ch]);
-          sacc[hf][kt] = mfma(kh, qh[ds], sacc[hf][kt]);
-          sacc[hf][kt] = mfma(kh, ql[ds], sacc[hf][kt]);
-          sacc[hf][kt] = mfma(kl, qh[ds], sacc[hf][kt]);
+#pragma unroll
+          for (int hh = 0; hh < HPW; ++hh) {
+            sacc[hh][hf][kt] = mfma(kh, qh[hh][ds], sacc[hh][hf][kt]);
+            sacc[hh][hf][kt] = mfma(kh, ql[hh][ds], sacc[hh][hf][kt]);
+            sacc[hh][hf][kt] = mfma(kl, qh[hh][ds], sacc[hh][hf][kt]);
+          }
         }
       }
-    const int lim = t < ctiles ? n_keys - t * kTileKeys : block;  // valid keys of this tile
-    float sv[16];
-    float mx = -INFINITY;
+    float p[HPW][16];
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
+    for (int hh = 0; hh < HPW; ++hh) {
+      float sv[16];
+      float mx = -INFINITY;
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = hf * 32 + 8 * g + 4 * kt + i;
-          const float x = key < lim ? sacc[hf][kt][i] * scale : -INFINITY;
-          sv[hf * 8 + kt * 4 + i] = x;
-          mx = fmaxf(mx, x);
-        }
-    mx = fmaxf(mx, shfl_xor_f(mx, 16));
-    mx = fmaxf(mx, shfl_xor_f(mx, 32));
-    const float m_new = fmaxf(m, mx);
-    const float corr = expf(m - m_new);
-    float p[16], ps = 0.f;
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      p[j] = expf(sv[j] - m_new);
-      ps += p[j];
+          for (int i = 0; i < 4; ++i) {
+            const int key = hf * 32 + 8 * g + 4 * kt + i;
+            const float x = key < lim ? sacc[hh][hf][kt][i] * scale : -INFINITY;
+            sv[hf * 8 + kt * 4 + i] = x;
+            mx = fmaxf(mx, x);
+          }
+      mx = fmaxf(mx, shfl_xor_f(mx, 16));
+      mx = fmaxf(mx, shfl_xor_f(mx, 32));
+      const float m_new = fmaxf(m[hh], mx);
+      constexpr float kLog2e = 1.4426950408889634f;
+      const float corr = fast_exp2((m[hh] - m_new) * kLog2e);
+      float ps = 0.f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        p[hh][j] = fast_exp2((sv[j] - m_new) * kLog2e);
+        ps += p[hh][j];
+      }
+      ps += shfl_xor_f(ps, 16);
+      ps += shfl_xor_f(ps, 32);
+      l[hh] = l[hh] * corr + ps;
+      m[hh] = m_new;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[hh][dt] *= corr;
     }
-    ps += shfl_xor_f(ps, 16);
-    ps += shfl_xor_f(ps, 32);
-    l = l * corr + ps;
-    m = m_new;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[dt] *= corr;
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
-      bf16x8 ph, pl;
-      split_frag(p + hf * 8, ph, pl);
+      bf16x8 ph[HPW], pl[HPW];
+#pragma unroll
+      for (int hh = 0; hh < HPW; ++hh) split_frag(p[hh] + hf * 8, ph[hh], pl[hh]);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const int drow = dt * 16 + c;
         const int ch = (hf * 4 + g) ^ v_swz(drow);
         const bf16x8 vh = __builtin_bit_cast(bf16x8, lds[2 * PL + drow * 8 + ch]);
         const bf16x8 vl = __builtin_bit_cast(bf16x8, lds[3 * PL + drow * 8 + ch]);
-        o[dt] = mfma(vh, ph, o[dt]);
-        o[dt] = mfma(vh, pl, o[dt]);
-        o[dt] = mfma(vl, ph, o[dt]);
+#pragma unroll
+        for (int hh = 0; hh < HPW; ++hh) {
+          o[hh][dt] = mfma(vh, ph[hh], o[hh][dt]);
+          o[hh][dt] = mfma(vh, pl[hh], o[hh][dt]);
+          o[hh][dt] = mfma(vl, ph[hh], o[hh][dt]);
+        }
       }
     }
   }
   if (!comp) return;
-  if (splits == 1) {
-    if (!qvalid) return;
-    const float inv = 1.0f / l;
-    const size_t ob = qrow * (n_q * D) + h * D + g * 4;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+  for (int hh = 0; hh < HPW; ++hh) {
+    const int h = h0 + hh;
+    if (splits == 1) {
+      if (!qvalid) continue;
+      const float inv = 1.0f / l[hh];
+      const size_t ob = qrow * (n_q * D) + h * D + g * 4;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        u16 hv, lv;
-        split_pair(o[dt][i] * inv, hv, lv);
-        o_hi[ob + dt * 16 + i] = hv;
-        o_lo[ob + dt * 16 + i] = lv;
-      }
-    return;
-  }
-  const size_t pidx = ((size_t)(b * n_q + h) * qtiles + qt) * splits + s;
-  float* po = part_o + pidx * 16 * D + c * D + g * 4;
+      for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16) = o[dt];
-  if (g == 0) {
-    part_ml[pidx * 32 + c] = m;
-    part_ml[pidx * 32 + 16 + c] = l;
+        for (int i = 0; i < 4; ++i) {
+          u16 hv, lv;
+          split_pair(o[hh][dt][i] * inv, hv, lv);
+          o_hi[ob + dt * 16 + i] = hv;
+          o_lo[ob + dt * 16 + i] = lv;
+        }
+      continue;
+    }
+    const size_t pidx = ((size_t)(b * n_q + h) * qtiles + qt) * splits + s;
+    float* po = part_o + pidx * 16 * D + c * D + g * 4;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16) = o[hh][dt];
+    if (g == 0) {
+      part_ml[pidx * 32 + c] = m[hh];
+      part_ml[pidx * 32 + 16 + c] = l[hh];
+    }
   }
 }
 
@@ -1569,27 +1635,47 @@ size_t attention_ml_bytes(int n_seqs, int n_q, int qtiles, int splits) {
   return (size_t)n_seqs * n_q * qtiles * splits * 32 * sizeof(float);
 }
 
+template <int D, bool GRP, int HPW, typename GT>
+static hipError_t attention_tiles(int nw, dim3 grid, const u16* q_hi, const u16* q_lo, const u16* kv,
+                                  int64_t kv_tiles, const u16* bkv, int bkv_tiles, float* part_o, float* part_ml,
+                                  u16* o_hi, u16* o_lo, int block, int n_q, int n_kv, int splits, float scale,
+                                  const SeqTable& st, const GT& grp, hipStream_t s) {
+  if (nw <= 4)
+    hipLaunchKernelGGL((k_attn_tiles<D, 4, GRP, HPW>), grid, dim3(256), 0, s, q_hi, q_lo, kv, kv_tiles, bkv,
+                       bkv_tiles, part_o, part_ml, o_hi, o_lo, block, n_q, n_kv, splits, scale, st, grp);
+  else if (nw <= 8)
+    hipLaunchKernelGGL((k_attn_tiles<D, 8, GRP, HPW>), grid, dim3(512), 0, s, q_hi, q_lo, kv, kv_tiles, bkv,
+                       bkv_tiles, part_o, part_ml, o_hi, o_lo, block, n_q, n_kv, splits, scale, st, grp);
+  else if (nw <= 16)
+    hipLaunchKernelGGL((k_attn_tiles<D, 16, GRP, HPW>), grid, dim3(1024), 0, s, q_hi, q_lo, kv, kv_tiles, bkv,
+                       bkv_tiles, part_o, part_ml, o_hi, o_lo, block, n_q, n_kv, splits, scale, st, grp);
+  else
+    return hipErrorInvalidValue;
+  return hipSuccess;
+}
+
 template <int D>
 static hipError_t attention_dispatch(const u16* q_hi, const u16* q_lo, const u16* kv, int64_t kv_tiles,
                                      const u16* bkv, float* part_o, float* part_ml, u16* o_hi, u16* o_lo, int n_seqs,
                                      int block, int n_q, int n_kv, int splits, const SeqTable& st,
-                                     hipStream_t s) {
-  const int units = (n_q / n_kv) * ((block + 15) / 16);
+                                     const AttnGroups* groups, hipStream_t s) {
   const float scale = (float)(1.0 / sqrt((double)D));
-  const dim3 grid(n_seqs * n_kv * splits);
-  if (units <= 4)
-    hipLaunchKernelGGL((k_attn_tiles<D, 4>), grid, dim3(256), 0, s, q_hi, q_lo, kv, kv_tiles, bkv, n_seqs,
-                       part_o, part_ml,
-                       o_hi, o_lo, block, n_q, n_kv, splits, scale, st);
-  else if (units <= 8)
-    hipLaunchKernelGGL((k_attn_tiles<D, 8>), grid, dim3(512), 0, s, q_hi, q_lo, kv, kv_tiles, bkv, n_seqs,
-                       part_o, part_ml,
-                       o_hi, o_lo, block, n_q, n_kv, splits, scale, st);
-  else if (units <= 16)
-    hipLaunchKernelGGL((k_attn_tiles<D, 16>), grid, dim3(1024), 0, s, q_hi, q_lo, kv, kv_tiles, bkv, n_seqs,
-                       part_o, part_ml, o_hi, o_lo, block, n_q, n_kv, splits, scale, st);
-  else
-    return hipErrorInvalidValue;
+  const int hpw = attention_heads_per_wave(n_q, n_kv, groups != nullptr);
+  const int upb = (n_q / n_kv / hpw) * ((block + 15) / 16);  // query waves per block
+  hipError_t e;
+  if (groups) {
+    const int nw = attention_group_size(n_q, n_kv, block) * upb;
+    const dim3 grid(groups->n * n_kv * splits);
+#define DFLASH_ATTN_GRP(H)                                                                                         \
+  attention_tiles<D, true, H>(nw, grid, q_hi, q_lo, kv, kv_tiles, bkv, n_seqs, part_o, part_ml, o_hi, o_lo, block, \
+                              n_q, n_kv, splits, scale, st, *groups, s)
+    e = hpw == 4 ? DFLASH_ATTN_GRP(4) : hpw == 2 ? DFLASH_ATTN_GRP(2) : DFLASH_ATTN_GRP(1);
+#undef DFLASH_ATTN_GRP
+  } else {
+    e = attention_tiles<D, false, 1>(upb, dim3(n_seqs * n_kv * splits), q_hi, q_lo, kv, kv_tiles, bkv, n_seqs,
+                                     part_o, part_ml, o_hi, o_lo, block, n_q, n_kv, splits, scale, st, 0, s);
+  }
+  if (e != hipSuccess) return e;
   if (splits > 1) {
     const int units = n_seqs * n_q * ((block + 15) / 16);
     hipLaunchKernelGGL(k_attn_merge<D>, dim3(units * 4), dim3(256), 0, s, part_o, part_ml, o_hi, o_lo, block, n_q,
@@ -1598,17 +1684,32 @@ static hipError_t attention_dispatch(const u16* q_hi, const u16* q_lo, const u16
   return hipGetLastError();
 }
 
+// Grouped launches serve two query heads per wave (each K / V fragment read
+// from LDS feeds both; four heads per wave spill registers); one-block
+// launches, which are latency-bound at decode sizes, keep one head per wave.
+int attention_heads_per_wave(int n_q, int n_kv, bool grouped) {
+  const int G = n_q / n_kv;
+  return grouped && G % 2 == 0 ? 2 : 1;
+}
+
+int attention_group_size(int n_q, int n_kv, int block) {
+  const int upb = (n_q / n_kv / attention_heads_per_wave(n_q, n_kv, true)) * ((block + 15) / 16);
+  const int gs = 16 / (upb > 0 ? upb : 1);
+  return gs < 1 ? 1 : (gs > kAttnGroup ? kAttnGroup : gs);
+}
+
 hipError_t launch_attention(const u16* q_hi, const u16* q_lo, const u16* kv_cache, int64_t kv_tiles,
                             const u16* blk_kv, float* part_o, float* part_ml, u16* o_hi, u16* o_lo, int n_seqs,
                             int block, int n_q, int n_kv, int head_dim, int splits, const SeqTable& st,
-                            hipStream_t s) {
+                            const AttnGroups* groups, hipStream_t s) {
   if (block > kTileKeys) return hipErrorInvalidValue;
+  if (groups && (!blk_kv || groups->n < 1 || groups->n > kMaxSeqs)) return hipErrorInvalidValue;
   if (head_dim == 128)
     return attention_dispatch<128>(q_hi, q_lo, kv_cache, kv_tiles, blk_kv, part_o, part_ml, o_hi, o_lo, n_seqs,
-                                   block, n_q, n_kv, splits, st, s);
+                                   block, n_q, n_kv, splits, st, groups, s);
   if (head_dim == 64)
     return attention_dispatch<64>(q_hi, q_lo, kv_cache, kv_tiles, blk_kv, part_o, part_ml, o_hi, o_lo, n_seqs,
-                                  block, n_q, n_kv, splits, st, s);
+                                  block, n_q, n_kv, splits, st, groups, s);
   return hipErrorInvalidValue;
 }
 
