@@ -1669,7 +1669,7 @@ static hipError_t attention_dispatch(const u16* q_hi, const u16* q_lo, const u16
 #define DFLASH_ATTN_GRP(H)                                                                                         \
   attention_tiles<D, true, H>(nw, grid, q_hi, q_lo, kv, kv_tiles, bkv, n_seqs, part_o, part_ml, o_hi, o_lo, block, \
                               n_q, n_kv, splits, scale, st, *groups, s)
-    e = hpw == 4 ? DFLASH_ATTN_GRP(4) : hpw == 2 ? DFLASH_ATTN_GRP(2) : DFLASH_ATTN_GRP(1);
+    e = hpw == 2 ? DFLASH_ATTN_GRP(2) : DFLASH_ATTN_GRP(1);
 #undef DFLASH_ATTN_GRP
   } else {
     e = attention_tiles<D, false, 1>(upb, dim3(n_seqs * n_kv * splits), q_hi, q_lo, kv, kv_tiles, bkv, n_seqs,
