@@ -19,7 +19,8 @@ STATUS = {0: "DFLASH_OK", -1: "DFLASH_EINVAL", -2: "DFLASH_ESHAPE", -3: "DFLASH_
           -4: "DFLASH_EWORKSPACE", -5: "DFLASH_EALIGN", -6: "DFLASH_EHIP", -7: "DFLASH_EUNSUPPORTED"}
 
 # Every symbol include/dflash.h declares.
-EXPORTS = ("dflash_weight_count", "dflash_model_create", "dflash_model_destroy", "dflash_ctx_bytes",
+EXPORTS = ("dflash_weight_count", "dflash_model_create", "dflash_model_destroy", "dflash_model_pack_bytes",
+           "dflash_model_pack", "dflash_ctx_bytes",
            "dflash_ctx_create", "dflash_ctx_destroy", "dflash_ctx_length", "dflash_ctx_truncate",
            "dflash_workspace_bytes", "dflash_fuse_ctx", "dflash_draft_block", "dflash_draft_refine", "dflash_draft_anchored", "dflash_draft_sample",
     "dflash_verify_workspace_bytes", "dflash_verify_sample", "dflash_step", "dflash_step_sample", "dflash_accept_len",
@@ -66,6 +67,10 @@ def lib():
         L.dflash_model_create.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(vp), ctypes.POINTER(vp)]
         L.dflash_model_create.restype = ctypes.c_int
         L.dflash_model_destroy.argtypes = [vp]
+        L.dflash_model_pack_bytes.restype = sz
+        L.dflash_model_pack_bytes.argtypes = [vp]
+        L.dflash_model_pack.restype = ctypes.c_int
+        L.dflash_model_pack.argtypes = [vp, vp, sz, vp]
         L.dflash_model_destroy.restype = None
         L.dflash_ctx_bytes.argtypes = [ctypes.POINTER(Config), i32, ctypes.POINTER(i64)]
         L.dflash_ctx_bytes.restype = sz
@@ -141,6 +146,21 @@ class Model:
         h = ctypes.c_void_p()
         check(lib().dflash_model_create(ctypes.byref(cfg), arr, ctypes.byref(h)))
         self.handle = h
+
+    def pack_bytes(self) -> int:
+        return int(lib().dflash_model_pack_bytes(self.handle))
+
+    def pack(self, device="cuda", stream=None) -> None:
+        """Write the packed weight copy (dflash_model_pack) into a buffer kept here."""
+        import torch
+        n = self.pack_bytes()
+        self._packed = torch.empty(n, dtype=torch.uint8, device=device)
+        check(lib().dflash_model_pack(self.handle, _ptr(self._packed), n, _stream(stream)))
+
+    def unpack(self) -> None:
+        """Go back to the original (row-major) weights."""
+        check(lib().dflash_model_pack(self.handle, None, 0, _stream(None)))
+        self._packed = None
 
     def close(self) -> None:
         if getattr(self, "handle", None):

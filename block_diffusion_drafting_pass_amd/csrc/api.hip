@@ -215,12 +215,20 @@ struct Probe {
   }
 };
 
+// Packed copies (dflash_model_pack) of the weights the few-row GEMM streams.
+struct PackedLayer {
+  const u16 *qkv = nullptr, *o = nullptr, *gate_up = nullptr, *down = nullptr;
+};
+
 struct dflash_model {
   dflash_config cfg;
   const u16* w_fc;
   const u16* embed;
   const u16* final_norm;
   std::vector<LayerW> layers;
+  const u16* pk_fc = nullptr;  // packed fusion map, or null
+  const u16* pk_lm = nullptr;  // packed LM head, or null
+  std::vector<PackedLayer> pk_layers;
   mutable Probe probe;
   ~dflash_model() { probe.release(); }
 };
@@ -289,6 +297,113 @@ int dflash_model_create(const dflash_config* cfg, const void* const* weights, df
 }
 
 void dflash_model_destroy(dflash_model* m) { delete m; }
+
+}  // extern "C"
+
+namespace {
+
+// The few-row GEMMs whose weights dflash_model_pack rearranges, in buffer
+// order: the fusion map, the LM head, then per layer q|k|v, O, gate|up and
+// down.  fn(args, which, layer) is called for each with the launch's weight
+// map filled in.
+enum PackSlot { PACK_FC, PACK_LM, PACK_QKV, PACK_O, PACK_GATE_UP, PACK_DOWN };
+
+template <typename F>
+void for_each_packed(const dflash_model* m, F&& fn) {
+  const dflash_config& c = m->cfg;
+  const int H = c.hidden, QD = c.n_q_heads * c.head_dim, I = c.intermediate;
+  auto args = [&](int map, int n_tiles, int K) {
+    GemmArgs g;
+    memset(&g, 0, sizeof(g));
+    g.map = map;
+    g.n_tiles = n_tiles;
+    g.K = K;
+    g.ep.n_q = c.n_q_heads;
+    g.ep.n_kv = c.n_kv_heads;
+    g.ep.head_dim = c.head_dim;
+    return g;
+  };
+  GemmArgs g = args(MAP_PLAIN, H / 16, c.n_target_layers * H);
+  g.w.w0 = m->w_fc;
+  fn(g, PACK_FC, -1);
+  g = args(MAP_PLAIN, c.vocab / 16, H);
+  g.w.w0 = m->embed;
+  fn(g, PACK_LM, -1);
+  for (int l = 0; l < c.n_layers; ++l) {
+    const LayerW& Lw = m->layers[l];
+    g = args(MAP_QKV, (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim / 16, H);
+    g.w.w0 = Lw.wq;
+    g.w.w1 = Lw.wk;
+    g.w.w2 = Lw.wv;
+    fn(g, PACK_QKV, l);
+    g = args(MAP_PLAIN, H / 16, QD);
+    g.w.w0 = Lw.wo;
+    fn(g, PACK_O, l);
+    g = args(MAP_SWIGLU, I / 8, H);
+    g.w.w0 = Lw.wgate;
+    g.w.w1 = Lw.wup;
+    fn(g, PACK_GATE_UP, l);
+    g = args(MAP_PLAIN, H / 16, I);
+    g.w.w0 = Lw.wdown;
+    fn(g, PACK_DOWN, l);
+  }
+}
+
+size_t packed_bytes(const GemmArgs& g) { return align_up(packed_elems(g.n_tiles, g.K) * sizeof(u16)); }
+
+}  // namespace
+
+extern "C" {
+
+size_t dflash_model_pack_bytes(const dflash_model* model) {
+  if (!model) return 0;
+  size_t total = 0;
+  for_each_packed(model, [&](const GemmArgs& g, int, int) { total += packed_bytes(g); });
+  return total;
+}
+
+int dflash_model_pack(dflash_model* model, void* dev_buf, size_t bytes, dflash_stream stream) {
+  if (!model) return fail(DFLASH_EINVAL, "model is NULL");
+  auto unpack = [&]() {
+    model->pk_fc = model->pk_lm = nullptr;
+    model->pk_layers.clear();
+  };
+  if (!dev_buf) {  // back to the row-major weights
+    unpack();
+    return DFLASH_OK;
+  }
+  if (!aligned(dev_buf, kAlign)) return fail(DFLASH_EALIGN, "dev_buf must be %zu-byte aligned", kAlign);
+  const size_t need = dflash_model_pack_bytes(model);
+  if (bytes < need) return fail(DFLASH_EWORKSPACE, "pack buffer holds %zu bytes, %zu needed", bytes, need);
+  // the model switches to the packed copy only once every pack kernel has
+  // been launched; on a launch error it keeps the row-major weights
+  std::vector<PackedLayer> layers(model->layers.size());
+  const u16 *fc = nullptr, *lm = nullptr;
+  char* at = (char*)dev_buf;
+  hipError_t e = hipSuccess;
+  for_each_packed(model, [&](const GemmArgs& g, int which, int l) {
+    if (e != hipSuccess) return;
+    e = launch_pack_weights(g, (u16*)at, (hipStream_t)stream);
+    const u16* p = (const u16*)at;
+    switch (which) {
+      case PACK_FC: fc = p; break;
+      case PACK_LM: lm = p; break;
+      case PACK_QKV: layers[l].qkv = p; break;
+      case PACK_O: layers[l].o = p; break;
+      case PACK_GATE_UP: layers[l].gate_up = p; break;
+      default: layers[l].down = p; break;
+    }
+    at += packed_bytes(g);
+  });
+  if (e != hipSuccess) {
+    unpack();
+    return hip_fail(e, "model_pack: pack kernels");
+  }
+  model->pk_fc = fc;
+  model->pk_lm = lm;
+  model->pk_layers = std::move(layers);
+  return DFLASH_OK;
+}
 
 size_t dflash_ctx_bytes(const dflash_config* cfg, int32_t n_seqs, const int64_t* capacity) {
   if (check_config(cfg)) return 0;
@@ -421,6 +536,7 @@ int dflash_fuse_ctx(const dflash_model* model, dflash_ctx* ctx, const void* feat
     f.K = fw;
     f.n_tiles = c.hidden / 16;
     f.w.w0 = model->w_fc;
+    f.wpack = model->pk_fc;
     f.map = MAP_PLAIN;
     f.epi = EPI_PARTIAL;
     f.ep.M = R;
@@ -634,6 +750,7 @@ int draft_impl(const dflash_model* model, const dflash_ctx* ctx, const Blocks& b
     f.K = fw;
     f.n_tiles = H / 16;
     f.w.w0 = model->w_fc;
+    f.wpack = model->pk_fc;
     f.map = MAP_PLAIN;
     f.epi = EPI_PARTIAL;
     f.ep.M = R;
@@ -660,7 +777,9 @@ int draft_impl(const dflash_model* model, const dflash_ctx* ctx, const Blocks& b
   if (e != hipSuccess) return hip_fail(e, "draft_block: embed + attention norm");
   for (int l = 0; l < c.n_layers; ++l) {
     const LayerW& Lw = model->layers[l];
+    const PackedLayer Pw = model->pk_layers.empty() ? PackedLayer{} : model->pk_layers[l];
     GemmArgs g = base_args(qin_hi, qin_lo, H, H, nqkv / 16, EPI_PARTIAL, MAP_QKV);
+    g.wpack = Pw.qkv;
     g.a_rows = Mq;
     g.q_rows = R > 0 ? M : 0;  // appended rows need only their K / V
     g.ep.M = Mq;
@@ -690,6 +809,7 @@ int draft_impl(const dflash_model* model, const dflash_ctx* ctx, const Blocks& b
 
     g = base_args(a_hi, a_lo, QD, QD, H / 16, EPI_PARTIAL, MAP_PLAIN);
     g.w.w0 = Lw.wo;
+    g.wpack = Pw.o;
     g.ep.out_f32 = part;
     g.ep.ldo = H;
     model->probe.start(DFLASH_STAGE_OPROJ, s);
@@ -704,6 +824,7 @@ int draft_impl(const dflash_model* model, const dflash_ctx* ctx, const Blocks& b
     g = base_args(a_hi, a_lo, H, H, I / 8, EPI_SWIGLU, MAP_SWIGLU);
     g.w.w0 = Lw.wgate;
     g.w.w1 = Lw.wup;
+    g.wpack = Pw.gate_up;
     g.ep.out_hi = b_hi;
     g.ep.out_lo = b_lo;
     g.ep.ldh = I;
@@ -714,6 +835,7 @@ int draft_impl(const dflash_model* model, const dflash_ctx* ctx, const Blocks& b
 
     g = base_args(b_hi, b_lo, I, I, H / 16, EPI_PARTIAL, MAP_PLAIN);
     g.w.w0 = Lw.wdown;
+    g.wpack = Pw.down;
     g.ep.out_f32 = part;
     g.ep.ldo = H;
     model->probe.start(DFLASH_STAGE_DOWN, s);
@@ -729,6 +851,7 @@ int draft_impl(const dflash_model* model, const dflash_ctx* ctx, const Blocks& b
   }
   GemmArgs g = base_args(a_hi, a_lo, H, H, c.vocab / 16, EPI_ARGMAX, MAP_PLAIN);
   g.w.w0 = model->embed;
+  g.wpack = model->pk_lm;
   g.ep.amax_part = amax;
   g.ep.logits = logits;
   g.ep.vocab = c.vocab;

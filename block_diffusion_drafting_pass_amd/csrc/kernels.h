@@ -73,6 +73,7 @@ struct EpiParams {
 constexpr unsigned long long kPurposeDraft = 1, kPurposeAccept = 2, kPurposeResidual = 3;
 
 struct GemmArgs {
+  const u16* wpack;  // packed weights of this launch's mapped rows (few-row GEMM only), or null
   const u16* a_hi;   // A rows (bf16); with split A this is the hi plane
   const u16* a_lo;   // lo plane or null (single product)
   int lda;           // row stride of A in elements
@@ -102,6 +103,16 @@ constexpr int kMaxKc = 16;       // most K chunks a GEMM is split into
 inline int rows_pad(int m) { return m <= 32 ? (m + 15) / 16 * 16 : (m + 127) / 128 * 128; }
 
 hipError_t launch_gemm(const GemmArgs& g, const SeqTable& st, int Mp, hipStream_t s);
+
+// Packed weights of one few-row GEMM launch: the launch's mapped weight rows
+// (map, w, ep.n_q / n_kv / head_dim, n_tiles, K of g) rearranged so that
+// column tile t, k-step s (32 k) is one contiguous 1 KB block in MFMA lane
+// order: elements ((t K / 32 + s) 64 + lane) 8 .. + 7 hold mapped row
+// 16 t + c, columns 32 s + 8 q .. + 7, for lane = 16 q + c.  A wave's weight
+// loads then read 1 KB contiguous each.  Layout only: the GEMM over packed
+// weights computes the same sums in the same order.
+inline size_t packed_elems(int n_tiles, int K) { return (size_t)n_tiles * 16 * K; }
+hipError_t launch_pack_weights(const GemmArgs& g, u16* dst, hipStream_t s);
 
 // x[row] = E[token] (token: anchor for block row 0; for rows i >= 1 the mask
 // id, or block_tokens[seq][i-1] when given), or

@@ -58,6 +58,10 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ bf16x8 ld_frag(const u16* p) {
   return *reinterpret_cast<const bf16x8*>(p);
 }
+// Streaming load of a weight fragment that is read once (non-temporal hint).
+__device__ __forceinline__ bf16x8 ld_frag_stream(const u16* p) {
+  return __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
+}
 __device__ __forceinline__ bf16x8 zero_frag() {
   const u32x4 z = {0u, 0u, 0u, 0u};
   return __builtin_bit_cast(bf16x8, z);
@@ -298,7 +302,9 @@ __device__ __forceinline__ void argmax_tail(const EpiParams& ep, int tile0, f32x
 // ---------------------------------------------------------------------------
 // Skinny weight-streaming GEMM: Y[M<=32][N] = A[M][K] W^T, W [N][K] bf16.
 // Workgroup (x, y) owns NC 16-column tiles and K chunk y of gridDim.y; its
-// KS waves (four; eight for narrow split-K outputs) split the chunk.  Each wave streams its NC weight-row
+// KS waves (four; eight for narrow split-K outputs) split the chunk.  PK:
+// the weights come packed (launch_pack_weights), so every weight load reads
+// 1 KB contiguous per wave, with the non-temporal hint (read once).  Each wave streams its NC weight-row
 // slices straight into MFMA B registers (16 B per lane per tile and k-step,
 // two 32-k steps per batch, the next batch in flight while the current one
 // is multiplied) and reuses every A fragment for all NC tiles.  Partial sums
@@ -307,9 +313,11 @@ __device__ __forceinline__ void argmax_tail(const EpiParams& ep, int tile0, f32x
 // kernel sums the chunks in order.
 // ---------------------------------------------------------------------------
 
-template <int EPI, int MAP, int NC, int RG, bool SPLIT, int KS = kSkinnyWaves>
+template <int EPI, int MAP, int NC, int RG, bool SPLIT, int KS = kSkinnyWaves, bool PK = false>
 __global__ __launch_bounds__(KS * 64) void k_skinny(GemmArgs ga, SeqTable st) {
   constexpr int U = 2;
+  // packed weights: k advances 16 elements per k (one 1 KB block per 32 k)
+  constexpr int KM = PK ? 16 : 1;
   const int lane = threadIdx.x & 63, ks = threadIdx.x >> 6;
   const int c = lane & 15, g = lane >> 4;
   const int tile0 = blockIdx.x * NC;
@@ -319,7 +327,10 @@ __global__ __launch_bounds__(KS * 64) void k_skinny(GemmArgs ga, SeqTable st) {
 
   const u16* wp[NC];
 #pragma unroll
-  for (int j = 0; j < NC; ++j) wp[j] = weight_row<MAP>(ga.w, ga.ep, tile0 + j, c, ga.K) + g * 8;
+  for (int j = 0; j < NC; ++j)
+    wp[j] = PK ? ga.wpack + ((size_t)(tile0 + j) * (ga.K / 32) * 64 + lane) * 8
+               : weight_row<MAP>(ga.w, ga.ep, tile0 + j, c, ga.K) + g * 8;
+  auto ldw = [&](int j, int k) { return PK ? ld_frag_stream(wp[j] + (size_t)k * KM) : ld_frag(wp[j] + k); };
   // Rows past a_rows read row a_rows - 1 instead: an output row depends only
   // on its own A row, and no epilogue consumes rows >= M (M <= a_rows).
   const u16* ah[RG];
@@ -345,7 +356,7 @@ __global__ __launch_bounds__(KS * 64) void k_skinny(GemmArgs ga, SeqTable st) {
 #pragma unroll
   for (int u = 0; u < U; ++u)
 #pragma unroll
-    for (int j = 0; j < NC; ++j) wf[u][j] = ld_frag(wp[j] + kb + u * 32);
+    for (int j = 0; j < NC; ++j) wf[u][j] = ldw(j, kb + u * 32);
   for (int k = kb; k < ke; k += 32 * U) {
     bf16x8 wn[U][NC];
     const bool more = k + 32 * U < ke;
@@ -353,7 +364,7 @@ __global__ __launch_bounds__(KS * 64) void k_skinny(GemmArgs ga, SeqTable st) {
 #pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int j = 0; j < NC; ++j) wn[u][j] = ld_frag(wp[j] + k + 32 * U + u * 32);
+        for (int j = 0; j < NC; ++j) wn[u][j] = ldw(j, k + 32 * U + u * 32);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -1546,20 +1557,20 @@ GemmPlan gemm_plan(int n_tiles, int K, int Mp, bool may_split) {
   return p;
 }
 
-template <int EPI, int MAP, bool SPLIT, int RG>
+template <int EPI, int MAP, bool SPLIT, int RG, bool PK>
 static hipError_t skinny_nc(const GemmArgs& g, const SeqTable& st, const GemmPlan& p, hipStream_t s) {
   const dim3 grid(g.n_tiles / p.nc, p.kc), blk(p.ks * 64);
   if (p.ks == 8) {
     if (p.nc != 8) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((k_skinny<EPI, MAP, 8, RG, SPLIT, 8>), grid, blk, 0, s, g, st);
+    hipLaunchKernelGGL((k_skinny<EPI, MAP, 8, RG, SPLIT, 8, PK>), grid, blk, 0, s, g, st);
     return hipGetLastError();
   }
   if (p.ks != kSkinnyWaves) return hipErrorInvalidValue;
   switch (p.nc) {
-    case 8: hipLaunchKernelGGL((k_skinny<EPI, MAP, 8, RG, SPLIT>), grid, blk, 0, s, g, st); break;
-    case 4: hipLaunchKernelGGL((k_skinny<EPI, MAP, 4, RG, SPLIT>), grid, blk, 0, s, g, st); break;
-    case 2: hipLaunchKernelGGL((k_skinny<EPI, MAP, 2, RG, SPLIT>), grid, blk, 0, s, g, st); break;
-    default: hipLaunchKernelGGL((k_skinny<EPI, MAP, 1, RG, SPLIT>), grid, blk, 0, s, g, st); break;
+    case 8: hipLaunchKernelGGL((k_skinny<EPI, MAP, 8, RG, SPLIT, kSkinnyWaves, PK>), grid, blk, 0, s, g, st); break;
+    case 4: hipLaunchKernelGGL((k_skinny<EPI, MAP, 4, RG, SPLIT, kSkinnyWaves, PK>), grid, blk, 0, s, g, st); break;
+    case 2: hipLaunchKernelGGL((k_skinny<EPI, MAP, 2, RG, SPLIT, kSkinnyWaves, PK>), grid, blk, 0, s, g, st); break;
+    default: hipLaunchKernelGGL((k_skinny<EPI, MAP, 1, RG, SPLIT, kSkinnyWaves, PK>), grid, blk, 0, s, g, st); break;
   }
   return hipGetLastError();
 }
@@ -1594,7 +1605,13 @@ static hipError_t gemm_dispatch(const GemmArgs& g, const SeqTable& st, int Mp, h
   const GemmPlan p = gemm_plan(g.n_tiles, g.K, Mp, EPI == EPI_PARTIAL);
   if (Mp <= 32) {
     if (g.K % (p.kc * p.ks * 64) || Mp % 16) return hipErrorInvalidValue;
-    return Mp <= 16 ? skinny_nc<EPI, MAP, SPLIT, 1>(g, st, p, s) : skinny_nc<EPI, MAP, SPLIT, 2>(g, st, p, s);
+    if (g.wpack) {
+      if (MAP == MAP_KVL) return hipErrorInvalidValue;  // never packed
+      return Mp <= 16 ? skinny_nc<EPI, MAP, SPLIT, 1, true>(g, st, p, s)
+                      : skinny_nc<EPI, MAP, SPLIT, 2, true>(g, st, p, s);
+    }
+    return Mp <= 16 ? skinny_nc<EPI, MAP, SPLIT, 1, false>(g, st, p, s)
+                    : skinny_nc<EPI, MAP, SPLIT, 2, false>(g, st, p, s);
   }
   if (Mp % 128) return hipErrorInvalidValue;
   return dl_dispatch<EPI, MAP, SPLIT>(g, st, Mp, p, s);
@@ -1711,6 +1728,32 @@ hipError_t launch_attention(const u16* q_hi, const u16* q_lo, const u16* kv_cach
     return attention_dispatch<64>(q_hi, q_lo, kv_cache, kv_tiles, blk_kv, part_o, part_ml, o_hi, o_lo, n_seqs,
                                   block, n_q, n_kv, splits, st, groups, s);
   return hipErrorInvalidValue;
+}
+
+// One thread per 16-byte chunk of the packed layout (see packed_elems).
+template <int MAP>
+__global__ __launch_bounds__(256) void k_pack_weights(GemmArgs g, u16* __restrict__ dst) {
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const int S = g.K / 32;
+  if (idx >= (size_t)g.n_tiles * S * 64) return;
+  const int lane = (int)(idx % 64), c = lane & 15, q = lane >> 4;
+  const size_t ts = idx / 64;
+  const int s = (int)(ts % S), t = (int)(ts / S);
+  const u16* src = weight_row<MAP>(g.w, g.ep, t, c, g.K) + 32 * s + 8 * q;
+  *reinterpret_cast<u32x4*>(dst + idx * 8) = *reinterpret_cast<const u32x4*>(src);
+}
+
+hipError_t launch_pack_weights(const GemmArgs& g, u16* dst, hipStream_t s) {
+  if (g.K % 32 || g.n_tiles < 1) return hipErrorInvalidValue;
+  const size_t chunks = (size_t)g.n_tiles * (g.K / 32) * 64;
+  const dim3 grid((unsigned)((chunks + 255) / 256));
+  switch (g.map) {
+    case MAP_PLAIN: hipLaunchKernelGGL(k_pack_weights<MAP_PLAIN>, grid, dim3(256), 0, s, g, dst); break;
+    case MAP_SWIGLU: hipLaunchKernelGGL(k_pack_weights<MAP_SWIGLU>, grid, dim3(256), 0, s, g, dst); break;
+    case MAP_QKV: hipLaunchKernelGGL(k_pack_weights<MAP_QKV>, grid, dim3(256), 0, s, g, dst); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 int argmax_parts(int n_tiles, int Mp) {

@@ -98,6 +98,31 @@ int32_t dflash_weight_count(const dflash_config* cfg);
 int dflash_model_create(const dflash_config* cfg, const void* const* weights, dflash_model** out);
 void dflash_model_destroy(dflash_model* model);
 
+/* Bytes of the packed weight copy dflash_model_pack writes (0 if model is
+ * NULL): the fusion map, the LM head and every layer's q|k|v, O, gate|up and
+ * down matrices, each padded to 256 bytes (3.34 GB for the 5-layer,
+ * hidden-4096 drafter). */
+size_t dflash_model_pack_bytes(const dflash_model* model);
+
+/* Optional speed-up for few-row calls (decode steps of one or two
+ * sequences).  Writes, on `stream`, a copy of the weights listed above into
+ * dev_buf (caller-owned device memory, 256-byte aligned, at least
+ * dflash_model_pack_bytes bytes) in the order the few-row GEMM streams them:
+ * for each GEMM's output rows, in the row order its kernel maps them
+ * (q|k|v stacked; gate and up rows interleaved eight and eight), column
+ * tile t (16 rows) and k-step s (32 columns) form one contiguous 1 KB block
+ * in MFMA lane order, so each wave load reads 1 KB contiguous.  This is a
+ * layout change only: results are bitwise identical with and without it.
+ * The model then reads the copy for calls of at most 32 GEMM rows; the
+ * original weights stay in use for everything else and must stay valid.
+ * dev_buf must stay valid and unmodified while the model uses it; calls on
+ * other streams must first wait for `stream`.  dev_buf = NULL switches the
+ * model back to the original weights.  Errors: DFLASH_EINVAL (model NULL),
+ * DFLASH_EALIGN, DFLASH_EWORKSPACE (bytes too small), DFLASH_EHIP (launch
+ * failure; the model keeps its previous weights).  Not thread-safe against
+ * concurrent calls that use the same model. */
+int dflash_model_pack(dflash_model* model, void* dev_buf, size_t bytes, dflash_stream stream);
+
 /* Device bytes needed for a context of n_seqs sequences holding up to
  * capacity[b] verified positions each (host array).  Per layer and kv head
  * the cache is a run of 64-slot tiles, each one contiguous block of four

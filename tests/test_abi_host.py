@@ -152,6 +152,22 @@ def test_workspace_bytes():
     L.dflash_model_destroy(m)
 
 
+def test_model_pack_size_and_validation():
+    L = _lib()
+    cfg, m = _fake_model("q8b_ctx1024")
+    H, I_, V = cfg.hidden, cfg.intermediate, cfg.vocab
+    qkv = (cfg.n_q_heads + 2 * cfg.n_kv_heads) * cfg.head_dim
+    per_layer = (qkv * H + H * cfg.n_q_heads * cfg.head_dim + 2 * I_ * H + H * I_) * 2
+    expect = H * cfg.n_target_layers * H * 2 + V * H * 2 + cfg.n_layers * per_layer
+    assert L.dflash_model_pack_bytes(m) == expect  # every matrix a multiple of 256 bytes here
+    assert L.dflash_model_pack_bytes(None) == 0
+    assert _err(L.dflash_model_pack(None, 0x1000, 1 << 40, None)) == "DFLASH_EINVAL"
+    assert _err(L.dflash_model_pack(m, 0x1000 + 16, 1 << 40, None)) == "DFLASH_EALIGN"
+    assert _err(L.dflash_model_pack(m, 0x1000, expect - 1, None)) == "DFLASH_EWORKSPACE"
+    assert L.dflash_model_pack(m, None, 0, None) == 0  # back to the row-major weights: no launch
+    L.dflash_model_destroy(m)
+
+
 def test_accept_len_validation():
     L = _lib()
     assert _err(L.dflash_accept_len(None, None, -1, 16, None, None, None)) == "DFLASH_EINVAL"

@@ -14,7 +14,7 @@ import pytest
 from block_diffusion_drafting_pass_amd import binding as B
 from block_diffusion_drafting_pass_amd import inputs as I
 from oracle import dflash_oracle as O
-from tests.gpu_harness import LOGIT_TOL, GpuRun, accept_check, assert_parity, oracle_run, say
+from tests.gpu_harness import LOGIT_TOL, GpuRun, accept_check, assert_parity, oracle_run, say, to_dev_bf16
 
 pytestmark = pytest.mark.gpu
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -287,6 +287,66 @@ def test_step_capacity_error_leaves_lengths(torch_cuda):
 def test_step_q8_ctx1024(q8):
     spec5, w, dev = q8
     _step_case(spec5, w, dev, (1008,), (16,), 16, "5-layer step ctx 1008+16")
+
+
+# ----------------------------------------------------------------------------
+# packed weights (dflash_model_pack): a layout change only, so every output is
+# bitwise equal to the row-major run's (which the tests above hold to the
+# oracle)
+# ----------------------------------------------------------------------------
+
+def _packed_case(spec, dev_w, base_lens, n_new, block, label):
+    import torch
+    spec = spec.with_(ctx_lens=tuple(base_lens), block=block)
+    cap = [b + 2 * k + 8 for b, k in zip(base_lens, n_new)]
+    runs = [GpuRun(spec, dev_w, capacity=cap, max_new=sum(base_lens) + 2 * sum(n_new), max_block=32)
+            for _ in range(2)]
+    feats = [I.gen_features(spec, 1, b, c + 2 * k) for b, (c, k) in enumerate(zip(base_lens, n_new))]
+    for r in runs:
+        r.ingest([f[:c] for f, c in zip(feats, base_lens)])
+    runs[1].model.pack()
+    torch.cuda.synchronize()
+    say(f"{label}: packed {runs[1].model.pack_bytes() / 1e6:.1f} MB")
+    n = len(base_lens)
+    rows1 = to_dev_bf16(np.concatenate([f[c:c + k] for f, c, k in zip(feats, base_lens, n_new)], 0))
+    rows2 = to_dev_bf16(np.concatenate([f[c + k:c + 2 * k] for f, c, k in zip(feats, base_lens, n_new)], 0))
+    a = torch.from_numpy(I.gen_anchors(spec, 2)).cuda()
+    outs = []
+    for r in runs:
+        o = []
+        lg = torch.empty((n, block - 1, spec.vocab), dtype=torch.float32, device="cuda")
+        d = B.step(r.model, r.ctx, rows1, n_new, a, block, r.ws, logits=lg)  # fused: every packed GEMM
+        torch.cuda.synchronize()
+        o += [d.cpu().numpy(), lg.cpu().numpy().view(np.uint32)]
+        lg2 = torch.empty_like(lg)
+        d2 = B.draft_sample(r.model, r.ctx, a, block, 0.7, 11, r.ws, logits=lg2)
+        torch.cuda.synchronize()
+        o += [d2.cpu().numpy(), lg2.cpu().numpy().view(np.uint32)]
+        B.fuse_ctx(r.model, r.ctx, rows2, n_new, r.ws)  # the two-call path
+        d3, l3 = r.draft(I.gen_anchors(spec, 3), block)
+        o += [d3, l3.view(np.uint32)]
+        outs.append(o)
+    for i, (x, y) in enumerate(zip(outs[0], outs[1])):
+        assert np.array_equal(x, y), f"{label}: output {i} differs with packed weights"
+    runs[1].model.unpack()
+    d4, l4 = runs[1].draft(I.gen_anchors(spec, 4), block)
+    d5, l5 = runs[0].draft(I.gen_anchors(spec, 4), block)
+    assert np.array_equal(d4, d5) and np.array_equal(l4.view(np.uint32), l5.view(np.uint32))
+
+
+@pytest.mark.parametrize("base,new,block,label", [
+    ((112,), (16,), 16, "one seq, fused 16 + 16 rows"),
+    ((40, 9), (3, 5), 8, "two seqs ragged"),
+])
+def test_packed_weights_tiny(torch_cuda, base, new, block, label):
+    spec = I.spec("tiny")
+    w = I.gen_weights(spec, seed=7, std=0.05)
+    _packed_case(spec, B.upload_weights(spec, w), base, new, block, label)
+
+
+def test_packed_weights_q8_ctx1024(q8):
+    spec5, w, dev = q8
+    _packed_case(spec5, dev, (1008,), (16,), 16, "5-layer ctx 1008 + 16 + 16, packed")
 
 
 # ----------------------------------------------------------------------------
