@@ -1602,7 +1602,11 @@ static hipError_t dl_dispatch(const GemmArgs& g, const SeqTable& st, int Mp, con
 
 template <int EPI, int MAP, bool SPLIT>
 static hipError_t gemm_dispatch(const GemmArgs& g, const SeqTable& st, int Mp, hipStream_t s) {
-  const GemmPlan p = gemm_plan(g.n_tiles, g.K, Mp, EPI == EPI_PARTIAL);
+  GemmPlan p = gemm_plan(g.n_tiles, g.K, Mp, EPI == EPI_PARTIAL);
+  // the SwiGLU projection (192 workgroups at I = 12288) keeps more loads in
+  // flight with eight waves per workgroup: 44.8 -> 40.5 us over packed
+  // weights (cold), unchanged over row-major ones
+  if (EPI == EPI_SWIGLU && Mp <= 32 && p.nc == 8 && g.K % (8 * 64) == 0) p.ks = 8;
   if (Mp <= 32) {
     if (g.K % (p.kc * p.ks * 64) || Mp % 16) return hipErrorInvalidValue;
     if (g.wpack) {
