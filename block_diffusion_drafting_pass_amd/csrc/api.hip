@@ -61,6 +61,7 @@ int check_config(const dflash_config* c) {
       ((int64_t)c->n_target_layers * c->hidden) % 256)
     return fail(DFLASH_EUNSUPPORTED, "hidden, intermediate, n_q_heads*head_dim and n_target_layers*hidden must be multiples of 256");
   if (c->vocab % 64) return fail(DFLASH_EUNSUPPORTED, "vocab must be a multiple of 64");
+  if (c->hidden > kMaxHidden) return fail(DFLASH_EUNSUPPORTED, "hidden must be at most %d", kMaxHidden);
   return DFLASH_OK;
 }
 

@@ -9,6 +9,7 @@ namespace dflash {
 typedef uint16_t u16;
 
 constexpr int kMaxSeqs = 128;
+constexpr int kMaxHidden = 16384;  // widest hidden size the row kernels hold in registers
 constexpr int kMaxKvLayers = 8;  // layers one all-layer K/V projection launch covers
 
 // Per-call sequence table, passed to kernels by value.  Rows of sequence b in

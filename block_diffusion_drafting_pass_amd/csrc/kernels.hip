@@ -830,28 +830,35 @@ __global__ __launch_bounds__(NW * 64) void k_attn_tiles(const u16* __restrict__ 
 
 // Combine the key splits of each (sequence, q head, 16-row query tile) unit.
 // Workgroup = unit x 4-row quad; wave w owns one query row: lane s reads
-// split s's (m, l), the wave forms the log-sum-exp weights
-// exp(m_s - max) / sum_s l_s exp(m_s - max) into LDS, then each lane sums
-// its D/64 output columns over the splits in split order (loads unrolled)
-// and writes the hi/lo planes [row][n_q * D].
+// split s's (m, l) while every lane loads its D/64 output columns of the
+// first 32 / (D/64) splits; the wave forms the log-sum-exp weights
+// exp(m_s - max) / sum_s l_s exp(m_s - max) (lane s holds split s's), then
+// each lane sums its columns over the splits in split order and writes the
+// hi/lo planes [row][n_q * D].
 template <int D>
 __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ part_o,
                                                     const float* __restrict__ part_ml,
                                                     u16* __restrict__ o_hi, u16* __restrict__ o_lo,
                                                     int block, int n_q, int splits, SeqTable st) {
-  constexpr int PER = D / 64;
-  __shared__ float wgt[4][kMaxSplits];
+  constexpr int PER = D / 64, PF = 32 / PER;  // splits whose outputs are loaded with (m, l)
   const int quad = blockIdx.x & 3, unit = blockIdx.x >> 2;
   const int qtiles = (block + 15) / 16;
   const int qt = unit % qtiles, h = (unit / qtiles) % n_q, b = unit / (qtiles * n_q);
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int row = quad * 4 + wv, qi = qt * 16 + row;
+  if (qi >= block) return;  // wave-uniform; the wave owns its row alone
   const size_t p0 = (size_t)unit * splits;
+  const float* po = part_o + (p0 * 16 + row) * D + lane * PER;
   float m = -INFINITY, l = 0.f;
   if (lane < splits) {
     m = part_ml[(p0 + lane) * 32 + row];
     l = part_ml[(p0 + lane) * 32 + 16 + row];
   }
+  float pre[PF][PER];
+#pragma unroll
+  for (int s = 0; s < PF; ++s)
+#pragma unroll
+    for (int p = 0; p < PER; ++p) pre[s][p] = po[(size_t)min(s, splits - 1) * 16 * D + p];
   float M = m;
 #pragma unroll
   for (int k = 32; k >= 1; k >>= 1) M = fmaxf(M, shfl_xor_f(M, k));
@@ -859,18 +866,20 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pa
   float L = e * l;
 #pragma unroll
   for (int k = 32; k >= 1; k >>= 1) L += shfl_xor_f(L, k);
-  if (lane < splits) wgt[wv][lane] = e / L;
-  __syncthreads();
-  if (qi >= block) return;
+  const float w = e / L;  // lane s: the weight of split s
   float acc[PER];
 #pragma unroll
   for (int p = 0; p < PER; ++p) acc[p] = 0.f;
-  const float* po = part_o + (p0 * 16 + row) * D + lane * PER;
-#pragma unroll 8
-  for (int s = 0; s < splits; ++s) {
-    const float w = wgt[wv][s];
 #pragma unroll
-    for (int p = 0; p < PER; ++p) acc[p] += w * po[(size_t)s * 16 * D + p];
+  for (int s = 0; s < PF; ++s) {
+    const float ws = __shfl(w, s, 64);
+#pragma unroll
+    for (int p = 0; p < PER; ++p) acc[p] += s < splits ? ws * pre[s][p] : 0.f;
+  }
+  for (int s = PF; s < splits; ++s) {
+    const float ws = __shfl(w, s, 64);
+#pragma unroll
+    for (int p = 0; p < PER; ++p) acc[p] += ws * po[(size_t)s * 16 * D + p];
   }
   const size_t o = (size_t)(st.row_start[b] + qi) * (n_q * D) + h * D + lane * PER;
 #pragma unroll
@@ -887,11 +896,14 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pa
 // ---------------------------------------------------------------------------
 
 // One workgroup of 1024 threads per row.  x[row] = E[token] (embedding
-// mode) or x[row] += sum_{q < kc} part[q][row] (residual mode, fixed order,
-// all chunk loads issued together); then the RMSNorm of the new x row,
-// gain * x / sqrt(mean(x^2) + eps), is written as hi/lo planes.  Every thread
-// re-reads only the x elements it wrote itself.  Rows M..Mp-1 of the planes
-// are zero.
+// mode) or x[row] += sum_{q < kc} part[q][row] (residual mode, fixed order),
+// then the RMSNorm of the new x row, gain * x / sqrt(mean(x^2) + eps), is
+// written as hi/lo planes.  Thread t owns the NV 4-element chunks t + 1024 v
+// of the row: every load it needs (x, all chunk partials, the gains) is
+// issued at once, and the new x stays in registers for the norm, so the
+// kernel waits on memory once before its one workgroup reduction.  Rows
+// M..Mp-1 of the planes are zero.
+template <int NV>
 __global__ __launch_bounds__(1024) void k_resid_norm(float* __restrict__ x, const float* __restrict__ part,
                                                      int kc, int part_rows, const int32_t* __restrict__ anchors,
                                                      const int32_t* __restrict__ block_tokens,
@@ -938,24 +950,32 @@ __global__ __launch_bounds__(1024) void k_resid_norm(float* __restrict__ x, cons
     tok = tok < 0 ? 0 : (tok >= vocab ? vocab - 1 : tok);
     er = E + (size_t)tok * H;
   }
+  f32x4 xv[NV];
+  uint2 gw[NV];
   float ss = 0.f;
-  for (int j = tid * 4; j < H; j += 4096) {
-    f32x4 v;
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const int j = tid * 4 + v * 4096;
+    xv[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+    gw[v] = make_uint2(0u, 0u);
+    if (j >= H) continue;
+    gw[v] = *reinterpret_cast<const uint2*>(gain + j);
     if (er) {
       const uint2 w = *reinterpret_cast<const uint2*>(er + j);
-      v = f32x4{bf16_val(w.x & 0xFFFFu), bf16_val(w.x >> 16), bf16_val(w.y & 0xFFFFu), bf16_val(w.y >> 16)};
+      xv[v] = f32x4{bf16_val(w.x & 0xFFFFu), bf16_val(w.x >> 16), bf16_val(w.y & 0xFFFFu), bf16_val(w.y >> 16)};
     } else {
-      v = *reinterpret_cast<const f32x4*>(xr + j);
       f32x4 p[kMaxKc];
 #pragma unroll
       for (int q = 0; q < kMaxKc; ++q)
         if (q < kc) p[q] = *reinterpret_cast<const f32x4*>(part + ((size_t)q * part_rows + row) * H + j);
+      f32x4 t = *reinterpret_cast<const f32x4*>(xr + j);
 #pragma unroll
       for (int q = 0; q < kMaxKc; ++q)
-        if (q < kc) v += p[q];
+        if (q < kc) t += p[q];
+      xv[v] = t;
     }
-    *reinterpret_cast<f32x4*>(xr + j) = v;
-    ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+    *reinterpret_cast<f32x4*>(xr + j) = xv[v];
+    ss += xv[v][0] * xv[v][0] + xv[v][1] * xv[v][1] + xv[v][2] * xv[v][2] + xv[v][3] * xv[v][3];
   }
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) ss += shfl_xor_f(ss, m);
@@ -966,14 +986,15 @@ __global__ __launch_bounds__(1024) void k_resid_norm(float* __restrict__ x, cons
 #pragma unroll
   for (int w = 0; w < 16; ++w) tot += wsum[w];
   const float r = 1.0f / sqrtf(tot / (float)H + eps);
-  for (int j = tid * 4; j < H; j += 4096) {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(xr + j);
-    const uint2 gw = *reinterpret_cast<const uint2*>(gain + j);
-    const float gs[4] = {bf16_val(gw.x & 0xFFFFu), bf16_val(gw.x >> 16), bf16_val(gw.y & 0xFFFFu),
-                         bf16_val(gw.y >> 16)};
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const int j = tid * 4 + v * 4096;
+    if (j >= H) continue;
+    const float gs[4] = {bf16_val(gw[v].x & 0xFFFFu), bf16_val(gw[v].x >> 16), bf16_val(gw[v].y & 0xFFFFu),
+                         bf16_val(gw[v].y >> 16)};
     u16 hh[4], ll[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) split_pair(gs[i] * v[i] * r, hh[i], ll[i]);
+    for (int i = 0; i < 4; ++i) split_pair(gs[i] * xv[v][i] * r, hh[i], ll[i]);
     *reinterpret_cast<uint2*>(oh + j) =
         make_uint2((uint32_t)hh[0] | ((uint32_t)hh[1] << 16), (uint32_t)hh[2] | ((uint32_t)hh[3] << 16));
     *reinterpret_cast<uint2*>(ol + j) =
@@ -998,7 +1019,9 @@ __global__ __launch_bounds__(256) void k_reduce_split(const float* __restrict__ 
   out_lo[idx] = l;
 }
 
-// One thread per (row, head of [q | k | v], RoPE pair j < d/2).
+// One thread per (row, head of [q | k | v], RoPE pair j < d/2).  The chunk
+// partials and the RoPE table entries are loaded together, then summed in
+// chunk order.
 __global__ __launch_bounds__(256) void k_qkv_finish(const float* __restrict__ part, int kc, int M, int Mp,
                                                     int n_q, int n_kv, int d, const float* __restrict__ rc,
                                                     const float* __restrict__ rs, u16* __restrict__ q_hi,
@@ -1009,16 +1032,30 @@ __global__ __launch_bounds__(256) void k_qkv_finish(const float* __restrict__ pa
   if (idx >= M * nh * half) return;
   const int j = idx % half, t = idx / half;
   const int hh = t % nh, row = t / nh;
-  float a = 0.f, bv = 0.f;
-  for (int q = 0; q < kc; ++q) {
-    const float* p = part + ((size_t)q * Mp + row) * N + hh * d + j;
-    a += p[0];
-    bv += p[half];
-  }
   const int b = seq_of_row(st, row);
   const int pos = st.pos_base[b] + (row - st.row_start[b]);
-  if (hh < n_q + n_kv) {
-    const float cs = rc[(size_t)pos * half + j], sn = rs[(size_t)pos * half + j];
+  const bool rot = hh < n_q + n_kv;
+  float cs = 1.f, sn = 0.f;
+  if (rot) {
+    cs = rc[(size_t)pos * half + j];
+    sn = rs[(size_t)pos * half + j];
+  }
+  float pa[kMaxKc], pb[kMaxKc];
+#pragma unroll
+  for (int q = 0; q < kMaxKc; ++q)
+    if (q < kc) {
+      const float* p = part + ((size_t)q * Mp + row) * N + hh * d + j;
+      pa[q] = p[0];
+      pb[q] = p[half];
+    }
+  float a = 0.f, bv = 0.f;
+#pragma unroll
+  for (int q = 0; q < kMaxKc; ++q)
+    if (q < kc) {
+      a += pa[q];
+      bv += pb[q];
+    }
+  if (rot) {
     const float a2 = a * cs - bv * sn, b2 = bv * cs + a * sn;
     a = a2;
     bv = b2;
@@ -1232,18 +1269,36 @@ __global__ __launch_bounds__(256) void k_argmax_reduce(const u64* __restrict__ p
   }
 }
 
+// One wave per sequence: 64 positions are compared at once (all loads in
+// flight together); the first chunk with a mismatch gives the accepted
+// length, and the target token there (or at block - 1) the next anchor.
 __global__ __launch_bounds__(256) void k_accept(const int32_t* __restrict__ draft,
                                                 const int32_t* __restrict__ target, int n, int block,
                                                 int32_t* __restrict__ accept,
                                                 int32_t* __restrict__ next_anchor) {
-  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (b >= n) return;
   const int32_t* dr = draft + (size_t)b * (block - 1);
   const int32_t* tg = target + (size_t)b * block;
-  int k = 0;
-  while (k < block - 1 && dr[k] == tg[k]) ++k;
-  accept[b] = k;
-  if (next_anchor) next_anchor[b] = tg[k];
+  int k = -1, nxt = 0;
+  for (int base = 0; base < block && k < 0; base += 64) {
+    const int i = base + lane;
+    const int t = i < block ? tg[i] : 0;
+    const int d = i < block - 1 ? dr[i] : 0;
+    const u64 miss = __ballot(i < block - 1 && d != t);
+    int kk = -1;
+    if (miss) kk = base + __builtin_ctzll(miss);
+    else if (block - 1 < base + 64) kk = block - 1;
+    if (kk >= 0) {
+      k = kk;
+      nxt = __shfl(t, kk - base, 64);
+    }
+  }
+  if (lane == 0) {
+    accept[b] = k;
+    if (next_anchor) next_anchor[b] = nxt;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1478,9 +1533,18 @@ hipError_t launch_resid_norm(float* x, const float* part, int kc, int part_rows,
                              const int32_t* block_tokens, const u16* embed, int block, int mask_id, int vocab,
                              const u16* gain, u16* out_hi, u16* out_lo, int H, int M, int out_rows, float eps,
                              hipStream_t s) {
-  if (kc > kMaxKc || out_rows < M) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_resid_norm, dim3(out_rows), dim3(1024), 0, s, x, part, kc, part_rows, anchors, block_tokens,
-                     embed, block, mask_id, vocab, gain, out_hi, out_lo, H, M, eps);
+  if (kc > kMaxKc || out_rows < M || H % 4 || H > kMaxHidden) return hipErrorInvalidValue;
+  if (out_rows == 0) return hipSuccess;
+  const dim3 grid(out_rows), blk(1024);
+  if (H <= 4096)
+    hipLaunchKernelGGL(k_resid_norm<1>, grid, blk, 0, s, x, part, kc, part_rows, anchors, block_tokens, embed, block,
+                       mask_id, vocab, gain, out_hi, out_lo, H, M, eps);
+  else if (H <= 8192)
+    hipLaunchKernelGGL(k_resid_norm<2>, grid, blk, 0, s, x, part, kc, part_rows, anchors, block_tokens, embed, block,
+                       mask_id, vocab, gain, out_hi, out_lo, H, M, eps);
+  else
+    hipLaunchKernelGGL(k_resid_norm<4>, grid, blk, 0, s, x, part, kc, part_rows, anchors, block_tokens, embed, block,
+                       mask_id, vocab, gain, out_hi, out_lo, H, M, eps);
   return hipGetLastError();
 }
 
@@ -1506,6 +1570,7 @@ hipError_t launch_qkv_finish(const float* part, int kc, int M, int Mp, int n_q, 
                          rope_sin, q_hi, q_lo, kv_cache, kv_tiles, st);
     return hipGetLastError();
   }
+  if (kc > kMaxKc) return hipErrorInvalidValue;
   const int total = M * (n_q + 2 * n_kv) * (head_dim / 2);
   hipLaunchKernelGGL(k_qkv_finish, dim3((total + 255) / 256), dim3(256), 0, s, part, kc, M, Mp, n_q, n_kv, head_dim,
                      rope_cos, rope_sin, q_hi, q_lo, kv_cache, kv_tiles, st);
@@ -1822,7 +1887,7 @@ hipError_t launch_verify_sample(const int32_t* draft, const float* q_logits, con
 hipError_t launch_accept(const int32_t* draft, const int32_t* target, int n, int block,
                          int32_t* accept, int32_t* next_anchor, hipStream_t s) {
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_accept, dim3((n + 255) / 256), dim3(256), 0, s, draft, target, n, block, accept,
+  hipLaunchKernelGGL(k_accept, dim3((n + 3) / 4), dim3(256), 0, s, draft, target, n, block, accept,
                      next_anchor);
   return hipGetLastError();
 }

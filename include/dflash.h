@@ -65,8 +65,8 @@ typedef enum {
 /* Drafter hyper-parameters.  Supported: head_dim 64 or 128; hidden,
  * intermediate, n_q_heads*head_dim and n_target_layers*hidden multiples of
  * 256; n_q_heads a multiple of n_kv_heads with at most 8 query heads per kv
- * head; vocab a multiple of 64; 2 <= max_block <= 32.  mask_token_id is an
- * ordinary embedding row. */
+ * head; hidden at most 16384; vocab a multiple of 64; 2 <= max_block <= 32.
+ * mask_token_id is an ordinary embedding row. */
 typedef struct {
   int32_t n_layers;
   int32_t hidden;

@@ -63,6 +63,7 @@ def test_status_strings():
     ("head_dim", 96, "DFLASH_EUNSUPPORTED"),
     ("n_kv_heads", 3, "DFLASH_ESHAPE"),
     ("hidden", 200, "DFLASH_EUNSUPPORTED"),
+    ("hidden", 16640, "DFLASH_EUNSUPPORTED"),
     ("vocab", 4104, "DFLASH_EUNSUPPORTED"),
     ("max_block", 33, "DFLASH_EUNSUPPORTED"),
     ("max_block", 1, "DFLASH_EUNSUPPORTED"),
