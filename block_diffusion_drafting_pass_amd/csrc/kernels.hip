@@ -1599,6 +1599,11 @@ GemmPlan gemm_plan(int n_tiles, int K, int Mp, bool may_split) {
   if (Mp <= 32) {
     p.nc = (n_tiles % 8 == 0 && n_tiles >= 1024) ? 8 : (n_tiles % 4 == 0 ? 4 : (n_tiles % 2 == 0 ? 2 : 1));
     p.ks = kSkinnyWaves;
+    // wide unsplit outputs: six column tiles when that, and not eight, gives
+    // whole waves of workgroups over the 256 CUs (SwiGLU at I = 12288: 256
+    // workgroups instead of 192, 39.9 -> 38.6 us with cold weights)
+    if (!may_split && n_tiles >= 1024 && n_tiles % 6 == 0 && (n_tiles / 6) % 256 == 0 && (n_tiles / 8) % 256 != 0)
+      p.nc = 6;
     if (may_split) {
       // narrow split-K outputs (O, down, fusion at H = 4096): eight column
       // tiles and eight waves per workgroup stream a little faster (down
@@ -1626,9 +1631,17 @@ template <int EPI, int MAP, bool SPLIT, int RG, bool PK>
 static hipError_t skinny_nc(const GemmArgs& g, const SeqTable& st, const GemmPlan& p, hipStream_t s) {
   const dim3 grid(g.n_tiles / p.nc, p.kc), blk(p.ks * 64);
   if (p.ks == 8) {
-    if (p.nc != 8) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((k_skinny<EPI, MAP, 8, RG, SPLIT, 8, PK>), grid, blk, 0, s, g, st);
-    return hipGetLastError();
+    if (p.nc == 8) {
+      hipLaunchKernelGGL((k_skinny<EPI, MAP, 8, RG, SPLIT, 8, PK>), grid, blk, 0, s, g, st);
+      return hipGetLastError();
+    }
+    if constexpr (EPI == EPI_SWIGLU) {
+      if (p.nc == 6) {
+        hipLaunchKernelGGL((k_skinny<EPI, MAP, 6, RG, SPLIT, 8, PK>), grid, blk, 0, s, g, st);
+        return hipGetLastError();
+      }
+    }
+    return hipErrorInvalidValue;
   }
   if (p.ks != kSkinnyWaves) return hipErrorInvalidValue;
   switch (p.nc) {
@@ -1668,10 +1681,11 @@ static hipError_t dl_dispatch(const GemmArgs& g, const SeqTable& st, int Mp, con
 template <int EPI, int MAP, bool SPLIT>
 static hipError_t gemm_dispatch(const GemmArgs& g, const SeqTable& st, int Mp, hipStream_t s) {
   GemmPlan p = gemm_plan(g.n_tiles, g.K, Mp, EPI == EPI_PARTIAL);
-  // the SwiGLU projection (192 workgroups at I = 12288) keeps more loads in
-  // flight with eight waves per workgroup: 44.8 -> 40.5 us over packed
-  // weights (cold), unchanged over row-major ones
-  if (EPI == EPI_SWIGLU && Mp <= 32 && p.nc == 8 && g.K % (8 * 64) == 0) p.ks = 8;
+  // the SwiGLU projection keeps more loads in flight with eight waves per
+  // workgroup: 44.8 -> 40.5 us over packed weights (cold, 192 workgroups at
+  // I = 12288), unchanged over row-major ones.  The LM head stays at four
+  // (eight: 218.9 instead of 216.3 us in the decode step)
+  if (EPI == EPI_SWIGLU && Mp <= 32 && (p.nc == 8 || p.nc == 6) && g.K % (8 * 64) == 0) p.ks = 8;
   if (Mp <= 32) {
     if (g.K % (p.kc * p.ks * 64) || Mp % 16) return hipErrorInvalidValue;
     if (g.wpack) {

@@ -176,9 +176,11 @@ def test_draft_is_deterministic(torch_cuda):
 # Qwen3-8B-shaped drafter at the workload sizes
 # ----------------------------------------------------------------------------
 
-def _q8_case(q8, name, seqs=None, n_layers=None, label=""):
+def _q8_case(q8, name, seqs=None, n_layers=None, label="", ctx_lens=None):
     spec5, w, dev = q8
     spec = I.spec(name)
+    if ctx_lens is not None:
+        spec = spec.with_(ctx_lens=tuple(ctx_lens))
     nl = spec.n_layers
     dev_w = dev[: 3 + 9 * nl]
     lens = spec.ctx_lens
@@ -198,6 +200,12 @@ def _q8_case(q8, name, seqs=None, n_layers=None, label=""):
 
 def test_q8_ctx1024(q8):
     _q8_case(q8, "q8b_ctx1024", label="5-layer ctx1024")
+
+
+def test_q8_two_seqs_m32(q8):
+    # 32 block rows on the weight-streaming kernel: the SwiGLU projection
+    # with two row groups over six column tiles per workgroup
+    _q8_case(q8, "q8b_ctx1024", label="5-layer two seqs M32", ctx_lens=(512, 1000))
 
 
 def test_q8_ctx8192(q8):
