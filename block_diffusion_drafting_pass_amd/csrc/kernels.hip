@@ -208,6 +208,32 @@ __device__ __forceinline__ u16* kv_v_elem(u16* cache, int gk, int64_t slot, int6
          slot % kTileKeys;
 }
 
+// LM-head tile: for this lane's rows r0 + 4 (lane / 16) + i, the largest
+// draft score over the tile's 16 columns (lowest column on ties) as an
+// order-preserving key, 0 for rows that draft nothing; logits are written on
+// the way when asked for.  All 64 lanes must call this together.
+__device__ __forceinline__ void argmax_tile_keys(const EpiParams& ep, int tile, int r0, f32x4 v, int lane,
+                                                 u64 (&key)[4]) {
+  const int c = lane & 15, g = lane >> 4;
+  const int col = tile * 16 + c;
+  const f32x4 sc = draft_scores(ep, r0 + 4 * g, col, v);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = r0 + 4 * g + i;
+    const int bi = row % ep.block;
+    const bool draft_row = row < ep.M && bi != 0;
+    if (draft_row && ep.logits)
+      ep.logits[((size_t)(row / ep.block) * (ep.block - 1) + (bi - 1)) * ep.vocab + col] = v[i];
+    u64 k = draft_row ? argmax_key(sc[i], col) : 0ull;
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) {
+      const u64 o = shfl_xor_u64(k, m);
+      k = o > k ? o : k;
+    }
+    key[i] = k;
+  }
+}
+
 // v: the 16x16 fp32 tile in MFMA result layout (lane: column c = lane % 16,
 // rows r0 + 4 (lane / 16) + i).  All 64 lanes must call this together.
 // kc: the K chunk this tile sums (EPI_PARTIAL only).
@@ -240,22 +266,12 @@ __device__ __forceinline__ void epilogue(const EpiParams& ep, const SeqTable& st
       }
     }
   } else if (EPI == EPI_ARGMAX) {
-    const int col = tile * 16 + c;
-    const f32x4 sc = draft_scores(ep, r0 + 4 * g, col, v);
+    u64 key[4];
+    argmax_tile_keys(ep, tile, r0, v, lane, key);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = r0 + 4 * g + i;
-      const int bi = row % ep.block;
-      const bool draft_row = row < ep.M && bi != 0;
-      if (draft_row && ep.logits)
-        ep.logits[((size_t)(row / ep.block) * (ep.block - 1) + (bi - 1)) * ep.vocab + col] = v[i];
-      u64 key = draft_row ? argmax_key(sc[i], col) : 0ull;
-#pragma unroll
-      for (int m = 1; m < 16; m <<= 1) {
-        const u64 o = shfl_xor_u64(key, m);
-        key = o > key ? o : key;
-      }
-      if (c == 0 && row < ep.Mp) ep.amax_part[(size_t)tile * ep.Mp + row] = key;
+      if (c == 0 && row < ep.Mp) ep.amax_part[(size_t)tile * ep.Mp + row] = key[i];
     }
   }
 }
@@ -483,6 +499,11 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_dl(GemmArgs ga, SeqTable 
   __shared__ u32x4 st1[STAGE];
   __shared__ u32x4 st2[S > 2 ? STAGE : 1];
   __shared__ u32x4 st3[S > 3 ? STAGE : 1];
+  __shared__ u64 rk[EPI == EPI_ARGMAX ? BM : 1];  // LM head: per-row key of the workgroup's columns
+  if constexpr (EPI == EPI_ARGMAX) {
+    for (int i = threadIdx.x; i < BM; i += WM * WN * 64) rk[i] = 0;
+    __syncthreads();
+  }
 
   const int nwg = gridDim.x;
   const int bid = (nwg & 7) == 0 ? (int)(blockIdx.x & 7) * (nwg >> 3) + (int)(blockIdx.x >> 3) : (int)blockIdx.x;
@@ -556,13 +577,40 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_dl(GemmArgs ga, SeqTable 
       }
     }
   }
+  if constexpr (EPI == EPI_ARGMAX) {
+    // one key per row for the workgroup's 256 columns: the wave's tiles are
+    // combined in registers, the waves that share rows through LDS
 #pragma unroll
-  for (int ct = 0; ct < TN; ++ct) {
-    const int tile = tile0 + wn * TN + ct;
-    if (tile >= ga.n_tiles) break;  // uniform over the wave
+    for (int rg = 0; rg < TM; ++rg) {
+      const int r0 = row0 + wm * TM * 16 + rg * 16;
+      u64 best[4] = {0ull, 0ull, 0ull, 0ull};
 #pragma unroll
-    for (int rg = 0; rg < TM; ++rg)
-      epilogue<EPI>(ga.ep, st, tile, row0 + wm * TM * 16 + rg * 16, acc[rg][ct], lane, kc);
+      for (int ct = 0; ct < TN; ++ct) {
+        const int tile = tile0 + wn * TN + ct;
+        if (tile >= ga.n_tiles) break;  // uniform over the wave
+        u64 key[4];
+        argmax_tile_keys(ga.ep, tile, r0, acc[rg][ct], lane, key);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) best[i] = key[i] > best[i] ? key[i] : best[i];
+      }
+      if (c == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (best[i]) atomicMax(&rk[r0 - row0 + 4 * g + i], best[i]);
+      }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < BM; i += WM * WN * 64)
+      if (row0 + i < ga.ep.Mp) ga.ep.amax_part[(size_t)n_t * ga.ep.Mp + row0 + i] = rk[i];
+  } else {
+#pragma unroll
+    for (int ct = 0; ct < TN; ++ct) {
+      const int tile = tile0 + wn * TN + ct;
+      if (tile >= ga.n_tiles) break;  // uniform over the wave
+#pragma unroll
+      for (int rg = 0; rg < TM; ++rg)
+        epilogue<EPI>(ga.ep, st, tile, row0 + wm * TM * 16 + rg * 16, acc[rg][ct], lane, kc);
+    }
   }
 }
 
@@ -831,16 +879,16 @@ __global__ __launch_bounds__(NW * 64) void k_attn_tiles(const u16* __restrict__ 
 // Combine the key splits of each (sequence, q head, 16-row query tile) unit.
 // Workgroup = unit x 4-row quad; wave w owns one query row: lane s reads
 // split s's (m, l) while every lane loads its D/64 output columns of the
-// first 32 / (D/64) splits; the wave forms the log-sum-exp weights
+// first PF splits (4 when there are at most 4, else 32 / (D/64)); the wave forms the log-sum-exp weights
 // exp(m_s - max) / sum_s l_s exp(m_s - max) (lane s holds split s's), then
 // each lane sums its columns over the splits in split order and writes the
 // hi/lo planes [row][n_q * D].
-template <int D>
+template <int D, int PF>
 __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ part_o,
                                                     const float* __restrict__ part_ml,
                                                     u16* __restrict__ o_hi, u16* __restrict__ o_lo,
                                                     int block, int n_q, int splits, SeqTable st) {
-  constexpr int PER = D / 64, PF = 32 / PER;  // splits whose outputs are loaded with (m, l)
+  constexpr int PER = D / 64;  // PF: splits whose outputs are loaded with (m, l)
   const int quad = blockIdx.x & 3, unit = blockIdx.x >> 2;
   const int qtiles = (block + 15) / 16;
   const int qt = unit % qtiles, h = (unit / qtiles) % n_q, b = unit / (qtiles * n_q);
@@ -858,7 +906,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pa
 #pragma unroll
   for (int s = 0; s < PF; ++s)
 #pragma unroll
-    for (int p = 0; p < PER; ++p) pre[s][p] = po[(size_t)min(s, splits - 1) * 16 * D + p];
+    for (int p = 0; p < PER; ++p) pre[s][p] = s < splits ? po[(size_t)s * 16 * D + p] : 0.f;
   float M = m;
 #pragma unroll
   for (int k = 32; k >= 1; k >>= 1) M = fmaxf(M, shfl_xor_f(M, k));
@@ -876,6 +924,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pa
 #pragma unroll
     for (int p = 0; p < PER; ++p) acc[p] += s < splits ? ws * pre[s][p] : 0.f;
   }
+#pragma unroll 8
   for (int s = PF; s < splits; ++s) {
     const float ws = __shfl(w, s, 64);
 #pragma unroll
@@ -1722,9 +1771,14 @@ int attention_max_splits(int pairs) {
   return s < 1 ? 1 : (s > kMaxSplits ? kMaxSplits : s);
 }
 
+// As many splits as fit attention_max_splits with every split holding
+// ceil(max_tiles / splits) tiles, so that no split of the longest sequence is
+// left empty (129 tiles over at most 64 splits: 43 splits of 3).
 int attention_splits(int pairs, int max_tiles) {
   const int s = attention_max_splits(pairs);
-  return max_tiles < s ? (max_tiles < 1 ? 1 : max_tiles) : s;
+  if (max_tiles <= s) return max_tiles < 1 ? 1 : max_tiles;
+  const int tps = (max_tiles + s - 1) / s;
+  return (max_tiles + tps - 1) / tps;
 }
 
 size_t attention_partial_bytes(int n_seqs, int n_q, int qtiles, int splits, int head_dim) {
@@ -1778,8 +1832,12 @@ static hipError_t attention_dispatch(const u16* q_hi, const u16* q_lo, const u16
   if (e != hipSuccess) return e;
   if (splits > 1) {
     const int units = n_seqs * n_q * ((block + 15) / 16);
-    hipLaunchKernelGGL(k_attn_merge<D>, dim3(units * 4), dim3(256), 0, s, part_o, part_ml, o_hi, o_lo, block, n_q,
-                       splits, st);
+    if (splits <= 4)
+      hipLaunchKernelGGL((k_attn_merge<D, 4>), dim3(units * 4), dim3(256), 0, s, part_o, part_ml, o_hi, o_lo, block,
+                         n_q, splits, st);
+    else
+      hipLaunchKernelGGL((k_attn_merge<D, 32 / (D / 64)>), dim3(units * 4), dim3(256), 0, s, part_o, part_ml, o_hi,
+                         o_lo, block, n_q, splits, st);
   }
   return hipGetLastError();
 }
@@ -1840,7 +1898,7 @@ hipError_t launch_pack_weights(const GemmArgs& g, u16* dst, hipStream_t s) {
 }
 
 int argmax_parts(int n_tiles, int Mp) {
-  return Mp <= 32 ? n_tiles / gemm_plan(n_tiles, 0, Mp, false).nc : n_tiles;
+  return Mp <= 32 ? n_tiles / gemm_plan(n_tiles, 0, Mp, false).nc : (n_tiles + kBigBN / 16 - 1) / (kBigBN / 16);
 }
 
 // One workgroup per block tile; thread t covers slot-major elements of the
