@@ -878,11 +878,11 @@ __global__ __launch_bounds__(NW * 64) void k_attn_tiles(const u16* __restrict__ 
 
 // Combine the key splits of each (sequence, q head, 16-row query tile) unit.
 // Workgroup = unit x 4-row quad; wave w owns one query row: lane s reads
-// split s's (m, l) while every lane loads its D/64 output columns of the
-// first PF splits (4 when there are at most 4, else all of them); the wave forms the log-sum-exp weights
-// exp(m_s - max) / sum_s l_s exp(m_s - max) (lane s holds split s's), then
-// each lane sums its columns over the splits in split order and writes the
-// hi/lo planes [row][n_q * D].
+// split s's (m, l) while every lane loads its D/64 output columns of all
+// splits (PF >= splits, from a few fixed sizes); the wave forms the
+// log-sum-exp weights exp(m_s - max) / sum_s l_s exp(m_s - max) (lane s
+// holds split s's), then each lane sums its columns over the splits in split
+// order and writes the hi/lo planes [row][n_q * D].
 template <int D, int PF>
 __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ part_o,
                                                     const float* __restrict__ part_ml,
@@ -918,6 +918,8 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pa
   float acc[PER];
 #pragma unroll
   for (int p = 0; p < PER; ++p) acc[p] = 0.f;
+  // (no early exit here: a conditional use lets the compiler sink the loads
+  // above into this loop, one round trip per split)
 #pragma unroll
   for (int s = 0; s < PF; ++s) {
     const float ws = __shfl(w, s, 64);
@@ -1836,12 +1838,24 @@ static hipError_t attention_dispatch(const u16* q_hi, const u16* q_lo, const u16
   if (e != hipSuccess) return e;
   if (splits > 1) {
     const int units = n_seqs * n_q * ((block + 15) / 16);
+    // the merge loads every split at once: the smallest instantiation that
+    // holds them (each unused slot still costs a shuffle and a select)
+    static_assert(kMaxSplits == 64, "merge instantiations cover up to 64 splits");
+    const dim3 grid(units * 4), blk(256);
     if (splits <= 4)
-      hipLaunchKernelGGL((k_attn_merge<D, 4>), dim3(units * 4), dim3(256), 0, s, part_o, part_ml, o_hi, o_lo, block,
-                         n_q, splits, st);
+      hipLaunchKernelGGL((k_attn_merge<D, 4>), grid, blk, 0, s, part_o, part_ml, o_hi, o_lo, block, n_q, splits, st);
+    else if (splits <= 8)
+      hipLaunchKernelGGL((k_attn_merge<D, 8>), grid, blk, 0, s, part_o, part_ml, o_hi, o_lo, block, n_q, splits, st);
+    else if (splits <= 16)
+      hipLaunchKernelGGL((k_attn_merge<D, 16>), grid, blk, 0, s, part_o, part_ml, o_hi, o_lo, block, n_q, splits, st);
+    else if (splits <= 24)
+      hipLaunchKernelGGL((k_attn_merge<D, 24>), grid, blk, 0, s, part_o, part_ml, o_hi, o_lo, block, n_q, splits, st);
+    else if (splits <= 32)
+      hipLaunchKernelGGL((k_attn_merge<D, 32>), grid, blk, 0, s, part_o, part_ml, o_hi, o_lo, block, n_q, splits, st);
+    else if (splits <= 48)
+      hipLaunchKernelGGL((k_attn_merge<D, 48>), grid, blk, 0, s, part_o, part_ml, o_hi, o_lo, block, n_q, splits, st);
     else
-      hipLaunchKernelGGL((k_attn_merge<D, kMaxSplits>), dim3(units * 4), dim3(256), 0, s, part_o, part_ml, o_hi,
-                         o_lo, block, n_q, splits, st);
+      hipLaunchKernelGGL((k_attn_merge<D, 64>), grid, blk, 0, s, part_o, part_ml, o_hi, o_lo, block, n_q, splits, st);
   }
   return hipGetLastError();
 }
