@@ -126,6 +126,14 @@ def test_tiny_variants(torch_cuda, lens, block, jitter, std, label):
     _tiny_case(I.spec("tiny"), lens, block, jitter=jitter, std=std, label=label)
 
 
+# One sequence of the tiny drafter (two kv heads) at contexts whose key tiles
+# give 3, 7, 15, 20, 30, 45 and 60 attention splits of one tile, and 126
+# tiles in 63 splits of two: every size of the split merge.
+@pytest.mark.parametrize("ctx", [172, 428, 940, 1260, 1900, 2860, 3820, 8044])
+def test_tiny_attention_splits(torch_cuda, ctx):
+    _tiny_case(I.spec("tiny"), (ctx,), 16, std=0.05, label=f"ctx {ctx} splits")
+
+
 def test_tiny_incremental_append_and_truncate(torch_cuda):
     spec = I.spec("tiny").with_(ctx_lens=(0, 0))
     w = I.gen_weights(spec, seed=4, std=0.05)
