@@ -19,6 +19,10 @@ training sequence's target features as injected context (dflash_fuse_ctx)
 and drafts all of its anchored blocks (dflash_draft_anchored), each block
 seeing the context before its anchor and itself.
 
+--phase draft times the draft pass alone over a resident context: every
+position already ingested, one step = dflash_draft_block + dflash_accept_len
+(no append), the pass as the method statement defines it.
+
 --phase ingest times the other phase of the method instead: every
 sequence's whole context ingested from its target features (the fusion map
 and every layer's injected K/V, dflash_fuse_ctx), in ingested positions/s.
@@ -144,9 +148,11 @@ def step_work(spec):
 # ----------------------------------------------------------------------------
 
 class Workload:
-    def __init__(self, spec, weights, torch, B_, two_call=False, denoise_steps=1, temperature=0.0):
+    def __init__(self, spec, weights, torch, B_, two_call=False, denoise_steps=1, temperature=0.0,
+                 draft_only=False):
         self.spec, self.torch, self.B = spec, torch, B_
         self.two_call = two_call
+        self.draft_only = draft_only
         self.denoise_steps = denoise_steps
         self.temperature = temperature
         I = _inputs()
@@ -156,13 +162,14 @@ class Workload:
         self.ctx = B_.Context(self.model, list(spec.ctx_lens))
         self.ws = B_.workspace(self.model, n, blk, max(spec.ctx_lens) * n)
         # context: positions 0 .. c_b - B come from an initial ingest; the step
-        # appends c_b - B .. c_b - 1 (the same rows every step)
+        # appends c_b - B .. c_b - 1 (the same rows every step).  Draft only:
+        # every position is ingested up front and the step appends nothing.
         self.host_feats = [I.gen_features(spec, 1, b, c) for b, c in enumerate(spec.ctx_lens)]
-        self.base = [c - blk for c in spec.ctx_lens]
+        self.base = list(spec.ctx_lens) if draft_only else [c - blk for c in spec.ctx_lens]
         assert min(self.base) >= 0, "context shorter than a block"
         self._ingest([f[:c] for f, c in zip(self.host_feats, self.base)])
         step_rows = np.concatenate([f[c:] for f, c in zip(self.host_feats, self.base)], axis=0)
-        self.step_feats = self._dev_bf16(step_rows)
+        self.step_feats = None if draft_only else self._dev_bf16(step_rows)
         self.anchors = torch.from_numpy(I.gen_anchors(spec, 2)).cuda()
         self.draft = torch.empty((n, blk - 1), dtype=torch.int32, device="cuda")
         self.accept = torch.empty(n, dtype=torch.int32, device="cuda")
@@ -212,7 +219,9 @@ class Workload:
                 B_.verify_sample(self.draft, self.q_logits, self.p_logits, s.block, self.temperature, 1234,
                                  ws=self.verify_ws, accept=self.accept, next_token=self.next_anchor)
             return
-        if self.two_call:
+        if self.draft_only:
+            B_.draft_block(self.model, self.ctx, self.anchors, s.block, self.ws, draft=self.draft)
+        elif self.two_call:
             B_.fuse_ctx(self.model, self.ctx, self.step_feats, self.n_new, self.ws)
             B_.draft_block(self.model, self.ctx, self.anchors, s.block, self.ws, draft=self.draft)
         else:
@@ -229,7 +238,8 @@ class Workload:
         s = self.spec
         for b, c in enumerate(self.base):
             self.ctx.truncate(b, c)
-        self.B.fuse_ctx(self.model, self.ctx, self.step_feats, self.n_new, self.ws)
+        if not self.draft_only:
+            self.B.fuse_ctx(self.model, self.ctx, self.step_feats, self.n_new, self.ws)
         lg = t.empty((s.n_seqs, s.block - 1, s.vocab), dtype=t.float32, device="cuda")
         d = self.B.draft_block(self.model, self.ctx, self.anchors, s.block, self.ws, logits=lg)
         t.cuda.synchronize()
@@ -414,9 +424,10 @@ def blas_threads() -> int:
     return len(os.sched_getaffinity(0))
 
 
-def cpu_baseline(spec, weights, ws_target_s=10.0, max_reps=3):
-    """The oracle's step (append B, draft, accept) on one sequence, timed on
-    the host cores until about ws_target_s seconds of work (1..max_reps steps)."""
+def cpu_baseline(spec, weights, ws_target_s=10.0, max_reps=3, draft_only=False):
+    """The oracle's step (append B, draft, accept; draft_only: draft, accept
+    over the whole context) on one sequence, timed on the host cores until
+    about ws_target_s seconds of work (1..max_reps steps)."""
     from oracle import dflash_oracle as O
     I = _inputs()
     sub = spec.with_(ctx_lens=spec.ctx_lens[:1])
@@ -425,14 +436,16 @@ def cpu_baseline(spec, weights, ws_target_s=10.0, max_reps=3):
     ctx = O.OracleContext(model, 1)
     feats = I.gen_features(spec, 1, 0, c)
     anchors = I.gen_anchors(spec, 2)[:1]
+    base = c if draft_only else c - blk
     t0 = time.perf_counter()
-    O.fuse_ctx(model, ctx, 0, feats[: c - blk])
-    log(f"oracle ingest of {c - blk} positions: {time.perf_counter() - t0:.1f} s")
+    O.fuse_ctx(model, ctx, 0, feats[:base])
+    log(f"oracle ingest of {base} positions: {time.perf_counter() - t0:.1f} s")
     times, res = [], None
     while len(times) < max_reps and sum(times) < ws_target_s:
-        O.truncate_ctx(ctx, 0, c - blk)
+        O.truncate_ctx(ctx, 0, base)
         t0 = time.perf_counter()
-        O.fuse_ctx(model, ctx, 0, feats[c - blk:])
+        if not draft_only:
+            O.fuse_ctx(model, ctx, 0, feats[base:])
         res = O.draft_block(model, ctx, anchors, blk)
         K, r, bonus = I.gen_accept_construction(sub, 4, n_seqs=1)
         O.accept_len(res.drafts, I.make_targets(res.drafts, K, r, bonus, sub.vocab))
@@ -444,7 +457,8 @@ def cpu_baseline(spec, weights, ws_target_s=10.0, max_reps=3):
         "unit": "draft tokens/s",
         "cores": blas_threads(),
         "kind": "oracle",
-        "sample": (f"{len(times)} oracle step(s) of sequence 0 (append {blk}, draft, accept; context {c}), "
+        "sample": (f"{len(times)} oracle step(s) of sequence 0 ({'' if draft_only else f'append {blk}, '}draft, "
+                   f"accept; context {c}), "
                    f"numpy float64, median {t:.2f} s/step; {len(os.sched_getaffinity(0))} host CPUs visible, "
                    f"{platform.processor() or platform.machine()}"),
     }, res
@@ -524,8 +538,10 @@ def main(argv=None) -> int:
                     help="step as dflash_fuse_ctx + dflash_draft_block instead of the fused dflash_step")
     ap.add_argument("--denoise-steps", type=int, default=1,
                     help="draft passes per block (1 = the single-pass drafter)")
-    ap.add_argument("--phase", choices=("decode", "ingest"), default="decode",
-                    help="decode: the draft step (default); ingest: whole-context ingest of every sequence")
+    ap.add_argument("--phase", choices=("decode", "draft", "ingest"), default="decode",
+                    help="decode: the steady-state step, append + draft + accept (default); draft: the draft "
+                         "pass + accept alone over a resident context; ingest: whole-context ingest of every "
+                         "sequence")
     ap.add_argument("--temperature", type=float, default=0.0,
                     help="sampled drafts at this temperature, verified losslessly (0 = greedy)")
     ap.add_argument("--no-pack", action="store_true",
@@ -572,6 +588,11 @@ def main(argv=None) -> int:
     if train and (S > 1 or args.two_call or args.temperature > 0):
         print("--denoise-steps, --two-call and --temperature apply to decode workloads only", file=sys.stderr)
         return 2
+    draft_only = args.phase == "draft"
+    if draft_only and (train or S > 1 or args.two_call or args.temperature > 0):
+        print("--phase draft takes a decode workload and none of --denoise-steps, --two-call, --temperature",
+              file=sys.stderr)
+        return 2
     if args.temperature > 0 and (S > 1 or args.two_call):
         print("--temperature combines with neither --denoise-steps nor --two-call", file=sys.stderr)
         return 2
@@ -581,7 +602,7 @@ def main(argv=None) -> int:
         wl = TrainWorkload(spec, weights, torch, B_)
     else:
         wl = Workload(spec, weights, torch, B_, two_call=args.two_call, denoise_steps=S,
-                      temperature=args.temperature)
+                      temperature=args.temperature, draft_only=draft_only)
     if not args.no_pack:
         # one-time layout copy of the streamed weights, outside the timed region
         # like the weight upload itself (results are bitwise identical)
@@ -632,6 +653,8 @@ def main(argv=None) -> int:
         by, fl = ingest_work(spec)
     elif train:
         by, fl = train_step_work(wl)
+    elif draft_only:
+        by, fl = pass_work(spec)
     else:
         by, fl = step_work(spec)
         if S > 1:
@@ -699,7 +722,7 @@ def main(argv=None) -> int:
     elif not args.no_cpu:
         d_gpu, lg_gpu = wl.logits()
         log("timing the CPU oracle on the host cores")
-        cpu, ref = cpu_baseline(spec, weights)
+        cpu, ref = cpu_baseline(spec, weights, draft_only=draft_only)
         from oracle import dflash_oracle as O
         sure = O.top2_gap(ref.logits) > 0.05
         parity = {"seq": 0, "max_abs_logit_err": float(np.max(np.abs(lg_gpu[:1] - ref.logits))),
@@ -729,8 +752,10 @@ def main(argv=None) -> int:
                     f"{spec.n_q_heads}/{spec.n_kv_heads} heads x {spec.head_dim}, SwiGLU {spec.intermediate}, "
                     f"vocab {spec.vocab}, fusion {spec.fused_width}->{spec.hidden}; {n} sequence(s), "
                     f"context {spec.ctx_lens[0] if n == 1 else list(spec.ctx_lens)}, block {blk}; "
-                    f"step = append {blk} verified positions + draft pass + accept scan"
-                    f"{' (two calls)' if args.two_call else ' (dflash_step)'}"
+                    + (f"step = draft pass + accept scan over the resident context (dflash_draft_block + "
+                       f"dflash_accept_len)" if draft_only else
+                       f"step = append {blk} verified positions + draft pass + accept scan"
+                       f"{' (two calls)' if args.two_call else ' (dflash_step)'}") +
                     f"{f' + {S - 1} refinement pass(es)' if S > 1 else ''}"
                     f"{f'; drafts sampled at temperature {args.temperature} and verified losslessly' if args.temperature > 0 else ''}")
     out = {
