@@ -676,6 +676,7 @@ int draft_impl(const dflash_model* model, const dflash_ctx* ctx, const Blocks& b
     sq.row_start[e] = off;
   }
   int max_tiles = 1, attn_units = n;
+  int64_t unit_tiles = 0;
   AttnGroups groups;
   groups.n = 0;
   if (bk.sep) {
@@ -706,10 +707,14 @@ int draft_impl(const dflash_model* model, const dflash_ctx* ctx, const Blocks& b
     }
     attn_units = groups.n;
   } else {
-    for (int b = 0; b < n; ++b)
-      max_tiles = std::max<int>(max_tiles, (int)((bk.pos[b] + block + kTileKeys - 1) / kTileKeys));
+    for (int b = 0; b < n; ++b) {
+      const int t = (int)((bk.pos[b] + block + kTileKeys - 1) / kTileKeys);
+      max_tiles = std::max(max_tiles, t);
+      unit_tiles += (int64_t)t * c.n_kv_heads;
+    }
   }
-  const int splits = std::min(W.max_splits, attention_splits(attn_units * c.n_kv_heads, max_tiles));
+  const int splits =
+      attention_splits(attn_units * c.n_kv_heads, max_tiles, unit_tiles, bk.sep, W.max_splits);
 
   auto base_args = [&](const u16* ah, const u16* al, int lda, int K, int n_tiles, int epi, int map) {
     GemmArgs g;

@@ -201,9 +201,11 @@ __host__ __device__ inline size_t kv_tile_offset(int g, int64_t tile, int64_t kv
   return ((size_t)g * kv_tiles + tile) * (size_t)(4 * kTileKeys * d);
 }
 
-// Key splits per (sequence, kv head) for the attention pass: enough
-// workgroups to fill the chip, never more than there are tiles.
-int attention_splits(int pairs, int max_tiles);
+// Key splits per (unit, kv head) for the attention pass: the call's tile work
+// spread over the CUs, never more than there are tiles (unit_tiles: tiles
+// summed over units and kv heads; grouped: units are groups of anchored
+// blocks).  attention_max_splits bounds it for sizing the workspace.
+int attention_splits(int pairs, int max_tiles, int64_t unit_tiles, bool grouped, int max_splits);
 int attention_max_splits(int pairs);
 size_t attention_partial_bytes(int n_seqs, int n_q, int qtiles, int splits, int head_dim);
 size_t attention_ml_bytes(int n_seqs, int n_q, int qtiles, int splits);
