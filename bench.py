@@ -424,7 +424,7 @@ def blas_threads() -> int:
     return len(os.sched_getaffinity(0))
 
 
-def cpu_baseline(spec, weights, ws_target_s=10.0, max_reps=3, draft_only=False):
+def cpu_baseline(spec, weights, ws_target_s=10.0, max_reps=8, draft_only=False):
     """The oracle's step (append B, draft, accept; draft_only: draft, accept
     over the whole context) on one sequence, timed on the host cores until
     about ws_target_s seconds of work (1..max_reps steps)."""
