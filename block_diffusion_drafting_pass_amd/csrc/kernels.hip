@@ -929,8 +929,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pa
 #pragma unroll
     for (int p = 0; p < PER; ++p) acc[p] += s < splits ? ws * pre[s][p] : 0.f;
   }
-#pragma unroll 8
-  for (int s = PF; s < splits; ++s) {
+  for (int s = PF; s < splits; ++s) {  // splits beyond the prefetched ones (none as launched)
     const float ws = __shfl(w, s, 64);
 #pragma unroll
     for (int p = 0; p < PER; ++p) acc[p] += ws * po[(size_t)s * 16 * D + p];
