@@ -814,7 +814,7 @@ int draft_impl(const dflash_model* model, const dflash_ctx* ctx, const Blocks& b
 
     model->probe.start(DFLASH_STAGE_ATTENTION, s);
     e = launch_attention(q_hi, q_lo, ctx->kv_cache(l), ctx->kv_tiles(), bk.sep ? bkv : nullptr, part_o, part_ml,
-                         a_hi, a_lo, n, block, c.n_q_heads, c.n_kv_heads, c.head_dim, splits, st, bk.sep ? &groups : nullptr, s);
+                         a_hi, a_lo, n, block, c.n_q_heads, c.n_kv_heads, c.head_dim, splits, max_tiles, st, bk.sep ? &groups : nullptr, s);
     model->probe.stop(DFLASH_STAGE_ATTENTION, s);
     if (e != hipSuccess) return hip_fail(e, "draft_block: attention");
 

@@ -160,11 +160,12 @@ int attention_group_size(int n_q, int n_kv, int block);
 // keys.  blk_kv null: the block keys follow the context keys in the cache;
 // otherwise they are tile b of blk_kv (n_seqs tiles per kv head), and the
 // cache is only read.  groups (only with blk_kv): one workgroup per group of
-// blocks and kv head instead of per block and kv head.
+// blocks and kv head instead of per block and kv head.  max_tiles: key tiles
+// of the longest unit (chooses the launch shape only).
 hipError_t launch_attention(const u16* q_hi, const u16* q_lo, const u16* kv_cache, int64_t kv_tiles,
                             const u16* blk_kv, float* part_o, float* part_ml, u16* o_hi, u16* o_lo, int n_seqs,
-                            int block, int n_q, int n_kv, int head_dim, int splits, const SeqTable& st,
-                            const AttnGroups* groups, hipStream_t s);
+                            int block, int n_q, int n_kv, int head_dim, int splits, int max_tiles,
+                            const SeqTable& st, const AttnGroups* groups, hipStream_t s);
 // Zero slots block .. kTileKeys-1 of the n_blocks x n_kv block tiles of a
 // separate block K/V area (slots the block never writes; attention masks
 // them, and zeros keep 0 * value finite).

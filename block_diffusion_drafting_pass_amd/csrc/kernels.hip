@@ -1868,7 +1868,7 @@ static hipError_t attention_tiles(int nw, dim3 grid, const u16* q_hi, const u16*
 template <int D>
 static hipError_t attention_dispatch(const u16* q_hi, const u16* q_lo, const u16* kv, int64_t kv_tiles,
                                      const u16* bkv, float* part_o, float* part_ml, u16* o_hi, u16* o_lo, int n_seqs,
-                                     int block, int n_q, int n_kv, int splits, const SeqTable& st,
+                                     int block, int n_q, int n_kv, int splits, int max_tiles, const SeqTable& st,
                                      const AttnGroups* groups, hipStream_t s) {
   const float scale = (float)(1.0 / sqrt((double)D));
   const int hpw = attention_heads_per_wave(n_q, n_kv, groups != nullptr);
@@ -1883,9 +1883,11 @@ static hipError_t attention_dispatch(const u16* q_hi, const u16* q_lo, const u16
     e = hpw == 2 ? DFLASH_ATTN_GRP(2) : DFLASH_ATTN_GRP(1);
 #undef DFLASH_ATTN_GRP
   } else {
-    // two waves per query unit, each taking half of every tile's keys
-    // (32 sequences: 133.0 -> 122.3 us per layer; 8192 keys 24.0 -> 23.1)
-    e = upb <= 4 ? attention_tiles<D, false, 1, true>(2 * upb, dim3(n_seqs * n_kv * splits), q_hi, q_lo, kv,
+    // two waves per query unit, each taking half of every tile's keys, when
+    // splits hold several tiles (32 sequences: 133.0 -> 122.3 us per layer;
+    // 8192 keys 24.0 -> 23.1; splits of one tile, context 1024: 8.2 -> 9.0)
+    const bool halves = upb <= 4 && (max_tiles + splits - 1) / splits >= 2;
+    e = halves ? attention_tiles<D, false, 1, true>(2 * upb, dim3(n_seqs * n_kv * splits), q_hi, q_lo, kv,
                                                       kv_tiles, bkv, n_seqs, part_o, part_ml, o_hi, o_lo, block,
                                                       n_q, n_kv, splits, scale, st, 0, s)
                  : attention_tiles<D, false, 1, false>(upb, dim3(n_seqs * n_kv * splits), q_hi, q_lo, kv, kv_tiles,
@@ -1933,16 +1935,16 @@ int attention_group_size(int n_q, int n_kv, int block) {
 
 hipError_t launch_attention(const u16* q_hi, const u16* q_lo, const u16* kv_cache, int64_t kv_tiles,
                             const u16* blk_kv, float* part_o, float* part_ml, u16* o_hi, u16* o_lo, int n_seqs,
-                            int block, int n_q, int n_kv, int head_dim, int splits, const SeqTable& st,
-                            const AttnGroups* groups, hipStream_t s) {
+                            int block, int n_q, int n_kv, int head_dim, int splits, int max_tiles,
+                            const SeqTable& st, const AttnGroups* groups, hipStream_t s) {
   if (block > kTileKeys) return hipErrorInvalidValue;
   if (groups && (!blk_kv || groups->n < 1 || groups->n > kMaxSeqs)) return hipErrorInvalidValue;
   if (head_dim == 128)
     return attention_dispatch<128>(q_hi, q_lo, kv_cache, kv_tiles, blk_kv, part_o, part_ml, o_hi, o_lo, n_seqs,
-                                   block, n_q, n_kv, splits, st, groups, s);
+                                   block, n_q, n_kv, splits, max_tiles, st, groups, s);
   if (head_dim == 64)
     return attention_dispatch<64>(q_hi, q_lo, kv_cache, kv_tiles, blk_kv, part_o, part_ml, o_hi, o_lo, n_seqs,
-                                  block, n_q, n_kv, splits, st, groups, s);
+                                  block, n_q, n_kv, splits, max_tiles, st, groups, s);
   return hipErrorInvalidValue;
 }
 
