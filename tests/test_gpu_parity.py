@@ -134,6 +134,15 @@ def test_tiny_attention_splits(torch_cuda, ctx):
     _tiny_case(I.spec("tiny"), (ctx,), 16, std=0.05, label=f"ctx {ctx} splits")
 
 
+# Long contexts whose splits hold several tiles, so that each query unit
+# runs as two waves over the two halves of every tile (blocks of 4, 16 and
+# 32; the last tile holds 44, 48, 64 and 28 keys: at context 12300 its second
+# half has no valid key).
+@pytest.mark.parametrize("ctx,block", [(9000, 4), (20000, 16), (20000, 32), (12300, 16)])
+def test_tiny_attention_halves(torch_cuda, ctx, block):
+    _tiny_case(I.spec("tiny"), (ctx,), block, std=0.05, label=f"ctx {ctx} B{block} halves")
+
+
 def test_tiny_incremental_append_and_truncate(torch_cuda):
     spec = I.spec("tiny").with_(ctx_lens=(0, 0))
     w = I.gen_weights(spec, seed=4, std=0.05)
