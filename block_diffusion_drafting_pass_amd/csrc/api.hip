@@ -314,6 +314,14 @@ namespace {
 // map filled in.
 enum PackSlot { PACK_FC, PACK_LM, PACK_QKV, PACK_O, PACK_GATE_UP, PACK_DOWN };
 
+// Packed order per matrix.  The LM head, q|k|v and gate|up go k-major (the
+// 1 KB blocks of one 32-k step of every column tile side by side), so that
+// the workgroups at the same k stream one contiguous stretch together; the
+// fusion map, O and down stay tile-major.  Measured over the few-row GEMM at
+// 16 rows: LM head 220 -> 188 us (5.65 -> 6.62 TB/s), gate|up 37.6 -> 34.4,
+// q|k|v 15.3 -> 14.3 us; O 8.4 -> 9.0 us, down and fusion unchanged.
+constexpr int pack_kmajor(int which) { return which == PACK_LM || which == PACK_QKV || which == PACK_GATE_UP; }
+
 template <typename F>
 void for_each_packed(const dflash_model* m, F&& fn) {
   const dflash_config& c = m->cfg;
@@ -331,9 +339,11 @@ void for_each_packed(const dflash_model* m, F&& fn) {
   };
   GemmArgs g = args(MAP_PLAIN, H / 16, c.n_target_layers * H);
   g.w.w0 = m->w_fc;
+  g.pk_kmajor = pack_kmajor(PACK_FC);
   fn(g, PACK_FC, -1);
   g = args(MAP_PLAIN, c.vocab / 16, H);
   g.w.w0 = m->embed;
+  g.pk_kmajor = pack_kmajor(PACK_LM);
   fn(g, PACK_LM, -1);
   for (int l = 0; l < c.n_layers; ++l) {
     const LayerW& Lw = m->layers[l];
@@ -341,16 +351,20 @@ void for_each_packed(const dflash_model* m, F&& fn) {
     g.w.w0 = Lw.wq;
     g.w.w1 = Lw.wk;
     g.w.w2 = Lw.wv;
+    g.pk_kmajor = pack_kmajor(PACK_QKV);
     fn(g, PACK_QKV, l);
     g = args(MAP_PLAIN, H / 16, QD);
     g.w.w0 = Lw.wo;
+    g.pk_kmajor = pack_kmajor(PACK_O);
     fn(g, PACK_O, l);
     g = args(MAP_SWIGLU, I / 8, H);
     g.w.w0 = Lw.wgate;
     g.w.w1 = Lw.wup;
+    g.pk_kmajor = pack_kmajor(PACK_GATE_UP);
     fn(g, PACK_GATE_UP, l);
     g = args(MAP_PLAIN, H / 16, I);
     g.w.w0 = Lw.wdown;
+    g.pk_kmajor = pack_kmajor(PACK_DOWN);
     fn(g, PACK_DOWN, l);
   }
 }
@@ -791,6 +805,7 @@ int draft_impl(const dflash_model* model, const dflash_ctx* ctx, const Blocks& b
     const PackedLayer Pw = model->pk_layers.empty() ? PackedLayer{} : model->pk_layers[l];
     GemmArgs g = base_args(qin_hi, qin_lo, H, H, nqkv / 16, EPI_PARTIAL, MAP_QKV);
     g.wpack = Pw.qkv;
+    g.pk_kmajor = pack_kmajor(PACK_QKV);
     g.a_rows = Mq;
     g.q_rows = R > 0 ? M : 0;  // appended rows need only their K / V
     g.ep.M = Mq;
@@ -836,6 +851,7 @@ int draft_impl(const dflash_model* model, const dflash_ctx* ctx, const Blocks& b
     g.w.w0 = Lw.wgate;
     g.w.w1 = Lw.wup;
     g.wpack = Pw.gate_up;
+    g.pk_kmajor = pack_kmajor(PACK_GATE_UP);
     g.ep.out_hi = b_hi;
     g.ep.out_lo = b_lo;
     g.ep.ldh = I;
@@ -863,6 +879,7 @@ int draft_impl(const dflash_model* model, const dflash_ctx* ctx, const Blocks& b
   GemmArgs g = base_args(a_hi, a_lo, H, H, c.vocab / 16, EPI_ARGMAX, MAP_PLAIN);
   g.w.w0 = model->embed;
   g.wpack = model->pk_lm;
+  g.pk_kmajor = pack_kmajor(PACK_LM);
   g.ep.amax_part = amax;
   g.ep.logits = logits;
   g.ep.vocab = c.vocab;

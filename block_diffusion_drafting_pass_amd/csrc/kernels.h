@@ -75,6 +75,7 @@ constexpr unsigned long long kPurposeDraft = 1, kPurposeAccept = 2, kPurposeResi
 
 struct GemmArgs {
   const u16* wpack;  // packed weights of this launch's mapped rows (few-row GEMM only), or null
+  int pk_kmajor;     // wpack order: 0 tile-major (block (t, s) at t K/32 + s), 1 k-major (at s n_tiles + t)
   const u16* a_hi;   // A rows (bf16); with split A this is the hi plane
   const u16* a_lo;   // lo plane or null (single product)
   int lda;           // row stride of A in elements

@@ -320,7 +320,9 @@ __device__ __forceinline__ void argmax_tail(const EpiParams& ep, int tile0, f32x
 // Workgroup (x, y) owns NC 16-column tiles and K chunk y of gridDim.y; its
 // KS waves (four; eight for narrow split-K outputs) split the chunk.  PK:
 // the weights come packed (launch_pack_weights), so every weight load reads
-// 1 KB contiguous per wave, with the non-temporal hint (read once).  Each wave streams its NC weight-row
+// 1 KB contiguous per wave, with the non-temporal hint (read once); in the
+// k-major order the NC tiles of one k-step are adjacent too, and workgroups
+// at the same k read one stretch together.  Each wave streams its NC weight-row
 // slices straight into MFMA B registers (16 B per lane per tile and k-step,
 // two 32-k steps per batch, the next batch in flight while the current one
 // is multiplied) and reuses every A fragment for all NC tiles.  Partial sums
@@ -332,8 +334,10 @@ __device__ __forceinline__ void argmax_tail(const EpiParams& ep, int tile0, f32x
 template <int EPI, int MAP, int NC, int RG, bool SPLIT, int KS = kSkinnyWaves, bool PK = false>
 __global__ __launch_bounds__(KS * 64) void k_skinny(GemmArgs ga, SeqTable st) {
   constexpr int U = 2;
-  // packed weights: k advances 16 elements per k (one 1 KB block per 32 k)
-  constexpr int KM = PK ? 16 : 1;
+  // packed weights: one 1 KB block per (tile, 32 k); k advances 16 elements
+  // per k tile-major, 16 n_tiles k-major
+  const size_t KM = PK ? (ga.pk_kmajor ? (size_t)16 * ga.n_tiles : 16) : 1;
+  const size_t TM = ga.pk_kmajor ? 1 : ga.K / 32;  // blocks per tile step
   const int lane = threadIdx.x & 63, ks = threadIdx.x >> 6;
   const int c = lane & 15, g = lane >> 4;
   const int tile0 = blockIdx.x * NC;
@@ -344,7 +348,7 @@ __global__ __launch_bounds__(KS * 64) void k_skinny(GemmArgs ga, SeqTable st) {
   const u16* wp[NC];
 #pragma unroll
   for (int j = 0; j < NC; ++j)
-    wp[j] = PK ? ga.wpack + ((size_t)(tile0 + j) * (ga.K / 32) * 64 + lane) * 8
+    wp[j] = PK ? ga.wpack + ((size_t)(tile0 + j) * TM * 64 + lane) * 8
                : weight_row<MAP>(ga.w, ga.ep, tile0 + j, c, ga.K) + g * 8;
   auto ldw = [&](int j, int k) { return PK ? ld_frag_stream(wp[j] + (size_t)k * KM) : ld_frag(wp[j] + k); };
   // Rows past a_rows read row a_rows - 1 instead: an output row depends only
@@ -1948,7 +1952,9 @@ hipError_t launch_attention(const u16* q_hi, const u16* q_lo, const u16* kv_cach
   return hipErrorInvalidValue;
 }
 
-// One thread per 16-byte chunk of the packed layout (see packed_elems).
+// One thread per 16-byte chunk of the packed layout (see packed_elems): the
+// 1 KB block (tile t, k-step s) goes to block t K/32 + s tile-major or
+// s n_tiles + t k-major.
 template <int MAP>
 __global__ __launch_bounds__(256) void k_pack_weights(GemmArgs g, u16* __restrict__ dst) {
   const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
@@ -1958,7 +1964,8 @@ __global__ __launch_bounds__(256) void k_pack_weights(GemmArgs g, u16* __restric
   const size_t ts = idx / 64;
   const int s = (int)(ts % S), t = (int)(ts / S);
   const u16* src = weight_row<MAP>(g.w, g.ep, t, c, g.K) + 32 * s + 8 * q;
-  *reinterpret_cast<u32x4*>(dst + idx * 8) = *reinterpret_cast<const u32x4*>(src);
+  const size_t blk = g.pk_kmajor ? (size_t)s * g.n_tiles + t : ts;
+  *reinterpret_cast<u32x4*>(dst + (blk * 64 + lane) * 8) = *reinterpret_cast<const u32x4*>(src);
 }
 
 hipError_t launch_pack_weights(const GemmArgs& g, u16* dst, hipStream_t s) {

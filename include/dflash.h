@@ -111,7 +111,9 @@ size_t dflash_model_pack_bytes(const dflash_model* model);
  * for each GEMM's output rows, in the row order its kernel maps them
  * (q|k|v stacked; gate and up rows interleaved eight and eight), column
  * tile t (16 rows) and k-step s (32 columns) form one contiguous 1 KB block
- * in MFMA lane order, so each wave load reads 1 KB contiguous.  This is a
+ * in MFMA lane order, so each wave load reads 1 KB contiguous; the blocks go
+ * tile-major (fusion map, O, down) or k-major, all tiles of one k-step side
+ * by side (LM head, q|k|v, gate|up).  This is a
  * layout change only: results are bitwise identical with and without it.
  * The model then reads the copy for calls of at most 32 GEMM rows; the
  * original weights stay in use for everything else and must stay valid.
