@@ -362,6 +362,8 @@ def _packed_case(spec, dev_w, base_lens, n_new, block, label):
 @pytest.mark.parametrize("base,new,block,label", [
     ((112,), (16,), 16, "one seq, fused 16 + 16 rows"),
     ((40, 9), (3, 5), 8, "two seqs ragged"),
+    ((30, 41, 7, 64, 19, 33, 50, 12, 25), (20, 3, 17, 9, 31, 1, 12, 8, 24), 16,
+     "nine seqs: many-row GEMMs over the packed copy"),
 ])
 def test_packed_weights_tiny(torch_cuda, base, new, block, label):
     spec = I.spec("tiny")
@@ -372,6 +374,13 @@ def test_packed_weights_tiny(torch_cuda, base, new, block, label):
 def test_packed_weights_q8_ctx1024(q8):
     spec5, w, dev = q8
     _packed_case(spec5, dev, (1008,), (16,), 16, "5-layer ctx 1008 + 16 + 16, packed")
+
+
+def test_packed_weights_q8_many_rows(q8):
+    # 64 block rows and 64 appended rows: every GEMM takes the many-row kernel,
+    # which copies its weight tiles from the packed blocks
+    spec5, w, dev = q8
+    _packed_case(spec5, dev, (200, 300, 150, 250), (16, 16, 16, 16), 16, "5-layer 4 seqs, many-row packed")
 
 
 # ----------------------------------------------------------------------------
