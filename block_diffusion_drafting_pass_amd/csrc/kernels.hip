@@ -372,12 +372,14 @@ __global__ __launch_bounds__(KS * 64) void k_skinny(GemmArgs ga, SeqTable st) {
   if (MAP == MAP_QKV && RG > 1 && ga.q_rows > 0 && (tile0 + NC) * 16 <= ga.ep.n_q * ga.ep.head_dim)
     rg_end = (ga.q_rows + 15) / 16;
 
-  // With one row group the A fragments travel one batch ahead with the
-  // weights: loads complete in issue order, so a batch's A loaded after the
-  // next batch's weights would make every wave wait for those weights before
-  // multiplying (LM head 187 -> 183 us, gate|up 35.7 -> 33.5 us).  Two row
-  // groups load A in the multiply: their registers would spill otherwise.
-  constexpr bool APF = RG == 1;
+  // A fragments travel one batch ahead with the weights: loads complete in
+  // issue order, so a batch's A loaded after the next batch's weights would
+  // make every wave wait for those weights before multiplying (16 rows: LM
+  // head 187 -> 183 us, gate|up 35.7 -> 33.5 us; 32 rows: LM head 263 -> 222,
+  // gate|up 39.1 -> 37.2 us).  Two row groups of split-K partial outputs (the
+  // q|k|v, O and down projections) and eight-tile, eight-wave shapes load A
+  // in the multiply: there the extra registers cost occupancy or spill.
+  constexpr bool APF = RG == 1 || (EPI != EPI_PARTIAL && !(NC == 8 && KS == 8));
   constexpr int NPL = SPLIT ? 2 : 1;
   auto lda_ = [&](int pl, int rg, int k) { return ld_frag((pl ? al[rg] : ah[rg]) + k); };
   bf16x8 wf[U][NC], af[APF ? U : 1][RG][NPL];
@@ -385,7 +387,10 @@ __global__ __launch_bounds__(KS * 64) void k_skinny(GemmArgs ga, SeqTable st) {
   for (int u = 0; u < U; ++u) {
     if constexpr (APF)
 #pragma unroll
-      for (int pl = 0; pl < NPL; ++pl) af[u][0][pl] = lda_(pl, 0, kb + u * 32);
+      for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+        for (int pl = 0; pl < NPL; ++pl)
+          if (rg < rg_end) af[u][rg][pl] = lda_(pl, rg, kb + u * 32);
 #pragma unroll
     for (int j = 0; j < NC; ++j) wf[u][j] = ldw(j, kb + u * 32);
   }
@@ -397,7 +402,10 @@ __global__ __launch_bounds__(KS * 64) void k_skinny(GemmArgs ga, SeqTable st) {
       for (int u = 0; u < U; ++u) {
         if constexpr (APF)
 #pragma unroll
-          for (int pl = 0; pl < NPL; ++pl) an[u][0][pl] = lda_(pl, 0, k + 32 * U + u * 32);
+          for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+            for (int pl = 0; pl < NPL; ++pl)
+              if (rg < rg_end) an[u][rg][pl] = lda_(pl, rg, k + 32 * U + u * 32);
 #pragma unroll
         for (int j = 0; j < NC; ++j) wn[u][j] = ldw(j, k + 32 * U + u * 32);
       }
@@ -411,7 +419,7 @@ __global__ __launch_bounds__(KS * 64) void k_skinny(GemmArgs ga, SeqTable st) {
         for (int pl = 0; pl < NPL; ++pl) {
           bf16x8 a;
           if constexpr (APF)
-            a = af[u][0][pl];
+            a = af[u][rg][pl];
           else
             a = lda_(pl, rg, k + u * 32);
 #pragma unroll
@@ -426,7 +434,9 @@ __global__ __launch_bounds__(KS * 64) void k_skinny(GemmArgs ga, SeqTable st) {
         for (int j = 0; j < NC; ++j) wf[u][j] = wn[u][j];
         if constexpr (APF)
 #pragma unroll
-          for (int pl = 0; pl < NPL; ++pl) af[u][0][pl] = an[u][0][pl];
+          for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+            for (int pl = 0; pl < NPL; ++pl) af[u][rg][pl] = an[u][rg][pl];
       }
     }
   }
