@@ -821,7 +821,7 @@ int draft_impl(const dflash_model* model, const dflash_ctx* ctx, const Blocks& b
     model->probe.start(DFLASH_STAGE_QKV, s);
     e = launch_gemm(g, st, Mqp, s);
     if (e == hipSuccess)
-      e = launch_qkv_finish(part, kc_qkv, Mq, Mqp, c.n_q_heads, c.n_kv_heads, c.head_dim, ctx->rope_cos(),
+      e = launch_qkv_finish(part, kc_qkv, Mq, R > 0 ? M : Mq, Mqp, c.n_q_heads, c.n_kv_heads, c.head_dim, ctx->rope_cos(),
                             ctx->rope_sin(), q_hi, q_lo, bk.sep ? bkv : ctx->kv_cache(l),
                             bk.sep ? (int64_t)n : ctx->kv_tiles(), sq, s);
     model->probe.stop(DFLASH_STAGE_QKV, s);

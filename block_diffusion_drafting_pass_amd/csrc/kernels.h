@@ -132,8 +132,10 @@ hipError_t launch_resid_norm(float* x, const float* part, int kc, int part_rows,
 hipError_t launch_reduce_split(const float* part, int kc, int part_rows, int N, u16* out_hi, u16* out_lo, int M,
                                int out_rows, hipStream_t s);
 // Reduce q|k|v partials [kc][Mp][(n_q + 2 n_kv) d]; RoPE on q and k at each
-// row's position; q -> q_hi/lo [row][n_q d]; k, v -> the layer's cache slots.
-hipError_t launch_qkv_finish(const float* part, int kc, int M, int Mp, int n_q, int n_kv, int head_dim,
+// row's position; q -> q_hi/lo [row][n_q d] for rows < q_rows (later rows are
+// appended context rows, which need only their K / V; the few-row GEMM leaves
+// their q partials unwritten); k, v -> the layer's cache slots.
+hipError_t launch_qkv_finish(const float* part, int kc, int M, int q_rows, int Mp, int n_q, int n_kv, int head_dim,
                              const float* rope_cos, const float* rope_sin, u16* q_hi, u16* q_lo,
                              u16* kv_cache, int64_t kv_tiles, const SeqTable& st, hipStream_t s);
 // Reduce all-layer k|v partials [kc][Mp][n_layers 2 n_kv d]; RoPE on k;

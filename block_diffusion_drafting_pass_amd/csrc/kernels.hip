@@ -451,6 +451,7 @@ __global__ __launch_bounds__(KS * 64) void k_skinny(GemmArgs ga, SeqTable st) {
     argmax_tail<RG, NC, KS>(ga.ep, tile0, red, lane, ks);
   } else {
     for (int it = ks; it < RG * NC; it += KS) {
+      if (it / NC >= rg_end) break;  // row groups this workgroup skipped: nothing to store
       f32x4 s = red[0][it][lane];
 #pragma unroll
       for (int q = 1; q < KS; ++q) s += red[q][it][lane];
@@ -1146,8 +1147,8 @@ __global__ __launch_bounds__(256) void k_reduce_split(const float* __restrict__ 
 // One thread per (row, head of [q | k | v], RoPE pair j < d/2).  The chunk
 // partials and the RoPE table entries are loaded together, then summed in
 // chunk order.
-__global__ __launch_bounds__(256) void k_qkv_finish(const float* __restrict__ part, int kc, int M, int Mp,
-                                                    int n_q, int n_kv, int d, const float* __restrict__ rc,
+__global__ __launch_bounds__(256) void k_qkv_finish(const float* __restrict__ part, int kc, int M, int q_rows,
+                                                    int Mp, int n_q, int n_kv, int d, const float* __restrict__ rc,
                                                     const float* __restrict__ rs, u16* __restrict__ q_hi,
                                                     u16* __restrict__ q_lo, u16* __restrict__ kv, int64_t kv_tiles,
                                                     SeqTable st) {
@@ -1156,6 +1157,7 @@ __global__ __launch_bounds__(256) void k_qkv_finish(const float* __restrict__ pa
   if (idx >= M * nh * half) return;
   const int j = idx % half, t = idx / half;
   const int hh = t % nh, row = t / nh;
+  if (hh < n_q && row >= q_rows) return;  // appended context rows: no q
   const int b = seq_of_row(st, row);
   const int pos = st.pos_base[b] + (row - st.row_start[b]);
   const bool rot = hh < n_q + n_kv;
@@ -1680,7 +1682,7 @@ hipError_t launch_reduce_split(const float* part, int kc, int part_rows, int N, 
   return hipGetLastError();
 }
 
-hipError_t launch_qkv_finish(const float* part, int kc, int M, int Mp, int n_q, int n_kv, int head_dim,
+hipError_t launch_qkv_finish(const float* part, int kc, int M, int q_rows, int Mp, int n_q, int n_kv, int head_dim,
                              const float* rope_cos, const float* rope_sin, u16* q_hi, u16* q_lo,
                              u16* kv_cache, int64_t kv_tiles, const SeqTable& st, hipStream_t s) {
   if (M == 0) return hipSuccess;
@@ -1696,8 +1698,8 @@ hipError_t launch_qkv_finish(const float* part, int kc, int M, int Mp, int n_q, 
   }
   if (kc > kMaxKc) return hipErrorInvalidValue;
   const int total = M * (n_q + 2 * n_kv) * (head_dim / 2);
-  hipLaunchKernelGGL(k_qkv_finish, dim3((total + 255) / 256), dim3(256), 0, s, part, kc, M, Mp, n_q, n_kv, head_dim,
-                     rope_cos, rope_sin, q_hi, q_lo, kv_cache, kv_tiles, st);
+  hipLaunchKernelGGL(k_qkv_finish, dim3((total + 255) / 256), dim3(256), 0, s, part, kc, M, q_rows, Mp, n_q, n_kv,
+                     head_dim, rope_cos, rope_sin, q_hi, q_lo, kv_cache, kv_tiles, st);
   return hipGetLastError();
 }
 
