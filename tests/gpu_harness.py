@@ -89,6 +89,8 @@ def assert_parity(gpu_logits: Optional[np.ndarray], gpu_drafts: np.ndarray, ref:
         assert err <= LOGIT_TOL, f"{label}: logits max-abs error {err:.3e} > {LOGIT_TOL}"
     bad = np.argwhere(sure & (gpu_drafts != ref.drafts))
     assert bad.size == 0, f"{label}: drafts differ on rows with gap > {GAP}: {bad[:10].tolist()}"
+    # a case where no row is decided would compare no draft at all
+    assert stats["sure_rows"] >= 1, f"{label}: no row has an oracle top-2 gap above {GAP}"
     say(f"{label}: {stats}")
     return stats
 

@@ -485,3 +485,81 @@ def test_train_anchor_placement_is_valid(seq_len, n, blk, prompt):
     a = I.gen_train_anchors(seq_len, n, blk, seed=1, prompt_len=prompt)
     assert len(a) == n and a[0] >= prompt and a[-1] + blk <= seq_len
     assert np.all(np.diff(a) >= blk)
+
+
+# ----------------------------------------------------------------------------
+# the parity bar's helper (top-2 gap) and context truncation
+# ----------------------------------------------------------------------------
+
+def test_top2_gap_hand_cases():
+    """Gap = largest minus second largest, never negative; a tie at the top
+    gives 0 (so a tied row is never counted as decided)."""
+    x = np.array([[3.0, 1.0, 2.0], [5.0, 5.0, 1.0], [1.0, 2.0, 3.0], [-4.0, -1.0, -2.5],
+                  [0.0, 0.0, 0.0], [7.0, -7.0, 6.5]])
+    assert O.top2_gap(x).tolist() == [1.0, 0.0, 1.0, 1.5, 0.0, 0.5]
+
+
+def test_top2_gap_matches_sorting_on_random_rows():
+    """Against Python's own sort of each row (no numpy partition), over shapes
+    with leading batch axes as the parity checks use them."""
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((3, 5, 97)) * 2.0
+    x[0, 1, 10] = x[0, 1, 20] = 50.0  # an exact tie at the top
+    got = O.top2_gap(x)
+    assert got.shape == (3, 5)
+    for idx in np.ndindex(3, 5):
+        s = sorted(x[idx].tolist())
+        assert got[idx] == s[-1] - s[-2]
+    assert got[0, 1] == 0.0 and np.all(got >= 0.0)
+
+
+def test_truncate_then_reappend_equals_fresh_ingest():
+    """Truncating a sequence to n positions and appending the same features
+    again gives exactly the K/V a context that took the same appends without
+    the detour holds, for every layer, K and V alike; the other sequence is
+    untouched; and the drafts over both contexts are bitwise equal."""
+    spec = I.spec("tiny").with_(ctx_lens=(40, 25))
+    model, _ = _model(spec, 4, std=0.05)
+    fa = I.gen_features(spec, 9, 0, 40)
+    fb = I.gen_features(spec, 9, 1, 25)
+    extra = I.gen_features(spec, 10, 0, 12)
+    ctx = O.OracleContext(model, 2)
+    O.fuse_ctx(model, ctx, 0, fa[:30])
+    O.fuse_ctx(model, ctx, 0, fa[30:])
+    O.fuse_ctx(model, ctx, 1, fb)
+    O.fuse_ctx(model, ctx, 0, extra)          # 52 positions, then take the last 22 back
+    k_before = [k.copy() for k in ctx.k[0]]
+    O.truncate_ctx(ctx, 0, 30)
+    assert ctx.length(0) == 30 and ctx.length(1) == 25
+    for l in range(model.n_layers):
+        assert ctx.k[0][l].shape[0] == 30 and ctx.v[0][l].shape[0] == 30
+        np.testing.assert_array_equal(ctx.k[0][l], k_before[l][:30])
+    O.fuse_ctx(model, ctx, 0, fa[30:])
+    fresh = O.OracleContext(model, 2)
+    O.fuse_ctx(model, fresh, 0, fa[:30])
+    O.fuse_ctx(model, fresh, 0, fa[30:])
+    O.fuse_ctx(model, fresh, 1, fb)
+    for b in range(2):
+        for l in range(model.n_layers):
+            np.testing.assert_array_equal(ctx.k[b][l], fresh.k[b][l])
+            np.testing.assert_array_equal(ctx.v[b][l], fresh.v[b][l])
+    anchors = I.gen_anchors(spec, 9)
+    r1 = O.draft_block(model, ctx, anchors, spec.block)
+    r2 = O.draft_block(model, fresh, anchors, spec.block)
+    np.testing.assert_array_equal(r1.logits, r2.logits)
+
+
+def test_truncate_to_zero_and_to_full_length():
+    spec = I.spec("tiny").with_(ctx_lens=(20,))
+    model, _ = _model(spec, 5, std=0.05)
+    f = I.gen_features(spec, 3, 0, 20)
+    ctx = O.OracleContext(model, 1)
+    O.fuse_ctx(model, ctx, 0, f)
+    full = [(k.copy(), v.copy()) for k, v in zip(ctx.k[0], ctx.v[0])]
+    O.truncate_ctx(ctx, 0, 20)  # no-op
+    for l, (k, v) in enumerate(full):
+        np.testing.assert_array_equal(ctx.k[0][l], k)
+        np.testing.assert_array_equal(ctx.v[0][l], v)
+    O.truncate_ctx(ctx, 0, 0)
+    assert ctx.length(0) == 0
+    assert all(k.shape[0] == 0 for k in ctx.k[0]) and all(v.shape[0] == 0 for v in ctx.v[0])
