@@ -495,8 +495,15 @@ size_t dflash_workspace_bytes(const dflash_model* model, int32_t n_seqs, int32_t
   return ws_layout(&model->cfg, n_seqs, block, max_new_tokens).total();
 }
 
-int dflash_fuse_ctx(const dflash_model* model, dflash_ctx* ctx, const void* features, const int32_t* n_new,
-                    void* ws, size_t ws_bytes, dflash_stream stream) {
+}  // extern "C"
+
+namespace {
+
+// Validate and enqueue an append (fusion, then every layer's injected K/V at
+// positions length(b) ..) without changing any length: the caller advances
+// the lengths once every launch of its call is enqueued.
+int fuse_impl(const dflash_model* model, dflash_ctx* ctx, const void* features, const int32_t* n_new, void* ws,
+              size_t ws_bytes, hipStream_t s) {
   if (!model || !ctx) return fail(DFLASH_EINVAL, "model or ctx is NULL");
   if (!same_config(model->cfg, ctx->cfg)) return fail(DFLASH_ESHAPE, "ctx was created for another configuration");
   if (!n_new) return fail(DFLASH_EINVAL, "n_new is NULL");
@@ -518,7 +525,6 @@ int dflash_fuse_ctx(const dflash_model* model, dflash_ctx* ctx, const void* feat
   if (ws_bytes < W.ingest_end)
     return fail(DFLASH_EWORKSPACE, "workspace holds %zu bytes, %zu needed", ws_bytes, W.ingest_end);
 
-  hipStream_t s = (hipStream_t)stream;
   char* wsb = (char*)ws;
   u16* h_hi = (u16*)(wsb + W.h_hi);
   u16* h_lo = (u16*)(wsb + W.h_lo);
@@ -602,6 +608,17 @@ int dflash_fuse_ctx(const dflash_model* model, dflash_ctx* ctx, const void* feat
       if (e != hipSuccess) return hip_fail(e, "fuse_ctx: K/V projection");
     }
   }
+  return DFLASH_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dflash_fuse_ctx(const dflash_model* model, dflash_ctx* ctx, const void* features, const int32_t* n_new,
+                    void* ws, size_t ws_bytes, dflash_stream stream) {
+  const int rc = fuse_impl(model, ctx, features, n_new, ws, ws_bytes, (hipStream_t)stream);
+  if (rc) return rc;
   for (int b = 0; b < ctx->n_seqs; ++b) ctx->len[b] += n_new[b];
   return DFLASH_OK;
 }
@@ -1023,15 +1040,19 @@ int step_impl(const dflash_model* model, dflash_ctx* ctx, const void* features, 
   const WsLayout W = ws_layout(&c, n, block, total);
   if (ws_bytes < W.total()) return fail(DFLASH_EWORKSPACE, "workspace holds %zu bytes, %zu needed", ws_bytes, W.total());
   const int M = n * block;
-  if (total == 0 || M > 32 || M + total > 32) {
-    // too many rows for one fused weight sweep: append, then draft
-    rc = dflash_fuse_ctx(model, ctx, features, n_new, ws, ws_bytes, stream);
-    if (rc) return rc;
-    return smp ? dflash_draft_sample(model, ctx, anchors, block, smp, draft, logits, ws, ws_bytes, stream)
-               : dflash_draft_block(model, ctx, anchors, block, draft, logits, ws, ws_bytes, stream);
-  }
   std::vector<int64_t> lens(n);
   for (int b = 0; b < n; ++b) lens[b] = ctx->len[b] + n_new[b];
+  if (total == 0 || M > 32 || M + total > 32) {
+    // too many rows for one fused weight sweep: append, then draft at the
+    // new lengths; the lengths change only once both are enqueued
+    rc = fuse_impl(model, ctx, features, n_new, ws, ws_bytes, (hipStream_t)stream);
+    if (rc) return rc;
+    rc = draft_impl(model, ctx, seq_blocks(ctx, lens.data()), anchors, nullptr, block, draft, logits, (char*)ws, W,
+                    (hipStream_t)stream, nullptr, smp);
+    if (rc) return rc;
+    ctx->len = lens;
+    return DFLASH_OK;
+  }
   Append ap;
   ap.features = (const u16*)features;
   ap.R = (int)total;
