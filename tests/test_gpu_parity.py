@@ -110,7 +110,9 @@ def test_tiny_config(torch_cuda):
 
 
 @pytest.mark.parametrize("lens,block,jitter,std,label", [
-    ((0,), 16, 0.0, 0.02, "empty context"),
+    # the benchmark's 0.02 weights leave every row of the tiny drafter's
+    # context-free pass within 0.04 of its runner-up, so nothing would be decided
+    ((0,), 16, 0.0, 0.05, "empty context"),
     ((37, 5, 0), 4, 0.0, 0.05, "ragged 3 seqs B4"),
     ((10, 20), 16, 0.0, 0.05, "two seqs M32 skinny"),
     ((100, 64, 33), 16, 0.0, 0.05, "three seqs M48 tiled"),
