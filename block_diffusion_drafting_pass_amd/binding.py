@@ -23,7 +23,8 @@ EXPORTS = ("dflash_weight_count", "dflash_model_create", "dflash_model_destroy",
            "dflash_model_pack", "dflash_ctx_bytes",
            "dflash_ctx_create", "dflash_ctx_destroy", "dflash_ctx_length", "dflash_ctx_truncate",
            "dflash_workspace_bytes", "dflash_fuse_ctx", "dflash_draft_block", "dflash_draft_refine", "dflash_draft_anchored", "dflash_draft_sample",
-    "dflash_verify_workspace_bytes", "dflash_verify_sample", "dflash_step", "dflash_step_sample", "dflash_accept_len",
+    "dflash_verify_workspace_bytes", "dflash_verify_sample", "dflash_step", "dflash_step_noalloc",
+           "dflash_step_sample", "dflash_accept_len",
            "dflash_probe_arm", "dflash_probe_read", "dflash_status_str", "dflash_last_error")
 
 # Stages a measurement probe can bracket (dflash_stage in include/dflash.h).
@@ -104,6 +105,8 @@ def lib():
         L.dflash_verify_sample.restype = ctypes.c_int
         L.dflash_step.argtypes = [vp, vp, vp, ctypes.POINTER(i32), vp, i32, vp, vp, vp, sz, vp]
         L.dflash_step.restype = ctypes.c_int
+        L.dflash_step_noalloc.argtypes = [vp, vp, vp, ctypes.POINTER(i32), vp, i32, vp, vp, vp]
+        L.dflash_step_noalloc.restype = ctypes.c_int
         L.dflash_accept_len.argtypes = [vp, vp, i32, i32, vp, vp, vp]
         L.dflash_accept_len.restype = ctypes.c_int
         L.dflash_probe_arm.argtypes = [vp, ctypes.c_int, i32]
@@ -321,6 +324,18 @@ def step(model: Model, ctx: Context, features, n_new: Sequence[int], anchors, bl
     arr = (ctypes.c_int32 * ctx.n_seqs)(*[int(v) for v in n_new])
     check(lib().dflash_step(model.handle, ctx.handle, _ptr(features), arr, _ptr(anchors), block, _ptr(draft),
                             _ptr(logits), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    return draft
+
+
+def step_noalloc(model: Model, ctx: Context, features, n_new: Sequence[int], anchors, block: int, draft=None,
+                 logits=None, stream=None):
+    """dflash_step without a workspace argument: the library's static device scratch."""
+    import torch
+    if draft is None:
+        draft = torch.empty((ctx.n_seqs, block - 1), dtype=torch.int32, device=anchors.device)
+    arr = (ctypes.c_int32 * ctx.n_seqs)(*[int(v) for v in n_new])
+    check(lib().dflash_step_noalloc(model.handle, ctx.handle, _ptr(features), arr, _ptr(anchors), block,
+                                    _ptr(draft), _ptr(logits), _stream(stream)))
     return draft
 
 

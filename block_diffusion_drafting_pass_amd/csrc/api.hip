@@ -7,6 +7,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -1065,9 +1066,68 @@ int step_impl(const dflash_model* model, dflash_ctx* ctx, const void* features, 
   return DFLASH_OK;
 }
 
+// Device scratch of dflash_step_noalloc.  Each GPU the library runs on holds
+// its own copy until the process ends.  In host code the array's name is
+// only a stand-in for the symbol: device_scratch() asks the runtime for the
+// current device's copy once per device (hipGetSymbolAddress) and every
+// launch receives that pointer.
+static __device__ __align__(256) unsigned char scratch[DFLASH_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+struct DeviceScratch {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+DeviceScratch g_scratch[kMaxDevices];
+
+// This device's copy of `scratch` (the current device, which must be the
+// stream's device).
+int device_scratch(hipStream_t s, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "step_noalloc: hipGetDevice");
+  if (s) {
+    hipDevice_t sd = -1;
+    e = hipStreamGetDevice(s, &sd);
+    if (e != hipSuccess) return hip_fail(e, "step_noalloc: hipStreamGetDevice");
+    if (sd != dev) return fail(DFLASH_EINVAL, "stream belongs to device %d but device %d is current", (int)sd, dev);
+  }
+  if (dev < 0 || dev >= kMaxDevices) return fail(DFLASH_EUNSUPPORTED, "device %d outside [0, %d)", dev, kMaxDevices);
+  DeviceScratch& d = g_scratch[dev];
+  std::call_once(d.once, [&d] { d.err = hipGetSymbolAddress(&d.ptr, HIP_SYMBOL(scratch)); });
+  if (d.err != hipSuccess) return hip_fail(d.err, "step_noalloc: hipGetSymbolAddress");
+  if (!d.ptr) return fail(DFLASH_EHIP, "step_noalloc: no address for the device scratch");
+  *out = d.ptr;
+  return DFLASH_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int dflash_step_noalloc(const dflash_model* model, dflash_ctx* ctx, const void* features, const int32_t* n_new,
+                        const int32_t* anchors, int32_t block, int32_t* draft, float* logits, dflash_stream stream) {
+  // the size check comes first, so an oversized request never touches the device
+  if (!model || !ctx) return fail(DFLASH_EINVAL, "model or ctx is NULL");
+  if (!n_new) return fail(DFLASH_EINVAL, "n_new is NULL");
+  if (block < 2 || block > model->cfg.max_block)
+    return fail(DFLASH_EINVAL, "block %d outside [2, %d]", block, model->cfg.max_block);
+  int64_t total = 0;
+  for (int b = 0; b < ctx->n_seqs; ++b) {
+    if (n_new[b] < 0) return fail(DFLASH_EINVAL, "n_new[%d] < 0", b);
+    total += n_new[b];
+  }
+  const size_t need = ws_layout(&model->cfg, ctx->n_seqs, block, total).total();
+  if (need > DFLASH_NOALLOC_SCRATCH_BYTES)
+    return fail(DFLASH_EWORKSPACE, "this step needs %zu bytes of scratch; the static device scratch holds %zu", need,
+                (size_t)DFLASH_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  const int rc = device_scratch((hipStream_t)stream, &ws);
+  if (rc) return rc;
+  return step_impl(model, ctx, features, n_new, anchors, block, nullptr, draft, logits, ws,
+                   DFLASH_NOALLOC_SCRATCH_BYTES, stream);
+}
 
 int dflash_step(const dflash_model* model, dflash_ctx* ctx, const void* features, const int32_t* n_new,
                 const int32_t* anchors, int32_t block, int32_t* draft, float* logits, void* ws, size_t ws_bytes,

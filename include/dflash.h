@@ -22,7 +22,10 @@
  *   - Every device pointer is owned by the caller (e.g. allocated through
  *     PyTorch).  The library never allocates, frees or retains device memory;
  *     the host descriptors it creates (dflash_model, dflash_ctx) hold only
- *     pointers into caller memory and host-side metadata.
+ *     pointers into caller memory and host-side metadata.  The one exception
+ *     is the fixed-size static scratch of dflash_step_noalloc, a device array
+ *     in the library's code object that the runtime places on each GPU the
+ *     library runs on.
  *   - Calls are stream-ordered and asynchronous: they enqueue kernels on the
  *     given stream and return.  Only dflash_ctx_create waits for its own
  *     stream (it uploads a host-computed RoPE table).
@@ -287,6 +290,31 @@ int dflash_draft_anchored(const dflash_model* model, const dflash_ctx* ctx, int3
 int dflash_step(const dflash_model* model, dflash_ctx* ctx, const void* features, const int32_t* n_new,
                 const int32_t* anchors, int32_t block, int32_t* draft, float* logits, void* ws, size_t ws_bytes,
                 dflash_stream stream);
+
+/* Bytes of the library-held device scratch of dflash_step_noalloc (per GPU). */
+#define DFLASH_NOALLOC_SCRATCH_BYTES ((size_t)48 << 20)
+
+/* dflash_step for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.  It
+ * takes no workspace argument: its kernels use a scratch array of
+ * DFLASH_NOALLOC_SCRATCH_BYTES (48 MiB) that the library holds in device
+ * memory, one copy per GPU it runs on, kept until the process ends.  The call
+ * itself allocates nothing (no hipMalloc, no allocating library routine);
+ * its first call on a device looks up that device's copy.  The caller still
+ * passes every input and output as for dflash_step, and the results are the
+ * same.  Enough for decode-sized steps: one or two sequences at block 16, or
+ * one at block 32, of the 5-layer hidden-4096 drafter.
+ *   - Larger steps (dflash_workspace_bytes(model, n_seqs, block, sum n_new)
+ *     above the limit) are rejected with DFLASH_EWORKSPACE before any work is
+ *     enqueued.
+ *   - `stream` must belong to the current device (DFLASH_EINVAL otherwise).
+ *   - Every call on one GPU shares that GPU's scratch and leaves its contents
+ *     behind; no kernel reads a scratch byte its own call has not written.
+ *     Calls that overlap on one GPU (different streams or host threads) race
+ *     on it: serialise them.
+ * Other errors as for dflash_step. */
+int dflash_step_noalloc(const dflash_model* model, dflash_ctx* ctx, const void* features, const int32_t* n_new,
+                        const int32_t* anchors, int32_t block, int32_t* draft, float* logits, dflash_stream stream);
 
 /* dflash_step with sampled drafts (as dflash_draft_sample). */
 int dflash_step_sample(const dflash_model* model, dflash_ctx* ctx, const void* features, const int32_t* n_new,
