@@ -241,6 +241,23 @@ def test_q8_ragged_b32(q8):
     _q8_case(q8, "q8b_l3_b32_ragged", seqs=seqs, label="3-layer ragged B32")
 
 
+def _short_ragged(seed, n, lo=64, hi=300):
+    rng = np.random.default_rng(seed)
+    return tuple(int(v) for v in rng.integers(lo, hi + 1, size=n))
+
+
+def test_q8_conc32_every_sequence(q8):
+    # the 32-sequence shape (512 block rows on the many-row kernels) over
+    # short ragged contexts, so that the oracle runs every sequence
+    _q8_case(q8, "q8b_conc32", label="5-layer 32 seqs short ctx, all compared", ctx_lens=_short_ragged(77, 32))
+
+
+def test_q8_l3_b32_every_sequence(q8):
+    # the 3-layer block-32 batch of eight sequences, every sequence compared
+    _q8_case(q8, "q8b_l3_b32_ragged", label="3-layer B32 8 seqs short ctx, all compared",
+             ctx_lens=_short_ragged(78, 8))
+
+
 # ----------------------------------------------------------------------------
 # dflash_step: append + draft in one call (fused weight sweep when <= 32 rows)
 # ----------------------------------------------------------------------------
