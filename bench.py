@@ -42,11 +42,18 @@ Inputs are seeded synthetic tensors already resident in HBM.  The default
 workload is the 5-layer Qwen3-8B-shaped drafter at context 1024, block 16,
 one sequence.
 
-Printed (stdout, one JSON line): draft tokens/s over the K timed steps, the
-roofline fraction of the dominant kernel (the LM head), timed live with HIP
-events that the library records around that kernel's launches on the same
-stream, and the CPU oracle timed on the host cores on a bounded sample.
-Progress goes to stderr.
+Printed (stdout, one JSON line): draft tokens/s over the K timed steps (two
+events around the K steps and nothing else recorded between them), the
+per-step p10 / p50 / p90 from a second loop of K steps, the roofline fraction
+of the dominant kernel (the LM head), timed live with HIP events that the
+library records around that kernel's launches on the same stream in a third
+loop, and the CPU oracle timed on the host cores on a bounded sample.  For the
+decode workloads the line also carries the draft pass alone over the resident
+context (phase_d: dflash_draft_block + dflash_accept_len, K more iterations)
+with its fractions of HBM and bf16 matrix-core peak, the executed matrix-core
+fraction and busy share when a rocprofv3 counter summary of the current
+kernels is committed, and the pass-level aim with whether it is met
+(pass_target).  Progress goes to stderr.
 """
 from __future__ import annotations
 
@@ -66,6 +73,10 @@ if ROOT not in sys.path:
 METRIC = "draft tokens/sec at block 16, 5-layer, ctx 1024, conc 1; % HBM/MFMA peak"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, datasheet
 MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 matrix peak, datasheet (no sparsity)
+# Pass-level aims of the draft pass alone over a resident context (phase D):
+# the single-sequence workloads are weight-streaming (fraction of HBM peak),
+# the 32-sequence one is matrix-core work (algorithmic bf16 fraction).
+PASS_TARGETS = {"q8b_ctx1024": ("hbm", 0.60), "q8b_ctx8192": ("hbm", 0.60), "q8b_conc32": ("mfma", 0.40)}
 
 
 def log(msg: str) -> None:
@@ -403,6 +414,67 @@ def copy_bandwidth(torch, nbytes=1 << 30, reps=10) -> float:
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
+def time_steps(torch, run, steps: int):
+    """Mean ms per step over `steps` back-to-back calls, bracketed by two events."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps, (time.perf_counter() - w0) / steps * 1e3
+
+
+def step_spread(torch, run, steps: int):
+    """p10 / p50 / p90 of the per-step time (ms), one event between every two
+    steps (a separate loop, so the headline timing carries no extra events)."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for i in range(steps):
+        run()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    t = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
+    return {"p10_ms": round(float(np.percentile(t, 10)), 4), "p50_ms": round(float(np.percentile(t, 50)), 4),
+            "p90_ms": round(float(np.percentile(t, 90)), 4)}
+
+
+def measured_counters(workload: str):
+    """(executed bf16 flops per draft pass, MFMA busy share) from the committed
+    rocprofv3 counter summary of this workload's draft pass, while the kernel
+    sources are unchanged since it was taken; else None."""
+    from block_diffusion_drafting_pass_amd import profsum
+    got = profsum.read_counters(os.path.join(ROOT, "profiles", f"mfma_{workload}_counters.txt"))
+    if got is None or got[2] != profsum.kernel_sources_sha256():
+        return None
+    return got[0], got[1]
+
+
+def host_description() -> str:
+    """CPU model and the BLAS library numpy runs on (for the oracle baseline)."""
+    cpu = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    cpu = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = "unknown BLAS"
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if libs:
+            blas = f"{libs[0].get('internal_api', '?')} {libs[0].get('version', '')}".strip()
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        pass
+    return f"CPU {cpu}, BLAS {blas}"
+
+
 # ----------------------------------------------------------------------------
 # CPU oracle baseline
 # ----------------------------------------------------------------------------
@@ -460,7 +532,7 @@ def cpu_baseline(spec, weights, ws_target_s=10.0, max_reps=8, draft_only=False):
         "sample": (f"{len(times)} oracle step(s) of sequence 0 ({'' if draft_only else f'append {blk}, '}draft, "
                    f"accept; context {c}), "
                    f"numpy float64, median {t:.2f} s/step; {len(os.sched_getaffinity(0))} host CPUs visible, "
-                   f"{platform.processor() or platform.machine()}"),
+                   f"{host_description()}"),
     }, res
 
 
@@ -487,7 +559,7 @@ def cpu_baseline_ingest(spec, weights, max_pos=512):
         "kind": "oracle",
         "sample": (f"{len(times)} oracle ingest(s) of the first {T} positions of sequence 0 (fusion + every layer's "
                    f"K/V), numpy float64, median {t:.2f} s; {len(os.sched_getaffinity(0))} host CPUs visible, "
-                   f"{platform.processor() or platform.machine()}"),
+                   f"{host_description()}"),
     }
 
 
@@ -518,7 +590,7 @@ def cpu_baseline_train(spec, weights, wl, n_blk=2):
         "sample": (f"sequence 0: ingest of {T} positions ({t_ing:.1f} s) and {len(sel)} of its "
                    f"{spec.train_blocks} anchored blocks ({t_blk:.1f} s), extrapolated to all its blocks; numpy "
                    f"float64; {len(os.sched_getaffinity(0))} host CPUs visible, "
-                   f"{platform.processor() or platform.machine()}"),
+                   f"{host_description()}"),
     }, res, sel
 
 
@@ -617,7 +689,6 @@ def main(argv=None) -> int:
     n_launch = 64 * S if (train or ingest) else {"lm_head": S, "fusion": 1}.get(args.probe, spec.n_layers * S)
     run = wl.step
     if args.graph:
-        # the probe's events are not captured: arm it after capture only for eager replays
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             wl.step()
@@ -625,25 +696,37 @@ def main(argv=None) -> int:
         for _ in range(3):
             g.replay()
         run = g.replay
-    else:
-        B_.probe_arm(wl.model, args.probe, n_launch * args.steps)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    w0 = time.perf_counter()
-    e0.record()
+    # the headline: K steps between two events, nothing else recorded
+    ms_step, wall_ms = time_steps(torch, run, args.steps)
+    log(f"{args.steps} steps: {ms_step:.3f} ms/step (wall {wall_ms:.3f} ms/step)")
+    spread = step_spread(torch, run, args.steps)
+    log(f"per-step spread over another {args.steps} steps: {spread}")
+    # the dominant kernel: library events around its launches, on eager steps
+    # of their own (the probe's events are not captured into graphs)
+    B_.probe_arm(wl.model, args.probe, n_launch * args.steps)
     for _ in range(args.steps):
-        run()
-    e1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    ms_step = e0.elapsed_time(e1) / args.steps
-    if args.graph:
-        # time the dominant kernel on eager steps right after the graph replays
-        B_.probe_arm(wl.model, args.probe, n_launch * args.steps)
-        for _ in range(args.steps):
-            wl.step()
+        wl.step()
     probe_ms, probe_n, probe_missed = B_.probe_read(wl.model)
-    log(f"{args.steps} steps: {ms_step:.3f} ms/step (wall {wall * 1e3 / args.steps:.3f} ms/step)")
+
+    # the draft pass alone over the resident context (phase D): after one step
+    # every context position is ingested; each iteration is dflash_draft_block
+    # + dflash_accept_len, which change no length
+    phase_d = None
+    decode = not (train or ingest)
+    if decode and not draft_only and S == 1 and args.temperature == 0:
+        wl.step()
+
+        def run_d():
+            B_.draft_block(wl.model, wl.ctx, wl.anchors, spec.block, wl.ws, draft=wl.draft)
+            B_.accept_len(wl.draft, wl.target, spec.block, wl.accept, wl.next_anchor)
+
+        for _ in range(args.warmup):
+            run_d()
+        d_ms, _ = time_steps(torch, run_d, args.steps)
+        phase_d = {"ms_per_step": round(d_ms, 4), **step_spread(torch, run_d, args.steps)}
+        log(f"draft pass alone: {d_ms:.3f} ms/step; {phase_d}")
+    elif decode and draft_only:
+        phase_d = {"ms_per_step": round(ms_step, 4), **spread}
 
     n, blk = spec.n_seqs, spec.block
     n_units = wl.n_blocks if train else n
@@ -680,6 +763,22 @@ def main(argv=None) -> int:
     roof.update({"traffic": measured_traffic(spec.name, args.probe), "kernel": args.probe,
                  "avg_launch_ms": round(avg_ms, 4), "launches_timed": probe_n, "alg_bytes_per_launch": pb,
                  "alg_flops_per_launch": pf})
+
+    pass_target = None
+    if phase_d is not None:
+        pbd, pfd = pass_work(spec)
+        t_d = phase_d["ms_per_step"] * 1e-3
+        phase_d.update({"draft_tok_s": round(n * (blk - 1) / t_d, 1), "alg_bytes": pbd, "alg_flops": pfd,
+                        "hbm_frac": round(pbd / t_d / (HBM_PEAK_GBS * 1e9), 4),
+                        "mfma_frac": round(pfd / t_d / (MFMA_BF16_PEAK_TFS * 1e12), 5)})
+        ctr = measured_counters(spec.name)
+        phase_d["exec_mfma_frac"] = None if ctr is None else round(ctr[0] / t_d / (MFMA_BF16_PEAK_TFS * 1e12), 4)
+        phase_d["mfma_busy"] = None if ctr is None else round(ctr[1], 4)
+        if spec.name in PASS_TARGETS:
+            bound, aim = PASS_TARGETS[spec.name]
+            frac = phase_d["hbm_frac"] if bound == "hbm" else phase_d["mfma_frac"]
+            pass_target = {"phase": "D (draft pass + accept over a resident context)", "bound": bound,
+                           "frac": frac, "target": aim, "met": bool(frac >= aim)}
 
     breakdown = None
     if args.breakdown:
@@ -781,6 +880,9 @@ def main(argv=None) -> int:
             "parallelism": "single GPU",
             "packed_weights": not args.no_pack,
         },
+        "step_spread": spread,
+        "phase_d": phase_d,
+        "pass_target": pass_target,
         "blocks_per_s": round(n_units / (ms_step * 1e-3), 1),
         "step_alg_bytes": by,
         "step_alg_flops": fl,

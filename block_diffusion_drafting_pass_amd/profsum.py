@@ -3,6 +3,7 @@
     python -m block_diffusion_drafting_pass_amd.profsum trace KERNEL_STATS_CSV OUT_TXT --cmd "..."
     python -m block_diffusion_drafting_pass_amd.profsum traffic FETCH_CSV WRITE_CSV OUT_TXT \
         --kernel SUBSTRING --copy-bytes N --cmd "..." --cmd "..."
+    python -m block_diffusion_drafting_pass_amd.profsum counters PMC_CSV OUT_TXT [--simds N] --cmd "..."
 
 ``trace`` lists every kernel of a ``--kernel-trace --stats`` run (calls,
 average / min / max duration, share of GPU time).  ``traffic`` takes two
@@ -10,8 +11,12 @@ average / min / max duration, share of GPU time).  ``traffic`` takes two
 plain device-to-device copy of ``--copy-bytes`` bytes that bench.py makes
 before its timed region, derives from it the factor between what each counter
 reads and the bytes actually moved, and applies that factor to the chosen
-kernel.  The summary records a hash of the kernel sources so that bench.py
-only reports the traffic while the kernels are unchanged.
+kernel.  ``counters`` takes one ``--pmc SQ_INSTS_VALU_MFMA_MOPS_BF16
+SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE`` run and sums, per draft pass, the
+bf16 matrix-core flops the kernels executed (hi/lo products and padding rows
+included) and the share of SIMD cycles the matrix cores were busy.  The
+summaries record a hash of the kernel sources so that bench.py only reports
+their figures while the kernels are unchanged.
 """
 from __future__ import annotations
 
@@ -91,6 +96,94 @@ def traffic(fetch_csv: str, write_csv: str, out: str, kernel: str, copy_bytes: i
         f.write("\n".join(lines) + "\n")
 
 
+def _is_lm_head(name: str) -> bool:
+    # the LM head is the GEMM instance with the argmax epilogue (first template argument 1)
+    return "k_skinny<1," in name or "k_gemm_dl<1," in name
+
+
+def _agent_gpu(csv_path: str):
+    """(SIMDs, XCDs) of the GPU from the run_agent_info.csv beside a counter file, or None."""
+    path = os.path.join(os.path.dirname(csv_path), "run_agent_info.csv")
+    if not os.path.exists(path):
+        return None
+    for r in csv.DictReader(open(path)):
+        if r.get("Agent_Type") == "GPU":
+            return int(r["Simd_Count"]), int(r["Num_Xcc"])
+    return None
+
+
+def counters(csv_path: str, out: str, cmds: List[str], simds: int, xcds: int) -> None:
+    """Executed matrix-core work per draft pass from one --pmc run with
+    SQ_INSTS_VALU_MFMA_MOPS_BF16, SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE.
+    A pass is every library kernel dispatched after one LM-head dispatch up
+    to and including the next (setup work before the first LM head, such as
+    the context ingest and the weight packing, is left out); figures are
+    averages over those passes.  The one-time weight packing is left out
+    wherever it falls.  rocprofv3 sums GRBM_GUI_ACTIVE over the XCDs, so the
+    GPU's active cycles are that sum over the XCD count."""
+    got = _agent_gpu(csv_path)
+    if got is not None:
+        simds, xcds = got
+    disp = {}
+    for r in csv.DictReader(open(csv_path)):
+        d = disp.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"], "c": {},
+                                                     "t": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+        d["c"][r["Counter_Name"]] = d["c"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    order = [disp[k] for k in sorted(disp)
+             if "dflash::" in disp[k]["name"] and "k_pack_weights" not in disp[k]["name"]]
+    heads = [i for i, d in enumerate(order) if _is_lm_head(d["name"])]
+    if len(heads) < 2:
+        raise SystemExit("fewer than two LM-head dispatches: no whole pass in the counter file")
+    passes = len(heads) - 1
+    per = {}
+    for d in order[heads[0] + 1:heads[-1] + 1]:
+        e = per.setdefault(d["name"], {"n": 0, "mops": 0.0, "busy": 0.0, "active": 0.0, "t": 0})
+        e["n"] += 1
+        e["mops"] += d["c"].get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0)
+        e["busy"] += d["c"].get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
+        e["active"] += d["c"].get("GRBM_GUI_ACTIVE", 0.0) / xcds
+        e["t"] += d["t"]
+    tot_flops = sum(e["mops"] for e in per.values()) * 512.0 / passes
+    tot_busy = sum(e["busy"] for e in per.values())
+    tot_active = sum(e["active"] for e in per.values())
+    tot_t = sum(e["t"] for e in per.values()) / passes
+    lines = ["# executed matrix-core work of one draft pass from rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 "
+             "SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE",
+             "# (bf16 MFMA flops = MOPS x 512; MFMA busy = busy cycles / (active cycles x SIMDs), the active",
+             "# cycles being GRBM_GUI_ACTIVE summed over the XCDs divided by their count)",
+             "# command(s):"]
+    lines += [f"#   {c}" for c in cmds]
+    lines += [f"kernel_sources_sha256: {kernel_sources_sha256()}",
+              f"passes: {passes}",
+              f"simds: {simds}",
+              f"xcds: {xcds}",
+              f"exec_bf16_flops_per_pass: {tot_flops:.6e}",
+              f"mfma_busy_pass: {tot_busy / max(tot_active * simds, 1.0):.4f}",
+              f"profiled_kernel_us_per_pass: {tot_t / 1e3:.1f}",
+              f"{'per_pass':>8} {'exec_GFLOP':>11} {'busy':>6} {'us':>8}  kernel"]
+    for name, e in sorted(per.items(), key=lambda kv: -kv[1]["mops"]):
+        lines.append(f"{e['n'] / passes:8.1f} {e['mops'] * 512.0 / passes / 1e9:11.2f} "
+                     f"{e['busy'] / max(e['active'] * simds, 1.0):6.3f} {e['t'] / passes / 1e3:8.1f}  {name[:140]}")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def read_counters(path: str):
+    """(exec_bf16_flops_per_pass, mfma_busy_pass, kernel_sources_sha256) from a counters summary, or None."""
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for ln in open(path):
+        if ln.startswith("#") or ":" not in ln:
+            continue
+        k, v = ln.split(":", 1)
+        kv[k.strip()] = v.strip()
+    try:
+        return float(kv["exec_bf16_flops_per_pass"]), float(kv["mfma_busy_pass"]), kv["kernel_sources_sha256"]
+    except KeyError:
+        return None
+
+
 def read_traffic(path: str):
     """(traffic_bytes_per_dispatch, kernel_sources_sha256) from a traffic summary, or None."""
     if not os.path.exists(path):
@@ -121,9 +214,18 @@ def main(argv=None) -> None:
     p.add_argument("--kernel", required=True)
     p.add_argument("--copy-bytes", type=int, default=1 << 30)
     p.add_argument("--cmd", action="append", default=[])
+    c = sub.add_parser("counters")
+    c.add_argument("pmc_csv")
+    c.add_argument("out")
+    c.add_argument("--simds", type=int, default=1024, help="SIMDs of the GPU (MI355X: 256 CUs x 4), if the "
+                   "run_agent_info.csv beside the counter file does not give them")
+    c.add_argument("--xcds", type=int, default=8, help="XCDs of the GPU (MI355X: 8), likewise")
+    c.add_argument("--cmd", action="append", default=[])
     a = ap.parse_args(argv)
     if a.mode == "trace":
         trace(a.stats_csv, a.out, a.cmd)
+    elif a.mode == "counters":
+        counters(a.pmc_csv, a.out, a.cmd, a.simds, a.xcds)
     else:
         traffic(a.fetch_csv, a.write_csv, a.out, a.kernel, a.copy_bytes, a.cmd)
 
