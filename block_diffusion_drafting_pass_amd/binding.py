@@ -157,12 +157,20 @@ class Model:
         """Write the packed weight copy (dflash_model_pack) into a buffer kept here."""
         import torch
         n = self.pack_bytes()
+        old = getattr(self, "_packed", None)
+        if old is not None:
+            torch.cuda.synchronize()  # passes already queued may still read the old copy
         self._packed = torch.empty(n, dtype=torch.uint8, device=device)
         check(lib().dflash_model_pack(self.handle, _ptr(self._packed), n, _stream(stream)))
 
     def unpack(self) -> None:
         """Go back to the original (row-major) weights."""
+        import torch
         check(lib().dflash_model_pack(self.handle, None, 0, _stream(None)))
+        if getattr(self, "_packed", None) is not None:
+            # queued passes (on any stream) may still read the packed copy:
+            # wait for them before its memory returns to the allocator
+            torch.cuda.synchronize()
         self._packed = None
 
     def close(self) -> None:

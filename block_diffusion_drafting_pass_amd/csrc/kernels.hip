@@ -722,11 +722,21 @@ __global__ __launch_bounds__(NW * 64) void k_attn_tiles(const u16* __restrict__ 
   constexpr int DS = D / 32, DT = D / 16;
   __shared__ u32x4 lds[TILE_CH];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // grid (kv head x split, unit).  The unit index comes straight from the
+  // launch, so its table entries are read together with the other kernel
+  // arguments: the prologue waits for argument memory once, not once per
+  // dependent lookup.  The wave index is the same on every lane of a wave,
+  // which keeps the per-wave lookups scalar.
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 15, g = lane >> 4;
-  const int s = blockIdx.x % splits;
-  const int pair = blockIdx.x / splits;
-  const int gkv = pair % n_kv, unit = pair / n_kv;  // unit: the block, or the group of blocks
+  const int unit = blockIdx.y;  // the block, or the group of blocks
+  int u_pos = 0, u_row = 0, u_slot = 0;
+  if constexpr (!GRP) {
+    u_pos = st.pos_base[unit];
+    u_row = st.row_start[unit];
+    u_slot = st.slot_base[unit];
+  }
+  const int s = blockIdx.x % splits, gkv = blockIdx.x / splits;
   const int G = n_q / n_kv, HG = G / HPW, qtiles = (block + 15) / 16, upb = HG * qtiles;
   // HV (one block per unit): waves upb .. 2 upb - 1 take the second 32 keys
   // of every tile for the same query units, and the two halves' (m, l, O)
@@ -754,14 +764,15 @@ __global__ __launch_bounds__(NW * 64) void k_attn_tiles(const u16* __restrict__ 
     for (int j = 0; j < nb; ++j)
       maxct = max(maxct, (st.pos_base[grp.member[unit][j]] + kTileKeys - 1) / kTileKeys);
   } else {
-    maxct = (st.pos_base[unit] + (sep ? 0 : block) + kTileKeys - 1) / kTileKeys;
+    maxct = (u_pos + (sep ? 0 : block) + kTileKeys - 1) / kTileKeys;
   }
-  const int n_keys = comp ? st.pos_base[b] + (sep ? 0 : block) : 0;
+  // one-block units: b is the unit whenever comp holds
+  const int n_keys = comp ? (GRP ? st.pos_base[b] : u_pos) + (sep ? 0 : block) : 0;
   const int ntile = maxct + (sep ? nb : 0);
   const int tps = (ntile + splits - 1) / splits;
   const int t0 = s * tps, t1 = min(ntile, t0 + tps);
   const u32x4* src = reinterpret_cast<const u32x4*>(
-      kv + kv_tile_offset(gkv, st.slot_base[b0] / kTileKeys, kv_tiles, D));
+      kv + kv_tile_offset(gkv, (GRP ? st.slot_base[b0] : u_slot) / kTileKeys, kv_tiles, D));
   auto tile_ptr = [&](int t) -> const u32x4* {
     if (t < maxct) return src + (size_t)t * TILE_CH;
     int mb = unit;
@@ -769,9 +780,17 @@ __global__ __launch_bounds__(NW * 64) void k_attn_tiles(const u16* __restrict__ 
     return reinterpret_cast<const u32x4*>(bkv + kv_tile_offset(gkv, mb, bkv_tiles, D));
   };
 
+  // the first tile's loads go out before q's: the tile is needed first
+  u32x4 stage[CPT];
+  if (t0 < t1) {
+    const u32x4* tp = tile_ptr(t0);
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) stage[j] = tp[tid + j * NT];
+  }
+
   const int qi = qt * 16 + c;
   const bool qvalid = comp && qi < block;
-  const size_t qrow = (size_t)(st.row_start[comp ? b : b0] + qi);
+  const size_t qrow = (size_t)((GRP ? st.row_start[comp ? b : b0] : u_row) + qi);
   bf16x8 qh[HPW][DS], ql[HPW][DS];
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) {
@@ -790,13 +809,6 @@ __global__ __launch_bounds__(NW * 64) void k_attn_tiles(const u16* __restrict__ 
     for (int dt = 0; dt < DT; ++dt) o[hh][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     m[hh] = -INFINITY;
     l[hh] = 0.f;
-  }
-
-  u32x4 stage[CPT];
-  if (t0 < t1) {
-    const u32x4* tp = tile_ptr(t0);
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) stage[j] = tp[tid + j * NT];
   }
   for (int t = t0; t < t1; ++t) {
     __syncthreads();
@@ -964,9 +976,12 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pa
                                                     u16* __restrict__ o_hi, u16* __restrict__ o_lo,
                                                     int block, int n_q, int splits, SeqTable st) {
   constexpr int PER = D / 64;  // PF: splits whose outputs are loaded with (m, l)
-  const int quad = blockIdx.x & 3, unit = blockIdx.x >> 2;
+  // grid (query tile x head x quad, sequence): the sequence's first row is
+  // read with the other arguments, not after them
+  const int b = blockIdx.y, b_row = st.row_start[b];
   const int qtiles = (block + 15) / 16;
-  const int qt = unit % qtiles, h = (unit / qtiles) % n_q, b = unit / (qtiles * n_q);
+  const int quad = blockIdx.x & 3, uh = blockIdx.x >> 2;  // uh = h * qtiles + qt
+  const int qt = uh % qtiles, h = uh / qtiles, unit = b * n_q * qtiles + uh;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int row = quad * 4 + wv, qi = qt * 16 + row;
   if (qi >= block) return;  // wave-uniform; the wave owns its row alone
@@ -1006,7 +1021,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pa
 #pragma unroll
     for (int p = 0; p < PER; ++p) acc[p] += ws * po[(size_t)s * 16 * D + p];
   }
-  const size_t o = (size_t)(st.row_start[b] + qi) * (n_q * D) + h * D + lane * PER;
+  const size_t o = (size_t)(b_row + qi) * (n_q * D) + h * D + lane * PER;
 #pragma unroll
   for (int p = 0; p < PER; ++p) {
     u16 hv, lv;
@@ -1687,6 +1702,9 @@ hipError_t launch_qkv_finish(const float* part, int kc, int M, int q_rows, int M
                              u16* kv_cache, int64_t kv_tiles, const SeqTable& st, hipStream_t s) {
   if (M == 0) return hipSuccess;
   if (M >= 1024 && (head_dim == 128 || head_dim == 64)) {  // many rows: 64-row blocks per head
+    // this form finishes q for every row; rows without q partials (q_rows <
+    // M, appended rows of a fused few-row step) never reach it
+    if (q_rows < M) return hipErrorInvalidValue;
     const dim3 grid((M + 63) / 64 * (n_q + 2 * n_kv));
     if (head_dim == 128)
       hipLaunchKernelGGL(k_qkv_finish_blk<128>, grid, dim3(256), 0, s, part, kc, M, Mp, n_q, n_kv, rope_cos,
@@ -1914,7 +1932,7 @@ static hipError_t attention_dispatch(const u16* q_hi, const u16* q_lo, const u16
   hipError_t e;
   if (groups) {
     const int nw = attention_group_size(n_q, n_kv, block) * upb;
-    const dim3 grid(groups->n * n_kv * splits);
+    const dim3 grid(n_kv * splits, groups->n);
 #define DFLASH_ATTN_GRP(H)                                                                                         \
   attention_tiles<D, true, H, false>(nw, grid, q_hi, q_lo, kv, kv_tiles, bkv, n_seqs, part_o, part_ml, o_hi, o_lo, block, \
                               n_q, n_kv, splits, scale, st, *groups, s)
@@ -1925,20 +1943,19 @@ static hipError_t attention_dispatch(const u16* q_hi, const u16* q_lo, const u16
     // splits hold several tiles (32 sequences: 133.0 -> 122.3 us per layer;
     // 8192 keys 24.0 -> 23.1; splits of one tile, context 1024: 8.2 -> 9.0)
     const bool halves = upb <= 4 && (max_tiles + splits - 1) / splits >= 2;
-    e = halves ? attention_tiles<D, false, 1, true>(2 * upb, dim3(n_seqs * n_kv * splits), q_hi, q_lo, kv,
-                                                      kv_tiles, bkv, n_seqs, part_o, part_ml, o_hi, o_lo, block,
-                                                      n_q, n_kv, splits, scale, st, 0, s)
-                 : attention_tiles<D, false, 1, false>(upb, dim3(n_seqs * n_kv * splits), q_hi, q_lo, kv, kv_tiles,
-                                                       bkv, n_seqs, part_o, part_ml, o_hi, o_lo, block, n_q, n_kv,
-                                                       splits, scale, st, 0, s);
+    const dim3 grid(n_kv * splits, n_seqs);
+    e = halves ? attention_tiles<D, false, 1, true>(2 * upb, grid, q_hi, q_lo, kv, kv_tiles, bkv, n_seqs, part_o,
+                                                      part_ml, o_hi, o_lo, block, n_q, n_kv, splits, scale, st, 0, s)
+                 : attention_tiles<D, false, 1, false>(upb, grid, q_hi, q_lo, kv, kv_tiles, bkv, n_seqs, part_o,
+                                                       part_ml, o_hi, o_lo, block, n_q, n_kv, splits, scale, st, 0,
+                                                       s);
   }
   if (e != hipSuccess) return e;
   if (splits > 1) {
-    const int units = n_seqs * n_q * ((block + 15) / 16);
     // the merge loads every split at once: the smallest instantiation that
     // holds them (each unused slot still costs a shuffle and a select)
     static_assert(kMaxSplits == 64, "merge instantiations cover up to 64 splits");
-    const dim3 grid(units * 4), blk(256);
+    const dim3 grid(n_q * ((block + 15) / 16) * 4, n_seqs), blk(256);
     if (splits <= 4)
       hipLaunchKernelGGL((k_attn_merge<D, 4>), grid, blk, 0, s, part_o, part_ml, o_hi, o_lo, block, n_q, splits, st);
     else if (splits <= 8)

@@ -88,6 +88,10 @@ SPECS: Dict[str, DraftSpec] = {
                       ctx_lens=(128,)),
     # 5-layer Qwen3-8B-shaped drafter, context 1024, block 16, concurrency 1.
     "q8b_ctx1024": DraftSpec("q8b_ctx1024", n_layers=5, block=16, ctx_lens=(1024,), **_Q8),
+    # The same widths and context with 1 and 3 layers: draft cost against
+    # drafter depth (the paper's Fig. 3 compares 1-, 3- and 5-layer drafters).
+    "q8b_l1_ctx1024": DraftSpec("q8b_l1_ctx1024", n_layers=1, block=16, ctx_lens=(1024,), **_Q8),
+    "q8b_l3_ctx1024": DraftSpec("q8b_l3_ctx1024", n_layers=3, block=16, ctx_lens=(1024,), **_Q8),
     # Same drafter with 8192 injected context positions.
     "q8b_ctx8192": DraftSpec("q8b_ctx8192", n_layers=5, block=16, ctx_lens=(8192,), **_Q8),
     # Same drafter at concurrency 32, context 2048 each.

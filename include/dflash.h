@@ -120,8 +120,9 @@ size_t dflash_model_pack_bytes(const dflash_model* model);
  * layout change only: results are bitwise identical with and without it.
  * The model then reads the copy for calls of at most 32 GEMM rows; the
  * original weights stay in use for everything else and must stay valid.
- * dev_buf must stay valid and unmodified while the model uses it; calls on
- * other streams must first wait for `stream`.  dev_buf = NULL switches the
+ * dev_buf must stay valid and unmodified while the model uses it, which
+ * includes passes already enqueued when the model is switched back or
+ * repacked; calls on other streams must first wait for `stream`.  dev_buf = NULL switches the
  * model back to the original weights.  Errors: DFLASH_EINVAL (model NULL),
  * DFLASH_EALIGN, DFLASH_EWORKSPACE (bytes too small), DFLASH_EHIP (launch
  * failure; the model keeps its previous weights).  Not thread-safe against
@@ -183,7 +184,11 @@ int dflash_fuse_ctx(const dflash_model* model, dflash_ctx* ctx, const void* feat
  *   anchors: device int32 [n_seqs];   draft: device int32 [n_seqs][block-1]
  *   logits:  NULL, or device fp32 [n_seqs][block-1][vocab] (written if given)
  * The block's K/V are written into the context's headroom slots (positions
- * >= length), which does not change any length.  2 <= block <= max_block. */
+ * >= length), which does not change any length.  2 <= block <= max_block.
+ * Token ids are not range-checked on the host (they live in device memory):
+ * an anchor (or, in the calls that take them, a block token) outside
+ * [0, vocab) is clamped to 0 or vocab - 1 before its embedding row is read,
+ * so it can never read outside the embedding; pass valid ids. */
 int dflash_draft_block(const dflash_model* model, const dflash_ctx* ctx, const int32_t* anchors,
                        int32_t block, int32_t* draft, float* logits, void* ws, size_t ws_bytes,
                        dflash_stream stream);
