@@ -36,6 +36,8 @@ enum EpiKind : int {
   EPI_SWIGLU = 0,   // out_hi/lo[row][8 t + c] = hi/lo(silu(gate) * up)
   EPI_ARGMAX = 1,   // per-row (max, lowest index) key over the tile, optional logits
   EPI_PARTIAL = 2,  // out_f32[kc][row][16 t + c] = y (K chunk kc's share; rows < M)
+  EPI_SAMPLE = 3,   // EPI_ARGMAX over logit / temp + Gumbel noise (sampled drafts; chosen
+                    // by launch_gemm for EPI_ARGMAX launches with ep.temp > 0)
 };
 
 struct WeightSeg {

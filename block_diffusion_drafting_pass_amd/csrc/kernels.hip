@@ -159,8 +159,9 @@ __device__ __forceinline__ float gumbel_f32(u64 w) {
 // logit / temp + Gumbel noise (a sample from softmax(logits / temp)), in
 // float32 like the logits; one Philox block serves the rows that share a
 // (block, position div 4).
+template <bool SAMPLE>
 __device__ __forceinline__ f32x4 draft_scores(const EpiParams& ep, int row0, int col, f32x4 v) {
-  if (ep.temp <= 0.0) return v;
+  if constexpr (!SAMPLE) return v;
   const float inv_t = (float)(1.0 / ep.temp);
   u64 w[4];
   int cur = -1;
@@ -212,11 +213,12 @@ __device__ __forceinline__ u16* kv_v_elem(u16* cache, int gk, int64_t slot, int6
 // draft score over the tile's 16 columns (lowest column on ties) as an
 // order-preserving key, 0 for rows that draft nothing; logits are written on
 // the way when asked for.  All 64 lanes must call this together.
+template <bool SAMPLE>
 __device__ __forceinline__ void argmax_tile_keys(const EpiParams& ep, int tile, int r0, f32x4 v, int lane,
                                                  u64 (&key)[4]) {
   const int c = lane & 15, g = lane >> 4;
   const int col = tile * 16 + c;
-  const f32x4 sc = draft_scores(ep, r0 + 4 * g, col, v);
+  const f32x4 sc = draft_scores<SAMPLE>(ep, r0 + 4 * g, col, v);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = r0 + 4 * g + i;
@@ -265,9 +267,9 @@ __device__ __forceinline__ void epilogue(const EpiParams& ep, const SeqTable& st
         ep.out_lo[o] = l;
       }
     }
-  } else if (EPI == EPI_ARGMAX) {
+  } else if (EPI == EPI_ARGMAX || EPI == EPI_SAMPLE) {
     u64 key[4];
-    argmax_tile_keys(ep, tile, r0, v, lane, key);
+    argmax_tile_keys<EPI == EPI_SAMPLE>(ep, tile, r0, v, lane, key);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = r0 + 4 * g + i;
@@ -281,7 +283,7 @@ __device__ __forceinline__ void epilogue(const EpiParams& ep, const SeqTable& st
 // combined in LDS (max is order-independent, so the result is deterministic)
 // and stored as this workgroup's partial; a small kernel reduces the
 // partials.  Logits are written on the way when asked for.
-template <int RG, int NC, int KS>
+template <int RG, int NC, int KS, bool SAMPLE>
 __device__ __forceinline__ void argmax_tail(const EpiParams& ep, int tile0, f32x4 (*red)[RG * NC][64], int lane,
                                             int ks) {
   __shared__ u64 rk[RG * 16];
@@ -293,7 +295,7 @@ __device__ __forceinline__ void argmax_tail(const EpiParams& ep, int tile0, f32x
 #pragma unroll
     for (int q = 1; q < KS; ++q) s += red[q][it][lane];
     const int col = (tile0 + it % NC) * 16 + c, r0 = (it / NC) * 16;
-    const f32x4 sc = draft_scores(ep, r0 + 4 * g, col, s);
+    const f32x4 sc = draft_scores<SAMPLE>(ep, r0 + 4 * g, col, s);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = r0 + 4 * g + i;
@@ -447,8 +449,8 @@ __global__ __launch_bounds__(KS * 64) void k_skinny(GemmArgs ga, SeqTable st) {
 #pragma unroll
     for (int j = 0; j < NC; ++j) red[ks][rg * NC + j][lane] = acc[rg][j];
   __syncthreads();
-  if constexpr (EPI == EPI_ARGMAX) {
-    argmax_tail<RG, NC, KS>(ga.ep, tile0, red, lane, ks);
+  if constexpr (EPI == EPI_ARGMAX || EPI == EPI_SAMPLE) {
+    argmax_tail<RG, NC, KS, EPI == EPI_SAMPLE>(ga.ep, tile0, red, lane, ks);
   } else {
     for (int it = ks; it < RG * NC; it += KS) {
       if (it / NC >= rg_end) break;  // row groups this workgroup skipped: nothing to store
@@ -538,13 +540,14 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_dl(GemmArgs ga, SeqTable 
   __shared__ u32x4 st1[STAGE];
   __shared__ u32x4 st2[S > 2 ? STAGE : 1];
   __shared__ u32x4 st3[S > 3 ? STAGE : 1];
-  __shared__ u64 rk[EPI == EPI_ARGMAX ? BM : 1];  // LM head: per-row key of the workgroup's columns
+  constexpr bool AMAX = EPI == EPI_ARGMAX || EPI == EPI_SAMPLE;
+  __shared__ u64 rk[AMAX ? BM : 1];  // LM head: per-row key of the workgroup's columns
 
   const int nwg = gridDim.x;
   const int bid = (nwg & 7) == 0 ? (int)(blockIdx.x & 7) * (nwg >> 3) + (int)(blockIdx.x >> 3) : (int)blockIdx.x;
   const int m_t = bid % mt, kc = (bid / mt) % kcn, n_t = bid / (mt * kcn);
   if (n_t * (BN / 16) >= ga.n_tiles) return;  // grid padding to whole rounds of eight XCDs
-  if constexpr (EPI == EPI_ARGMAX) {
+  if constexpr (AMAX) {
     for (int i = threadIdx.x; i < BM; i += WM * WN * 64) rk[i] = 0;
     __syncthreads();
   }
@@ -617,7 +620,7 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_dl(GemmArgs ga, SeqTable 
       }
     }
   }
-  if constexpr (EPI == EPI_ARGMAX) {
+  if constexpr (AMAX) {
     // one key per row for the workgroup's 256 columns: the wave's tiles are
     // combined in registers, the waves that share rows through LDS
 #pragma unroll
@@ -629,7 +632,7 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_dl(GemmArgs ga, SeqTable 
         const int tile = tile0 + wn * TN + ct;
         if (tile >= ga.n_tiles) break;  // uniform over the wave
         u64 key[4];
-        argmax_tile_keys(ga.ep, tile, r0, acc[rg][ct], lane, key);
+        argmax_tile_keys<EPI == EPI_SAMPLE>(ga.ep, tile, r0, acc[rg][ct], lane, key);
 #pragma unroll
         for (int i = 0; i < 4; ++i) best[i] = key[i] > best[i] ? key[i] : best[i];
       }
@@ -1850,8 +1853,9 @@ hipError_t launch_gemm(const GemmArgs& g, const SeqTable& st, int Mp, hipStream_
   switch (g.epi) {
     case EPI_SWIGLU:
       return gemm_dispatch<EPI_SWIGLU, MAP_SWIGLU, true>(g, st, Mp, s);
-    case EPI_ARGMAX:
-      return gemm_dispatch<EPI_ARGMAX, MAP_PLAIN, true>(g, st, Mp, s);
+    case EPI_ARGMAX:  // greedy drafts, or sampled ones (the Gumbel code only where it runs)
+      return g.ep.temp > 0.0 ? gemm_dispatch<EPI_SAMPLE, MAP_PLAIN, true>(g, st, Mp, s)
+                             : gemm_dispatch<EPI_ARGMAX, MAP_PLAIN, true>(g, st, Mp, s);
     case EPI_PARTIAL:
       if (g.map == MAP_QKV) return gemm_dispatch<EPI_PARTIAL, MAP_QKV, true>(g, st, Mp, s);
       if (g.map == MAP_KVL) return gemm_dispatch<EPI_PARTIAL, MAP_KVL, true>(g, st, Mp, s);

@@ -97,8 +97,9 @@ def traffic(fetch_csv: str, write_csv: str, out: str, kernel: str, copy_bytes: i
 
 
 def _is_lm_head(name: str) -> bool:
-    # the LM head is the GEMM instance with the argmax epilogue (first template argument 1)
-    return "k_skinny<1," in name or "k_gemm_dl<1," in name
+    # the LM head is the GEMM instance with an argmax epilogue (first template
+    # argument 1, greedy, or 3, sampled)
+    return any(f"{k}<{e}," in name for k in ("k_skinny", "k_gemm_dl") for e in (1, 3))
 
 
 def _agent_gpu(csv_path: str):
