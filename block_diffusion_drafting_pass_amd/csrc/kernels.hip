@@ -829,15 +829,19 @@ __global__ __launch_bounds__(NW * 64) void k_attn_tiles(const u16* __restrict__ 
     const int lim = t < maxct ? n_keys - t * kTileKeys : (t - maxct == mj ? block : 0);
     if (lim <= (HV ? half * 32 : 0)) continue;  // no valid key for this wave (uniform over the wave)
 
-    // every K fragment read from LDS serves all HPW heads of the wave
-    f32x4 sacc[HPW][2][2];
+    // every K fragment read from LDS serves all HPW heads of the wave.  A
+    // wave covers NHF 32-key halves of the tile: both, or with HV only its
+    // own (half), so that it neither scores nor exponentiates the other
+    // half's keys
+    constexpr int NHF = HV ? 1 : 2;
+    f32x4 sacc[HPW][NHF][2];
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
+    for (int h2 = 0; h2 < NHF; ++h2)
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
+        const int hf = HV ? half : h2;
 #pragma unroll
-        for (int hh = 0; hh < HPW; ++hh) sacc[hh][hf][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (HV && hf != half) continue;  // uniform over the wave
+        for (int hh = 0; hh < HPW; ++hh) sacc[hh][h2][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
         const int key = hf * 32 + 8 * (c >> 2) + 4 * kt + (c & 3);
         const int sw = k_swz(key) & (CH - 1);
 #pragma unroll
@@ -847,26 +851,29 @@ __global__ __launch_bounds__(NW * 64) void k_attn_tiles(const u16* __restrict__ 
           const bf16x8 kl = __builtin_bit_cast(bf16x8, lds[PL + key * CH + ch]);
 #pragma unroll
           for (int hh = 0; hh < HPW; ++hh) {
-            sacc[hh][hf][kt] = mfma(kh, qh[hh][ds], sacc[hh][hf][kt]);
-            sacc[hh][hf][kt] = mfma(kh, ql[hh][ds], sacc[hh][hf][kt]);
-            sacc[hh][hf][kt] = mfma(kl, qh[hh][ds], sacc[hh][hf][kt]);
+            sacc[hh][h2][kt] = mfma(kh, qh[hh][ds], sacc[hh][h2][kt]);
+            sacc[hh][h2][kt] = mfma(kh, ql[hh][ds], sacc[hh][h2][kt]);
+            sacc[hh][h2][kt] = mfma(kl, qh[hh][ds], sacc[hh][h2][kt]);
           }
         }
       }
-    float p[HPW][16];
+    // keys past lim are masked; a tile whose keys are all valid for this
+    // wave skips the comparisons (uniform over the wave)
+    const bool full = lim >= (HV ? (half + 1) * 32 : kTileKeys);
+    float p[HPW][NHF * 8];
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) {
-      float sv[16];
+      float sv[NHF * 8];
       float mx = -INFINITY;
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
+      for (int h2 = 0; h2 < NHF; ++h2)
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int key = hf * 32 + 8 * g + 4 * kt + i;
-            const float x = key < lim && (!HV || hf == half) ? sacc[hh][hf][kt][i] * scale : -INFINITY;
-            sv[hf * 8 + kt * 4 + i] = x;
+            const int key = (HV ? half : h2) * 32 + 8 * g + 4 * kt + i;
+            const float x = full || key < lim ? sacc[hh][h2][kt][i] * scale : -INFINITY;
+            sv[h2 * 8 + kt * 4 + i] = x;
             mx = fmaxf(mx, x);
           }
       mx = fmaxf(mx, shfl_xor_f(mx, 16));
@@ -876,7 +883,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn_tiles(const u16* __restrict__ 
       const float corr = fast_exp2((m[hh] - m_new) * kLog2e);
       float ps = 0.f;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
+      for (int j = 0; j < NHF * 8; ++j) {
         p[hh][j] = fast_exp2((sv[j] - m_new) * kLog2e);
         ps += p[hh][j];
       }
@@ -888,11 +895,11 @@ __global__ __launch_bounds__(NW * 64) void k_attn_tiles(const u16* __restrict__ 
       for (int dt = 0; dt < DT; ++dt) o[hh][dt] *= corr;
     }
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      if (HV && hf != half) continue;  // uniform over the wave
+    for (int h2 = 0; h2 < NHF; ++h2) {
+      const int hf = HV ? half : h2;
       bf16x8 ph[HPW], pl[HPW];
 #pragma unroll
-      for (int hh = 0; hh < HPW; ++hh) split_frag(p[hh] + hf * 8, ph[hh], pl[hh]);
+      for (int hh = 0; hh < HPW; ++hh) split_frag(p[hh] + h2 * 8, ph[hh], pl[hh]);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const int drow = dt * 16 + c;

@@ -4,6 +4,7 @@
     python -m block_diffusion_drafting_pass_amd.profsum traffic FETCH_CSV WRITE_CSV OUT_TXT \
         --kernel SUBSTRING --copy-bytes N --cmd "..." --cmd "..."
     python -m block_diffusion_drafting_pass_amd.profsum counters PMC_CSV OUT_TXT [--simds N] --cmd "..."
+    python -m block_diffusion_drafting_pass_amd.profsum kernel OUT_TXT PMC_CSV [PMC_CSV ...] --kernel SUBSTRING --cmd "..."
 
 ``trace`` lists every kernel of a ``--kernel-trace --stats`` run (calls,
 average / min / max duration, share of GPU time).  ``traffic`` takes two
@@ -14,7 +15,8 @@ reads and the bytes actually moved, and applies that factor to the chosen
 kernel.  ``counters`` takes one ``--pmc SQ_INSTS_VALU_MFMA_MOPS_BF16
 SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE`` run and sums, per draft pass, the
 bf16 matrix-core flops the kernels executed (hi/lo products and padding rows
-included) and the share of SIMD cycles the matrix cores were busy.  The
+included) and the share of SIMD cycles the matrix cores were busy.
+``kernel`` lists the counters of one kernel per dispatch and per wave.  The
 summaries record a hash of the kernel sources so that bench.py only reports
 their figures while the kernels are unchanged.
 """
@@ -169,6 +171,36 @@ def counters(csv_path: str, out: str, cmds: List[str], simds: int, xcds: int) ->
         f.write("\n".join(lines) + "\n")
 
 
+def kernel_counters(csv_paths: List[str], out: str, kernel: str, cmds: List[str]) -> None:
+    """Average counters per dispatch (and per wave) of every kernel whose name
+    contains `kernel`, from one or more --pmc runs of the same workload."""
+    lines = ["# rocprofv3 counters per dispatch of one kernel (averages over its dispatches; per wave = per"
+             " dispatch / waves launched)", "# command(s):"]
+    lines += [f"#   {c}" for c in cmds]
+    lines.append(f"kernel_sources_sha256: {kernel_sources_sha256()}")
+    for path in csv_paths:
+        disp = {}
+        for r in csv.DictReader(open(path)):
+            if kernel not in r["Kernel_Name"]:
+                continue
+            d = disp.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"], "c": {},
+                                                         "grid": int(r["Grid_Size"]), "wg": int(r["Workgroup_Size"]),
+                                                         "t": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+            d["c"][r["Counter_Name"]] = d["c"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        if not disp:
+            raise SystemExit(f"no dispatch of {kernel} in {path}")
+        ds = list(disp.values())
+        waves = ds[0]["grid"] / 64
+        lines.append(f"kernel: {ds[0]['name'][:160]}")
+        lines.append(f"dispatches: {len(ds)}  grid threads: {ds[0]['grid']}  workgroup: {ds[0]['wg']}  "
+                     f"profiled us per dispatch: {sum(d['t'] for d in ds) / len(ds) / 1e3:.2f}")
+        for name in sorted(ds[0]["c"]):
+            v = sum(d["c"].get(name, 0.0) for d in ds) / len(ds)
+            lines.append(f"{name}: {v:.1f}  per wave {v / waves:.1f}")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def read_counters(path: str):
     """(exec_bf16_flops_per_pass, mfma_busy_pass, kernel_sources_sha256) from a counters summary, or None."""
     if not os.path.exists(path):
@@ -222,8 +254,15 @@ def main(argv=None) -> None:
                    "run_agent_info.csv beside the counter file does not give them")
     c.add_argument("--xcds", type=int, default=8, help="XCDs of the GPU (MI355X: 8), likewise")
     c.add_argument("--cmd", action="append", default=[])
+    k = sub.add_parser("kernel")
+    k.add_argument("out")
+    k.add_argument("pmc_csv", nargs="+")
+    k.add_argument("--kernel", required=True)
+    k.add_argument("--cmd", action="append", default=[])
     a = ap.parse_args(argv)
-    if a.mode == "trace":
+    if a.mode == "kernel":
+        kernel_counters(a.pmc_csv, a.out, a.kernel, a.cmd)
+    elif a.mode == "trace":
         trace(a.stats_csv, a.out, a.cmd)
     elif a.mode == "counters":
         counters(a.pmc_csv, a.out, a.cmd, a.simds, a.xcds)
