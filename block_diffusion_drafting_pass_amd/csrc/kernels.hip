@@ -1952,10 +1952,13 @@ static hipError_t attention_dispatch(const u16* q_hi, const u16* q_lo, const u16
   } else {
     // two waves per query unit, each taking half of every tile's keys, when
     // splits hold several tiles (32 sequences: 133.0 -> 122.3 us per layer;
-    // 8192 keys 24.0 -> 23.1; splits of one tile, context 1024: 8.2 -> 9.0)
+    // 8192 keys 24.0 -> 23.1; splits of one tile, context 1024: 8.2 -> 9.0).
+    // Sixteen waves, the surplus ones only staging: each thread then stages
+    // a quarter of a tile instead of half and the kernel needs 124 VGPRs
+    // instead of 152 (32 sequences 120.0 -> 103.6 us, 8192 keys 22.1 -> 19.4)
     const bool halves = upb <= 4 && (max_tiles + splits - 1) / splits >= 2;
     const dim3 grid(n_kv * splits, n_seqs);
-    e = halves ? attention_tiles<D, false, 1, true>(2 * upb, grid, q_hi, q_lo, kv, kv_tiles, bkv, n_seqs, part_o,
+    e = halves ? attention_tiles<D, false, 1, true>(16, grid, q_hi, q_lo, kv, kv_tiles, bkv, n_seqs, part_o,
                                                       part_ml, o_hi, o_lo, block, n_q, n_kv, splits, scale, st, 0, s)
                  : attention_tiles<D, false, 1, false>(upb, grid, q_hi, q_lo, kv, kv_tiles, bkv, n_seqs, part_o,
                                                        part_ml, o_hi, o_lo, block, n_q, n_kv, splits, scale, st, 0,
