@@ -973,6 +973,229 @@ __global__ __launch_bounds__(NW * 64) void k_attn_tiles(const u16* __restrict__ 
   }
 }
 
+// The same attention for one-block units whose query units are at most four
+// (one 16-row query tile per q head of the GQA group), with two waves per query unit (one per
+// 32-key half of every tile), for splits of a few tiles.  Roles are split
+// and the tile buffer doubled, so that one barrier per tile suffices and the
+// copy into LDS leaves the critical path: waves 8 .. 15 only stage (each
+// thread a sixteenth of a tile, the next tile in registers) and write tile
+// t + 1 into one LDS buffer while the computing waves read tile t from the
+// other.  A computing wave reads the K (V) fragments of the next k-step (d
+// tile) before multiplying the current ones.  Every product and sum is the
+// one k_attn_tiles forms, in the same order, so the two give bitwise equal
+// results (8192 keys in 26 splits of five tiles: 20.3 -> 18.7 us per layer;
+// 4096 keys, 13 splits: 16.1 -> 13.8 us; with 33-tile splits, 32 x 2048, it
+// measured 3% slower, so those keep k_attn_tiles).
+template <int D>
+__global__ __launch_bounds__(1024) void k_attn_staged(const u16* __restrict__ q_hi, const u16* __restrict__ q_lo,
+                                                      const u16* __restrict__ kv, int64_t kv_tiles,
+                                                      float* __restrict__ part_o, float* __restrict__ part_ml,
+                                                      u16* __restrict__ o_hi, u16* __restrict__ o_lo, int block,
+                                                      int n_q, int n_kv, int splits, float scale, SeqTable st) {
+  constexpr int CH = D / 8, PL = kTileKeys * CH, TILE_CH = 4 * PL;
+  constexpr int NS = 512, CPS = TILE_CH / NS;  // staging threads, 16-byte chunks of a tile per staging thread
+  constexpr int DS = D / 32, DT = D / 16;
+  constexpr float kLog2e = 1.4426950408889634f;
+  __shared__ u32x4 ldsb[2 * TILE_CH];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c = lane & 15, g = lane >> 4;
+  const int unit = blockIdx.y;
+  const int u_pos = st.pos_base[unit], u_row = st.row_start[unit], u_slot = st.slot_base[unit];
+  const int s = blockIdx.x % splits, gkv = blockIdx.x / splits;
+  const int G = n_q / n_kv, qtiles = (block + 15) / 16, upb = G * qtiles;
+  const bool stager = wave >= 8;
+  const int half = wave / upb, wu = wave % upb;
+  const bool comp = !stager && wave < 2 * upb;
+  const int h = gkv * G + wu % G, qt = wu / G;
+  const int n_keys = u_pos + block;
+  const int ntile = (n_keys + kTileKeys - 1) / kTileKeys;
+  const int tps = (ntile + splits - 1) / splits;
+  const int t0 = s * tps, t1 = min(ntile, t0 + tps);
+  const u32x4* src = reinterpret_cast<const u32x4*>(kv + kv_tile_offset(gkv, u_slot / kTileKeys, kv_tiles, D));
+
+  if (stager) {
+    // Loads are issued unconditionally (past the split's last tile they
+    // re-read it from L2), which keeps the compiler's wait before each LDS
+    // write to exactly the loads of the tile being written.  Barriers match
+    // the computing waves' one for one.
+    const int sid = tid - NS;
+    const int tl = max(t1 - 1, 0);
+    auto tile_src = [&](int t) { return src + (size_t)min(t, tl) * TILE_CH + sid; };
+    u32x4 sa[CPS];
+    const u32x4* pa = tile_src(t0);
+#pragma unroll
+    for (int j = 0; j < CPS; ++j) sa[j] = pa[j * NS];
+    if (t0 < t1) {
+#pragma unroll
+      for (int j = 0; j < CPS; ++j) ldsb[lds_chunk<D>(sid + j * NS)] = sa[j];
+      pa = tile_src(t0 + 1);
+#pragma unroll
+      for (int j = 0; j < CPS; ++j) sa[j] = pa[j * NS];
+    }
+    __syncthreads();
+    for (int t = t0; t < t1; ++t) {
+      if (t + 1 < t1) {
+        u32x4* dst = ldsb + ((t - t0 + 1) & 1) * TILE_CH;
+#pragma unroll
+        for (int j = 0; j < CPS; ++j) dst[lds_chunk<D>(sid + j * NS)] = sa[j];
+        pa = tile_src(t + 2);
+#pragma unroll
+        for (int j = 0; j < CPS; ++j) sa[j] = pa[j * NS];
+      }
+      __syncthreads();
+    }
+    __syncthreads();  // the two barriers of the halves' combine
+    __syncthreads();
+    return;
+  }
+
+  const int qi = qt * 16 + c;
+  const bool qvalid = comp && qi < block;
+  const size_t qrow = (size_t)(u_row + qi);
+  bf16x8 qh[DS], ql[DS];
+  {
+    const size_t qoff = qrow * (n_q * D) + h * D + g * 8;
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      qh[ds] = qvalid ? ld_frag(q_hi + qoff + ds * 32) : zero_frag();
+      ql[ds] = qvalid ? ld_frag(q_lo + qoff + ds * 32) : zero_frag();
+    }
+  }
+  f32x4 o[DT];
+  float m = -INFINITY, l = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // MFMA row rho of 16-key tile kt is key 8 (rho / 4) + 4 kt + rho % 4 of
+  // the half, as in k_attn_tiles; both tiles are scored together
+  const int key0 = half * 32 + 8 * (c >> 2) + (c & 3), key1 = key0 + 4;
+  const int sw0 = k_swz(key0) & (CH - 1), sw1 = k_swz(key1) & (CH - 1);
+  auto tile = [&](const u32x4* lds, int t) {
+    const int lim = n_keys - t * kTileKeys;  // valid keys of the tile
+    if (lim <= half * 32) return;            // none in this wave's half (uniform)
+    f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    bf16x8 kf[2][4];
+    auto kld = [&](bf16x8* f, int ds) {
+      f[0] = __builtin_bit_cast(bf16x8, lds[key0 * CH + ((ds * 4 + g) ^ sw0)]);
+      f[1] = __builtin_bit_cast(bf16x8, lds[PL + key0 * CH + ((ds * 4 + g) ^ sw0)]);
+      f[2] = __builtin_bit_cast(bf16x8, lds[key1 * CH + ((ds * 4 + g) ^ sw1)]);
+      f[3] = __builtin_bit_cast(bf16x8, lds[PL + key1 * CH + ((ds * 4 + g) ^ sw1)]);
+    };
+    kld(kf[0], 0);
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      if (ds + 1 < DS) kld(kf[(ds + 1) & 1], ds + 1);
+      __builtin_amdgcn_sched_barrier(0);  // keep the next k-step's reads ahead of these products
+      const bf16x8* f = kf[ds & 1];
+      sacc[0] = mfma(f[0], qh[ds], sacc[0]);
+      sacc[1] = mfma(f[2], qh[ds], sacc[1]);
+      sacc[0] = mfma(f[0], ql[ds], sacc[0]);
+      sacc[1] = mfma(f[2], ql[ds], sacc[1]);
+      sacc[0] = mfma(f[1], qh[ds], sacc[0]);
+      sacc[1] = mfma(f[3], qh[ds], sacc[1]);
+    }
+    const bool full = lim >= (half + 1) * 32;
+    float p[8], sv[8];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = half * 32 + 8 * g + 4 * kt + i;
+        const float x = full || key < lim ? sacc[kt][i] * scale : -INFINITY;
+        sv[kt * 4 + i] = x;
+        mx = fmaxf(mx, x);
+      }
+    mx = fmaxf(mx, shfl_xor_f(mx, 16));
+    mx = fmaxf(mx, shfl_xor_f(mx, 32));
+    const float m_new = fmaxf(m, mx);
+    const float corr = fast_exp2((m - m_new) * kLog2e);
+    float ps = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      p[j] = fast_exp2((sv[j] - m_new) * kLog2e);
+      ps += p[j];
+    }
+    ps += shfl_xor_f(ps, 16);
+    ps += shfl_xor_f(ps, 32);
+    l = l * corr + ps;
+    m = m_new;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt] *= corr;
+    bf16x8 ph, pl;
+    split_frag(p, ph, pl);
+    bf16x8 vf[2][2];
+    auto vld = [&](bf16x8* f, int dt) {
+      const int drow = dt * 16 + c;
+      const int ch = (half * 4 + g) ^ v_swz(drow);
+      f[0] = __builtin_bit_cast(bf16x8, lds[2 * PL + drow * 8 + ch]);
+      f[1] = __builtin_bit_cast(bf16x8, lds[3 * PL + drow * 8 + ch]);
+    };
+    vld(vf[0], 0);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      if (dt + 1 < DT) vld(vf[(dt + 1) & 1], dt + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      const bf16x8* f = vf[dt & 1];
+      o[dt] = mfma(f[0], ph, o[dt]);
+      o[dt] = mfma(f[0], pl, o[dt]);
+      o[dt] = mfma(f[1], ph, o[dt]);
+    }
+  };
+  __syncthreads();  // tile t0 staged
+  for (int t = t0; t < t1; ++t) {
+    if (comp) tile(ldsb + ((t - t0) & 1) * TILE_CH, t);
+    __syncthreads();  // tile t used; tile t + 1 staged
+  }
+
+  // the second half's waves hand (m, l, O) to the first half's through LDS
+  float* xo = reinterpret_cast<float*>(ldsb) + (size_t)wu * (DT * 4 + 2) * 64;
+  __syncthreads();
+  if (comp && half == 1) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xo[(dt * 4 + i) * 64 + lane] = o[dt][i];
+    xo[DT * 4 * 64 + lane] = m;
+    xo[(DT * 4 + 1) * 64 + lane] = l;
+  }
+  __syncthreads();
+  if (!comp || half != 0) return;
+  const float m1 = xo[DT * 4 * 64 + lane], l1 = xo[(DT * 4 + 1) * 64 + lane];
+  const float M = fmaxf(m, m1);
+  if (M != -INFINITY) {
+    const float w0 = fast_exp2((m - M) * kLog2e), w1 = fast_exp2((m1 - M) * kLog2e);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[dt][i] = o[dt][i] * w0 + xo[(dt * 4 + i) * 64 + lane] * w1;
+    l = l * w0 + l1 * w1;
+    m = M;
+  }
+  if (splits == 1) {
+    if (!qvalid) return;
+    const float inv = 1.0f / l;
+    const size_t ob = qrow * (n_q * D) + h * D + g * 4;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        u16 hv, lv;
+        split_pair(o[dt][i] * inv, hv, lv);
+        o_hi[ob + dt * 16 + i] = hv;
+        o_lo[ob + dt * 16 + i] = lv;
+      }
+    return;
+  }
+  const size_t pidx = ((size_t)(unit * n_q + h) * qtiles + qt) * splits + s;
+  float* po = part_o + pidx * 16 * D + c * D + g * 4;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16) = o[dt];
+  if (g == 0) {
+    part_ml[pidx * 32 + c] = m;
+    part_ml[pidx * 32 + 16 + c] = l;
+  }
+}
+
 // Combine the key splits of each (sequence, q head, 16-row query tile) unit.
 // Workgroup = unit x 4-row quad; wave w owns one query row: lane s reads
 // split s's (m, l) while every lane loads its D/64 output columns of all
@@ -1956,13 +2179,20 @@ static hipError_t attention_dispatch(const u16* q_hi, const u16* q_lo, const u16
     // Sixteen waves, the surplus ones only staging: each thread then stages
     // a quarter of a tile instead of half and the kernel needs 124 VGPRs
     // instead of 152 (32 sequences 120.0 -> 103.6 us, 8192 keys 22.1 -> 19.4)
-    const bool halves = upb <= 4 && (max_tiles + splits - 1) / splits >= 2;
+    const int tps = (max_tiles + splits - 1) / splits;
+    const bool halves = upb <= 4 && tps >= 2;
     const dim3 grid(n_kv * splits, n_seqs);
-    e = halves ? attention_tiles<D, false, 1, true>(16, grid, q_hi, q_lo, kv, kv_tiles, bkv, n_seqs, part_o,
-                                                      part_ml, o_hi, o_lo, block, n_q, n_kv, splits, scale, st, 0, s)
-                 : attention_tiles<D, false, 1, false>(upb, grid, q_hi, q_lo, kv, kv_tiles, bkv, n_seqs, part_o,
-                                                       part_ml, o_hi, o_lo, block, n_q, n_kv, splits, scale, st, 0,
-                                                       s);
+    if (halves && tps <= 8 && !bkv) {  // splits of a few tiles: the double-buffered form
+      hipLaunchKernelGGL((k_attn_staged<D>), grid, dim3(1024), 0, s, q_hi, q_lo, kv, kv_tiles, part_o, part_ml, o_hi,
+                         o_lo, block, n_q, n_kv, splits, scale, st);
+      e = hipSuccess;
+    } else if (halves) {
+      e = attention_tiles<D, false, 1, true>(16, grid, q_hi, q_lo, kv, kv_tiles, bkv, n_seqs, part_o, part_ml, o_hi,
+                                             o_lo, block, n_q, n_kv, splits, scale, st, 0, s);
+    } else {
+      e = attention_tiles<D, false, 1, false>(upb, grid, q_hi, q_lo, kv, kv_tiles, bkv, n_seqs, part_o, part_ml, o_hi,
+                                              o_lo, block, n_q, n_kv, splits, scale, st, 0, s);
+    }
   }
   if (e != hipSuccess) return e;
   if (splits > 1) {

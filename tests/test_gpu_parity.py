@@ -145,6 +145,14 @@ def test_tiny_attention_halves(torch_cuda, ctx, block):
     _tiny_case(I.spec("tiny"), (ctx,), block, std=0.05, label=f"ctx {ctx} B{block} halves")
 
 
+# The splits above hold at most eight tiles, which the double-buffered
+# attention kernel takes; eight sequences of 135-141 tiles give splits of
+# nine tiles, which take the single-buffer sixteen-wave one (as 32 x 2048 does).
+def test_tiny_attention_long_splits(torch_cuda):
+    lens = (8900, 8700, 9000, 8950, 8800, 8999, 8600, 8912)
+    _tiny_case(I.spec("tiny"), lens, 16, std=0.05, label="8 seqs ~8900 long splits")
+
+
 def test_tiny_incremental_append_and_truncate(torch_cuda):
     spec = I.spec("tiny").with_(ctx_lens=(0, 0))
     w = I.gen_weights(spec, seed=4, std=0.05)
