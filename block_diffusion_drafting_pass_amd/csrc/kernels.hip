@@ -83,6 +83,33 @@ __device__ __forceinline__ void split_frag(const float* v, bf16x8& hi, bf16x8& l
 }
 
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
+
+// Max / sum of v over lanes l and l ^ 16 (l ^ 32).  The gfx950 lane-swap
+// instructions hand every lane both values in registers, without the LDS
+// round trip of a shuffle; the pair comes in either order, and max and + are
+// commutative, so the results equal max(v, shfl_xor(v, m)) and
+// v + shfl_xor(v, m) bit for bit.
+template <int M>
+__device__ __forceinline__ void xor_pair(float v, float& a, float& b) {
+  static_assert(M == 16 || M == 32, "lane swaps exist for 16 and 32");
+  const uint32_t u = __float_as_uint(v);
+  const auto r = M == 16 ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
+                         : __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+template <int M>
+__device__ __forceinline__ float max_xor(float v) {
+  float a, b;
+  xor_pair<M>(v, a, b);
+  return fmaxf(a, b);
+}
+template <int M>
+__device__ __forceinline__ float sum_xor(float v) {
+  float a, b;
+  xor_pair<M>(v, a, b);
+  return a + b;
+}
 __device__ __forceinline__ u64 shfl_xor_u64(u64 v, int m) {
   const uint32_t lo = __shfl_xor((uint32_t)v, m, 64);
   const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m, 64);
@@ -668,8 +695,9 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_dl(GemmArgs ga, SeqTable 
 // only stage).  A group's blocks are sorted by anchor; its context tiles
 // are those of its longest prefix, and a wave skips tiles past its own
 // block's prefix.  Each K / V fragment a wave reads from LDS feeds all HPW
-// of its heads.  Softmax weights use the hardware base-2 exponential with
-// log2(e) folded into the argument.  Each 64-key cache tile is
+// of its heads.  Scores are taken in base-2 units (scaled by
+// scale log2(e), so the running max is too) and each softmax weight is one
+// fma and one hardware base-2 exponential.  Each 64-key cache tile is
 // copied once from HBM (contiguous, prefetched into registers while the
 // previous tile is used) into LDS, where every query unit of the group reads
 // it.  Per 32-key half a wave computes S^T = K Q^T with keys as MFMA rows, so
@@ -723,6 +751,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn_tiles(const u16* __restrict__ 
   constexpr int CPT = TILE_CH / NT;
   static_assert(TILE_CH % NT == 0, "tile must split evenly over the threads");
   constexpr int DS = D / 32, DT = D / 16;
+  const float su = scale * 1.4426950408889634f;  // scale log2(e): scores to base-2 units
   __shared__ u32x4 lds[TILE_CH];
 
   // grid (kv head x split, unit).  The unit index comes straight from the
@@ -858,37 +887,39 @@ __global__ __launch_bounds__(NW * 64) void k_attn_tiles(const u16* __restrict__ 
         }
       }
     // keys past lim are masked; a tile whose keys are all valid for this
-    // wave skips the comparisons (uniform over the wave)
+    // wave skips the comparisons (uniform over the wave).  The running max m
+    // is kept in base-2 units of the scaled score, u = s scale log2(e), so
+    // that each weight is one fma and one exp2
     const bool full = lim >= (HV ? (half + 1) * 32 : kTileKeys);
     float p[HPW][NHF * 8];
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) {
       float sv[NHF * 8];
       float mx = -INFINITY;
+      if (full) {
 #pragma unroll
-      for (int h2 = 0; h2 < NHF; ++h2)
+        for (int j = 0; j < NHF * 8; ++j) {
+          sv[j] = sacc[hh][j / 8][(j / 4) & 1][j & 3];
+          mx = fmaxf(mx, sv[j]);
+        }
+      } else {
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = (HV ? half : h2) * 32 + 8 * g + 4 * kt + i;
-            const float x = full || key < lim ? sacc[hh][h2][kt][i] * scale : -INFINITY;
-            sv[h2 * 8 + kt * 4 + i] = x;
-            mx = fmaxf(mx, x);
-          }
-      mx = fmaxf(mx, shfl_xor_f(mx, 16));
-      mx = fmaxf(mx, shfl_xor_f(mx, 32));
-      const float m_new = fmaxf(m[hh], mx);
-      constexpr float kLog2e = 1.4426950408889634f;
-      const float corr = fast_exp2((m[hh] - m_new) * kLog2e);
+        for (int j = 0; j < NHF * 8; ++j) {
+          const int key = (HV ? half : j / 8) * 32 + 8 * g + 4 * ((j / 4) & 1) + (j & 3);
+          sv[j] = key < lim ? sacc[hh][j / 8][(j / 4) & 1][j & 3] : -INFINITY;
+          mx = fmaxf(mx, sv[j]);
+        }
+      }
+      mx = max_xor<32>(max_xor<16>(mx));
+      const float m_new = fmaxf(m[hh], mx * su);  // su > 0: the max of the scaled scores
+      const float corr = fast_exp2(m[hh] - m_new);
       float ps = 0.f;
 #pragma unroll
       for (int j = 0; j < NHF * 8; ++j) {
-        p[hh][j] = fast_exp2((sv[j] - m_new) * kLog2e);
+        p[hh][j] = fast_exp2(fmaf(sv[j], su, -m_new));
         ps += p[hh][j];
       }
-      ps += shfl_xor_f(ps, 16);
-      ps += shfl_xor_f(ps, 32);
+      ps = sum_xor<32>(sum_xor<16>(ps));
       l[hh] = l[hh] * corr + ps;
       m[hh] = m_new;
 #pragma unroll
@@ -917,8 +948,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn_tiles(const u16* __restrict__ 
   }
   if constexpr (HV) {
     // the second half's waves hand (m, l, O) to the first half's through
-    // the tile buffer; weights exp(m_half - max) as in the online softmax
-    constexpr float kLog2e = 1.4426950408889634f;
+    // the tile buffer; weights 2^(m_half - max) as in the online softmax
     float* xo = reinterpret_cast<float*>(lds) + (size_t)wu * (DT * 4 + 2) * 64;
     __syncthreads();  // every wave is done with the last tile
     if (comp && half == 1) {
@@ -934,7 +964,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn_tiles(const u16* __restrict__ 
     const float m1 = xo[DT * 4 * 64 + lane], l1 = xo[(DT * 4 + 1) * 64 + lane];
     const float M = fmaxf(m[0], m1);
     if (M != -INFINITY) {
-      const float w0 = fast_exp2((m[0] - M) * kLog2e), w1 = fast_exp2((m1 - M) * kLog2e);
+      const float w0 = fast_exp2(m[0] - M), w1 = fast_exp2(m1 - M);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -995,7 +1025,7 @@ __global__ __launch_bounds__(1024) void k_attn_staged(const u16* __restrict__ q_
   constexpr int CH = D / 8, PL = kTileKeys * CH, TILE_CH = 4 * PL;
   constexpr int NS = 512, CPS = TILE_CH / NS;  // staging threads, 16-byte chunks of a tile per staging thread
   constexpr int DS = D / 32, DT = D / 16;
-  constexpr float kLog2e = 1.4426950408889634f;
+  const float su = scale * 1.4426950408889634f;  // scale log2(e): scores to base-2 units
   __shared__ u32x4 ldsb[2 * TILE_CH];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 15, g = lane >> 4;
@@ -1093,30 +1123,34 @@ __global__ __launch_bounds__(1024) void k_attn_staged(const u16* __restrict__ q_
       sacc[0] = mfma(f[1], qh[ds], sacc[0]);
       sacc[1] = mfma(f[3], qh[ds], sacc[1]);
     }
+    // the online softmax of k_attn_tiles, m in base-2 units of the scaled score
     const bool full = lim >= (half + 1) * 32;
     float p[8], sv[8];
     float mx = -INFINITY;
+    if (full) {
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = half * 32 + 8 * g + 4 * kt + i;
-        const float x = full || key < lim ? sacc[kt][i] * scale : -INFINITY;
-        sv[kt * 4 + i] = x;
-        mx = fmaxf(mx, x);
+      for (int j = 0; j < 8; ++j) {
+        sv[j] = sacc[j / 4][j & 3];
+        mx = fmaxf(mx, sv[j]);
       }
-    mx = fmaxf(mx, shfl_xor_f(mx, 16));
-    mx = fmaxf(mx, shfl_xor_f(mx, 32));
-    const float m_new = fmaxf(m, mx);
-    const float corr = fast_exp2((m - m_new) * kLog2e);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int key = half * 32 + 8 * g + j;
+        sv[j] = key < lim ? sacc[j / 4][j & 3] : -INFINITY;
+        mx = fmaxf(mx, sv[j]);
+      }
+    }
+    mx = max_xor<32>(max_xor<16>(mx));
+    const float m_new = fmaxf(m, mx * su);
+    const float corr = fast_exp2(m - m_new);
     float ps = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      p[j] = fast_exp2((sv[j] - m_new) * kLog2e);
+      p[j] = fast_exp2(fmaf(sv[j], su, -m_new));
       ps += p[j];
     }
-    ps += shfl_xor_f(ps, 16);
-    ps += shfl_xor_f(ps, 32);
+    ps = sum_xor<32>(sum_xor<16>(ps));
     l = l * corr + ps;
     m = m_new;
 #pragma unroll
@@ -1163,7 +1197,7 @@ __global__ __launch_bounds__(1024) void k_attn_staged(const u16* __restrict__ q_
   const float m1 = xo[DT * 4 * 64 + lane], l1 = xo[(DT * 4 + 1) * 64 + lane];
   const float M = fmaxf(m, m1);
   if (M != -INFINITY) {
-    const float w0 = fast_exp2((m - M) * kLog2e), w1 = fast_exp2((m1 - M) * kLog2e);
+    const float w0 = fast_exp2(m - M), w1 = fast_exp2(m1 - M);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -1200,8 +1234,8 @@ __global__ __launch_bounds__(1024) void k_attn_staged(const u16* __restrict__ q_
 // Workgroup = unit x 4-row quad; wave w owns one query row: lane s reads
 // split s's (m, l) while every lane loads its D/64 output columns of all
 // splits (PF >= splits, from a few fixed sizes); the wave forms the
-// log-sum-exp weights exp(m_s - max) / sum_s l_s exp(m_s - max) (lane s
-// holds split s's), then each lane sums its columns over the splits in split
+// log-sum-exp weights 2^(m_s - max) / sum_s l_s 2^(m_s - max) (the maxima
+// are in base-2 units; lane s holds split s's), then each lane sums its columns over the splits in split
 // order and writes the hi/lo planes [row][n_q * D].
 template <int D, int PF>
 __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ part_o,
@@ -1233,7 +1267,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pa
   float M = m;
 #pragma unroll
   for (int k = 32; k >= 1; k >>= 1) M = fmaxf(M, shfl_xor_f(M, k));
-  const float e = lane < splits ? expf(m - M) : 0.f;
+  const float e = lane < splits ? fast_exp2(m - M) : 0.f;  // m in base-2 units
   float L = e * l;
 #pragma unroll
   for (int k = 32; k >= 1; k >>= 1) L += shfl_xor_f(L, k);
