@@ -110,10 +110,39 @@ __device__ __forceinline__ float sum_xor(float v) {
   xor_pair<M>(v, a, b);
   return a + b;
 }
-__device__ __forceinline__ u64 shfl_xor_u64(u64 v, int m) {
-  const uint32_t lo = __shfl_xor((uint32_t)v, m, 64);
-  const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m, 64);
+
+// Largest 64-bit key over the 16 lanes of each row of a wave, every lane of
+// the row ending with it, by DPP lane permutations (no LDS round trips):
+// quad_perm [1,0,3,2] (lane ^ 1), quad_perm [2,3,0,1] (lane ^ 2), the mirror
+// within 8 lanes, the mirror within 16.  Max is order-independent, so any
+// pairing that reaches every lane gives the same key.
+template <int CTRL>
+__device__ __forceinline__ u64 dpp_u64(u64 v) {
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)v, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
   return ((u64)hi << 32) | lo;
+}
+__device__ __forceinline__ u64 max_u64(u64 a, u64 b) { return a > b ? a : b; }
+__device__ __forceinline__ u64 max_row16_u64(u64 k) {
+  k = max_u64(k, dpp_u64<0xB1>(k));
+  k = max_u64(k, dpp_u64<0x4E>(k));
+  k = max_u64(k, dpp_u64<0x141>(k));
+  return max_u64(k, dpp_u64<0x140>(k));
+}
+// ... over the whole wave: the rows' keys then meet by the lane swaps (both
+// halves of a key move by the same lane mapping)
+__device__ __forceinline__ u64 max_wave_u64(u64 k) {
+  k = max_row16_u64(k);
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const uint32_t lo = (uint32_t)k, hi = (uint32_t)(k >> 32);
+    const auto rl = half == 0 ? __builtin_amdgcn_permlane16_swap(lo, lo, false, false)
+                              : __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+    const auto rh = half == 0 ? __builtin_amdgcn_permlane16_swap(hi, hi, false, false)
+                              : __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    k = max_u64(((u64)rh[0] << 32) | rl[0], ((u64)rh[1] << 32) | rl[1]);
+  }
+  return k;
 }
 
 // Sequence owning `row` in the current row space (row_start is ascending).
@@ -253,13 +282,7 @@ __device__ __forceinline__ void argmax_tile_keys(const EpiParams& ep, int tile, 
     const bool draft_row = row < ep.M && bi != 0;
     if (draft_row && ep.logits)
       ep.logits[((size_t)(row / ep.block) * (ep.block - 1) + (bi - 1)) * ep.vocab + col] = v[i];
-    u64 k = draft_row ? argmax_key(sc[i], col) : 0ull;
-#pragma unroll
-    for (int m = 1; m < 16; m <<= 1) {
-      const u64 o = shfl_xor_u64(k, m);
-      k = o > k ? o : k;
-    }
-    key[i] = k;
+    key[i] = max_row16_u64(draft_row ? argmax_key(sc[i], col) : 0ull);
   }
 }
 
@@ -330,12 +353,7 @@ __device__ __forceinline__ void argmax_tail(const EpiParams& ep, int tile0, f32x
       const bool draft_row = row < ep.M && bi != 0;
       if (draft_row && ep.logits)
         ep.logits[((size_t)(row / ep.block) * (ep.block - 1) + (bi - 1)) * ep.vocab + col] = s[i];
-      u64 key = draft_row ? argmax_key(sc[i], col) : 0ull;
-#pragma unroll
-      for (int m = 1; m < 16; m <<= 1) {
-        const u64 o = shfl_xor_u64(key, m);
-        key = o > key ? o : key;
-      }
+      const u64 key = max_row16_u64(draft_row ? argmax_key(sc[i], col) : 0ull);
       if (c == 0 && key) atomicMax(&rk[row], key);
     }
   }
@@ -1662,11 +1680,7 @@ __global__ __launch_bounds__(256) void k_argmax_reduce(const u64* __restrict__ p
     const u64 v = part[(size_t)t * Mp + row];
     best = v > best ? v : best;
   }
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const u64 o = shfl_xor_u64(best, m);
-    best = o > best ? o : best;
-  }
+  best = max_wave_u64(best);
   __shared__ u64 wbest[4];
   if ((threadIdx.x & 63) == 0) wbest[threadIdx.x >> 6] = best;
   __syncthreads();
