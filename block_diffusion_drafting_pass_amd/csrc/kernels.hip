@@ -82,13 +82,10 @@ __device__ __forceinline__ void split_frag(const float* v, bf16x8& hi, bf16x8& l
   lo = __builtin_bit_cast(bf16x8, l);
 }
 
-__device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
-
 // Max / sum of v over lanes l and l ^ 16 (l ^ 32).  The gfx950 lane-swap
 // instructions hand every lane both values in registers, without the LDS
 // round trip of a shuffle; the pair comes in either order, and max and + are
-// commutative, so the results equal max(v, shfl_xor(v, m)) and
-// v + shfl_xor(v, m) bit for bit.
+// commutative, so the results equal those of an xor shuffle by m bit for bit.
 template <int M>
 __device__ __forceinline__ void xor_pair(float v, float& a, float& b) {
   static_assert(M == 16 || M == 32, "lane swaps exist for 16 and 32");
@@ -143,6 +140,29 @@ __device__ __forceinline__ u64 max_wave_u64(u64 k) {
     k = max_u64(((u64)rh[0] << 32) | rl[0], ((u64)rh[1] << 32) | rl[1]);
   }
   return k;
+}
+
+// Sum / max of v over the 64 lanes of a wave, every lane ending with the same
+// bits: the DPP butterflies above within each 16-lane row, then the lane
+// swaps across rows.  The pairing is fixed and + and max are commutative, so
+// the result depends only on the 64 inputs.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float sum_wave(float v) {
+  v += dpp_f32<0xB1>(v);
+  v += dpp_f32<0x4E>(v);
+  v += dpp_f32<0x141>(v);
+  v += dpp_f32<0x140>(v);
+  return sum_xor<32>(sum_xor<16>(v));
+}
+__device__ __forceinline__ float max_wave(float v) {
+  v = fmaxf(v, dpp_f32<0xB1>(v));
+  v = fmaxf(v, dpp_f32<0x4E>(v));
+  v = fmaxf(v, dpp_f32<0x141>(v));
+  v = fmaxf(v, dpp_f32<0x140>(v));
+  return max_xor<32>(max_xor<16>(v));
 }
 
 // Sequence owning `row` in the current row space (row_start is ascending).
@@ -304,7 +324,7 @@ __device__ __forceinline__ void epilogue(const EpiParams& ep, const SeqTable& st
   } else if (EPI == EPI_SWIGLU) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float up = shfl_xor_f(v[i], 8);  // lane c+8 holds the up projection
+      const float up = dpp_f32<0x128>(v[i]);  // lane c+8 holds the up projection (DPP row_ror:8: lane ^ 8)
       const int row = r0 + 4 * g + i;
       if (c < 8 && row < ep.Mp) {
         u16 h = 0, l = 0;
@@ -1282,14 +1302,10 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pa
   for (int s = 0; s < PF; ++s)
 #pragma unroll
     for (int p = 0; p < PER; ++p) pre[s][p] = s < splits ? po[(size_t)s * 16 * D + p] : 0.f;
-  float M = m;
-#pragma unroll
-  for (int k = 32; k >= 1; k >>= 1) M = fmaxf(M, shfl_xor_f(M, k));
+  const float M = max_wave(m);
   const float e = lane < splits ? fast_exp2(m - M) : 0.f;  // m in base-2 units
-  float L = e * l;
-#pragma unroll
-  for (int k = 32; k >= 1; k >>= 1) L += shfl_xor_f(L, k);
-  const float w = e / L;  // lane s: the weight of split s
+  const float L = sum_wave(e * l);
+  const float w = e / L;  // lane s: the weight of split s; read by every lane with readlane
   float acc[PER];
 #pragma unroll
   for (int p = 0; p < PER; ++p) acc[p] = 0.f;
@@ -1297,12 +1313,12 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pa
   // above into this loop, one round trip per split)
 #pragma unroll
   for (int s = 0; s < PF; ++s) {
-    const float ws = __shfl(w, s, 64);
+    const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), s));
 #pragma unroll
     for (int p = 0; p < PER; ++p) acc[p] += s < splits ? ws * pre[s][p] : 0.f;
   }
   for (int s = PF; s < splits; ++s) {  // splits beyond the prefetched ones (none as launched)
-    const float ws = __shfl(w, s, 64);
+    const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), s));
 #pragma unroll
     for (int p = 0; p < PER; ++p) acc[p] += ws * po[(size_t)s * 16 * D + p];
   }
@@ -1402,8 +1418,7 @@ __global__ __launch_bounds__(1024) void k_resid_norm(float* __restrict__ x, cons
     *reinterpret_cast<f32x4*>(xr + j) = xv[v];
     ss += xv[v][0] * xv[v][0] + xv[v][1] * xv[v][1] + xv[v][2] * xv[v][2] + xv[v][3] * xv[v][3];
   }
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) ss += shfl_xor_f(ss, m);
+  ss = sum_wave(ss);
   __shared__ float wsum[16];
   if ((tid & 63) == 0) wsum[tid >> 6] = ss;
   __syncthreads();
