@@ -593,13 +593,17 @@ __device__ __forceinline__ int big_swz(int row, int ch) {
   return row * CPR + (ch ^ ((row >> 1) & (CPR - 1)));
 }
 
-template <int EPI, int MAP, bool SPLIT, int BM, int WM, int WN, int S>
+template <int EPI, int MAP, bool SPLIT, int BM, int WM, int WN, int S, int BN = kBigBN>
 __global__ __launch_bounds__(WM * WN * 64) void k_gemm_dl(GemmArgs ga, SeqTable st, int mt, int kcn) {
-  constexpr int BN = kBigBN, BK = 32, NP = SPLIT ? 2 : 1, NW = WM * WN, CPR = BK / 8;
+  constexpr int BK = 32, NP = SPLIT ? 2 : 1, NW = WM * WN, CPR = BK / 8;
   constexpr int TM = BM / WM / 16, TN = BN / WN / 16;
-  constexpr int ACH = BM * CPR, WCH = BN * CPR, STAGE = NP * ACH + WCH;
-  constexpr int IPW = STAGE / 64 / NW;  // copies per wave per slab
-  static_assert(STAGE % (64 * NW) == 0 && ACH % 64 == 0, "a stage must split into whole wave copies");
+  static_assert(BN % (WN * 16) == 0, "whole MFMA tiles per wave");
+  constexpr int ACH = BM * CPR, WCH = BN * CPR, REAL = NP * ACH + WCH;
+  // copies per wave per slab; a stage that does not split into whole wave
+  // copies (192-column tiles) is padded: the surplus copies repeat A chunks
+  // into a pad area at the end of the stage, which nothing reads
+  constexpr int IPW = (REAL + 64 * NW - 1) / (64 * NW), STAGE = IPW * 64 * NW;
+  static_assert(ACH % 64 == 0 && STAGE - REAL <= ACH, "pad copies repeat A chunks");
   static_assert(S >= 2 && S <= 4, "two to four stages");
   __shared__ u32x4 st0[STAGE];
   __shared__ u32x4 st1[STAGE];
@@ -625,8 +629,9 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_dl(GemmArgs ga, SeqTable 
   const u16* gp[IPW];
 #pragma unroll
   for (int j = 0; j < IPW; ++j) {
-    const int p = (wave * IPW + j) * 64 + lane;  // physical chunk of the stage
-    const int plane = p / ACH;                   // 0 .. NP-1: A planes; NP: weights
+    const int pp = (wave * IPW + j) * 64 + lane;  // physical chunk of the stage
+    const int p = pp < REAL ? pp : pp - REAL;      // a pad copy loads an A chunk again
+    const int plane = p / ACH;                     // 0 .. NP-1: A planes; NP: weights
     const int q = p - (plane < NP ? plane : NP) * ACH;
     const int r = q / CPR, lc = (q % CPR) ^ ((r >> 1) & (CPR - 1));
     if (plane < NP) {
@@ -2093,12 +2098,12 @@ static hipError_t skinny_nc(const GemmArgs& g, const SeqTable& st, const GemmPla
   return hipGetLastError();
 }
 
-template <int EPI, int MAP, bool SPLIT, int BM, int WM, int WN, int S>
+template <int EPI, int MAP, bool SPLIT, int BM, int WM, int WN, int S, int BN = kBigBN>
 static hipError_t dl_launch(const GemmArgs& g, const SeqTable& st, int Mp, const GemmPlan& p, hipStream_t s) {
   if (Mp % BM || g.K % (p.kc * 32) || g.a_rows < 1) return hipErrorInvalidValue;
-  const int mt = Mp / BM, nt = (g.n_tiles + p.nc - 1) / p.nc;
+  const int mt = Mp / BM, nt = (g.n_tiles + BN / 16 - 1) / (BN / 16);
   const int wgs = mt * p.kc * nt, padded = (wgs + 7) / 8 * 8;
-  hipLaunchKernelGGL((k_gemm_dl<EPI, MAP, SPLIT, BM, WM, WN, S>), dim3(padded), dim3(WM * WN * 64), 0, s, g,
+  hipLaunchKernelGGL((k_gemm_dl<EPI, MAP, SPLIT, BM, WM, WN, S, BN>), dim3(padded), dim3(WM * WN * 64), 0, s, g,
                      st, mt, p.kc);
   return hipGetLastError();
 }
@@ -2112,6 +2117,39 @@ static hipError_t dl_launch(const GemmArgs& g, const SeqTable& st, int Mp, const
 // workgroups: 162 us with two stages, 138 us with four).
 template <int EPI, int MAP, bool SPLIT>
 static hipError_t dl_dispatch(const GemmArgs& g, const SeqTable& st, int Mp, const GemmPlan& p, hipStream_t s) {
+  if constexpr (SPLIT && EPI != EPI_ARGMAX && EPI != EPI_SAMPLE) {
+    // hi/lo activations: the tile shape whose whole rounds of workgroups
+    // over the CUs take least time.  A round's time per shape (us at K 4096,
+    // SwiGLU projection, one box): 256 x 256 three stages 210, 256 x 192
+    // 177, 128-row tiles with two stages (two workgroups per CU) 236 (x 256)
+    // and 195 (x 192), with four stages (one per CU) 130 and 119.  So 512
+    // rows of the SwiGLU projection take one round of 256 x 192 tiles
+    // (214.8 -> 177.5 us), 256 rows one of 128 x 192 (130.0 -> 119.3 us).
+    // The K chunks stay the plan's, which sized the partial buffers; the
+    // column tiles of any width sum their K range in the same order, so
+    // every shape gives the same bits.  The argmax epilogues keep 256
+    // columns (their per-workgroup partials are counted per 256).
+    struct Shape { int bm, bn, per_cu, round_us; };
+    const Shape shapes[6] = {{256, 256, 1, 210}, {256, 192, 1, 177}, {128, 256, 2, 236},
+                             {128, 192, 2, 195}, {128, 256, 1, 130}, {128, 192, 1, 119}};
+    int best = -1;
+    long best_t = 0;
+    for (int i = 0; i < 6; ++i) {
+      if (Mp % shapes[i].bm) continue;
+      const long wgs = (long)(Mp / shapes[i].bm) * p.kc * ((g.n_tiles + shapes[i].bn / 16 - 1) / (shapes[i].bn / 16));
+      const long t = (wgs + 256 * shapes[i].per_cu - 1) / (256 * shapes[i].per_cu) * shapes[i].round_us;
+      if (best < 0 || t < best_t) best = i, best_t = t;
+    }
+    switch (best) {
+      case 0: return dl_launch<EPI, MAP, SPLIT, 256, 4, 4, 3>(g, st, Mp, p, s);
+      case 1: return dl_launch<EPI, MAP, SPLIT, 256, 4, 4, 3, 192>(g, st, Mp, p, s);
+      case 2: return dl_launch<EPI, MAP, SPLIT, 128, 2, 4, 2>(g, st, Mp, p, s);
+      case 3: return dl_launch<EPI, MAP, SPLIT, 128, 2, 4, 2, 192>(g, st, Mp, p, s);
+      case 4: return dl_launch<EPI, MAP, SPLIT, 128, 2, 4, 4>(g, st, Mp, p, s);
+      case 5: return dl_launch<EPI, MAP, SPLIT, 128, 2, 4, 4, 192>(g, st, Mp, p, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
   const int nt = (g.n_tiles + p.nc - 1) / p.nc;
   if (Mp % 256 == 0 && (Mp / 256) * nt * p.kc >= 256)
     return dl_launch<EPI, MAP, SPLIT, 256, 4, 4, 3>(g, st, Mp, p, s);
