@@ -2115,6 +2115,18 @@ static hipError_t dl_launch(const GemmArgs& g, const SeqTable& st, int Mp, const
 // covers the CUs, and with four stages (one per CU) on a smaller grid, which
 // the dispatcher would otherwise pack two to a CU, leaving CUs idle (at 192
 // workgroups: 162 us with two stages, 138 us with four).
+// Column width of the many-row LM head's 256-row tiles: 240 (twelve waves of
+// 64 x 80 columns) when its whole rounds over the CUs take less time than
+// 256's (round times 201 and 210 us at K 4096); the argmax partials are
+// counted per tile of this width.  151,936 columns at 256 rows: 634 tiles
+// (2.48 rounds) instead of 594 (2.32), 643.6 -> 607.4 us; at 512 rows 1068
+// -> 1034 us; the per-row keys are the same.
+static int lm_head_bn(int n_tiles, int Mp) {
+  const long mt = Mp / 256, t256 = (n_tiles + 15) / 16, t240 = (n_tiles + 14) / 15;
+  if (Mp % 256 || mt * t256 < 256) return kBigBN;  // not a 256-row-tile launch
+  return (mt * t240 + 255) / 256 * 201 < (mt * t256 + 255) / 256 * 210 ? 240 : kBigBN;
+}
+
 template <int EPI, int MAP, bool SPLIT>
 static hipError_t dl_dispatch(const GemmArgs& g, const SeqTable& st, int Mp, const GemmPlan& p, hipStream_t s) {
   if constexpr (SPLIT && EPI != EPI_ARGMAX && EPI != EPI_SAMPLE) {
@@ -2151,8 +2163,11 @@ static hipError_t dl_dispatch(const GemmArgs& g, const SeqTable& st, int Mp, con
     }
   }
   const int nt = (g.n_tiles + p.nc - 1) / p.nc;
-  if (Mp % 256 == 0 && (Mp / 256) * nt * p.kc >= 256)
+  if (Mp % 256 == 0 && (Mp / 256) * nt * p.kc >= 256) {
+    if constexpr (EPI == EPI_ARGMAX || EPI == EPI_SAMPLE)
+      if (lm_head_bn(g.n_tiles, Mp) == 240) return dl_launch<EPI, MAP, SPLIT, 256, 4, 3, 3, 240>(g, st, Mp, p, s);
     return dl_launch<EPI, MAP, SPLIT, 256, 4, 4, 3>(g, st, Mp, p, s);
+  }
   if ((Mp / 128) * nt * p.kc >= 256) return dl_launch<EPI, MAP, SPLIT, 128, 2, 4, 2>(g, st, Mp, p, s);
   return dl_launch<EPI, MAP, SPLIT, 128, 2, 4, 4>(g, st, Mp, p, s);
 }
@@ -2378,7 +2393,9 @@ hipError_t launch_pack_weights(const GemmArgs& g, u16* dst, hipStream_t s) {
 }
 
 int argmax_parts(int n_tiles, int Mp) {
-  return Mp <= 32 ? n_tiles / gemm_plan(n_tiles, 0, Mp, false).nc : (n_tiles + kBigBN / 16 - 1) / (kBigBN / 16);
+  if (Mp <= 32) return n_tiles / gemm_plan(n_tiles, 0, Mp, false).nc;
+  const int tw = lm_head_bn(n_tiles, Mp) / 16;  // MFMA tiles per workgroup column tile
+  return (n_tiles + tw - 1) / tw;
 }
 
 // One workgroup per block tile; thread t covers slot-major elements of the

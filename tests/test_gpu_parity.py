@@ -683,6 +683,27 @@ def test_sampled_draft_q8_ctx1024(q8):
     _check_sampled(gl, d.cpu().numpy(), ref.logits, 0.7, 2026, "5-layer sampled T0.7")
 
 
+def test_sampled_draft_q8_many_rows(q8):
+    # sixteen sequences of the 5-layer drafter: 256 block rows, so the sampled
+    # LM head runs on the many-row kernel at the full vocabulary
+    import torch
+    spec5, w, dev = q8
+    lens = _short_ragged(91, 16)
+    spec = spec5.with_(ctx_lens=lens)
+    run = GpuRun(spec, dev, capacity=[c + 8 for c in lens], max_new=sum(lens))
+    feats = _feats(spec, 1, lens)
+    run.ingest(feats)
+    anchors = I.gen_anchors(spec, 2)
+    lg = torch.empty((len(lens), 15, spec.vocab), dtype=torch.float32, device="cuda")
+    d = B.draft_sample(run.model, run.ctx, torch.from_numpy(anchors).cuda(), 16, 0.8, 4049, run.ws, logits=lg)
+    torch.cuda.synchronize()
+    ref = oracle_run(spec, w, feats, anchors, 16)
+    gl = lg.cpu().numpy()
+    assert float(np.max(np.abs(gl - ref.logits))) <= LOGIT_TOL
+    # logits of every sequence above; the samples of four (0.1 s of oracle per position)
+    _check_sampled(gl, d.cpu().numpy(), ref.logits, 0.8, 4049, "5-layer 16 seqs sampled T0.8", n_check=4)
+
+
 def _verify_case(n, block, V, T, seed, scale, label, qp_same=False):
     import torch
     from oracle import sampling as S
