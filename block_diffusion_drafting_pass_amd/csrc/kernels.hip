@@ -1046,19 +1046,20 @@ __global__ __launch_bounds__(NW * 64) void k_attn_tiles(const u16* __restrict__ 
   }
 }
 
-// The same attention for one-block units whose query units are at most four
-// (one 16-row query tile per q head of the GQA group), with two waves per query unit (one per
-// 32-key half of every tile), for splits of a few tiles.  Roles are split
-// and the tile buffer doubled, so that one barrier per tile suffices and the
-// copy into LDS leaves the critical path: waves 8 .. 15 only stage (each
-// thread a sixteenth of a tile, the next tile in registers) and write tile
-// t + 1 into one LDS buffer while the computing waves read tile t from the
-// other.  A computing wave reads the K (V) fragments of the next k-step (d
-// tile) before multiplying the current ones.  Every product and sum is the
-// one k_attn_tiles forms, in the same order, so the two give bitwise equal
-// results (8192 keys in 26 splits of five tiles: 20.3 -> 18.7 us per layer;
-// 4096 keys, 13 splits: 16.1 -> 13.8 us; with 33-tile splits, 32 x 2048, it
-// measured 3% slower, so those keep k_attn_tiles).
+// The same attention for one-block units with at most four query units (q
+// heads of the GQA group x 16-row query tiles), with two waves per query
+// unit (one per 32-key half of every tile), for splits of a few tiles.
+// Roles are split and the tile buffer doubled, so that one barrier per tile
+// suffices and the copy into LDS leaves the critical path: waves 8 .. 15
+// only stage (each holding an eighth of the next tile in registers) and
+// write tile t + 1 into one LDS buffer while the computing waves read tile t
+// from the other.  A computing wave reads the K (V) fragments of the next
+// k-step (d tile) before multiplying the current ones.  Every product and sum
+// is the one k_attn_tiles forms, in the same order, and the two give bitwise
+// equal results (checked at 1 to 26 splits, 4096 to 8192 keys, 8 and 32
+// sequences).  8192 keys in 26 splits of five tiles: 20.3 -> 18.7 us per
+// layer; 4096 keys, 13 splits: 16.1 -> 13.8 us; with 33-tile splits, 32 x
+// 2048, it measured 3% slower, so those keep k_attn_tiles.
 template <int D>
 __global__ __launch_bounds__(1024) void k_attn_staged(const u16* __restrict__ q_hi, const u16* __restrict__ q_lo,
                                                       const u16* __restrict__ kv, int64_t kv_tiles,
@@ -2139,8 +2140,8 @@ static hipError_t dl_dispatch(const GemmArgs& g, const SeqTable& st, int Mp, con
     // (214.8 -> 177.5 us), 256 rows one of 128 x 192 (130.0 -> 119.3 us).
     // The K chunks stay the plan's, which sized the partial buffers; the
     // column tiles of any width sum their K range in the same order, so
-    // every shape gives the same bits.  The argmax epilogues keep 256
-    // columns (their per-workgroup partials are counted per 256).
+    // every shape gives the same bits.  The argmax epilogues take their
+    // width from lm_head_bn, which also counts their per-workgroup partials.
     struct Shape { int bm, bn, per_cu, round_us; };
     const Shape shapes[6] = {{256, 256, 1, 210}, {256, 192, 1, 177}, {128, 256, 2, 236},
                              {128, 192, 2, 195}, {128, 256, 1, 130}, {128, 192, 1, 119}};
