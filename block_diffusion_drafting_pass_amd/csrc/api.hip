@@ -775,6 +775,13 @@ int draft_impl(const dflash_model* model, const dflash_ctx* ctx, const Blocks& b
   const int nqkv = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
   const int kc_qkv = gemm_plan(nqkv / 16, H, Mqp, true).kc;
   const int kc_o = gemm_plan(H / 16, QD, Mp, true).kc;
+  // One 16-row block: the O projection runs whole-K and finishes the residual
+  // and the MLP norm's gain in its epilogue; the gate|up GEMM applies the
+  // norm's per-row factor.  That takes a reduce-and-normalise launch out of
+  // every layer.  The projection's output rows go to the q|k|v input planes,
+  // which are free between the q|k|v GEMM and the next layer's norm (rows
+  // < M only: appended rows keep their fused features there).
+  const bool whole_o = gemm_whole_k_fits(H / 16, QD, Mp);
   const int kc_d = gemm_plan(H / 16, I, Mp, true).kc;
   // the q|k|v GEMM reads its own A planes (block rows, then appended rows)
   u16* qin_hi = qa_hi;
@@ -851,21 +858,33 @@ int draft_impl(const dflash_model* model, const dflash_ctx* ctx, const Blocks& b
     model->probe.stop(DFLASH_STAGE_ATTENTION, s);
     if (e != hipSuccess) return hip_fail(e, "draft_block: attention");
 
-    g = base_args(a_hi, a_lo, QD, QD, H / 16, EPI_PARTIAL, MAP_PLAIN);
+    g = base_args(a_hi, a_lo, QD, QD, H / 16, whole_o ? EPI_RESID : EPI_PARTIAL, MAP_PLAIN);
     g.w.w0 = Lw.wo;
     g.wpack = Pw.o;
-    g.ep.out_f32 = part;
+    g.pk_kmajor = pack_kmajor(PACK_O);
     g.ep.ldo = H;
+    if (whole_o) {
+      g.ep.x = x;
+      g.ep.gain = Lw.mlp_norm;
+      g.ep.out_hi = qin_hi;
+      g.ep.out_lo = qin_lo;
+      g.ep.ldh = H;
+      g.ep.ssq = part;
+    } else {
+      g.ep.out_f32 = part;
+    }
     model->probe.start(DFLASH_STAGE_OPROJ, s);
     e = launch_gemm(g, st, Mp, s);
     model->probe.stop(DFLASH_STAGE_OPROJ, s);
     if (e != hipSuccess) return hip_fail(e, "draft_block: output projection");
 
-    e = launch_resid_norm(x, part, kc_o, Mp, nullptr, nullptr, nullptr, block, 0, c.vocab,
-                          Lw.mlp_norm, a_hi, a_lo, H, M, M, c.rms_eps, s);
-    if (e != hipSuccess) return hip_fail(e, "draft_block: MLP norm");
+    if (!whole_o) {
+      e = launch_resid_norm(x, part, kc_o, Mp, nullptr, nullptr, nullptr, block, 0, c.vocab,
+                            Lw.mlp_norm, a_hi, a_lo, H, M, M, c.rms_eps, s);
+      if (e != hipSuccess) return hip_fail(e, "draft_block: MLP norm");
+    }
 
-    g = base_args(a_hi, a_lo, H, H, I / 8, EPI_SWIGLU, MAP_SWIGLU);
+    g = base_args(whole_o ? qin_hi : a_hi, whole_o ? qin_lo : a_lo, H, H, I / 8, EPI_SWIGLU, MAP_SWIGLU);
     g.w.w0 = Lw.wgate;
     g.w.w1 = Lw.wup;
     g.wpack = Pw.gate_up;
@@ -873,6 +892,12 @@ int draft_impl(const dflash_model* model, const dflash_ctx* ctx, const Blocks& b
     g.ep.out_hi = b_hi;
     g.ep.out_lo = b_lo;
     g.ep.ldh = I;
+    if (whole_o) {
+      g.ep.ssq_in = part;
+      g.ep.n_ssq = H / 16;
+      g.ep.norm_n = H;
+      g.ep.eps = c.rms_eps;
+    }
     model->probe.start(DFLASH_STAGE_GATE_UP, s);
     e = launch_gemm(g, st, Mp, s);
     model->probe.stop(DFLASH_STAGE_GATE_UP, s);

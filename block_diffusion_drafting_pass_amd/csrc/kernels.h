@@ -38,6 +38,9 @@ enum EpiKind : int {
   EPI_PARTIAL = 2,  // out_f32[kc][row][16 t + c] = y (K chunk kc's share; rows < M)
   EPI_SAMPLE = 3,   // EPI_ARGMAX over logit / temp + Gumbel noise (sampled drafts; chosen
                     // by launch_gemm for EPI_ARGMAX launches with ep.temp > 0)
+  EPI_RESID = 4,    // whole-K few-row GEMM only (rows < M): x[row][16 t + c] += y, then
+                    // out_hi/lo[row][16 t + c] = hi/lo(gain * x) (not yet normalised) and
+                    // ssq[row][t] = sum of x^2 over the tile's 16 columns
 };
 
 struct WeightSeg {
@@ -54,10 +57,22 @@ struct EpiParams {
   // EPI_PARTIAL
   float* out_f32;
   int ldo;
-  // EPI_SWIGLU
+  // EPI_SWIGLU, EPI_RESID
   u16* out_hi;
   u16* out_lo;
   int ldh;
+  // EPI_RESID: the residual rows x (row stride ldo, updated in place), the
+  // next RMSNorm's gain, and the per-tile row sums of squares [Mp][n_tiles]
+  float* x;
+  const u16* gain;
+  float* ssq;
+  // EPI_SWIGLU after an EPI_RESID launch: the A rows are gain * x, not yet
+  // normalised; each row's products are first scaled by RMSNorm's factor
+  // 1 / sqrt(sum(ssq_in[row][0 .. n_ssq)) / norm_n + eps) (null: no scaling)
+  const float* ssq_in;
+  int n_ssq;
+  int norm_n;
+  float eps;
   // MAP_QKV / MAP_KVL
   int n_q, n_kv, head_dim;
   // EPI_ARGMAX: per-row argmax keys of each column tile (many-row GEMM) or of
@@ -107,6 +122,10 @@ constexpr int kMaxKc = 16;       // most K chunks a GEMM is split into
 inline int rows_pad(int m) { return m <= 32 ? (m + 15) / 16 * 16 : (m + 127) / 128 * 128; }
 
 hipError_t launch_gemm(const GemmArgs& g, const SeqTable& st, int Mp, hipStream_t s);
+// Whether the whole-K few-row GEMM (EPI_RESID) takes this shape: 16 padded
+// rows, K a multiple of 256 up to 4096, and at most 256 column tiles (the
+// SwiGLU launch that follows reads a row's tile sums with one load per lane).
+bool gemm_whole_k_fits(int n_tiles, int K, int Mp);
 
 // Packed weights of one few-row GEMM launch: the launch's mapped weight rows
 // (map, w, ep.n_q / n_kv / head_dim, n_tiles, K of g) rearranged so that

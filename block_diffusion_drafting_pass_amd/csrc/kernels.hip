@@ -150,13 +150,13 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {
   return __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v), CTRL, 0xF, 0xF, false));
 }
-__device__ __forceinline__ float sum_wave(float v) {
+__device__ __forceinline__ float sum_row16(float v) {  // ... over each 16-lane row only
   v += dpp_f32<0xB1>(v);
   v += dpp_f32<0x4E>(v);
   v += dpp_f32<0x141>(v);
-  v += dpp_f32<0x140>(v);
-  return sum_xor<32>(sum_xor<16>(v));
+  return v + dpp_f32<0x140>(v);
 }
+__device__ __forceinline__ float sum_wave(float v) { return sum_xor<32>(sum_xor<16>(sum_row16(v))); }
 __device__ __forceinline__ float max_wave(float v) {
   v = fmaxf(v, dpp_f32<0xB1>(v));
   v = fmaxf(v, dpp_f32<0x4E>(v));
@@ -398,8 +398,8 @@ __device__ __forceinline__ void argmax_tail(const EpiParams& ep, int tile0, f32x
 // kernel sums the chunks in order.
 // ---------------------------------------------------------------------------
 
-template <int EPI, int MAP, int NC, int RG, bool SPLIT, int KS = kSkinnyWaves, bool PK = false>
-__global__ __launch_bounds__(KS * 64) void k_skinny(GemmArgs ga, SeqTable st) {
+template <int EPI, int MAP, int NC, int RG, bool SPLIT, int KS, bool PK>
+__device__ __forceinline__ void skinny_body(const GemmArgs& ga, const SeqTable& st, int tile0, int kc, int nkc) {
   constexpr int U = 2;
   // packed weights: one 1 KB block per (tile, 32 k); k advances 16 elements
   // per k tile-major, 16 n_tiles k-major
@@ -407,9 +407,7 @@ __global__ __launch_bounds__(KS * 64) void k_skinny(GemmArgs ga, SeqTable st) {
   const size_t TM = ga.pk_kmajor ? 1 : ga.K / 32;  // blocks per tile step
   const int lane = threadIdx.x & 63, ks = threadIdx.x >> 6;
   const int c = lane & 15, g = lane >> 4;
-  const int tile0 = blockIdx.x * NC;
-  const int kc = blockIdx.y;
-  const int kw = ga.K / ((int)gridDim.y * KS);
+  const int kw = ga.K / (nkc * KS);
   const int kb = (kc * KS + ks) * kw, ke = kb + kw;
 
   const u16* wp[NC];
@@ -427,6 +425,20 @@ __global__ __launch_bounds__(KS * 64) void k_skinny(GemmArgs ga, SeqTable st) {
     const int row = min(rg * 16 + c, ga.a_rows - 1);
     ah[rg] = ga.a_hi + (size_t)row * ga.lda + g * 8;
     al[rg] = SPLIT ? ga.a_lo + (size_t)row * ga.lda + g * 8 : nullptr;
+  }
+  // SwiGLU over gain * x rows not yet normalised (ep.ssq_in; one row group):
+  // wave ks's rows ks, ks + KS, .. load their per-tile sums of squares ahead
+  // of the weights and reduce them once the products are done
+  constexpr bool NORM = EPI == EPI_SWIGLU && RG == 1;
+  constexpr int NRW = NORM ? (16 + KS - 1) / KS : 1;
+  const bool norm = NORM && ga.ep.ssq_in != nullptr;
+  f32x4 sqv[NRW];
+#pragma unroll
+  for (int j = 0; j < NRW; ++j) {
+    sqv[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int row = ks + KS * j;
+    if (norm && row < RG * 16 && lane * 4 < ga.ep.n_ssq)
+      sqv[j] = *reinterpret_cast<const f32x4*>(ga.ep.ssq_in + (size_t)row * ga.ep.n_ssq + lane * 4);
   }
   f32x4 acc[RG][NC];
 #pragma unroll
@@ -461,22 +473,7 @@ __global__ __launch_bounds__(KS * 64) void k_skinny(GemmArgs ga, SeqTable st) {
 #pragma unroll
     for (int j = 0; j < NC; ++j) wf[u][j] = ldw(j, kb + u * 32);
   }
-  for (int k = kb; k < ke; k += 32 * U) {
-    bf16x8 wn[U][NC], an[APF ? U : 1][RG][NPL];
-    const bool more = k + 32 * U < ke;
-    if (more) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if constexpr (APF)
-#pragma unroll
-          for (int rg = 0; rg < RG; ++rg)
-#pragma unroll
-            for (int pl = 0; pl < NPL; ++pl)
-              if (rg < rg_end) an[u][rg][pl] = lda_(pl, rg, k + 32 * U + u * 32);
-#pragma unroll
-        for (int j = 0; j < NC; ++j) wn[u][j] = ldw(j, k + 32 * U + u * 32);
-      }
-    }
+  auto multiply = [&](int k) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
 #pragma unroll
@@ -494,20 +491,49 @@ __global__ __launch_bounds__(KS * 64) void k_skinny(GemmArgs ga, SeqTable st) {
         }
       }
     }
-    if (more) {
+  };
+  // Weight batches travel one ahead of the products.  The last batch is
+  // multiplied after the loop, so every trip issues the next batch
+  // unconditionally and the compiler waits only for the current batch before
+  // multiplying it; with the next batch's loads in a branch it waited for
+  // both (16-row pass: 0.680 -> 0.671 ms, the same box).
+  int k = kb;
+  for (; k + 32 * U < ke; k += 32 * U) {
+    bf16x8 wn[U][NC], an[APF ? U : 1][RG][NPL];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < U; ++u) {
+      if constexpr (APF)
 #pragma unroll
-        for (int j = 0; j < NC; ++j) wf[u][j] = wn[u][j];
-        if constexpr (APF)
+        for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
-          for (int rg = 0; rg < RG; ++rg)
+          for (int pl = 0; pl < NPL; ++pl)
+            if (rg < rg_end) an[u][rg][pl] = lda_(pl, rg, k + 32 * U + u * 32);
 #pragma unroll
-            for (int pl = 0; pl < NPL; ++pl) af[u][rg][pl] = an[u][rg][pl];
-      }
+      for (int j = 0; j < NC; ++j) wn[u][j] = ldw(j, k + 32 * U + u * 32);
+    }
+    multiply(k);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int j = 0; j < NC; ++j) wf[u][j] = wn[u][j];
+      if constexpr (APF)
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+          for (int pl = 0; pl < NPL; ++pl) af[u][rg][pl] = an[u][rg][pl];
     }
   }
+  multiply(k);
 
+  __shared__ float rnorm[RG * 16];
+  if (norm) {
+#pragma unroll
+    for (int j = 0; j < NRW; ++j) {
+      const int row = ks + KS * j;
+      const float t = sum_wave((sqv[j][0] + sqv[j][1]) + (sqv[j][2] + sqv[j][3]));
+      if (lane == 0 && row < RG * 16) rnorm[row] = 1.0f / sqrtf(t / (float)ga.ep.norm_n + ga.ep.eps);
+    }
+  }
   __shared__ f32x4 red[KS][RG * NC][64];
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg)
@@ -522,9 +548,114 @@ __global__ __launch_bounds__(KS * 64) void k_skinny(GemmArgs ga, SeqTable st) {
       f32x4 s = red[0][it][lane];
 #pragma unroll
       for (int q = 1; q < KS; ++q) s += red[q][it][lane];
+      if (norm) {
+        const int r0 = (it / NC) * 16 + 4 * g;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[i] *= rnorm[r0 + i];
+      }
       epilogue<EPI>(ga.ep, st, tile0 + it % NC, (it / NC) * 16, s, lane, kc);
     }
   }
+}
+
+// Workgroup (x, y) takes NC column tiles from tile x NC and K chunk y.
+template <int EPI, int MAP, int NC, int RG, bool SPLIT, int KS = kSkinnyWaves, bool PK = false>
+__global__ __launch_bounds__(KS * 64) void k_skinny(GemmArgs ga, SeqTable st) {
+  skinny_body<EPI, MAP, NC, RG, SPLIT, KS, PK>(ga, st, blockIdx.x * NC, blockIdx.y, gridDim.y);
+}
+
+// ---------------------------------------------------------------------------
+// Whole-K few-row GEMM (16 rows): one 16-column tile per workgroup, its K over
+// kWholeKWaves waves of SPW 32-k steps each and not split across workgroups,
+// so the epilogue sees finished sums.  Every weight and A fragment a wave
+// needs is loaded before its first product (a scheduling barrier keeps the
+// compiler from interleaving loads and products), so each CU has its whole
+// share of the weights in flight at once; the waves' tiles then meet in LDS
+// in a fixed order.  Weights come as tile-major packed blocks (the tile's
+// K / 32 blocks of 1 KB are contiguous) or as row-major rows: the same sums
+// in the same order.  The epilogue is EPI_RESID: the residual add and the
+// first half of the next RMSNorm (gain * x and the per-tile sums of squares;
+// the following SwiGLU GEMM applies the per-row factor), which takes the
+// place of a separate reduce-and-normalise kernel after a split-K GEMM.
+// ---------------------------------------------------------------------------
+constexpr int kWholeKWaves = 8;
+
+template <int SPW, bool PK>
+__global__ __launch_bounds__(kWholeKWaves * 64) void k_whole_k(GemmArgs ga) {
+  constexpr int W = kWholeKWaves;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, c = lane & 15, g = lane >> 4;
+  const int tile = blockIdx.x, col = tile * 16 + c, s0 = wv * SPW;
+  const EpiParams& ep = ga.ep;
+  // wave 0's epilogue operands (x of its four rows at this column, the gain)
+  // are loaded first, so they have landed before the products
+  float xv[4] = {0.f, 0.f, 0.f, 0.f}, gv = 0.f;
+  if (wv == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (4 * g + i < ep.M) xv[i] = ep.x[(size_t)(4 * g + i) * ep.ldo + col];
+    gv = bf16_val(ep.gain[col]);
+  }
+  const u16* wp = PK ? ga.wpack + ((size_t)tile * (ga.K / 32) * 64 + lane) * 8 + (size_t)s0 * 512
+                     : ga.w.w0 + (size_t)col * ga.K + g * 8 + s0 * 32;
+  const int row = min(c, ga.a_rows - 1);
+  const u16* ah = ga.a_hi + (size_t)row * ga.lda + g * 8 + s0 * 32;
+  const u16* al = ga.a_lo + (size_t)row * ga.lda + g * 8 + s0 * 32;
+  bf16x8 wf[SPW], fh[SPW], fl[SPW];
+#pragma unroll
+  for (int s = 0; s < SPW; ++s) {
+    wf[s] = PK ? ld_frag_stream(wp + s * 512) : ld_frag(wp + s * 32);
+    fh[s] = ld_frag(ah + s * 32);
+    fl[s] = ld_frag(al + s * 32);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < SPW; ++s) {
+    acc = mfma(fh[s], wf[s], acc);
+    acc = mfma(fl[s], wf[s], acc);
+  }
+  __shared__ f32x4 red[W][64];
+  red[wv][lane] = acc;
+  __syncthreads();
+  if (wv != 0) return;
+  f32x4 v = red[0][lane];
+#pragma unroll
+  for (int q = 1; q < W; ++q) v += red[q][lane];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * g + i;
+    float xn = 0.f;
+    if (r < ep.M) {
+      xn = xv[i] + v[i];
+      ep.x[(size_t)r * ep.ldo + col] = xn;
+      u16 h, l;
+      split_pair(gv * xn, h, l);
+      ep.out_hi[(size_t)r * ep.ldh + col] = h;
+      ep.out_lo[(size_t)r * ep.ldh + col] = l;
+    }
+    const float sq = sum_row16(xn * xn);
+    if (c == 0) ep.ssq[(size_t)r * ga.n_tiles + tile] = sq;
+  }
+}
+
+bool gemm_whole_k_fits(int n_tiles, int K, int Mp) {
+  if (Mp != 16 || n_tiles < 1 || n_tiles > 256 || n_tiles % 4 || K % (32 * kWholeKWaves)) return false;
+  const int spw = K / (32 * kWholeKWaves);
+  return spw == 1 || spw == 2 || spw == 4 || spw == 8 || spw == 16;
+}
+
+template <bool PK>
+static hipError_t whole_k_launch(const GemmArgs& g, hipStream_t s) {
+  const dim3 grid(g.n_tiles), blk(kWholeKWaves * 64);
+  switch (g.K / (32 * kWholeKWaves)) {
+    case 1: hipLaunchKernelGGL((k_whole_k<1, PK>), grid, blk, 0, s, g); break;
+    case 2: hipLaunchKernelGGL((k_whole_k<2, PK>), grid, blk, 0, s, g); break;
+    case 4: hipLaunchKernelGGL((k_whole_k<4, PK>), grid, blk, 0, s, g); break;
+    case 8: hipLaunchKernelGGL((k_whole_k<8, PK>), grid, blk, 0, s, g); break;
+    case 16: hipLaunchKernelGGL((k_whole_k<16, PK>), grid, blk, 0, s, g); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -2197,7 +2328,15 @@ static hipError_t gemm_dispatch(const GemmArgs& g, const SeqTable& st, int Mp, h
 
 hipError_t launch_gemm(const GemmArgs& g, const SeqTable& st, int Mp, hipStream_t s) {
   const bool split = g.a_lo != nullptr;
+  // the norm factor of a SwiGLU launch (16 rows only) is read with one
+  // 16-byte load per lane
+  if (g.epi == EPI_SWIGLU && g.ep.ssq_in && (Mp > 16 || g.ep.n_ssq > 256 || g.ep.n_ssq % 4 || g.ep.norm_n < 1))
+    return hipErrorInvalidValue;
   switch (g.epi) {
+    case EPI_RESID:
+      if (!gemm_whole_k_fits(g.n_tiles, g.K, Mp) || g.map != MAP_PLAIN || !split || (g.wpack && g.pk_kmajor))
+        return hipErrorInvalidValue;
+      return g.wpack ? whole_k_launch<true>(g, s) : whole_k_launch<false>(g, s);
     case EPI_SWIGLU:
       return gemm_dispatch<EPI_SWIGLU, MAP_SWIGLU, true>(g, st, Mp, s);
     case EPI_ARGMAX:  // greedy drafts, or sampled ones (the Gumbel code only where it runs)
