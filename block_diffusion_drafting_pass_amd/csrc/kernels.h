@@ -176,7 +176,7 @@ struct AttnGroups {
 };
 // Query heads one attention wave serves from each K / V fragment it reads
 // (grouped launches), and the most blocks one group may hold at this shape
-// (16 waves per workgroup).
+// (16 waves per workgroup, 8 when each wave serves two heads).
 int attention_heads_per_wave(int n_q, int n_kv, bool grouped);
 int attention_group_size(int n_q, int n_kv, int block);
 // Block queries of sequence b (rows row_start[b] ..) against pos_base[b]

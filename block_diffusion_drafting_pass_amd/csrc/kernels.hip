@@ -2483,8 +2483,11 @@ int attention_heads_per_wave(int n_q, int n_kv, bool grouped) {
 }
 
 int attention_group_size(int n_q, int n_kv, int block) {
-  const int upb = (n_q / n_kv / attention_heads_per_wave(n_q, n_kv, true)) * ((block + 15) / 16);
-  const int gs = 16 / (upb > 0 ? upb : 1);
+  const int hpw = attention_heads_per_wave(n_q, n_kv, true);
+  const int upb = (n_q / n_kv / hpw) * ((block + 15) / 16);
+  // waves serving two heads each hold twice the fragments: at most eight of
+  // them per workgroup (sixteen leave 128 registers a wave and spill)
+  const int gs = (hpw == 2 ? 8 : 16) / (upb > 0 ? upb : 1);
   return gs < 1 ? 1 : (gs > kAttnGroup ? kAttnGroup : gs);
 }
 
