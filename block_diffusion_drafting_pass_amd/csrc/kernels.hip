@@ -2199,10 +2199,13 @@ GemmPlan gemm_plan(int n_tiles, int K, int Mp, bool may_split) {
     // K chunks for about 256 workgroups of 128-row tiles (128 of 256-row
     // tiles): fewer partial sums to write and re-read than with 512 (draft
     // pass of eight ragged block-32 sequences 1.647 -> 1.582 ms, of 32
-    // sequences 3.767 -> 3.716-3.748 ms)
+    // sequences 3.767 -> 3.716-3.748 ms).  Long K ranges, where the partial
+    // sums weigh little against the products, keep about 512 (the fusion
+    // map, K 20480, at 1024 rows: 256 workgroups made the ingest of 1024
+    // positions 0.39 -> 0.48 ms)
     if (may_split) {
-      const int wgs = (Mp / 128) * ((n_tiles + p.nc - 1) / p.nc);
-      while (p.kc * 2 <= kMaxKc && p.kc * 2 * wgs <= 256 && K % (p.kc * 2 * 32) == 0) p.kc *= 2;
+      const int wgs = (Mp / 128) * ((n_tiles + p.nc - 1) / p.nc), cap = K >= 16384 ? 512 : 256;
+      while (p.kc * 2 <= kMaxKc && p.kc * 2 * wgs <= cap && K % (p.kc * 2 * 32) == 0) p.kc *= 2;
     }
   }
   return p;
