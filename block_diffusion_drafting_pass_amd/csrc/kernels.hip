@@ -2368,22 +2368,24 @@ int attention_max_splits(int pairs) {
 
 // Key splits of one call (at most max_splits), evened out so that no split of
 // the longest unit (max_tiles tiles) is left empty.  One-block units: each
-// split of the longest unit takes about unit_tiles / 256 tiles, the call's
+// split of the longest unit takes about unit_tiles / 192 tiles, the call's
 // whole tile work (unit_tiles: tiles summed over units and kv heads) spread
-// over the CUs; that keeps ragged batches from waiting on their longest
-// sequence (block 32, eight contexts of 512..4096: 7 splits, 1.4% faster per
-// step than 4).  Grouped units (workgroups of up to sixteen waves): about
-// 256 workgroups over the pairs.  Longer splits beat more of them once the
-// work fills the chip (8192 keys: 26 splits of five tiles 23.7 us per layer
-// against 43 of three 25.1 us; the training forward 1% faster per step with
-// one split than with two).
+// over three quarters of the CUs; that keeps ragged batches from waiting on
+// their longest sequence (block 32, eight contexts of 512..4096: 7 splits,
+// 1.4% faster per step than 4).  Grouped units (workgroups of up to sixteen
+// waves): about 256 workgroups over the pairs.  Longer splits beat more of
+// them once the work fills the chip: 8192 keys, 26 splits of five tiles 23.7
+// us per layer against 43 of three 25.1 us, and 22 of six (the 192 rule)
+// against 26 of five, draft pass 0.733 -> 0.726 ms; 32 of four, 20.1 against
+// 18.2 us per layer; the training forward 1% faster per step with one split
+// than with two.
 int attention_splits(int pairs, int max_tiles, int64_t unit_tiles, bool grouped, int max_splits) {
   if (max_tiles < 1) return 1;
   int s;
   if (grouped) {
     s = (256 + pairs - 1) / pairs;
   } else {
-    const int64_t tps = std::max<int64_t>(1, (unit_tiles + 255) / 256);
+    const int64_t tps = std::max<int64_t>(1, (unit_tiles + 191) / 192);
     s = (int)((max_tiles + tps - 1) / tps);
   }
   s = std::max(1, std::min({s, max_splits, kMaxSplits, max_tiles}));
