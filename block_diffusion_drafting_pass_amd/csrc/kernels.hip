@@ -725,7 +725,8 @@ __device__ __forceinline__ int big_swz(int row, int ch) {
 }
 
 template <int EPI, int MAP, bool SPLIT, int BM, int WM, int WN, int S, int BN = kBigBN>
-__global__ __launch_bounds__(WM * WN * 64) void k_gemm_dl(GemmArgs ga, SeqTable st, int mt, int kcn) {
+__global__ __launch_bounds__(WM * WN * 64) void k_gemm_dl(GemmArgs ga, SeqTable st, int mt, int kcn, int nt0,
+                                                          int nt_end, int slot0) {
   constexpr int BK = 32, NP = SPLIT ? 2 : 1, NW = WM * WN, CPR = BK / 8;
   constexpr int TM = BM / WM / 16, TN = BN / WN / 16;
   static_assert(BN % (WN * 16) == 0, "whole MFMA tiles per wave");
@@ -745,8 +746,8 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_dl(GemmArgs ga, SeqTable 
 
   const int nwg = gridDim.x;
   const int bid = (nwg & 7) == 0 ? (int)(blockIdx.x & 7) * (nwg >> 3) + (int)(blockIdx.x >> 3) : (int)blockIdx.x;
-  const int m_t = bid % mt, kc = (bid / mt) % kcn, n_t = bid / (mt * kcn);
-  if (n_t * (BN / 16) >= ga.n_tiles) return;  // grid padding to whole rounds of eight XCDs
+  const int m_t = bid % mt, kc = (bid / mt) % kcn, n_t = nt0 + bid / (mt * kcn);
+  if (n_t >= nt_end) return;  // grid padding to whole rounds of eight XCDs
   if constexpr (AMAX) {
     for (int i = threadIdx.x; i < BM; i += WM * WN * 64) rk[i] = 0;
     __syncthreads();
@@ -844,8 +845,9 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_dl(GemmArgs ga, SeqTable 
       }
     }
     __syncthreads();
+    const size_t slot = (size_t)(slot0 + n_t - nt0);  // this column tile's partial keys
     for (int i = threadIdx.x; i < BM; i += WM * WN * 64)
-      if (row0 + i < ga.ep.Mp) ga.ep.amax_part[(size_t)n_t * ga.ep.Mp + row0 + i] = rk[i];
+      if (row0 + i < ga.ep.Mp) ga.ep.amax_part[slot * ga.ep.Mp + row0 + i] = rk[i];
   } else {
 #pragma unroll
     for (int ct = 0; ct < TN; ++ct) {
@@ -2237,13 +2239,19 @@ static hipError_t skinny_nc(const GemmArgs& g, const SeqTable& st, const GemmPla
   return hipGetLastError();
 }
 
+// Column tiles [nt0, nt0 + nt) of width BN (nt < 0: all from nt0 on); an
+// argmax epilogue stores tile nt0 + i's partial keys in slot slot0 + i
+// (slot0 < 0: slot nt0 + i).
 template <int EPI, int MAP, bool SPLIT, int BM, int WM, int WN, int S, int BN = kBigBN>
-static hipError_t dl_launch(const GemmArgs& g, const SeqTable& st, int Mp, const GemmPlan& p, hipStream_t s) {
+static hipError_t dl_launch(const GemmArgs& g, const SeqTable& st, int Mp, const GemmPlan& p, hipStream_t s,
+                            int nt0 = 0, int nt = -1, int slot0 = -1) {
   if (Mp % BM || g.K % (p.kc * 32) || g.a_rows < 1) return hipErrorInvalidValue;
-  const int mt = Mp / BM, nt = (g.n_tiles + BN / 16 - 1) / (BN / 16);
+  const int mt = Mp / BM, nt_all = (g.n_tiles + BN / 16 - 1) / (BN / 16);
+  if (nt < 0) nt = nt_all - nt0;
+  if (nt0 < 0 || nt < 1 || nt0 + nt > nt_all) return hipErrorInvalidValue;
   const int wgs = mt * p.kc * nt, padded = (wgs + 7) / 8 * 8;
   hipLaunchKernelGGL((k_gemm_dl<EPI, MAP, SPLIT, BM, WM, WN, S, BN>), dim3(padded), dim3(WM * WN * 64), 0, s, g,
-                     st, mt, p.kc);
+                     st, mt, p.kc, nt0, nt0 + nt, slot0 < 0 ? nt0 : slot0);
   return hipGetLastError();
 }
 
@@ -2264,6 +2272,25 @@ static int lm_head_bn(int n_tiles, int Mp) {
   const long mt = Mp / 256, t256 = (n_tiles + 15) / 16, t240 = (n_tiles + 14) / 15;
   if (Mp % 256 || mt * t256 < 256) return kBigBN;  // not a 256-row-tile launch
   return (mt * t240 + 255) / 256 * 201 < (mt * t256 + 255) / 256 * 210 ? 240 : kBigBN;
+}
+
+// A last round of 240-column tiles that is at most half full: the columns
+// past the whole rounds (*nm tiles of 240) go to a second launch of 128 x 256
+// tiles with four stages (eight waves of 64 x 64, one workgroup per CU), one
+// round of which takes about two thirds of a round of 256 x 240 tiles.  It
+// needs the split on a 256-column boundary.  Returns the second launch's
+// column tiles (0: one launch).
+static int lm_head_tail(int n_tiles, int Mp, int* nm) {
+  *nm = 0;
+  if (lm_head_bn(n_tiles, Mp) != 240) return 0;
+  const int mt = Mp / 256, t240 = (n_tiles + 14) / 15, wgs = mt * t240, full = wgs / 256 * 256;
+  if (full == wgs || full % mt) return 0;
+  const int main_tiles = full / mt;
+  if (main_tiles % 16) return 0;  // 240 * main_tiles not a multiple of 256
+  const int tail = (n_tiles - main_tiles * 15 + 15) / 16;
+  if (2 * mt * tail > 256) return 0;
+  *nm = main_tiles;
+  return tail;
 }
 
 template <int EPI, int MAP, bool SPLIT>
@@ -2304,7 +2331,17 @@ static hipError_t dl_dispatch(const GemmArgs& g, const SeqTable& st, int Mp, con
   const int nt = (g.n_tiles + p.nc - 1) / p.nc;
   if (Mp % 256 == 0 && (Mp / 256) * nt * p.kc >= 256) {
     if constexpr (EPI == EPI_ARGMAX || EPI == EPI_SAMPLE)
-      if (lm_head_bn(g.n_tiles, Mp) == 240) return dl_launch<EPI, MAP, SPLIT, 256, 4, 3, 3, 240>(g, st, Mp, p, s);
+      if (lm_head_bn(g.n_tiles, Mp) == 240) {
+        int nm;
+        if (const int tail = lm_head_tail(g.n_tiles, Mp, &nm)) {
+          // partial keys: slots 0 .. nm-1 for the 240-column tiles, then
+          // one per 256-column tile of the tail
+          const hipError_t e = dl_launch<EPI, MAP, SPLIT, 256, 4, 3, 3, 240>(g, st, Mp, p, s, 0, nm);
+          if (e != hipSuccess) return e;
+          return dl_launch<EPI, MAP, SPLIT, 128, 2, 4, 4>(g, st, Mp, p, s, nm * 15 / 16, tail, nm);
+        }
+        return dl_launch<EPI, MAP, SPLIT, 256, 4, 3, 3, 240>(g, st, Mp, p, s);
+      }
     return dl_launch<EPI, MAP, SPLIT, 256, 4, 4, 3>(g, st, Mp, p, s);
   }
   if ((Mp / 128) * nt * p.kc >= 256) return dl_launch<EPI, MAP, SPLIT, 128, 2, 4, 2>(g, st, Mp, p, s);
@@ -2546,6 +2583,8 @@ hipError_t launch_pack_weights(const GemmArgs& g, u16* dst, hipStream_t s) {
 
 int argmax_parts(int n_tiles, int Mp) {
   if (Mp <= 32) return n_tiles / gemm_plan(n_tiles, 0, Mp, false).nc;
+  int nm;
+  if (const int tail = lm_head_tail(n_tiles, Mp, &nm)) return nm + tail;
   const int tw = lm_head_bn(n_tiles, Mp) / 16;  // MFMA tiles per workgroup column tile
   return (n_tiles + tw - 1) / tw;
 }
