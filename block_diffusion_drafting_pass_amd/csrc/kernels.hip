@@ -2306,7 +2306,8 @@ static hipError_t dl_dispatch(const GemmArgs& g, const SeqTable& st, int Mp, con
     // The K chunks stay the plan's, which sized the partial buffers; the
     // column tiles of any width sum their K range in the same order, so
     // every shape gives the same bits.  The argmax epilogues take their
-    // width from lm_head_bn, which also counts their per-workgroup partials.
+    // width from lm_head_bn and lm_head_tail, which argmax_parts also uses
+    // to count their per-workgroup partials.
     struct Shape { int bm, bn, per_cu, round_us; };
     const Shape shapes[6] = {{256, 256, 1, 210}, {256, 192, 1, 177}, {128, 256, 2, 236},
                              {128, 192, 2, 195}, {128, 256, 1, 130}, {128, 192, 1, 119}};
