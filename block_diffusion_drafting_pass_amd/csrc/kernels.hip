@@ -564,6 +564,21 @@ __global__ __launch_bounds__(KS * 64) void k_skinny(GemmArgs ga, SeqTable st) {
   skinny_body<EPI, MAP, NC, RG, SPLIT, KS, PK>(ga, st, blockIdx.x * NC, blockIdx.y, gridDim.y);
 }
 
+// q|k|v over the rows of a fused step (the block's rows, then appended
+// context rows that need only K / V): the first q_groups column groups (the
+// q columns) take the one-row-group body, which keeps A one batch ahead of
+// the products, and the k|v groups take both row groups.  Rows 0..15 get the
+// same products in the same order either way (16-row block + 16 appended
+// rows: 14.3 -> about 12.8 us per layer, draft step 0.710 -> 0.702 ms, same
+// box).
+template <int NC, bool SPLIT, int KS, bool PK>
+__global__ __launch_bounds__(KS * 64) void k_skinny_qkv_rows(GemmArgs ga, SeqTable st, int q_groups) {
+  if ((int)blockIdx.x < q_groups)
+    skinny_body<EPI_PARTIAL, MAP_QKV, NC, 1, SPLIT, KS, PK>(ga, st, blockIdx.x * NC, blockIdx.y, gridDim.y);
+  else
+    skinny_body<EPI_PARTIAL, MAP_QKV, NC, 2, SPLIT, KS, PK>(ga, st, blockIdx.x * NC, blockIdx.y, gridDim.y);
+}
+
 // ---------------------------------------------------------------------------
 // Whole-K few-row GEMM (16 rows): one 16-column tile per workgroup, its K over
 // kWholeKWaves waves of SPW 32-k steps each and not split across workgroups,
@@ -2216,6 +2231,13 @@ GemmPlan gemm_plan(int n_tiles, int K, int Mp, bool may_split) {
 template <int EPI, int MAP, bool SPLIT, int RG, bool PK>
 static hipError_t skinny_nc(const GemmArgs& g, const SeqTable& st, const GemmPlan& p, hipStream_t s) {
   const dim3 grid(g.n_tiles / p.nc, p.kc), blk(p.ks * 64);
+  if constexpr (MAP == MAP_QKV && RG == 2 && EPI == EPI_PARTIAL) {
+    const int qt = g.ep.n_q * g.ep.head_dim / 16;  // q column tiles, a whole number of groups
+    if (g.q_rows > 0 && g.q_rows <= 16 && p.ks == kSkinnyWaves && p.nc == 4 && qt % 4 == 0 && qt < g.n_tiles) {
+      hipLaunchKernelGGL((k_skinny_qkv_rows<4, SPLIT, kSkinnyWaves, PK>), grid, blk, 0, s, g, st, qt / 4);
+      return hipGetLastError();
+    }
+  }
   if (p.ks == 8) {
     if (p.nc == 8) {
       hipLaunchKernelGGL((k_skinny<EPI, MAP, 8, RG, SPLIT, 8, PK>), grid, blk, 0, s, g, st);
