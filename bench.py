@@ -347,6 +347,16 @@ def _decode_rows(wl, stage: str) -> int:
     return n * s.block
 
 
+def lm_head_executed_flops(spec, n_blocks: int) -> float:
+    """bf16 matrix-core flops one LM-head launch executes: every padded block
+    row (anchor rows and row padding included: 16-row groups up to 32 rows,
+    128-row groups above) against every vocabulary column, and two bf16
+    products per multiply-add (the activations are hi/lo pairs)."""
+    m = n_blocks * spec.block
+    mp = (m + 15) // 16 * 16 if m <= 32 else (m + 127) // 128 * 128
+    return 2.0 * 2.0 * mp * spec.vocab * spec.hidden
+
+
 def stage_total(wl, stage: str):
     """Algorithmic (bytes, flops) of every launch of `stage` in one step."""
     s = wl.spec
@@ -763,6 +773,14 @@ def main(argv=None) -> int:
     roof.update({"traffic": measured_traffic(spec.name, args.probe), "kernel": args.probe,
                  "avg_launch_ms": round(avg_ms, 4), "launches_timed": probe_n, "alg_bytes_per_launch": pb,
                  "alg_flops_per_launch": pf})
+    if args.probe == "lm_head":
+        # what the matrix cores execute: with hi/lo activations and padded rows
+        # a launch of a few hundred rows sits above the ridge though its
+        # algorithmic intensity is below it
+        ef = lm_head_executed_flops(spec, n_units)
+        roof["executed"] = {"flops_per_launch": ef, "intensity": round(ef / pb, 1),
+                            "bound": "mfma" if ef / pb >= ridge else "hbm",
+                            "mfma_frac": round(ef / (avg_ms * 1e-3) / (MFMA_BF16_PEAK_TFS * 1e12), 4)}
 
     pass_target = None
     if phase_d is not None:

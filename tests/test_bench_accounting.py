@@ -55,3 +55,20 @@ def test_lm_head_bytes():
     by, fl = bench.stage_work(I.spec("q8b_ctx1024"), "lm_head", 15)
     assert by == 151936 * 4096 * 2
     assert fl == 2 * 15 * 4096 * 151936
+
+
+@pytest.mark.parametrize("name,rows,bound", [
+    ("q8b_ctx1024", 16, "hbm"),          # 16 rows: 64 flop per weight byte executed
+    ("q8b_l3_b32_ragged", 256, "mfma"),  # 8 blocks of 32: 512 flop/B, above the ridge
+    ("q8b_conc32", 512, "mfma"),
+])
+def test_lm_head_executed_intensity(name, rows, bound):
+    # executed bf16 flops of one LM-head launch: every padded row, two bf16
+    # products per multiply-add (hi/lo activations); the ridge of 2.5 PFLOP/s
+    # over 8 TB/s is about 315 flop/B
+    s = I.spec(name)
+    ef = bench.lm_head_executed_flops(s, s.n_seqs)
+    assert ef == 4 * rows * s.vocab * s.hidden
+    weight_bytes = s.vocab * s.hidden * 2
+    ridge = bench.MFMA_BF16_PEAK_TFS * 1e12 / (bench.HBM_PEAK_GBS * 1e9)
+    assert ("mfma" if ef / weight_bytes >= ridge else "hbm") == bound
