@@ -164,6 +164,7 @@ WsLayout ws_layout(const dflash_config* c, int n_seqs, int block, int64_t max_ne
     size_t pb = part_bytes(nqkv / 16, (int)H, (int)Mq, nqkv);
     pb = std::max(pb, part_bytes((int)H / 16, (int)QD, W.Mp, (int)H));
     pb = std::max(pb, part_bytes((int)H / 16, (int)I, W.Mp, (int)H));
+    pb = std::max(pb, (size_t)swiglu_kc((int)I / 8, (int)H, W.Mp) * W.Mp * 2 * I * sizeof(float));
     if (W.Mp <= 32)
       for (int r = 16; r <= 32; r += 16)  // fusion of the appended rows on a fused step
         pb = std::max(pb, part_bytes((int)H / 16, fw, r, (int)H));
@@ -892,6 +893,7 @@ int draft_impl(const dflash_model* model, const dflash_ctx* ctx, const Blocks& b
     g.ep.out_hi = b_hi;
     g.ep.out_lo = b_lo;
     g.ep.ldh = I;
+    g.ep.out_f32 = part;  // the K-chunk partials of a split many-row projection (swiglu_kc)
     if (whole_o) {
       g.ep.ssq_in = part;
       g.ep.n_ssq = H / 16;

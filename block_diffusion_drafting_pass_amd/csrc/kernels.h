@@ -122,6 +122,10 @@ constexpr int kMaxKc = 16;       // most K chunks a GEMM is split into
 inline int rows_pad(int m) { return m <= 32 ? (m + 15) / 16 * 16 : (m + 127) / 128 * 128; }
 
 hipError_t launch_gemm(const GemmArgs& g, const SeqTable& st, int Mp, hipStream_t s);
+// K chunks (1 or 2) of a many-row SwiGLU projection of n_tiles 16-column
+// tiles; with 2, launch_gemm writes partial sums [2][Mp][16 n_tiles] fp32 to
+// ep.out_f32 (which must then hold them) before the SwiGLU kernel.
+int swiglu_kc(int n_tiles, int K, int Mp);
 // Whether the whole-K few-row GEMM (EPI_RESID) takes this shape: 16 padded
 // rows, K a multiple of 256 up to 4096, and at most 256 column tiles (the
 // SwiGLU launch that follows reads a row's tile sums with one load per lane).
