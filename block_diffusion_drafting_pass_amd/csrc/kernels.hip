@@ -390,7 +390,8 @@ __device__ __forceinline__ void argmax_tail(const EpiParams& ep, int tile0, f32x
 // ---------------------------------------------------------------------------
 // Skinny weight-streaming GEMM: Y[M<=32][N] = A[M][K] W^T, W [N][K] bf16.
 // Workgroup (x, y) owns NC 16-column tiles and K chunk y of gridDim.y; its
-// KS waves (four; eight for narrow split-K outputs) split the chunk.  PK:
+// KS waves (four; eight for narrow split-K outputs and the SwiGLU
+// projection) split the chunk.  PK:
 // the weights come packed (launch_pack_weights), so every weight load reads
 // 1 KB contiguous per wave, with the non-temporal hint (read once); in the
 // k-major order the NC tiles of one k-step are adjacent too, and workgroups
@@ -679,10 +680,12 @@ static hipError_t whole_k_launch(const GemmArgs& g, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
-// Many-row GEMM (M a multiple of 128): BM x 256 output tile per workgroup of
-// BM / 64 x WN waves, each 64 rows x 256 / WN columns (4 x 16 / WN MFMA tiles), over
-// K chunk kc of gridDim / (mt nt) chunks.  K runs in 32-wide slabs; each
-// slab (the A planes' BM rows and the 256 weight rows) is copied by
+// Many-row GEMM (M a multiple of 128): BM x BN output tile (BN 256, 240 or
+// 192) per workgroup of BM / 64 x WN waves, each 64 rows x BN / WN columns,
+// over K chunk kc of the launch's K chunks; a launch covers the column tiles
+// [nt0, nt_end) of width BN (all of them, or one part of an LM head split
+// into two launches).  K runs in 32-wide slabs; each
+// slab (the A planes' BM rows and the BN weight rows) is copied by
 // global_load_lds (16 bytes per lane, 1 KB per wave instruction) straight
 // into one of S stage arrays in LDS, so S - 1 slabs are in flight without
 // holding registers.  Lane l of a wave's j-th copy writes physical 16-byte
@@ -2509,7 +2512,10 @@ int attention_max_splits(int pairs) {
 // us per layer against 43 of three 25.1 us, and 22 of six (the 192 rule)
 // against 26 of five, draft pass 0.733 -> 0.726 ms; 32 of four, 20.1 against
 // 18.2 us per layer; the training forward 1% faster per step with one split
-// than with two.
+// than with two.  Every unit's splits are its own tiles evened out over the
+// split count: splits sized to the longest unit's share for every unit (a
+// shorter unit leaving its later splits empty) measured slower on the
+// ragged block-32 batch (1.600 against 1.663 ms at the same split count).
 int attention_splits(int pairs, int max_tiles, int64_t unit_tiles, bool grouped, int max_splits) {
   if (max_tiles < 1) return 1;
   int s;
